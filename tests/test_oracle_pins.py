@@ -1,0 +1,311 @@
+"""Pins for the fp64 CPU oracle, checked against things other than itself.
+
+* hand-derived closed forms (tests/golden/hand_cases.json): layout reading
+  (nibble order, zero-point order, scale index, row stride), the +8 default,
+  the fp32 -> fp16 -> bf16 double rounding with ties in both directions,
+  subnormals, overflow, bf16 activations rounded to fp16 first;
+* exhaustive checks of the three rounding routines against numpy and torch;
+* an exact integer recomputation of every sum, rounded to fp16 by an
+  integer routine of its own, on random inputs of several shapes;
+* structured brute force on tiny inputs with a per-block closed form;
+* invariants: zp = q gives 0, scales x2 gives y x2, NULL zp == zp 8, column
+  permutation, row independence, sign symmetry, column sampling.
+
+A plausible mistake anywhere in the oracle (a swapped nibble, a wrong block
+or column index, a missing zero-point subtract, a wrong rounding mode or a
+flushed subnormal) fails at least one test here.
+"""
+import numpy as np
+import pytest
+import torch
+
+from tests.hand_cases import build_case, load_cases
+
+CASES = load_cases()
+
+
+# ---------------------------------------------------------------- hand cases
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_hand_case(oracle_mod, case):
+    c = build_case(case)
+    r = oracle_mod.matmul_nbits(c["A"], c["a_is_bf16"], c["B"], c["scales"],
+                                c["zp"], c["m"], c["K"], c["N"])
+    assert np.array_equal(r["f64"], c["value"]), (r["f64"], c["value"])
+    assert np.array_equal(r["f16"], c["f16"]), [hex(x) for x in r["f16"].ravel()]
+    assert np.array_equal(r["bf16"], c["bf16"]), [hex(x) for x in r["bf16"].ravel()]
+
+
+# ------------------------------------------------------ rounding, exhaustive
+def _torch_f32_to_bf16_bits(x32):
+    t = torch.from_numpy(np.ascontiguousarray(x32, np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_f16_to_bf16_exhaustive(oracle_mod):
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.f16_to_bf16(h)
+    x32 = h.view(np.float16).astype(np.float32)      # exact widening
+    ref = _torch_f32_to_bf16_bits(x32)               # torch RNE
+    nan = np.isnan(x32)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # NaN stays a quiet NaN with its sign
+    g = got[nan]
+    assert np.all((g & 0x7F80) == 0x7F80) and np.all((g & 0x0040) != 0)
+    assert np.array_equal(g >> 15, (h[nan] >> 15))
+
+
+def test_bf16_to_f16_exhaustive(oracle_mod):
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.bf16_to_f16(b)
+    x32 = (b.astype(np.uint32) << 16).view(np.float32)
+    with np.errstate(over="ignore"):
+        ref = x32.astype(np.float16).view(np.uint16)  # numpy RNE, gradual underflow
+    nan = np.isnan(x32)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.all(np.isnan(got[nan].view(np.float16)))
+
+
+def _all_f16_finite():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = h.view(np.float16)
+    return np.sort(np.unique(v[np.isfinite(v)].astype(np.float64)))
+
+
+def test_f64_to_f16_random_and_ties(oracle_mod):
+    rng = np.random.default_rng(12345)
+    n = 1_000_000
+    mag = np.exp2(rng.uniform(-30, 17.5, n))
+    x = mag * rng.choice([-1.0, 1.0], n)
+    vals = _all_f16_finite()
+    mids = (vals[:-1] + vals[1:]) / 2                 # every tie, exact in fp64
+    nudge = np.ldexp(np.abs(mids), -40)
+    extra = np.concatenate([vals, mids, mids + nudge, mids - nudge,
+                            [65504.0, 65519.99, 65520.0, -65520.0, 1e300, -1e300,
+                             2.0 ** -25, 2.0 ** -25 * (1 + 2 ** -40), 0.0, -0.0]])
+    x = np.concatenate([x, extra])
+    got = oracle_mod.f64_to_f16(x)
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).view(np.uint16)   # numpy rounds fp64 directly
+    assert np.array_equal(got, ref)
+    # the fp64-direct rounding differs from a detour through fp32 here
+    assert oracle_mod.f64_to_f16(1 + 2.0 ** -11 + 2.0 ** -40)[0] == 0x3C01
+
+
+# ------------------------------------------------ exact integer recomputation
+def _exact_f16_bits(S, shift):
+    """Round the exact rational S * 2^-shift (Python int S) to fp16 bits, RNE,
+    with integer arithmetic only."""
+    if S == 0:
+        return 0
+    sign = 0x8000 if S < 0 else 0
+    X = -S if S < 0 else S
+    e = X.bit_length() - 1 - shift            # floor(log2 |value|)
+    e_eff = max(e, -14)
+    sh = (e_eff - 10) + shift                  # quantum 2^(e_eff-10) in units of 2^-shift
+    if sh > 0:
+        n, rem = divmod(X, 1 << sh)
+        half = 1 << (sh - 1)
+        if rem > half or (rem == half and (n & 1)):
+            n += 1
+    else:
+        n = X << (-sh)
+    bits = ((e_eff + 15) << 10) + n - 1024
+    if bits >= 0x7C00:
+        return sign | 0x7C00
+    return sign | bits
+
+
+def test_exact_rounding_helper_matches_numpy():
+    rng = np.random.default_rng(7)
+    x = np.ldexp(rng.integers(-(1 << 40), 1 << 40, 20000).astype(np.float64), -40)
+    x = x * np.exp2(rng.integers(-20, 16, x.size))
+    for v in x[:20000]:
+        m, e = np.frexp(v)
+        S = int(np.ldexp(m, 53))
+        assert _exact_f16_bits(S, 53 - int(e)) == np.float16(v).view(np.uint16)
+
+
+def _exact_sums(A_bits, a_is_bf16, B, scales, zp, m, K, N, oracle_mod):
+    """Exact sums as Python ints in units of 2^-48.  fp16 values are integer
+    multiples of 2^-24, so a*(q-z)*s is an integer multiple of 2^-48."""
+    nb = K // 32
+    if a_is_bf16:
+        # activations: bf16 -> fp16 by numpy (float32 widening then RNE)
+        a16 = (A_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float16)
+    else:
+        a16 = A_bits.view(np.float16)
+    a_int = (a16.astype(np.float64) * 2.0 ** 24).astype(np.int64)      # exact
+    s_int = (scales.view(np.float16).astype(np.float64) * 2.0 ** 24).astype(np.int64)
+    q = np.empty((N, K), np.int64)
+    q[:, 0::2] = B & 0xF
+    q[:, 1::2] = B >> 4
+    if zp is None:
+        z = np.full((N, nb), 8, np.int64)
+    else:
+        z = np.empty((N, 2 * zp.shape[1]), np.int64)
+        z[:, 0::2] = zp & 0xF
+        z[:, 1::2] = zp >> 4
+        z = z[:, :nb]
+    d = (q.reshape(N, nb, 32) - z[:, :, None])                       # q - z
+    inner = np.einsum("rbk,nbk->rnb", a_int.reshape(m, nb, 32), d)   # < 2^50
+    out = np.empty((m, N), dtype=object)
+    for r in range(m):
+        for n in range(N):
+            out[r, n] = sum(int(inner[r, n, b]) * int(s_int[n, b]) for b in range(nb))
+    return out
+
+
+@pytest.mark.parametrize("m,K,N,bf16,asym,seed", [
+    (1, 1024, 48, False, False, 0),
+    (2, 2048, 40, False, True, 1),
+    (3, 96, 33, True, True, 2),      # odd block count, ragged everything
+    (8, 4096, 8, True, True, 3),
+    (1, 32, 64, False, True, 4),
+])
+def test_oracle_equals_exact_rounding(oracle_mod, m, K, N, bf16, asym, seed):
+    from block_wise_int4_matmulnbits_amd import workloads
+    d = workloads.generate(m, K, N, workloads.BF16 if bf16 else workloads.F16,
+                           asym, 0.002, 0.02, 1.0, seed)
+    A = d["A"][:m]
+    r = oracle_mod.matmul_nbits(A, bf16, d["B"], d["scales"], d["zp"], m, K, N)
+    ex = _exact_sums(A, bf16, d["B"], d["scales"], d["zp"], m, K, N, oracle_mod)
+    want = np.array([[_exact_f16_bits(ex[i, j], 48) for j in range(N)]
+                     for i in range(m)], np.uint16)
+    assert np.array_equal(r["f16"], want)
+    # fp64 sum within the textbook bound of the exact sum: |err| <= K u sum|p|
+    exact = np.array([[float(ex[i, j]) * 2.0 ** -48 for j in range(N)]
+                      for i in range(m)])
+    assert np.all(np.abs(r["f64"] - exact) <= K * 2.0 ** -53 * r["abs"] + 1e-300)
+
+
+# ------------------------------------------------------- structured brute force
+def test_brute_force_uniform_blocks(oracle_mod):
+    """K=64, N<=4, each (column, block) holds one nibble value from {0, 15},
+    zero points from {0, 8, 15}, small integer activations: the closed form
+    y = sum_b (q_b - z_b) s_b (sum_{k in b} a_k) is exact."""
+    rng = np.random.default_rng(99)
+    for trial in range(300):
+        N = int(rng.integers(1, 5))
+        K, nb = 64, 2
+        a = rng.integers(-3, 4, K).astype(np.float64)
+        qv = rng.choice([0, 15], (N, nb))
+        zv = rng.choice([0, 8, 15], (N, nb))
+        sv = rng.choice([0.25, 0.5, 1.0, 2.0], (N, nb))
+        use_null = trial % 5 == 0
+        if use_null:
+            zv[:] = 8
+        q = np.repeat(qv, 32, axis=1).astype(np.uint8)
+        B = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+        zp = None if use_null else (zv[:, 0] | (zv[:, 1] << 4)).astype(np.uint8)[:, None]
+        A = a.astype(np.float16).view(np.uint16)[None, :]
+        scales = sv.astype(np.float16).view(np.uint16)
+        r = oracle_mod.matmul_nbits(A, False, B, scales, zp, 1, K, N)
+        blocksum = a.reshape(nb, 32).sum(axis=1)
+        want = ((qv - zv) * sv * blocksum[None, :]).sum(axis=1)
+        assert np.array_equal(r["f64"][0], want)
+        assert np.array_equal(r["f16"][0], want.astype(np.float16).view(np.uint16))
+
+
+# ------------------------------------------------------------------ invariants
+def _gen(m, K, N, seed, asym=True, bf16=False):
+    from block_wise_int4_matmulnbits_amd import workloads
+    d = workloads.generate(m, K, N, workloads.BF16 if bf16 else workloads.F16,
+                           asym, 0.002, 0.02, 1.0, seed)
+    d["A"] = d["A"][:m]
+    return d
+
+
+def test_zp_equal_to_nibbles_gives_zero(oracle_mod):
+    rng = np.random.default_rng(5)
+    m, K, N = 2, 512, 24
+    nb = K // 32
+    z = rng.integers(0, 16, (N, nb)).astype(np.uint8)
+    q = np.repeat(z, 32, axis=1)
+    B = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    zp = (z[:, 0::2] | (z[:, 1::2] << 4)).astype(np.uint8)
+    d = _gen(m, K, N, 6)
+    r = oracle_mod.matmul_nbits(d["A"], False, B, d["scales"], zp, m, K, N)
+    assert np.all(r["f64"] == 0) and np.all((r["f16"] & 0x7FFF) == 0)
+
+
+def test_scales_times_two_doubles_y(oracle_mod):
+    m, K, N = 2, 1024, 32
+    d = _gen(m, K, N, 7)
+    s2 = (d["scales"].view(np.float16) * np.float16(2)).view(np.uint16)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    r2 = oracle_mod.matmul_nbits(d["A"], False, d["B"], s2, d["zp"], m, K, N)
+    assert np.array_equal(r2["f64"], 2 * r1["f64"])
+    normal = (r1["f16"] & 0x7C00) != 0
+    assert np.array_equal(r2["f16"][normal], r1["f16"][normal] + 0x0400)
+
+
+def test_null_zp_equals_explicit_eight(oracle_mod):
+    m, K, N = 3, 2048, 20
+    d = _gen(m, K, N, 8, asym=False)
+    zp8 = np.full((N, K // 64), 0x88, np.uint8)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], None, m, K, N)
+    r2 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], zp8, m, K, N)
+    for key in ("f16", "bf16", "f64"):
+        assert np.array_equal(r1[key], r2[key])
+
+
+def test_column_permutation(oracle_mod):
+    m, K, N = 2, 1024, 37
+    d = _gen(m, K, N, 9)
+    perm = np.random.default_rng(1).permutation(N)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    r2 = oracle_mod.matmul_nbits(d["A"], False, d["B"][perm], d["scales"][perm],
+                                 d["zp"][perm], m, K, N)
+    assert np.array_equal(r2["f16"], r1["f16"][:, perm])
+    assert np.array_equal(r2["bf16"], r1["bf16"][:, perm])
+
+
+def test_rows_independent(oracle_mod):
+    m, K, N = 5, 512, 16
+    d = _gen(m, K, N, 10, bf16=True)
+    r = oracle_mod.matmul_nbits(d["A"], True, d["B"], d["scales"], d["zp"], m, K, N)
+    for i in range(m):
+        ri = oracle_mod.matmul_nbits(d["A"][i:i + 1], True, d["B"], d["scales"],
+                                     d["zp"], 1, K, N)
+        assert np.array_equal(ri["f16"][0], r["f16"][i])
+
+
+def test_negated_activations_negate_y(oracle_mod):
+    m, K, N = 1, 1024, 64
+    d = _gen(m, K, N, 11)
+    An = d["A"] ^ np.uint16(0x8000)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    r2 = oracle_mod.matmul_nbits(An, False, d["B"], d["scales"], d["zp"], m, K, N)
+    assert np.array_equal(r2["f64"], -r1["f64"])
+    nz = (r1["f16"] & 0x7FFF) != 0
+    assert np.array_equal(r2["f16"][nz], r1["f16"][nz] ^ 0x8000)
+
+
+def test_column_sample_matches_full(oracle_mod):
+    m, K, N = 2, 512, 50
+    d = _gen(m, K, N, 12)
+    full = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    cols = np.array([49, 0, 17, 17, 3], np.int64)
+    part = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"],
+                                   m, K, N, cols=cols)
+    assert np.array_equal(part["f16"], full["f16"][:, cols])
+    assert np.array_equal(part["abs"], full["abs"][:, cols])
+
+
+def test_library_matmul_agrees(oracle_mod):
+    """numpy float64 GEMM of the materialised weights rounds to the same fp16
+    except where the sum sits within rounding noise of an fp16 tie."""
+    m, K, N = 4, 4096, 96
+    d = _gen(m, K, N, 13)
+    q = np.empty((N, K), np.float64)
+    q[:, 0::2] = d["B"] & 0xF
+    q[:, 1::2] = d["B"] >> 4
+    z = np.empty((N, 2 * d["zp"].shape[1]))
+    z[:, 0::2] = d["zp"] & 0xF
+    z[:, 1::2] = d["zp"] >> 4
+    s = d["scales"].view(np.float16).astype(np.float64)
+    W = (q - np.repeat(z[:, :K // 32], 32, axis=1)) * np.repeat(s, 32, axis=1)
+    y = d["A"].view(np.float16).astype(np.float64) @ W.T
+    r = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    np.testing.assert_allclose(r["f64"], y, rtol=0, atol=1e-9 * (1 + r["abs"].max()))
+    assert np.array_equal(r["f16"], y.astype(np.float16).view(np.uint16))
