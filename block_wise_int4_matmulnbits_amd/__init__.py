@@ -1,0 +1,247 @@
+"""Python binding of libmnb, the block-wise INT4 MatMulNBits decode GEMV for
+MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libmnb.so`` (built in-tree by ``build.py``).  Functions carry the
+names of the C entry points declared in ``include/mnb.h``.  torch supplies
+device memory and streams; nothing here computes on the host, and there is
+no fallback: if the library is missing, importing the entry points raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmnb.so")
+
+MNB_F16 = 0
+MNB_BF16 = 1
+MNB_MAX_M = 8
+
+STATUS = {
+    0: "MNB_OK", 1: "MNB_ERR_NULL", 2: "MNB_ERR_SHAPE", 3: "MNB_ERR_BLOCK",
+    4: "MNB_ERR_DTYPE", 5: "MNB_ERR_ALIGN", 6: "MNB_ERR_M_RANGE",
+    7: "MNB_ERR_HIP", 8: "MNB_ERR_ALIAS", 9: "MNB_ERR_PLAN",
+}
+
+
+class MnbError(RuntimeError):
+    def __init__(self, status, lib=None):
+        self.status = status
+        text = lib.mnb_status_string(status).decode() if lib is not None else ""
+        name = STATUS.get(status, str(status))
+        if status == 7 and lib is not None:
+            text += " (hipError_t %d)" % lib.mnb_last_hip_error()
+        super().__init__("%s: %s" % (name, text))
+
+
+class mnb_plan(ctypes.Structure):
+    _fields_ = [("lanes_per_col", ctypes.c_int32),
+                ("blocks_per_lane", ctypes.c_int32),
+                ("cols_per_tile", ctypes.c_int32),
+                ("workgroups", ctypes.c_int32),
+                ("threads_per_wg", ctypes.c_int32),
+                ("k_chunks", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class mnb_counters(ctypes.Structure):
+    _fields_ = [("calls", ctypes.c_uint64),
+                ("launches", ctypes.c_uint64),
+                ("elements_f16", ctypes.c_uint64),
+                ("elements_bf16_direct", ctypes.c_uint64),
+                ("row_batched_launches", ctypes.c_uint64)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class mnb_kernel_info(ctypes.Structure):
+    _fields_ = [("vgprs", ctypes.c_int32), ("sgprs", ctypes.c_int32),
+                ("lds_bytes", ctypes.c_int32), ("max_threads", ctypes.c_int32),
+                ("wgs_per_cu", ctypes.c_int32)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+_lock = threading.Lock()
+_lib = None
+
+EXPORTS = ("matmul_nbits", "matmul_nbits_planned", "mnb_plan_default",
+           "mnb_plan_check", "mnb_counters_get", "mnb_counters_reset",
+           "mnb_get_kernel_info", "mnb_status_string", "mnb_last_hip_error",
+           "mnb_abi_version")
+
+
+def lib():
+    """Load libmnb.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libmnb.so is not built (%s); run __graft_entry__.build() or "
+                "python block_wise_int4_matmulnbits_amd/build.py" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.matmul_nbits.restype = i32
+        L.matmul_nbits.argtypes = [vp, i32, i64, i64, i64, vp, vp, vp, i32, vp,
+                                   i32, vp]
+        L.matmul_nbits_planned.restype = i32
+        L.matmul_nbits_planned.argtypes = L.matmul_nbits.argtypes + [
+            ctypes.POINTER(mnb_plan)]
+        L.mnb_plan_default.restype = i32
+        L.mnb_plan_default.argtypes = [i64, i64, i64, i32, ctypes.POINTER(mnb_plan)]
+        L.mnb_plan_check.restype = i32
+        L.mnb_plan_check.argtypes = [i64, i64, i64, ctypes.POINTER(mnb_plan)]
+        L.mnb_counters_get.restype = None
+        L.mnb_counters_get.argtypes = [ctypes.POINTER(mnb_counters)]
+        L.mnb_counters_reset.restype = None
+        L.mnb_counters_reset.argtypes = []
+        L.mnb_get_kernel_info.restype = i32
+        L.mnb_get_kernel_info.argtypes = [i64, ctypes.POINTER(mnb_plan),
+                                          ctypes.POINTER(mnb_kernel_info)]
+        L.mnb_status_string.restype = ctypes.c_char_p
+        L.mnb_status_string.argtypes = [i32]
+        L.mnb_last_hip_error.restype = i32
+        L.mnb_last_hip_error.argtypes = []
+        L.mnb_abi_version.restype = i32
+        L.mnb_abi_version.argtypes = []
+        _lib = L
+        return L
+
+
+# ---------------------------------------------------------------- marshalling
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return MNB_F16
+    if t.dtype == torch.bfloat16:
+        return MNB_BF16
+    raise TypeError("expected float16 or bfloat16, got %s" % t.dtype)
+
+
+def _stream_handle(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, L):
+    if status != 0:
+        raise MnbError(status, L)
+
+
+def _tensor_args(A, Bpacked, scales, zero_points, out):
+    if A.dim() != 2 or out.dim() != 2 or Bpacked.dim() != 2 or scales.dim() != 2:
+        raise ValueError("A, Bpacked, scales and out must be 2-D")
+    m, K = A.shape
+    N = Bpacked.shape[0]
+    for name, t in (("A", A), ("Bpacked", Bpacked), ("scales", scales), ("out", out)):
+        if not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    if zero_points is not None and not zero_points.is_contiguous():
+        raise ValueError("zero_points must be contiguous")
+    if tuple(out.shape) != (m, N):
+        raise ValueError("out must be [m, N] = [%d, %d]" % (m, N))
+    if tuple(Bpacked.shape) != (N, K // 2) or Bpacked.element_size() != 1:
+        raise ValueError("Bpacked must be uint8 [N, K/2]")
+    if tuple(scales.shape) != (N, K // 32) or scales.element_size() != 2:
+        raise ValueError("scales must be 16-bit [N, K/32] (fp16 bit patterns)")
+    if zero_points is not None and (tuple(zero_points.shape) != (N, (K // 32 + 1) // 2)
+                                    or zero_points.element_size() != 1):
+        raise ValueError("zero_points must be uint8 [N, ceil(K/64)]")
+    return (A.data_ptr(), _dtype_code(A), m, K, N, Bpacked.data_ptr(),
+            scales.data_ptr(),
+            zero_points.data_ptr() if zero_points is not None else None,
+            out.data_ptr(), _dtype_code(out))
+
+
+def matmul_nbits(A, Bpacked, scales, zero_points, out, block=32, stream=None):
+    """out[m, N] = A[m, K] @ dequant(Bpacked, scales, zero_points)^T on the GPU.
+
+    A: fp16/bf16 [m, K]; Bpacked: uint8 [N, K/2]; scales: fp16 [N, K/32];
+    zero_points: uint8 [N, ceil(K/64)] or None (zero point 8);
+    out: fp16/bf16 [m, N], fully overwritten.  Queued on ``stream``
+    (default: torch's current stream on A's device); returns ``out``.
+    """
+    L = lib()
+    a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, o_ptr, o_dt = _tensor_args(
+        A, Bpacked, scales, zero_points, out)
+    st = L.matmul_nbits(a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, block, o_ptr,
+                        o_dt, _stream_handle(stream, A.device))
+    _check(st, L)
+    return out
+
+
+def matmul_nbits_planned(A, Bpacked, scales, zero_points, out, plan, block=32,
+                         stream=None):
+    """matmul_nbits with an explicit ``mnb_plan`` (or dict of its fields)."""
+    L = lib()
+    if isinstance(plan, dict):
+        plan = mnb_plan(**{k: v for k, v in plan.items()
+                           if k in dict(mnb_plan._fields_)})
+    a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, o_ptr, o_dt = _tensor_args(
+        A, Bpacked, scales, zero_points, out)
+    st = L.matmul_nbits_planned(a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, block,
+                                o_ptr, o_dt, _stream_handle(stream, A.device),
+                                ctypes.byref(plan))
+    _check(st, L)
+    return out
+
+
+def matmul_nbits_raw(A_ptr, a_dtype, m, K, N, B_ptr, scales_ptr, zp_ptr, block,
+                     out_ptr, out_dtype, stream=0):
+    """Direct C call with integer addresses; returns the status code."""
+    return lib().matmul_nbits(A_ptr, a_dtype, m, K, N, B_ptr, scales_ptr, zp_ptr,
+                              block, out_ptr, out_dtype, stream)
+
+
+def mnb_plan_default(m, K, N, num_cus):
+    p = mnb_plan()
+    L = lib()
+    _check(L.mnb_plan_default(m, K, N, num_cus, ctypes.byref(p)), L)
+    return p
+
+
+def mnb_plan_check(m, K, N, plan):
+    """Returns the status code; fills the derived fields of ``plan``."""
+    return lib().mnb_plan_check(m, K, N, ctypes.byref(plan))
+
+
+def mnb_counters_get():
+    c = mnb_counters()
+    lib().mnb_counters_get(ctypes.byref(c))
+    return c.as_dict()
+
+
+def mnb_counters_reset():
+    lib().mnb_counters_reset()
+
+
+def mnb_get_kernel_info(m, plan):
+    info = mnb_kernel_info()
+    L = lib()
+    _check(L.mnb_get_kernel_info(m, ctypes.byref(plan), ctypes.byref(info)), L)
+    return info.as_dict()
+
+
+def mnb_status_string(status):
+    return lib().mnb_status_string(status).decode()
+
+
+def mnb_last_hip_error():
+    return lib().mnb_last_hip_error()
+
+
+def mnb_abi_version():
+    return lib().mnb_abi_version()

@@ -1,0 +1,54 @@
+"""Build libmnb.so for gfx950 in-tree.
+
+hipcc compiles the kernels (mnb_gemv.hip); the host front end
+(mnb_api.cpp) is plain C++ built with g++; hipcc links both into one shared
+library next to this file.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libmnb.so")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 instructions anywhere in the device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-I", INCLUDE, "-I", CSRC,
+]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
+             "-I", CSRC]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+
+
+def build(verbose: bool = False, save_temps: bool = False) -> str:
+    """Compile and link libmnb.so (always recompiles). Returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    gemv_o = os.path.join(BUILD, "mnb_gemv.o")
+    api_o = os.path.join(BUILD, "mnb_api.o")
+    extra = ["-save-temps=obj"] if save_temps else []
+    _run(["hipcc", "-c", os.path.join(CSRC, "mnb_gemv.hip"), "-o", gemv_o]
+         + HIP_FLAGS + extra, verbose)
+    _run(["g++", "-c", os.path.join(CSRC, "mnb_api.cpp"), "-o", api_o] + CXX_FLAGS,
+         verbose)
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
+          gemv_o, api_o], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

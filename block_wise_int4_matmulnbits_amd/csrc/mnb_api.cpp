@@ -1,0 +1,270 @@
+// Host front end of libmnb: argument validation, launch planning, counters
+// and status strings.  Plain C++ (no HIP headers): everything here runs, and
+// is tested, without a GPU.  The kernels and their launch live in
+// mnb_gemv.hip.
+#include <atomic>
+#include <stdint.h>
+
+#include "mnb.h"
+#include "mnb_internal.h"
+
+namespace {
+
+std::atomic<uint64_t> g_calls{0}, g_launches{0}, g_f16{0}, g_bf16{0}, g_rows{0};
+thread_local int t_last_hip_error = 0;
+
+// Register budget: M rows x blocks_per_lane blocks of activations stay in
+// VGPRs (16 per block and row), at most 8 such blocks per lane.
+int max_blocks_per_lane(int64_t m) { return m == 1 ? 8 : m == 2 ? 4 : m <= 4 ? 2 : 1; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t pow2_ceil(int64_t x)
+{
+    int64_t p = 1;
+    while (p < x) p <<= 1;
+    return p;
+}
+
+int64_t pow2_floor(int64_t x)
+{
+    int64_t p = 1;
+    while (p * 2 <= x) p <<= 1;
+    return p;
+}
+
+bool is_pow2_in(int64_t x, int64_t lo, int64_t hi)
+{
+    return x >= lo && x <= hi && (x & (x - 1)) == 0;
+}
+
+bool overlaps(const void* a, int64_t an, const void* b, int64_t bn)
+{
+    if (!a || !b || an <= 0 || bn <= 0) return false;
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
+}
+
+// Target resident waves per CU when sizing the grid; the grid is then
+// clamped to what occupancy allows, so every workgroup is resident at once.
+constexpr int kTargetWavesPerCu = 16;
+
+int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+             const uint8_t* Bpacked, const uint16_t* scales,
+             const uint8_t* zero_points, int block, void* out, int out_dtype)
+{
+    if (m < 0 || m > MNB_MAX_M) return MNB_ERR_M_RANGE;
+    if (K < 0 || N < 0 || K > MNB_MAX_K || N > INT32_MAX) return MNB_ERR_SHAPE;
+    if (block != 32) return MNB_ERR_BLOCK;
+    if (K % 32 != 0) return MNB_ERR_SHAPE;
+    if ((a_dtype != MNB_F16 && a_dtype != MNB_BF16) ||
+        (out_dtype != MNB_F16 && out_dtype != MNB_BF16))
+        return MNB_ERR_DTYPE;
+    if (m == 0 || N == 0) return MNB_OK;
+    if (!out) return MNB_ERR_NULL;
+    if (K > 0 && (!A || !Bpacked || !scales)) return MNB_ERR_NULL;
+    if (((uintptr_t)A & 15) || ((uintptr_t)Bpacked & 15) ||
+        ((uintptr_t)scales & 1) || ((uintptr_t)out & 1))
+        return MNB_ERR_ALIGN;
+    const int64_t nb = K / 32;
+    const int64_t out_bytes = m * N * 2;
+    if (overlaps(out, out_bytes, A, m * K * 2) ||
+        overlaps(out, out_bytes, Bpacked, N * (K / 2)) ||
+        overlaps(out, out_bytes, scales, N * nb * 2) ||
+        overlaps(out, out_bytes, zero_points, N * ((nb + 1) / 2)))
+        return MNB_ERR_ALIAS;
+    return MNB_OK;
+}
+
+int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+        const uint8_t* Bpacked, const uint16_t* scales, const uint8_t* zero_points,
+        int block, void* out, int out_dtype, void* stream, const mnb_plan* explicit_plan)
+{
+    int st = validate(A, a_dtype, m, K, N, Bpacked, scales, zero_points, block, out,
+                      out_dtype);
+    if (st != MNB_OK) return st;
+    if (m == 0 || N == 0) {
+        g_calls.fetch_add(1, std::memory_order_relaxed);
+        return MNB_OK;
+    }
+    mnb_plan plan;
+    if (explicit_plan) {
+        plan = *explicit_plan;
+        if (mnb_plan_check(m, K, N, &plan) != MNB_OK) return MNB_ERR_PLAN;
+    } else {
+        int cus = 0;
+        int e = mnb::current_device_cus(&cus);
+        if (e != 0) {
+            t_last_hip_error = e;
+            return MNB_ERR_HIP;
+        }
+        st = mnb_plan_default(m, K, N, cus, &plan);
+        if (st != MNB_OK) return st;
+        // Keep the whole grid resident: columns are split into one
+        // contiguous range per lane group, so a second wave of workgroups
+        // would only lengthen the tail.  The grid size never changes the
+        // per-column summation order.
+        const int per_cu = mnb::workgroups_per_cu(m, plan);
+        if (per_cu > 0 && plan.workgroups > (int64_t)per_cu * cus)
+            plan.workgroups = per_cu * cus;
+    }
+    mnb::GemvArgs args{A, Bpacked, scales, zero_points, out, m, K, N,
+                       a_dtype == MNB_BF16, out_dtype == MNB_BF16};
+    int e = mnb::launch_gemv(args, plan, stream);
+    if (e != 0) {
+        t_last_hip_error = e;
+        return MNB_ERR_HIP;
+    }
+    g_calls.fetch_add(1, std::memory_order_relaxed);
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    if (out_dtype == MNB_BF16) g_bf16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
+    else g_f16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
+    if (m > 1) g_rows.fetch_add(1, std::memory_order_relaxed);
+    return MNB_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
+{
+    if (!plan || m < 1 || m > MNB_MAX_M || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
+    const int64_t lpc = plan->lanes_per_col;
+    const int64_t bpl = plan->blocks_per_lane;
+    const int64_t nc = plan->cols_per_tile;
+    const bool inwave = is_pow2_in(lpc, 16, 64);
+    const bool xwave = lpc % 64 == 0 && lpc >= 128 && lpc <= 512;
+    if (!inwave && !xwave) return MNB_ERR_PLAN;
+    if (!is_pow2_in(bpl, 1, 8) || m * bpl > 8) return MNB_ERR_PLAN;
+    if (!is_pow2_in(nc, 1, 8) || nc * bpl > 8 || nc * m > 32) return MNB_ERR_PLAN;
+    if (plan->workgroups < 1) return MNB_ERR_PLAN;
+    plan->threads_per_wg = inwave ? 256 : (int32_t)lpc;
+    const int64_t nb = K / 32;
+    const int64_t chunks = nb == 0 ? 1 : ceil_div(nb, lpc * bpl);
+    if (chunks > INT32_MAX) return MNB_ERR_PLAN;
+    plan->k_chunks = (int32_t)chunks;
+    return MNB_OK;
+}
+
+int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, mnb_plan* plan)
+{
+    if (!plan) return MNB_ERR_NULL;
+    if (m < 1 || m > MNB_MAX_M) return MNB_ERR_M_RANGE;
+    if (K < 0 || K % 32 || K > MNB_MAX_K || N < 1 || N > INT32_MAX) return MNB_ERR_SHAPE;
+    if (num_cus < 1) num_cus = 1;
+    const int64_t nb = K / 32;
+    const int64_t bmax = max_blocks_per_lane(m);
+    const int64_t bpl_pref = bmax < 2 ? bmax : 2;
+    int64_t lpc, bpl;
+    if (ceil_div(nb, bpl_pref) <= 64) {
+        // The whole K range fits one wave at two blocks per lane.
+        lpc = pow2_ceil(ceil_div(nb, bpl_pref));
+        if (lpc < 16) lpc = 16;
+        bpl = pow2_ceil(nb == 0 ? 1 : ceil_div(nb, lpc));
+    } else if (ceil_div(nb, bmax) <= 64) {
+        lpc = 64;
+        bpl = pow2_ceil(ceil_div(nb, 64));
+    } else {
+        // Several waves share a column; beyond 8 waves, K is chunked.
+        int64_t need = ceil_div(nb, bmax);
+        lpc = 64 * ceil_div(need, 64);
+        if (lpc > 512) lpc = 512;
+        bpl = pow2_ceil(ceil_div(nb, lpc));
+        if (bpl > bmax) bpl = bmax;
+    }
+    int64_t nc_max = 8 / bpl;
+    if (nc_max * m > 32) nc_max = pow2_floor(32 / m);
+    const bool inwave = lpc <= 64;
+    // lane groups resident per CU at the target wave count
+    const int64_t groups_per_cu = inwave ? kTargetWavesPerCu * (64 / lpc)
+                                         : (kTargetWavesPerCu + lpc / 64 - 1) / (lpc / 64);
+    const int64_t target_groups = groups_per_cu * num_cus;
+    int64_t nc = pow2_floor(N / target_groups > 0 ? N / target_groups : 1);
+    if (nc > nc_max) nc = nc_max;
+    int64_t groups = ceil_div(N, nc);
+    if (groups > target_groups) groups = target_groups;
+    const int64_t gpw = inwave ? 256 / lpc : 1;
+    const int64_t wgs = ceil_div(groups, gpw);
+    plan->lanes_per_col = (int32_t)lpc;
+    plan->blocks_per_lane = (int32_t)bpl;
+    plan->cols_per_tile = (int32_t)nc;
+    plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
+    return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
+}
+
+int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+                 const uint8_t* Bpacked, const uint16_t* scales,
+                 const uint8_t* zero_points, int block, void* out, int out_dtype,
+                 void* stream)
+{
+    return run(A, a_dtype, m, K, N, Bpacked, scales, zero_points, block, out, out_dtype,
+               stream, nullptr);
+}
+
+int matmul_nbits_planned(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+                         const uint8_t* Bpacked, const uint16_t* scales,
+                         const uint8_t* zero_points, int block, void* out, int out_dtype,
+                         void* stream, const mnb_plan* plan)
+{
+    if (!plan) return MNB_ERR_NULL;
+    return run(A, a_dtype, m, K, N, Bpacked, scales, zero_points, block, out, out_dtype,
+               stream, plan);
+}
+
+void mnb_counters_get(mnb_counters* out)
+{
+    if (!out) return;
+    out->calls = g_calls.load();
+    out->launches = g_launches.load();
+    out->elements_f16 = g_f16.load();
+    out->elements_bf16_direct = g_bf16.load();
+    out->row_batched_launches = g_rows.load();
+}
+
+void mnb_counters_reset(void)
+{
+    g_calls = 0;
+    g_launches = 0;
+    g_f16 = 0;
+    g_bf16 = 0;
+    g_rows = 0;
+}
+
+int mnb_get_kernel_info(int64_t m, const mnb_plan* plan, mnb_kernel_info* info)
+{
+    if (!plan || !info) return MNB_ERR_NULL;
+    mnb_plan p = *plan;
+    if (p.workgroups < 1) p.workgroups = 1;
+    if (mnb_plan_check(m, 32 * (int64_t)p.lanes_per_col, 1, &p) != MNB_OK) return MNB_ERR_PLAN;
+    int e = mnb::kernel_info(m, p, info);
+    if (e == -1) return MNB_ERR_PLAN;
+    if (e != 0) {
+        t_last_hip_error = e;
+        return MNB_ERR_HIP;
+    }
+    return MNB_OK;
+}
+
+const char* mnb_status_string(int status)
+{
+    switch (status) {
+    case MNB_OK: return "ok";
+    case MNB_ERR_NULL: return "a required pointer is NULL";
+    case MNB_ERR_SHAPE: return "bad shape (K must be a non-negative multiple of 32, N >= 0, within limits)";
+    case MNB_ERR_BLOCK: return "block size must be 32";
+    case MNB_ERR_DTYPE: return "dtype must be MNB_F16 or MNB_BF16";
+    case MNB_ERR_ALIGN: return "A and Bpacked must be 16-byte aligned, scales and out 2-byte aligned";
+    case MNB_ERR_M_RANGE: return "m must be in [0, 8]";
+    case MNB_ERR_HIP: return "HIP runtime error (see mnb_last_hip_error)";
+    case MNB_ERR_ALIAS: return "out overlaps an input";
+    case MNB_ERR_PLAN: return "launch plan not supported";
+    }
+    return "unknown status";
+}
+
+int mnb_last_hip_error(void) { return t_last_hip_error; }
+
+int mnb_abi_version(void) { return MNB_ABI_VERSION; }
+
+}  // extern "C"

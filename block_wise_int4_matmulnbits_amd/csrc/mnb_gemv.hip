@@ -1,0 +1,480 @@
+// Block-wise INT4 MatMulNBits decode GEMV, hand-written for gfx950 (CDNA4).
+//
+//   y[r][n] = sum_k a[r][k] * (q[n][k] - z[n][k/32]) * s[n][k/32]
+//
+// (onnx-genai pull request "perf(cuda): let the split-K decode GEMV store
+// bf16 directly", opening paragraphs: block-32 INT4 weights, split-K GEMV,
+// fp32 accumulator rounded to fp16 in the epilogue, bf16 narrowed from that
+// fp16; pull request "PORT-1 (offline bias+interleave)", "Why the premise
+// fails here", item 1: asymmetric per-block zero points, +8 when symmetric.)
+//
+// Work decomposition.  The K range of a column is cut into 32-weight blocks.
+// A "lane group" of lanes_per_col lanes shares one column at a time; lane l
+// of the group owns blocks l, l + lpc, l + 2*lpc, ... (blocks_per_lane of
+// them per K chunk).  Because that set is fixed for the life of the wave,
+// the lane's activations are loaded once, converted to fp16, permuted into
+// the pair order of the nibble unpack below and kept in VGPRs while the group
+// walks its contiguous range of columns, cols_per_tile at a time.  A group is
+// 16, 32 or 64 lanes of one wave (no barriers), or 2..8 whole waves that
+// combine their partial sums through LDS.
+//
+// Per 16-byte weight load (one block of one column) a lane does, for each of
+// its 4 dwords x (8 nibbles, k = 8d .. 8d+7), with one v_and_or_b32 each:
+//   (x & 0x000F000F)        | 0x64006400 -> fp16 pair (1024+q0, 1024+q4)
+//   (x & 0x00F000F0)        | 0x64006400 -> (1024+16q1, 1024+16q5)
+//   ((x >> 8) & 0x000F000F) | 0x64006400 -> (1024+q2, 1024+q6)
+//   ((x >> 8) & 0x00F000F0) | 0x64006400 -> (1024+16q3, 1024+16q7)
+// then one packed fp16 add of -(1024+z) (or -(1024+16z)) per pair, which
+// leaves q-z (or 16(q-z)) exactly, and one v_dot2_f32_f16 against the
+// matching activation pair into one of two fp32 accumulators (the 1x and
+// 16x families).  Every product a*(q-z) is exact in fp32, so the rounding
+// error of the sum is relative to sum |a*(q-z)|.  Per block the families are
+// combined exactly (hi/16 + lo) and the fp16 scale applied by one FMA:
+//   acc += (hi/16 + lo) * s.
+//
+// Reduction: a fixed DPP tree across the group's lanes inside a wave, then
+// (multi-wave groups) a fixed-order sum over waves through LDS.  No atomics:
+// equal inputs give equal bits.
+//
+// Epilogue (first page, paragraph on matmul_nbits_store_narrowed): one lane
+// per (row, column) rounds fp32 -> fp16 (RNE); when the launch-uniform
+// out_bf16 flag is set it narrows that fp16 to bf16 (RNE) and stores bf16
+// directly.  Each launch writes all m*N outputs.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <mutex>
+#include <type_traits>
+
+#include "mnb.h"
+#include "mnb_internal.h"
+
+namespace mnb {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+struct Params {
+    const uint16_t* A;       // [m][K]
+    const uint8_t* B;        // [N][K/2]
+    const uint16_t* scales;  // [N][nb]
+    const uint8_t* zp;       // [N][zb] or null
+    uint16_t* out;           // [m][N]
+    int64_t N;
+    int32_t K, nb, zb;
+    int32_t lpc;             // lanes per column group
+    int32_t chunks;          // K chunks of lpc*BPL blocks
+    int32_t a_bf16, out_bf16;
+};
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t w, float c)
+{
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
+                                  __builtin_bit_cast(half2_t, w), c, false);
+}
+
+// bf16 bits -> fp16 bits, round to nearest even through the exact fp32 value.
+__device__ __forceinline__ uint32_t bf16_to_f16(uint32_t b)
+{
+    const _Float16 h = (_Float16)__uint_as_float(b << 16);
+    return (uint32_t)__builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v)
+{
+    return bf16_to_f16(v & 0xFFFFu) | (bf16_to_f16(v >> 16) << 16);
+}
+
+// fp16 bits -> bf16 bits: exact widening to fp32, then RNE on the bit
+// pattern; NaN becomes a quiet NaN with its sign.
+__device__ __forceinline__ uint16_t f16_to_bf16(uint16_t h)
+{
+    uint32_t u = __float_as_uint((float)__builtin_bit_cast(_Float16, h));
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// v_and_or_b32 (x & mask) | orv in one VALU op.  gfx9 VOP3 takes no literal
+// constants, so the mask comes from an SGPR and the or-value from a VGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv)
+{
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));
+    return r;
+}
+
+// Exact fp16 pair q - z (or 16(q - z)) from a masked nibble pair, see above.
+__device__ __forceinline__ uint32_t nib_minus_zp(uint32_t x, uint32_t mask, uint32_t magic,
+                                                 uint32_t zneg)
+{
+    const half2_t v = __builtin_bit_cast(half2_t, and_or(x, mask, magic)) +
+                      __builtin_bit_cast(half2_t, zneg);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// v + (v of another lane) through a DPP lane permutation; lanes outside
+// ROW_MASK add 0 (they keep `old`).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_add(float v)
+{
+    const int t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false);
+    return v + __int_as_float(t);
+}
+
+// Fixed-order sum over groups of SPAN (16, 32, 64) lanes.  Inside a 16-lane
+// row: swap pairs, swap pairs of pairs, half-row mirror, row mirror -- every
+// lane of the row then holds the (bitwise identical) row sum.  Rows are then
+// combined with row broadcasts; the group total ends up in every lane of the
+// group's last row (lanes SPAN-16 .. SPAN-1 of the group).
+template <int SPAN>
+__device__ __forceinline__ float group_sum(float v)
+{
+    v = dpp_add<0xB1>(v);    // quad_perm [1,0,3,2]
+    v = dpp_add<0x4E>(v);    // quad_perm [2,3,0,1]
+    v = dpp_add<0x141>(v);   // row_half_mirror
+    v = dpp_add<0x140>(v);   // row_mirror
+    if constexpr (SPAN >= 32) v = dpp_add<0x142, 0xA>(v);   // row_bcast:15 into rows 1, 3
+    if constexpr (SPAN >= 64) v = dpp_add<0x143, 0xC>(v);   // row_bcast:31 into rows 2, 3
+    return v;
+}
+
+__device__ __forceinline__ int64_t uniform64(int64_t v)
+{
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Rough VGPR need of a variant, to ask the compiler for an occupancy it can
+// meet without spilling: activations 16*M*BPL, weights/scales/zero points
+// 6*NC*BPL, sums NC*M (counted thrice: live through reduction and
+// selection), block temporaries 2*M, addressing and constants.
+template <int M, int BPL, int NC>
+constexpr int kWavesPerEu()
+{
+    constexpr int est = 16 * M * BPL + 6 * NC * BPL + 3 * NC * M + 2 * M + 28;
+    return est <= 128 ? 4 : est <= 168 ? 3 : est <= 256 ? 2 : 1;
+}
+
+// UNI: lane groups are whole waves (lanes_per_col >= 64), so a group's
+// column range is wave-uniform and tile addresses live in SGPRs.
+template <int M, int BPL, int NC, bool UNI>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<M, BPL, NC>())))
+void mnb_gemv_kernel(Params p)
+{
+    constexpr int NV = NC * M;                  // partial sums per lane
+    __shared__ float red[2][8][NV];             // multi-wave groups only
+
+    const int tid = threadIdx.x;
+    const int lpc = p.lpc;
+    const bool xwave = lpc > 64;
+    const int lane = xwave ? tid : (tid & (lpc - 1));
+    const int grp = xwave ? 0 : (tid / lpc);
+    const int gpw = xwave ? 1 : (int)(blockDim.x / lpc);
+    const int64_t gg = (int64_t)blockIdx.x * gpw + grp;
+    const int64_t TG = (int64_t)gridDim.x * gpw;
+    int64_t c_begin = p.N * gg / TG;
+    int64_t c_end = p.N * (gg + 1) / TG;
+    if constexpr (UNI) {
+        c_begin = uniform64(c_begin);
+        c_end = uniform64(c_end);
+    }
+    const uint32_t row_bytes = (uint32_t)p.K / 2;
+    const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
+    const int zshift = (lane & 1) * 4;          // block parity == lane parity (lpc even)
+    const uint32_t magic = 0x64006400u;         // fp16 pair (1024, 1024)
+
+    uint32_t act[M][BPL][16];                   // permuted fp16 pairs
+
+    auto load_acts = [&](int ch) {
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+            const bool ok = b < nb;
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                uint4 v[4];
+                if (ok) {
+                    const uint4* src = reinterpret_cast<const uint4*>(
+                        p.A + (int64_t)r * p.K + 32 * (int64_t)b);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = src[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    uint32_t x = v[i].x, y = v[i].y, z = v[i].z, w = v[i].w;
+                    if (p.a_bf16) {
+                        x = bf16x2_to_f16x2(x);
+                        y = bf16x2_to_f16x2(y);
+                        z = bf16x2_to_f16x2(z);
+                        w = bf16x2_to_f16x2(w);
+                    }
+                    // halves: x=(a0,a1) y=(a2,a3) z=(a4,a5) w=(a6,a7)
+                    act[r][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
+                    act[r][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
+                    act[r][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
+                    act[r][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
+                }
+            }
+        }
+    };
+
+    if (p.chunks == 1) load_acts(0);
+
+    int buf = 0;
+    for (int64_t c0 = c_begin; c0 < c_end; c0 += NC) {
+        float acc[NC][M];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < M; ++r) acc[c][r] = 0.f;
+
+        // tile bases: scalar when the column range is wave-uniform
+        const uint8_t* Bt = p.B + c0 * row_bytes;
+        const uint16_t* St = p.scales + c0 * nb;
+        const uint8_t* Zt = p.zp ? p.zp + c0 * zb : nullptr;
+
+        for (int ch = 0; ch < p.chunks; ++ch) {
+            if (p.chunks > 1) load_acts(ch);
+
+            uint4 w[NC][BPL];
+            uint32_t sc[NC][BPL], zq[NC][BPL];
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bool col_ok = c0 + c < c_end;
+#pragma unroll
+                for (int j = 0; j < BPL; ++j) {
+                    const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+                    w[c][j] = make_uint4(0, 0, 0, 0);
+                    sc[c][j] = 0;
+                    zq[c][j] = 0x88;
+                    if (col_ok && b < nb) {
+                        w[c][j] = *reinterpret_cast<const uint4*>(Bt + (c * row_bytes + 16 * b));
+                        sc[c][j] = St[c * nb + b];
+                        if (Zt) zq[c][j] = Zt[c * zb + (b >> 1)];
+                    }
+                }
+            }
+
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+#pragma unroll
+                for (int j = 0; j < BPL; ++j) {
+                    const uint32_t xs[4] = {w[c][j].x, w[c][j].y, w[c][j].z, w[c][j].w};
+                    const uint32_t z = (zq[c][j] >> zshift) & 0xFu;
+                    const uint32_t zz = z | (z << 16);
+                    const uint32_t zneg1 = 0xE400E400u | zz;          // -(1024 + z), both halves
+                    const uint32_t zneg16 = 0xE400E400u | (zz << 4);  // -(1024 + 16z)
+                    float lo[M], hi[M];
+#pragma unroll
+                    for (int r = 0; r < M; ++r) { lo[r] = 0.f; hi[r] = 0.f; }
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const uint32_t x = xs[d];
+                        const uint32_t y = x >> 8;
+                        const uint32_t p0 = nib_minus_zp(x, 0x000F000Fu, magic, zneg1);   // (q0-z, q4-z)
+                        const uint32_t p1 = nib_minus_zp(x, 0x00F000F0u, magic, zneg16);  // 16(q1-z, q5-z)
+                        const uint32_t p2 = nib_minus_zp(y, 0x000F000Fu, magic, zneg1);   // (q2-z, q6-z)
+                        const uint32_t p3 = nib_minus_zp(y, 0x00F000F0u, magic, zneg16);  // 16(q3-z, q7-z)
+#pragma unroll
+                        for (int r = 0; r < M; ++r) {
+                            lo[r] = dot2(act[r][j][4 * d + 0], p0, lo[r]);
+                            hi[r] = dot2(act[r][j][4 * d + 1], p1, hi[r]);
+                            lo[r] = dot2(act[r][j][4 * d + 2], p2, lo[r]);
+                            hi[r] = dot2(act[r][j][4 * d + 3], p3, hi[r]);
+                        }
+                    }
+                    const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[c][j]);
+#pragma unroll
+                    for (int r = 0; r < M; ++r)
+                        acc[c][r] = fmaf(fmaf(hi[r], 0.0625f, lo[r]), sf, acc[c][r]);
+                }
+            }
+        }
+
+        // Split-K reduction inside the wave (fixed DPP tree).
+        const int span = xwave ? 64 : lpc;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int r = 0; r < M; ++r) {
+                if (UNI || span == 64) acc[c][r] = group_sum<64>(acc[c][r]);
+                else if (span == 32) acc[c][r] = group_sum<32>(acc[c][r]);
+                else acc[c][r] = group_sum<16>(acc[c][r]);
+            }
+
+        // Value `idx` (row idx / NC, column idx % NC) out of the registers.
+        auto pick = [&](int idx) {
+            float v = 0.f;
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (idx == i) v = acc[i % NC][i / NC];
+            return v;
+        };
+        auto store = [&](int idx, float v) {
+            const int c = idx % NC, r = idx / NC;
+            const int64_t col = c0 + c;
+            if (col < c_end) {
+                const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
+                uint16_t bits = __builtin_bit_cast(uint16_t, h);
+                if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
+                p.out[(int64_t)r * p.N + col] = bits;
+            }
+        };
+
+        // The totals sit in the last 16-lane row of each group.
+        const int first = (xwave ? 64 : lpc) - 16;
+        const int wl = xwave ? (tid & 63) : lane;
+        if (!xwave) {
+            if (wl >= first)
+                for (int idx = wl - first; idx < NV; idx += 16) store(idx, pick(idx));
+        } else {
+            const int wv = tid >> 6;
+            if (wl >= first)
+                for (int idx = wl - first; idx < NV; idx += 16) red[buf][wv][idx] = pick(idx);
+            __syncthreads();
+            if (tid < NV) {
+                const int nw = lpc >> 6;
+                float v = red[buf][0][tid];
+                for (int i = 1; i < nw; ++i) v += red[buf][i][tid];
+                store(tid, v);
+            }
+            buf ^= 1;
+        }
+    }
+}
+
+typedef void (*KernelFn)(Params);
+
+template <int M, int BPL, int NC>
+constexpr bool kValid = (M * BPL <= 8) && (NC * BPL <= 8) && (NC * M <= 32);
+
+template <int M, int BPL, int NC>
+KernelFn variant_if_valid(bool uni)
+{
+    if constexpr (kValid<M, BPL, NC>)
+        return uni ? mnb_gemv_kernel<M, BPL, NC, true> : mnb_gemv_kernel<M, BPL, NC, false>;
+    else return nullptr;
+}
+
+template <int M, int BPL>
+KernelFn by_nc(int nc, bool uni)
+{
+    switch (nc) {
+    case 1: return variant_if_valid<M, BPL, 1>(uni);
+    case 2: return variant_if_valid<M, BPL, 2>(uni);
+    case 4: return variant_if_valid<M, BPL, 4>(uni);
+    case 8: return variant_if_valid<M, BPL, 8>(uni);
+    }
+    return nullptr;
+}
+
+template <int M>
+KernelFn by_bpl(int bpl, int nc, bool uni)
+{
+    switch (bpl) {
+    case 1: return by_nc<M, 1>(nc, uni);
+    case 2: return by_nc<M, 2>(nc, uni);
+    case 4: return by_nc<M, 4>(nc, uni);
+    case 8: return by_nc<M, 8>(nc, uni);
+    }
+    return nullptr;
+}
+
+KernelFn lookup(int64_t m, const mnb_plan& plan)
+{
+    const int bpl = plan.blocks_per_lane, nc = plan.cols_per_tile;
+    const bool uni = plan.lanes_per_col >= 64;
+    switch (m) {
+    case 1: return by_bpl<1>(bpl, nc, uni);
+    case 2: return by_bpl<2>(bpl, nc, uni);
+    case 3: return by_bpl<3>(bpl, nc, uni);
+    case 4: return by_bpl<4>(bpl, nc, uni);
+    case 5: return by_bpl<5>(bpl, nc, uni);
+    case 6: return by_bpl<6>(bpl, nc, uni);
+    case 7: return by_bpl<7>(bpl, nc, uni);
+    case 8: return by_bpl<8>(bpl, nc, uni);
+    }
+    return nullptr;
+}
+
+}  // namespace
+
+int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
+{
+    KernelFn fn = lookup(a.m, plan);
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    Params p;
+    p.A = static_cast<const uint16_t*>(a.A);
+    p.B = a.B;
+    p.scales = a.scales;
+    p.zp = a.zp;
+    p.out = static_cast<uint16_t*>(a.out);
+    p.N = a.N;
+    p.K = (int32_t)a.K;
+    p.nb = (int32_t)(a.K / 32);
+    p.zb = (p.nb + 1) / 2;
+    p.lpc = plan.lanes_per_col;
+    p.chunks = plan.k_chunks;
+    p.a_bf16 = a.a_bf16;
+    p.out_bf16 = a.out_bf16;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
+                                   dim3((unsigned)plan.workgroups),
+                                   dim3((unsigned)plan.threads_per_wg), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    return (int)e;
+}
+
+int current_device_cus(int* num_cus)
+{
+    static std::mutex mu;
+    static int cache[64] = {0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    std::lock_guard<std::mutex> g(mu);
+    if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+        *num_cus = cache[dev];
+        return 0;
+    }
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev >= 0 && dev < 64) cache[dev] = n;
+    *num_cus = n;
+    return 0;
+}
+
+int workgroups_per_cu(int64_t m, const mnb_plan& plan)
+{
+    KernelFn fn = lookup(m, plan);
+    if (!fn) return 0;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
+                                                     plan.threads_per_wg, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+int kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
+{
+    KernelFn fn = lookup(m, plan);
+    if (!fn) return -1;
+    hipFuncAttributes attr;
+    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
+    if (e != hipSuccess) return (int)e;
+    info->vgprs = attr.numRegs;
+    info->sgprs = 0;
+    info->lds_bytes = (int32_t)attr.sharedSizeBytes;
+    info->max_threads = attr.maxThreadsPerBlock;
+    info->wgs_per_cu = workgroups_per_cu(m, plan);
+    return 0;
+}
+
+}  // namespace mnb

@@ -1,0 +1,36 @@
+// Internal interface between the host front end (mnb_api.cpp, plain C++)
+// and the HIP side (mnb_gemv.hip).  Not installed; not part of the C ABI.
+#pragma once
+
+#include <stdint.h>
+
+#include "mnb.h"
+
+namespace mnb {
+
+struct GemvArgs {
+    const void* A;
+    const uint8_t* B;
+    const uint16_t* scales;
+    const uint8_t* zp;      // may be null: every zero point is 8
+    void* out;
+    int64_t m, K, N;
+    int a_bf16, out_bf16;
+};
+
+// Queue one GEMV launch.  `plan` has passed mnb_plan_check.  Returns the
+// hipError_t of the launch (0 on success).
+int launch_gemv(const GemvArgs& args, const mnb_plan& plan, void* stream);
+
+// Compute units of the current device.  Returns a hipError_t.
+int current_device_cus(int* num_cus);
+
+// Occupancy-limited workgroups per CU for the kernel a plan selects
+// (0 if the query fails).  Cached per (device, variant).
+int workgroups_per_cu(int64_t m, const mnb_plan& plan);
+
+// Code-object facts of the variant.  Returns a hipError_t, or -1 when no
+// variant matches.
+int kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
+
+}  // namespace mnb

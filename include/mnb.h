@@ -1,0 +1,172 @@
+/*
+ * libmnb -- block-wise INT4 MatMulNBits decode GEMV for AMD MI355X (gfx950).
+ *
+ * C ABI.  Plain pointers and sizes only; every pointer marked "device" is a
+ * device address owned by the caller.  No call allocates device memory, and
+ * no call synchronises the stream it is given.
+ *
+ * The operation (onnx-genai pull request "perf(cuda): let the split-K decode
+ * GEMV store bf16 directly", first two paragraphs, and pull request "PORT-1
+ * (offline bias+interleave) -- measured NO-GO on the multicol asymmetric-zp
+ * GEMV", "Why the premise fails here", item 1):
+ *
+ *   y[r][n] = sum_k a[r][k] * (q[n][k] - z[n][k/32]) * s[n][k/32]
+ *
+ * for 0 <= r < m, 0 <= n < N, 0 <= k < K.  Weights q are 4-bit, packed two
+ * per byte along K in blocks of 32; each (column, block) has an fp16 scale s
+ * and a 4-bit zero point z (8 when no zero points are given: the symmetric
+ * "+8 bias" case).  Activations are fp16, or bf16 converted to fp16 (round
+ * to nearest even) for the dot product.  Products are accumulated in fp32,
+ * the sum is rounded once to fp16 (RNE), and for bf16 output that fp16 value
+ * is narrowed to bf16 (RNE) in the same kernel -- the fp32 -> fp16 -> bf16
+ * double rounding of the staged fp16-GEMV-then-cast route, reproduced bit
+ * for bit, with no staging buffer and no second launch.
+ */
+#ifndef MNB_H
+#define MNB_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MNB_ABI_VERSION 1
+
+/* Element types of A and of the output. */
+typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
+
+/* Status codes.  On any code other than MNB_OK nothing was launched, except
+ * MNB_ERR_HIP, which reports that the HIP launch itself failed. */
+typedef enum {
+    MNB_OK = 0,
+    MNB_ERR_NULL = 1,     /* a required pointer is NULL                      */
+    MNB_ERR_SHAPE = 2,    /* K < 0, N < 0, K not a multiple of 32, too large  */
+    MNB_ERR_BLOCK = 3,    /* block != 32                                     */
+    MNB_ERR_DTYPE = 4,    /* a_dtype or out_dtype not MNB_F16 / MNB_BF16      */
+    MNB_ERR_ALIGN = 5,    /* A or Bpacked not 16-byte aligned, scales or out
+                             not 2-byte aligned                              */
+    MNB_ERR_M_RANGE = 6,  /* m < 0 or m > MNB_MAX_M                           */
+    MNB_ERR_HIP = 7,      /* the HIP runtime reported an error; see
+                             mnb_last_hip_error()                            */
+    MNB_ERR_ALIAS = 8,    /* out overlaps an input buffer                    */
+    MNB_ERR_PLAN = 9      /* an explicit plan is not one the library runs   */
+} mnb_status;
+
+/* Row-batched decode bound: one launch serves 1 <= m <= 8 rows (the
+ * small-batch row loop of the first page, paragraph "What broke in #1549"). */
+#define MNB_MAX_M 8
+/* Largest K accepted (blocks are indexed with 32-bit integers). */
+#define MNB_MAX_K (1 << 24)
+
+/*
+ * matmul_nbits -- y = A * dequant(B)^T, one kernel launch on `stream`.
+ *
+ *   A            device, [m][K] row-major, fp16 or bf16 per a_dtype; 16-byte
+ *                aligned.  Must hold finite values that are finite in fp16.
+ *   a_dtype      MNB_F16 or MNB_BF16.
+ *   m            rows, 0 <= m <= 8.  m == 0 or N == 0: nothing to do, MNB_OK.
+ *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).
+ *   N            output columns.
+ *   Bpacked      device, [N][K/2] bytes; byte k/2 of row n holds weight k,
+ *                even k in the low nibble.  16-byte aligned.
+ *   scales       device, [N][K/32] fp16 bit patterns; 2-byte aligned.
+ *   zero_points  device, [N][ceil(K/64)] bytes, block b of row n in byte
+ *                b/2 (even b in the low nibble), or NULL for zero point 8.
+ *   block        must be 32.
+ *   out          device, [m][N] row-major, fp16 or bf16 per out_dtype;
+ *                2-byte aligned; must not overlap any input.  Every one of
+ *                the m*N elements is overwritten (no accumulation), by this
+ *                one launch.
+ *   out_dtype    MNB_F16 (fp32 -> fp16 RNE) or MNB_BF16 (fp32 -> fp16 RNE
+ *                -> bf16 RNE).
+ *   stream       hipStream_t, or NULL for the default stream.
+ *
+ * Asynchronous: returns after the launch is queued.  Inputs must stay valid
+ * and unmodified until the stream reaches this work.  The fp32 summation
+ * order is fixed by (m, K, N) and the device's compute-unit count, so equal
+ * inputs give bitwise equal outputs on the same device, and the bf16 output
+ * equals the fp16 output of the same call narrowed to bf16.
+ * Thread safety: may be called from several host threads at once.
+ */
+int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+                 const uint8_t* Bpacked, const uint16_t* scales,
+                 const uint8_t* zero_points, int block,
+                 void* out, int out_dtype, void* stream);
+
+/*
+ * Launch plan: how the K range of a column is split over lanes and how
+ * columns are tiled.  Every plan that mnb_plan_check() accepts computes the
+ * same function; plans differ only in fp32 summation order and speed.
+ */
+typedef struct {
+    int32_t lanes_per_col;   /* 16, 32, 64 (inside one wave) or 64*W, W=2..8 */
+    int32_t blocks_per_lane; /* 1, 2, 4 or 8; lanes_per_col*blocks_per_lane
+                                blocks of K are covered per chunk            */
+    int32_t cols_per_tile;   /* 1, 2, 4 or 8 columns in flight per lane group */
+    int32_t workgroups;      /* grid size, >= 1                              */
+    int32_t threads_per_wg;  /* 256 for lanes_per_col <= 64, else lanes_per_col */
+    int32_t k_chunks;        /* ceil((K/32) / (lanes_per_col*blocks_per_lane)) */
+} mnb_plan;
+
+/* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`
+ * compute units.  Host-only; touches no device.  Returns a status code. */
+int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus,
+                     mnb_plan* plan);
+
+/* Validate a plan for (m, K, N) and fill its derived fields
+ * (threads_per_wg, k_chunks).  Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */
+int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan);
+
+/* matmul_nbits with an explicit plan (after mnb_plan_check); same arguments,
+ * same contract.  Used by tests that cover every kernel variant and by
+ * tuning sweeps. */
+int matmul_nbits_planned(const void* A, int a_dtype, int64_t m, int64_t K,
+                         int64_t N, const uint8_t* Bpacked,
+                         const uint16_t* scales, const uint8_t* zero_points,
+                         int block, void* out, int out_dtype, void* stream,
+                         const mnb_plan* plan);
+
+/*
+ * Counters, updated atomically by every successful launch.  Tests assert
+ * them so that a silent change of route fails instead of passing (first
+ * page, "Tests" paragraph: the direct-store counter).
+ */
+typedef struct {
+    uint64_t calls;                /* matmul_nbits* calls that returned MNB_OK */
+    uint64_t launches;             /* kernel launches                          */
+    uint64_t elements_f16;         /* outputs stored as fp16                   */
+    uint64_t elements_bf16_direct; /* outputs narrowed and stored as bf16 by the
+                                      GEMV epilogue itself                     */
+    uint64_t row_batched_launches; /* launches that served m > 1 rows at once  */
+} mnb_counters;
+
+void mnb_counters_get(mnb_counters* out);
+void mnb_counters_reset(void);
+
+/* Registers and LDS of the kernel variant a plan selects, read from the
+ * loaded code object (needs a device).  Returns a status code. */
+typedef struct {
+    int32_t vgprs;        /* architected VGPRs per lane   */
+    int32_t sgprs;
+    int32_t lds_bytes;    /* static LDS per workgroup     */
+    int32_t max_threads;  /* launch bound of the variant  */
+    int32_t wgs_per_cu;   /* occupancy: workgroups per CU at threads_per_wg */
+} mnb_kernel_info;
+
+int mnb_get_kernel_info(int64_t m, const mnb_plan* plan, mnb_kernel_info* info);
+
+/* Human-readable text of a status code (static storage). */
+const char* mnb_status_string(int status);
+
+/* The hipError_t of the last MNB_ERR_HIP returned on this host thread. */
+int mnb_last_hip_error(void);
+
+/* MNB_ABI_VERSION of the loaded library. */
+int mnb_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MNB_H */

@@ -1,0 +1,117 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+the header declares, validates arguments before touching the device, and
+plans launches consistently."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_wise_int4_matmulnbits_amd as mnb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mnb.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*"
+                       r"([A-Za-z_][A-Za-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "defined")))
+
+
+def test_header_symbols_exported():
+    names = _declared_functions()
+    assert "matmul_nbits" in names and len(names) >= 10
+    lib = ctypes.CDLL(mnb.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), "libmnb.so does not export %s" % n
+    assert set(mnb.EXPORTS) == set(names)
+
+
+def test_abi_version_matches_header():
+    v = int(re.search(r"#define MNB_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert mnb.mnb_abi_version() == v
+
+
+FAKE = 0x10000  # never dereferenced: validation fails first
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(m=9), 6), (dict(m=-1), 6), (dict(K=33), 2), (dict(K=-32), 2),
+    (dict(N=-1), 2), (dict(block=64), 3), (dict(a_dtype=2), 4),
+    (dict(out_dtype=-1), 4), (dict(A=0), 1), (dict(B=0), 1), (dict(S=0), 1),
+    (dict(out=0), 1), (dict(A=FAKE + 8), 5), (dict(B=FAKE * 3 + 4), 5),
+    (dict(S=FAKE * 5 + 1), 5), (dict(out=FAKE * 7 + 1), 5),
+    (dict(out=FAKE + 64), 8), (dict(K=1 << 25), 2),
+])
+def test_validation_without_gpu(args, status):
+    a = dict(A=FAKE, a_dtype=0, m=1, K=64, N=4, B=FAKE * 3, S=FAKE * 5, Z=None,
+             block=32, out=FAKE * 7, out_dtype=0)
+    a.update(args)
+    c0 = mnb.mnb_counters_get()
+    st = mnb.matmul_nbits_raw(a["A"], a["a_dtype"], a["m"], a["K"], a["N"], a["B"],
+                              a["S"], a["Z"], a["block"], a["out"], a["out_dtype"])
+    assert st == status, mnb.mnb_status_string(st)
+    assert mnb.mnb_counters_get() == c0
+    assert mnb.mnb_status_string(st) != "unknown status"
+
+
+def test_empty_problem_is_ok_without_gpu():
+    c0 = mnb.mnb_counters_get()
+    assert mnb.matmul_nbits_raw(0, 0, 0, 64, 4, 0, 0, 0, 32, 0, 0) == 0
+    assert mnb.matmul_nbits_raw(0, 1, 3, 64, 0, 0, 0, 0, 32, 0, 1) == 0
+    c1 = mnb.mnb_counters_get()
+    assert c1["calls"] == c0["calls"] + 2 and c1["launches"] == c0["launches"]
+
+
+SHAPES = [(m, K, N) for m in range(1, 9)
+          for K in (0, 32, 96, 1024, 4096, 14336, 32 * 611, 65536, 262144)
+          for N in (1, 7, 1024, 4096, 28672, 151936)]
+
+
+def test_default_plans_are_valid_and_cover_k():
+    for m, K, N in SHAPES:
+        for cus in (1, 80, 256, 304):
+            p = mnb.mnb_plan_default(m, K, N, cus)
+            q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
+            assert mnb.mnb_plan_check(m, K, N, q) == 0
+            lpc, bpl, nc = p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile
+            assert lpc * bpl * p.k_chunks >= K // 32
+            assert m * bpl <= 8 and nc * bpl <= 8 and nc * m <= 32
+            assert p.threads_per_wg in (256, lpc) and p.threads_per_wg <= 512
+            gpw = 256 // lpc if lpc <= 64 else 1
+            groups = p.workgroups * gpw
+            assert 1 <= groups <= N + gpw - 1   # no workgroup without columns
+
+
+def test_summation_order_does_not_depend_on_n_or_device():
+    """The lane split (which fixes the fp32 summation order of a column)
+    depends only on (m, K): the same inputs give the same bits for any N
+    and on any compute-unit count."""
+    for m in range(1, 9):
+        for K in (32, 1024, 4096, 14336, 65536):
+            splits = {(p.lanes_per_col, p.blocks_per_lane, p.k_chunks)
+                      for N in (1, 1000, 151936) for cus in (1, 256, 304)
+                      for p in [mnb.mnb_plan_default(m, K, N, cus)]}
+            assert len(splits) == 1, (m, K, splits)
+
+
+@pytest.mark.parametrize("fields", [
+    dict(lanes_per_col=8), dict(lanes_per_col=96), dict(lanes_per_col=576),
+    dict(blocks_per_lane=3), dict(blocks_per_lane=16), dict(cols_per_tile=16),
+    dict(workgroups=0), dict(blocks_per_lane=8, cols_per_tile=2),
+])
+def test_plan_check_rejects(fields):
+    base = dict(lanes_per_col=64, blocks_per_lane=1, cols_per_tile=1, workgroups=1)
+    base.update(fields)
+    p = mnb.mnb_plan(**base)
+    assert mnb.mnb_plan_check(1, 4096, 100, p) == 9
+
+
+def test_plan_check_rows_limit():
+    p = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=4, workgroups=1)
+    assert mnb.mnb_plan_check(4, 4096, 100, p) == 0
+    p = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=4, workgroups=1)
+    assert mnb.mnb_plan_check(5, 4096, 100, p) == 9

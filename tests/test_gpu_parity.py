@@ -1,0 +1,270 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Every test here needs an MI355X; without one it fails rather than skips.
+Inputs are the seeded synthetic workloads (block_wise_int4_matmulnbits_amd
+.workloads); expected values come from the oracle or, for the hand cases,
+from tests/golden/hand_cases.json.
+"""
+import ctypes
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import block_wise_int4_matmulnbits_amd as mnb
+from block_wise_int4_matmulnbits_amd import workloads as W
+from tests import gpu_util as G
+from tests.hand_cases import build_case, load_cases
+
+pytestmark = pytest.mark.gpu
+
+_INPUTS = {}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    G.require_gpu()
+    mnb.lib()
+
+
+def _workload_inputs(name):
+    if name not in _INPUTS:
+        _INPUTS[name] = W.generate_workload(W.WORKLOADS[name])
+    return _INPUTS[name]
+
+
+def run(d, m, out_dtype, plan=None, stream=None):
+    A, B, S, Z = G.to_dev(d, m)
+    out = G.new_out(m, d["N"], out_dtype)
+    c0 = mnb.mnb_counters_get()
+    if plan is None:
+        mnb.matmul_nbits(A, B, S, Z, out, stream=stream)
+    else:
+        mnb.matmul_nbits_planned(A, B, S, Z, out, plan, stream=stream)
+    torch.cuda.synchronize()
+    c1 = mnb.mnb_counters_get()
+    return G.bits(out), {k: c1[k] - c0[k] for k in c0}
+
+
+def oracle_ref(oracle_mod, d, m):
+    return oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"],
+                                   d["scales"], d["zp"], m, d["K"], d["N"])
+
+
+def assert_parity(oracle_mod, d, m, label, plan=None, ref=None):
+    """Check 1 on the fp16 output, check 2 on the bf16 output, counters,
+    and that no output element kept the sentinel."""
+    G.log("[parity] %s m=%d K=%d N=%d plan=%s" % (label, m, d["K"], d["N"],
+                                                   None if plan is None else plan))
+    ref = oracle_ref(oracle_mod, d, m) if ref is None else ref
+    y16, c16 = run(d, m, W.F16, plan)
+    ybf, cbf = run(d, m, W.BF16, plan)
+    assert not np.any(y16 == 0xFFFF) and not np.any(ybf == 0xFFFF), "stale outputs"
+    ok, max_ulps = G.check1(y16, ref, oracle_mod)
+    assert ok.all(), "check 1 failed at %d of %d outputs" % ((~ok).sum(), ok.size)
+    ok2 = G.check2(ybf, y16, oracle_mod)
+    assert ok2.all(), "check 2 failed at %d of %d outputs" % ((~ok2).sum(), ok2.size)
+    n = m * d["N"]
+    assert c16["launches"] == 1 and c16["elements_f16"] == n and c16["elements_bf16_direct"] == 0
+    assert cbf["launches"] == 1 and cbf["elements_bf16_direct"] == n and cbf["elements_f16"] == 0
+    assert c16["row_batched_launches"] == (1 if m > 1 else 0)
+    exact = np.mean(y16 == ref["f16"])
+    G.log("[parity] %s ok: max err %.3f fp16 ulp, %.4f%% bit-equal to the oracle"
+          % (label, max_ulps, 100 * exact))
+    return y16, ybf, max_ulps
+
+
+# --------------------------------------------------------------- hand cases
+CASES = load_cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c["name"] for c in CASES])
+def test_hand_case_on_gpu(case):
+    c = build_case(case)
+    d = dict(A=c["A"], B=c["B"], scales=c["scales"], zp=c["zp"], m=c["m"],
+             K=c["K"], N=c["N"], a_dtype=W.BF16 if c["a_is_bf16"] else W.F16)
+    y16, _ = run(d, c["m"], W.F16)
+    ybf, cnt = run(d, c["m"], W.BF16)
+    assert np.array_equal(y16, c["f16"]), [hex(v) for v in y16.ravel()]
+    assert np.array_equal(ybf, c["bf16"]), [hex(v) for v in ybf.ravel()]
+    assert cnt["elements_bf16_direct"] == c["m"] * c["N"]
+
+
+# ---------------------------------------------------- the workloads, full size
+@pytest.mark.parametrize("name,m", [
+    ("tiny_1k", 1), ("asym_4k", 1), ("gate_up_bf16", 1),
+    ("down_rows_bf16", 2), ("down_rows_bf16", 4), ("down_rows_bf16", 8),
+    ("lm_head", 1),
+])
+def test_workload_parity(oracle_mod, name, m):
+    d = _workload_inputs(name)
+    assert_parity(oracle_mod, d, m, name)
+
+
+def test_down_rows_every_m(oracle_mod):
+    """The row-batched path for every m the down projection can take."""
+    d = _workload_inputs("down_rows_bf16")
+    ref8 = oracle_ref(oracle_mod, d, 8)
+    for m in (1, 3, 5, 6, 7):
+        ref = {k: v[:m] for k, v in ref8.items()}
+        assert_parity(oracle_mod, d, m, "down_rows_bf16", ref=ref)
+
+
+def test_deterministic():
+    for name, m in (("lm_head", 1), ("down_rows_bf16", 8)):
+        d = _workload_inputs(name)
+        a, _ = run(d, m, W.BF16)
+        b, _ = run(d, m, W.BF16)
+        assert np.array_equal(a, b)
+
+
+# --------------------------------------------------------------- metamorphic
+def test_null_zero_points_equal_explicit_eight():
+    d = W.generate(3, 4096, 1000, W.F16, False, 0.002, 0.02, 1.0, 21)
+    y_null, _ = run(d, 3, W.F16)
+    d8 = dict(d, zp=np.full((1000, 64), 0x88, np.uint8))
+    y8, _ = run(d8, 3, W.F16)
+    assert np.array_equal(y_null, y8)
+
+
+def test_scales_times_two():
+    d = W.generate(2, 4096, 2048, W.BF16, True, 0.002, 0.02, 1.0, 22)
+    y1, _ = run(d, 2, W.F16)
+    s2 = (d["scales"].view(np.float16) * np.float16(2)).view(np.uint16)
+    y2, _ = run(dict(d, scales=s2), 2, W.F16)
+    normal = ((y1 & 0x7C00) != 0) & ((y1 & 0x7C00) < 0x7800)
+    assert normal.mean() > 0.99
+    assert np.array_equal(y2[normal], y1[normal] + 0x0400)
+
+
+def test_column_permutation():
+    d = W.generate(1, 4096, 3000, W.F16, True, 0.002, 0.02, 1.0, 23)
+    perm = np.random.default_rng(3).permutation(3000)
+    y1, _ = run(d, 1, W.F16)
+    dp = dict(d, B=d["B"][perm], scales=d["scales"][perm], zp=d["zp"][perm])
+    y2, _ = run(dp, 1, W.F16)
+    assert np.array_equal(y2, y1[:, perm])
+
+
+def test_rows_equal_single_row_calls_under_one_plan():
+    """With the same lane split, row r of an m-row launch is bit-identical to
+    a one-row launch on row r (the row loop and the batched launch agree)."""
+    d = W.generate(8, 14336, 512, W.BF16, True, 0.001, 0.01, 0.5, 24)
+    plan = dict(lanes_per_col=448, blocks_per_lane=1, cols_per_tile=2, workgroups=64)
+    y8, _ = run(d, 8, W.BF16, plan)
+    for r in range(8):
+        dr = dict(d, A=d["A"][r:r + 1])
+        y1, _ = run(dr, 1, W.BF16, plan)
+        assert np.array_equal(y1[0], y8[r])
+
+
+# ------------------------------------------------------- every kernel variant
+def _variants():
+    out = []
+    for m in range(1, 9):
+        for bpl in (1, 2, 4, 8):
+            for nc in (1, 2, 4, 8):
+                if m * bpl <= 8 and nc * bpl <= 8 and nc * m <= 32:
+                    out.append((m, bpl, nc))
+    return out
+
+
+def test_every_variant_ragged(oracle_mod):
+    lpcs = [16, 32, 64, 128, 192, 320, 448, 512]
+    nbs = [1, 37, 130, 611]
+    rng = np.random.default_rng(0)
+    for i, (m, bpl, nc) in enumerate(_variants()):
+        for j in range(2):
+            lpc = lpcs[(2 * i + j) % len(lpcs)]
+            nb = nbs[(i + j) % len(nbs)]
+            K, N = 32 * nb, int(rng.integers(1, 90))
+            d = W.generate(m, K, N, W.BF16 if (i + j) % 2 else W.F16,
+                           (i + j) % 3 != 0, 0.002, 0.02, 1.0, 100 + i)
+            plan = dict(lanes_per_col=lpc, blocks_per_lane=bpl, cols_per_tile=nc,
+                        workgroups=int(rng.integers(1, 6)))
+            assert_parity(oracle_mod, d, m, "variant", plan)
+
+
+# ------------------------------------------------------------ edge shapes
+def test_k_zero_gives_zeros():
+    d = W.generate(2, 0, 40, W.F16, True, 0.002, 0.02, 1.0, 30)
+    d["zp"] = np.zeros((40, 0), np.uint8)
+    y, cnt = run(d, 2, W.BF16)
+    assert np.all(y == 0) and cnt["elements_bf16_direct"] == 80
+
+
+def test_empty_outputs_are_noops():
+    A = torch.zeros((0, 64), dtype=torch.float16, device="cuda")
+    B = torch.zeros((5, 32), dtype=torch.uint8, device="cuda")
+    S = torch.zeros((5, 2), dtype=torch.float16, device="cuda")
+    out = torch.zeros((0, 5), dtype=torch.float16, device="cuda")
+    c0 = mnb.mnb_counters_get()
+    mnb.matmul_nbits(A, B, S, None, out)
+    A1 = torch.zeros((1, 64), dtype=torch.float16, device="cuda")
+    B0 = torch.zeros((0, 32), dtype=torch.uint8, device="cuda")
+    S0 = torch.zeros((0, 2), dtype=torch.float16, device="cuda")
+    out0 = torch.zeros((1, 0), dtype=torch.float16, device="cuda")
+    mnb.matmul_nbits(A1, B0, S0, None, out0)
+    c1 = mnb.mnb_counters_get()
+    assert c1["launches"] == c0["launches"] and c1["calls"] == c0["calls"] + 2
+
+
+@pytest.mark.parametrize("m,K,N", [(1, 32, 1), (8, 32, 3), (1, 96, 257),
+                                   (5, 32 * 129, 65), (8, 65536, 33),
+                                   (1, 262144, 20), (2, 1024, 131071),
+                                   (8, 512, 70000)])   # 16-lane groups holding 32 sums each
+def test_edge_shapes(oracle_mod, m, K, N):
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 1.0, 40 + m)
+    assert_parity(oracle_mod, d, m, "edge")
+
+
+def test_max_rows_and_large_n(oracle_mod):
+    d = W.generate(8, 4096, 151936, W.F16, True, 0.001, 0.01, 1.0, 50)
+    assert_parity(oracle_mod, d, 8, "m8_lm_head_shape")
+
+
+# ------------------------------------------------------------- errors, streams
+def test_errors_do_not_launch():
+    d = W.generate(1, 256, 64, W.F16, True, 0.002, 0.02, 1.0, 60)
+    A, B, S, Z = G.to_dev(d)
+    out = G.new_out(1, 64, W.F16)
+    L = mnb.lib()
+    base = out.data_ptr()
+    c0 = mnb.mnb_counters_get()
+    # A two bytes off its 16-byte alignment
+    Abuf = torch.zeros(256 + 8, dtype=torch.float16, device="cuda")
+    st = L.matmul_nbits(Abuf.data_ptr() + 2, 0, 1, 256, 64, B.data_ptr(), S.data_ptr(),
+                        Z.data_ptr(), 32, base, 0, None)
+    assert st == 5
+    # out overlapping the activations
+    st = L.matmul_nbits(A.data_ptr(), 0, 1, 256, 64, B.data_ptr(), S.data_ptr(),
+                        Z.data_ptr(), 32, A.data_ptr(), 0, None)
+    assert st == 8
+    st = L.matmul_nbits(A.data_ptr(), 0, 9, 256, 64, B.data_ptr(), S.data_ptr(),
+                        Z.data_ptr(), 32, base, 0, None)
+    assert st == 6
+    torch.cuda.synchronize()
+    assert np.all(G.bits(out) == 0xFFFF)
+    assert mnb.mnb_counters_get()["launches"] == c0["launches"]
+
+
+def test_non_default_stream(oracle_mod):
+    d = W.generate(1, 4096, 4096, W.F16, True, 0.002, 0.02, 1.0, 70)
+    s = torch.cuda.Stream()
+    A, B, S, Z = G.to_dev(d)
+    out = G.new_out(1, 4096, W.F16)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        mnb.matmul_nbits(A, B, S, Z, out)
+    s.synchronize()
+    ref = oracle_ref(oracle_mod, d, 1)
+    ok, _ = G.check1(G.bits(out), ref, oracle_mod)
+    assert ok.all()
+
+
+def test_kernel_info():
+    plan = mnb.mnb_plan_default(1, 4096, 151936, 256)
+    info = mnb.mnb_get_kernel_info(1, plan)
+    G.log("[info] lm_head plan %s info %s" % (plan.as_dict(), info))
+    assert 0 < info["vgprs"] <= 512 and info["wgs_per_cu"] >= 1
