@@ -137,7 +137,7 @@ def main():
 
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     plan = mnb.mnb_plan_default(m, w.K, w.N, cus)
-    info = mnb.mnb_get_kernel_info(m, plan)
+    info = mnb.mnb_get_kernel_info(m, w.K, plan)
     log("[bench] plan %s kernel %s rotated copies %d" % (plan.as_dict(), info, R))
 
     for i in range(args.warmup):

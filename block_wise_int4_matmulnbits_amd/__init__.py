@@ -42,6 +42,7 @@ class mnb_plan(ctypes.Structure):
                 ("blocks_per_lane", ctypes.c_int32),
                 ("cols_per_tile", ctypes.c_int32),
                 ("workgroups", ctypes.c_int32),
+                ("interleave", ctypes.c_int32),
                 ("threads_per_wg", ctypes.c_int32),
                 ("k_chunks", ctypes.c_int32)]
 
@@ -105,7 +106,7 @@ def lib():
         L.mnb_counters_reset.restype = None
         L.mnb_counters_reset.argtypes = []
         L.mnb_get_kernel_info.restype = i32
-        L.mnb_get_kernel_info.argtypes = [i64, ctypes.POINTER(mnb_plan),
+        L.mnb_get_kernel_info.argtypes = [i64, i64, ctypes.POINTER(mnb_plan),
                                           ctypes.POINTER(mnb_kernel_info)]
         L.mnb_status_string.restype = ctypes.c_char_p
         L.mnb_status_string.argtypes = [i32]
@@ -228,10 +229,10 @@ def mnb_counters_reset():
     lib().mnb_counters_reset()
 
 
-def mnb_get_kernel_info(m, plan):
+def mnb_get_kernel_info(m, K, plan):
     info = mnb_kernel_info()
     L = lib()
-    _check(L.mnb_get_kernel_info(m, ctypes.byref(plan), ctypes.byref(info)), L)
+    _check(L.mnb_get_kernel_info(m, K, ctypes.byref(plan), ctypes.byref(info)), L)
     return info.as_dict()
 
 

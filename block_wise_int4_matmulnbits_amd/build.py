@@ -15,6 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmnb.so")
+PROBE_LIB = os.path.join(HERE, "libmnb_probe.so")
 ARCH = "gfx950"
 
 HIP_FLAGS = [
@@ -47,6 +48,11 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
           gemv_o, api_o], verbose)
     os.replace(tmp, LIB)
+    # measurement support: read-only HBM streaming probe (bench only)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    _run(["hipcc", "-shared", os.path.join(CSRC, "mnb_probe.hip"), "-o", tmp] + HIP_FLAGS,
+         verbose)
+    os.replace(tmp, PROBE_LIB)
     return LIB
 
 

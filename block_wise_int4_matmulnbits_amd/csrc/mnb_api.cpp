@@ -104,7 +104,7 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         // contiguous range per lane group, so a second wave of workgroups
         // would only lengthen the tail.  The grid size never changes the
         // per-column summation order.
-        const int per_cu = mnb::workgroups_per_cu(m, plan);
+        const int per_cu = mnb::workgroups_per_cu(m, K, plan);
         if (per_cu > 0 && plan.workgroups > (int64_t)per_cu * cus)
             plan.workgroups = per_cu * cus;
     }
@@ -138,7 +138,8 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (!inwave && !xwave) return MNB_ERR_PLAN;
     if (!is_pow2_in(bpl, 1, 8) || m * bpl > 8) return MNB_ERR_PLAN;
     if (!is_pow2_in(nc, 1, 8) || nc * bpl > 8 || nc * m > 32) return MNB_ERR_PLAN;
-    if (plan->workgroups < 1) return MNB_ERR_PLAN;
+    if (plan->workgroups < 1 || (plan->interleave != 0 && plan->interleave != 1))
+        return MNB_ERR_PLAN;
     plan->threads_per_wg = inwave ? 256 : (int32_t)lpc;
     const int64_t nb = K / 32;
     const int64_t chunks = nb == 0 ? 1 : ceil_div(nb, lpc * bpl);
@@ -190,6 +191,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, mnb_plan* pla
     plan->blocks_per_lane = (int32_t)bpl;
     plan->cols_per_tile = (int32_t)nc;
     plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
+    plan->interleave = 0;
     return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
 }
 
@@ -231,13 +233,13 @@ void mnb_counters_reset(void)
     g_rows = 0;
 }
 
-int mnb_get_kernel_info(int64_t m, const mnb_plan* plan, mnb_kernel_info* info)
+int mnb_get_kernel_info(int64_t m, int64_t K, const mnb_plan* plan, mnb_kernel_info* info)
 {
     if (!plan || !info) return MNB_ERR_NULL;
     mnb_plan p = *plan;
     if (p.workgroups < 1) p.workgroups = 1;
-    if (mnb_plan_check(m, 32 * (int64_t)p.lanes_per_col, 1, &p) != MNB_OK) return MNB_ERR_PLAN;
-    int e = mnb::kernel_info(m, p, info);
+    if (mnb_plan_check(m, K, 1, &p) != MNB_OK) return MNB_ERR_PLAN;
+    int e = mnb::kernel_info(m, K, p, info);
     if (e == -1) return MNB_ERR_PLAN;
     if (e != 0) {
         t_last_hip_error = e;

@@ -53,6 +53,20 @@ namespace mnb {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Weights, scales and zero points are read exactly once per call: stream
+// them with nontemporal loads (on gfx950 this raised a read-only probe from
+// 6.4 to 7.1 TB/s).
+#ifndef MNB_NT_LOADS
+#define MNB_NT_LOADS 1
+#endif
+template <typename T>
+__device__ __forceinline__ T stream_load(const T* p)
+{
+    if constexpr (MNB_NT_LOADS) return __builtin_nontemporal_load(p);
+    else return *p;
+}
 
 struct Params {
     const uint16_t* A;       // [m][K]
@@ -65,6 +79,7 @@ struct Params {
     int32_t lpc;             // lanes per column group
     int32_t chunks;          // K chunks of lpc*BPL blocks
     int32_t a_bf16, out_bf16;
+    int32_t interleave;      // tiles dealt round-robin to groups (else ranges)
 };
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t w, float c)
@@ -146,23 +161,42 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Next-tile prefetch (two register buffers) pays where a tile is small;
+// larger tiles already keep enough bytes in flight per wave.  Only for
+// wave-uniform column ranges (scalar addressing keeps the second buffer
+// cheap).
+template <int M, int BPL, int NC, bool UNI>
+constexpr bool kPrefetch = UNI && NC * BPL <= 2 && M <= 2;
+
 // Rough VGPR need of a variant, to ask the compiler for an occupancy it can
 // meet without spilling: activations 16*M*BPL, weights/scales/zero points
-// 6*NC*BPL, sums NC*M (counted thrice: live through reduction and
-// selection), block temporaries 2*M, addressing and constants.
-template <int M, int BPL, int NC>
+// 6*NC*BPL per tile buffer, sums NC*M (counted thrice: live through
+// reduction and selection), block temporaries 2*M, 64-bit per-lane
+// addresses when the column range is not wave-uniform, constants.
+template <int M, int BPL, int NC, bool UNI>
 constexpr int kWavesPerEu()
 {
-    constexpr int est = 16 * M * BPL + 6 * NC * BPL + 3 * NC * M + 2 * M + 28;
-    return est <= 128 ? 4 : est <= 168 ? 3 : est <= 256 ? 2 : 1;
+    constexpr int bufs = kPrefetch<M, BPL, NC, UNI> ? 2 : 1;
+    constexpr int est = 16 * M * BPL + bufs * (8 + (UNI ? 0 : 2)) * NC * BPL +
+                        3 * NC * M + 2 * M + 28 + 16;
+    constexpr int w = 512 / ((est + 7) / 8 * 8);
+    return w > 8 ? 8 : (w < 1 ? 1 : w);
 }
 
-// UNI: lane groups are whole waves (lanes_per_col >= 64), so a group's
-// column range is wave-uniform and tile addresses live in SGPRs.
-template <int M, int BPL, int NC, bool UNI>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<M, BPL, NC>())))
+// Kernel modes.  LANES: groups of 16 or 32 lanes inside a wave.  WAVES:
+// groups of one or more whole waves, so a group's column range is
+// wave-uniform and tile addresses live in SGPRs.  EXACT: WAVES with the K
+// range covered exactly once by lanes_per_col * BPL blocks (no ragged
+// blocks, no K chunks), which drops every per-lane bounds test.
+enum Mode { LANES = 0, WAVES = 1, EXACT = 2 };
+
+template <int M, int BPL, int NC, int MODE>
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(kWavesPerEu<M, BPL, NC, MODE != LANES>())))
 void mnb_gemv_kernel(Params p)
 {
+    constexpr bool UNI = MODE != LANES;
+    constexpr bool EXACT_K = MODE == EXACT;
     constexpr int NV = NC * M;                  // partial sums per lane
     __shared__ float red[2][8][NV];             // multi-wave groups only
 
@@ -174,11 +208,22 @@ void mnb_gemv_kernel(Params p)
     const int gpw = xwave ? 1 : (int)(blockDim.x / lpc);
     const int64_t gg = (int64_t)blockIdx.x * gpw + grp;
     const int64_t TG = (int64_t)gridDim.x * gpw;
-    int64_t c_begin = p.N * gg / TG;
-    int64_t c_end = p.N * (gg + 1) / TG;
+    // Column tiles of this group: a contiguous range of columns, or every
+    // TG-th tile (all groups then sweep the weights as one moving front).
+    int64_t c_first, c_step, c_stop;
+    if (p.interleave) {
+        c_first = gg * NC;
+        c_step = TG * NC;
+        c_stop = p.N;
+    } else {
+        c_first = p.N * gg / TG;
+        c_step = NC;
+        c_stop = p.N * (gg + 1) / TG;
+    }
     if constexpr (UNI) {
-        c_begin = uniform64(c_begin);
-        c_end = uniform64(c_end);
+        c_first = uniform64(c_first);
+        c_step = uniform64(c_step);
+        c_stop = uniform64(c_stop);
     }
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
@@ -191,7 +236,7 @@ void mnb_gemv_kernel(Params p)
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
             const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
-            const bool ok = b < nb;
+            const bool ok = EXACT_K || b < nb;
 #pragma unroll
             for (int r = 0; r < M; ++r) {
                 uint4 v[4];
@@ -223,80 +268,77 @@ void mnb_gemv_kernel(Params p)
         }
     };
 
-    if (p.chunks == 1) load_acts(0);
+    // Registers of one tile: NC columns x BPL blocks of this lane.
+    struct Tile {
+        u32x4 w[NC][BPL];
+        uint32_t sc[NC][BPL], zq[NC][BPL];
+    };
 
-    int buf = 0;
-    for (int64_t c0 = c_begin; c0 < c_end; c0 += NC) {
-        float acc[NC][M];
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int r = 0; r < M; ++r) acc[c][r] = 0.f;
-
-        // tile bases: scalar when the column range is wave-uniform
+    // Queue the loads of columns c0 .. c0+NC-1, K chunk ch.  Tile bases are
+    // scalar when the column range is wave-uniform; per-lane offsets are 32-bit.
+    auto issue = [&](Tile& t, int64_t c0, int ch) {
         const uint8_t* Bt = p.B + c0 * row_bytes;
         const uint16_t* St = p.scales + c0 * nb;
         const uint8_t* Zt = p.zp ? p.zp + c0 * zb : nullptr;
-
-        for (int ch = 0; ch < p.chunks; ++ch) {
-            if (p.chunks > 1) load_acts(ch);
-
-            uint4 w[NC][BPL];
-            uint32_t sc[NC][BPL], zq[NC][BPL];
 #pragma unroll
-            for (int c = 0; c < NC; ++c) {
-                const bool col_ok = c0 + c < c_end;
+        for (int c = 0; c < NC; ++c) {
+            const bool col_ok = c0 + c < c_stop;
 #pragma unroll
-                for (int j = 0; j < BPL; ++j) {
-                    const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
-                    w[c][j] = make_uint4(0, 0, 0, 0);
-                    sc[c][j] = 0;
-                    zq[c][j] = 0x88;
-                    if (col_ok && b < nb) {
-                        w[c][j] = *reinterpret_cast<const uint4*>(Bt + (c * row_bytes + 16 * b));
-                        sc[c][j] = St[c * nb + b];
-                        if (Zt) zq[c][j] = Zt[c * zb + (b >> 1)];
-                    }
-                }
-            }
-
-#pragma unroll
-            for (int c = 0; c < NC; ++c) {
-#pragma unroll
-                for (int j = 0; j < BPL; ++j) {
-                    const uint32_t xs[4] = {w[c][j].x, w[c][j].y, w[c][j].z, w[c][j].w};
-                    const uint32_t z = (zq[c][j] >> zshift) & 0xFu;
-                    const uint32_t zz = z | (z << 16);
-                    const uint32_t zneg1 = 0xE400E400u | zz;          // -(1024 + z), both halves
-                    const uint32_t zneg16 = 0xE400E400u | (zz << 4);  // -(1024 + 16z)
-                    float lo[M], hi[M];
-#pragma unroll
-                    for (int r = 0; r < M; ++r) { lo[r] = 0.f; hi[r] = 0.f; }
-#pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        const uint32_t x = xs[d];
-                        const uint32_t y = x >> 8;
-                        const uint32_t p0 = nib_minus_zp(x, 0x000F000Fu, magic, zneg1);   // (q0-z, q4-z)
-                        const uint32_t p1 = nib_minus_zp(x, 0x00F000F0u, magic, zneg16);  // 16(q1-z, q5-z)
-                        const uint32_t p2 = nib_minus_zp(y, 0x000F000Fu, magic, zneg1);   // (q2-z, q6-z)
-                        const uint32_t p3 = nib_minus_zp(y, 0x00F000F0u, magic, zneg16);  // 16(q3-z, q7-z)
-#pragma unroll
-                        for (int r = 0; r < M; ++r) {
-                            lo[r] = dot2(act[r][j][4 * d + 0], p0, lo[r]);
-                            hi[r] = dot2(act[r][j][4 * d + 1], p1, hi[r]);
-                            lo[r] = dot2(act[r][j][4 * d + 2], p2, lo[r]);
-                            hi[r] = dot2(act[r][j][4 * d + 3], p3, hi[r]);
-                        }
-                    }
-                    const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)sc[c][j]);
-#pragma unroll
-                    for (int r = 0; r < M; ++r)
-                        acc[c][r] = fmaf(fmaf(hi[r], 0.0625f, lo[r]), sf, acc[c][r]);
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+                t.w[c][j] = u32x4{0, 0, 0, 0};
+                t.sc[c][j] = 0;
+                t.zq[c][j] = 0x88;
+                if (col_ok && (EXACT_K || b < nb)) {
+                    t.w[c][j] = stream_load(reinterpret_cast<const u32x4*>(Bt + (c * row_bytes + 16 * b)));
+                    t.sc[c][j] = stream_load(St + (c * nb + b));
+                    if (Zt) t.zq[c][j] = stream_load(Zt + (c * zb + (b >> 1)));
                 }
             }
         }
+    };
 
-        // Split-K reduction inside the wave (fixed DPP tree).
+    // Unpack, subtract zero points, dot with the resident activations, scale.
+    auto compute = [&](const Tile& t, float (&acc)[NC][M]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t xs[4] = {t.w[c][j][0], t.w[c][j][1], t.w[c][j][2], t.w[c][j][3]};
+                const uint32_t z = (t.zq[c][j] >> zshift) & 0xFu;
+                const uint32_t zz = z | (z << 16);
+                const uint32_t zneg1 = 0xE400E400u | zz;          // -(1024 + z), both halves
+                const uint32_t zneg16 = 0xE400E400u | (zz << 4);  // -(1024 + 16z)
+                float lo[M], hi[M];
+#pragma unroll
+                for (int r = 0; r < M; ++r) { lo[r] = 0.f; hi[r] = 0.f; }
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const uint32_t x = xs[d];
+                    const uint32_t y = x >> 8;
+                    const uint32_t p0 = nib_minus_zp(x, 0x000F000Fu, magic, zneg1);   // (q0-z, q4-z)
+                    const uint32_t p1 = nib_minus_zp(x, 0x00F000F0u, magic, zneg16);  // 16(q1-z, q5-z)
+                    const uint32_t p2 = nib_minus_zp(y, 0x000F000Fu, magic, zneg1);   // (q2-z, q6-z)
+                    const uint32_t p3 = nib_minus_zp(y, 0x00F000F0u, magic, zneg16);  // 16(q3-z, q7-z)
+#pragma unroll
+                    for (int r = 0; r < M; ++r) {
+                        lo[r] = dot2(act[r][j][4 * d + 0], p0, lo[r]);
+                        hi[r] = dot2(act[r][j][4 * d + 1], p1, hi[r]);
+                        lo[r] = dot2(act[r][j][4 * d + 2], p2, lo[r]);
+                        hi[r] = dot2(act[r][j][4 * d + 3], p3, hi[r]);
+                    }
+                }
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)t.sc[c][j]);
+#pragma unroll
+                for (int r = 0; r < M; ++r)
+                    acc[c][r] = fmaf(fmaf(hi[r], 0.0625f, lo[r]), sf, acc[c][r]);
+            }
+        }
+    };
+
+    int buf = 0;
+    // Split-K reduction, fp16 rounding, optional bf16 narrowing, store.
+    auto finish = [&](int64_t c0, float (&acc)[NC][M]) {
         const int span = xwave ? 64 : lpc;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -318,7 +360,7 @@ void mnb_gemv_kernel(Params p)
         auto store = [&](int idx, float v) {
             const int c = idx % NC, r = idx / NC;
             const int64_t col = c0 + c;
-            if (col < c_end) {
+            if (col < c_stop) {
                 const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
                 uint16_t bits = __builtin_bit_cast(uint16_t, h);
                 if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
@@ -345,6 +387,53 @@ void mnb_gemv_kernel(Params p)
             }
             buf ^= 1;
         }
+    };
+
+    if (EXACT_K || (p.chunks == 1 && kPrefetch<M, BPL, NC, UNI>)) {
+        // Activations stay resident; with kPrefetch the next tile's loads
+        // are in flight while the current tile is computed (two register
+        // buffers).
+        load_acts(0);
+        if constexpr (!kPrefetch<M, BPL, NC, UNI>) {
+            for (int64_t c0 = c_first; c0 < c_stop; c0 += c_step) {
+                float acc[NC][M] = {};
+                Tile t;
+                issue(t, c0, 0);
+                compute(t, acc);
+                finish(c0, acc);
+            }
+            return;
+        }
+        Tile ta, tb;
+        int64_t c0 = c_first;
+        if (c0 < c_stop) issue(ta, c0, 0);
+        while (c0 < c_stop) {
+            float acc[NC][M] = {};
+            if (c0 + c_step < c_stop) issue(tb, c0 + c_step, 0);
+            compute(ta, acc);
+            finish(c0, acc);
+            c0 += c_step;
+            if (c0 >= c_stop) break;
+            float acc2[NC][M] = {};
+            if (c0 + c_step < c_stop) issue(ta, c0 + c_step, 0);
+            compute(tb, acc2);
+            finish(c0, acc2);
+            c0 += c_step;
+        }
+    } else if constexpr (!EXACT_K) {
+        // One tile at a time; with K longer than one pass of the group the
+        // activations are reloaded per chunk.
+        if (p.chunks == 1) load_acts(0);
+        for (int64_t c0 = c_first; c0 < c_stop; c0 += c_step) {
+            float acc[NC][M] = {};
+            for (int ch = 0; ch < p.chunks; ++ch) {
+                if (p.chunks > 1) load_acts(ch);
+                Tile t;
+                issue(t, c0, ch);
+                compute(t, acc);
+            }
+            finish(c0, acc);
+        }
     }
 }
 
@@ -354,50 +443,62 @@ template <int M, int BPL, int NC>
 constexpr bool kValid = (M * BPL <= 8) && (NC * BPL <= 8) && (NC * M <= 32);
 
 template <int M, int BPL, int NC>
-KernelFn variant_if_valid(bool uni)
+KernelFn variant_if_valid(int mode)
 {
-    if constexpr (kValid<M, BPL, NC>)
-        return uni ? mnb_gemv_kernel<M, BPL, NC, true> : mnb_gemv_kernel<M, BPL, NC, false>;
-    else return nullptr;
+    if constexpr (kValid<M, BPL, NC>) {
+        switch (mode) {
+        case LANES: return mnb_gemv_kernel<M, BPL, NC, LANES>;
+        case WAVES: return mnb_gemv_kernel<M, BPL, NC, WAVES>;
+        case EXACT: return mnb_gemv_kernel<M, BPL, NC, EXACT>;
+        }
+    }
+    return nullptr;
 }
 
 template <int M, int BPL>
-KernelFn by_nc(int nc, bool uni)
+KernelFn by_nc(int nc, int mode)
 {
     switch (nc) {
-    case 1: return variant_if_valid<M, BPL, 1>(uni);
-    case 2: return variant_if_valid<M, BPL, 2>(uni);
-    case 4: return variant_if_valid<M, BPL, 4>(uni);
-    case 8: return variant_if_valid<M, BPL, 8>(uni);
+    case 1: return variant_if_valid<M, BPL, 1>(mode);
+    case 2: return variant_if_valid<M, BPL, 2>(mode);
+    case 4: return variant_if_valid<M, BPL, 4>(mode);
+    case 8: return variant_if_valid<M, BPL, 8>(mode);
     }
     return nullptr;
 }
 
 template <int M>
-KernelFn by_bpl(int bpl, int nc, bool uni)
+KernelFn by_bpl(int bpl, int nc, int mode)
 {
     switch (bpl) {
-    case 1: return by_nc<M, 1>(nc, uni);
-    case 2: return by_nc<M, 2>(nc, uni);
-    case 4: return by_nc<M, 4>(nc, uni);
-    case 8: return by_nc<M, 8>(nc, uni);
+    case 1: return by_nc<M, 1>(nc, mode);
+    case 2: return by_nc<M, 2>(nc, mode);
+    case 4: return by_nc<M, 4>(nc, mode);
+    case 8: return by_nc<M, 8>(nc, mode);
     }
     return nullptr;
 }
 
-KernelFn lookup(int64_t m, const mnb_plan& plan)
+// Mode for a plan: EXACT when lanes_per_col * blocks_per_lane == K/32.
+int mode_of(int64_t K, const mnb_plan& plan)
+{
+    if (plan.lanes_per_col < 64) return LANES;
+    return (int64_t)plan.lanes_per_col * plan.blocks_per_lane == K / 32 ? EXACT : WAVES;
+}
+
+KernelFn lookup(int64_t m, int64_t K, const mnb_plan& plan)
 {
     const int bpl = plan.blocks_per_lane, nc = plan.cols_per_tile;
-    const bool uni = plan.lanes_per_col >= 64;
+    const int mode = mode_of(K, plan);
     switch (m) {
-    case 1: return by_bpl<1>(bpl, nc, uni);
-    case 2: return by_bpl<2>(bpl, nc, uni);
-    case 3: return by_bpl<3>(bpl, nc, uni);
-    case 4: return by_bpl<4>(bpl, nc, uni);
-    case 5: return by_bpl<5>(bpl, nc, uni);
-    case 6: return by_bpl<6>(bpl, nc, uni);
-    case 7: return by_bpl<7>(bpl, nc, uni);
-    case 8: return by_bpl<8>(bpl, nc, uni);
+    case 1: return by_bpl<1>(bpl, nc, mode);
+    case 2: return by_bpl<2>(bpl, nc, mode);
+    case 3: return by_bpl<3>(bpl, nc, mode);
+    case 4: return by_bpl<4>(bpl, nc, mode);
+    case 5: return by_bpl<5>(bpl, nc, mode);
+    case 6: return by_bpl<6>(bpl, nc, mode);
+    case 7: return by_bpl<7>(bpl, nc, mode);
+    case 8: return by_bpl<8>(bpl, nc, mode);
     }
     return nullptr;
 }
@@ -406,7 +507,7 @@ KernelFn lookup(int64_t m, const mnb_plan& plan)
 
 int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    KernelFn fn = lookup(a.m, plan);
+    KernelFn fn = lookup(a.m, a.K, plan);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     Params p;
     p.A = static_cast<const uint16_t*>(a.A);
@@ -422,6 +523,7 @@ int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.chunks = plan.k_chunks;
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
+    p.interleave = plan.interleave;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
                                    dim3((unsigned)plan.workgroups),
@@ -451,9 +553,9 @@ int current_device_cus(int* num_cus)
     return 0;
 }
 
-int workgroups_per_cu(int64_t m, const mnb_plan& plan)
+int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
 {
-    KernelFn fn = lookup(m, plan);
+    KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
@@ -462,9 +564,9 @@ int workgroups_per_cu(int64_t m, const mnb_plan& plan)
     return n;
 }
 
-int kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
+int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
 {
-    KernelFn fn = lookup(m, plan);
+    KernelFn fn = lookup(m, K, plan);
     if (!fn) return -1;
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
@@ -473,7 +575,7 @@ int kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
     info->sgprs = 0;
     info->lds_bytes = (int32_t)attr.sharedSizeBytes;
     info->max_threads = attr.maxThreadsPerBlock;
-    info->wgs_per_cu = workgroups_per_cu(m, plan);
+    info->wgs_per_cu = workgroups_per_cu(m, K, plan);
     return 0;
 }
 

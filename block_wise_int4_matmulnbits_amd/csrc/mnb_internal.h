@@ -27,10 +27,10 @@ int current_device_cus(int* num_cus);
 
 // Occupancy-limited workgroups per CU for the kernel a plan selects
 // (0 if the query fails).  Cached per (device, variant).
-int workgroups_per_cu(int64_t m, const mnb_plan& plan);
+int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan);
 
-// Code-object facts of the variant.  Returns a hipError_t, or -1 when no
+// Code-object facts of the variant (m, K and the plan select it).  Returns a hipError_t, or -1 when no
 // variant matches.
-int kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
+int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info);
 
 }  // namespace mnb

@@ -105,6 +105,9 @@ typedef struct {
                                 blocks of K are covered per chunk            */
     int32_t cols_per_tile;   /* 1, 2, 4 or 8 columns in flight per lane group */
     int32_t workgroups;      /* grid size, >= 1                              */
+    int32_t interleave;      /* 0: each lane group takes one contiguous range
+                                of columns; 1: column tiles are dealt to the
+                                groups round-robin                           */
     int32_t threads_per_wg;  /* 256 for lanes_per_col <= 64, else lanes_per_col */
     int32_t k_chunks;        /* ceil((K/32) / (lanes_per_col*blocks_per_lane)) */
 } mnb_plan;
@@ -144,8 +147,8 @@ typedef struct {
 void mnb_counters_get(mnb_counters* out);
 void mnb_counters_reset(void);
 
-/* Registers and LDS of the kernel variant a plan selects, read from the
- * loaded code object (needs a device).  Returns a status code. */
+/* Registers and LDS of the kernel variant that (m, K, plan) selects, read
+ * from the loaded code object (needs a device).  Returns a status code. */
 typedef struct {
     int32_t vgprs;        /* architected VGPRs per lane   */
     int32_t sgprs;
@@ -154,7 +157,8 @@ typedef struct {
     int32_t wgs_per_cu;   /* occupancy: workgroups per CU at threads_per_wg */
 } mnb_kernel_info;
 
-int mnb_get_kernel_info(int64_t m, const mnb_plan* plan, mnb_kernel_info* info);
+int mnb_get_kernel_info(int64_t m, int64_t K, const mnb_plan* plan,
+                        mnb_kernel_info* info);
 
 /* Human-readable text of a status code (static storage). */
 const char* mnb_status_string(int status);

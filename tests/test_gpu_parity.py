@@ -182,7 +182,7 @@ def test_every_variant_ragged(oracle_mod):
             d = W.generate(m, K, N, W.BF16 if (i + j) % 2 else W.F16,
                            (i + j) % 3 != 0, 0.002, 0.02, 1.0, 100 + i)
             plan = dict(lanes_per_col=lpc, blocks_per_lane=bpl, cols_per_tile=nc,
-                        workgroups=int(rng.integers(1, 6)))
+                        workgroups=int(rng.integers(1, 6)), interleave=(i + j) % 2)
             assert_parity(oracle_mod, d, m, "variant", plan)
 
 
@@ -265,6 +265,6 @@ def test_non_default_stream(oracle_mod):
 
 def test_kernel_info():
     plan = mnb.mnb_plan_default(1, 4096, 151936, 256)
-    info = mnb.mnb_get_kernel_info(1, plan)
+    info = mnb.mnb_get_kernel_info(1, 4096, plan)
     G.log("[info] lm_head plan %s info %s" % (plan.as_dict(), info))
     assert 0 < info["vgprs"] <= 512 and info["wgs_per_cu"] >= 1
