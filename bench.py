@@ -14,7 +14,6 @@ Prints one JSON line.  value = algorithmic bytes per call / time per call
 for the current kernel source (null if the kernel changed since).
 """
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -27,27 +26,23 @@ sys.path.insert(0, ROOT)
 METRIC = "m=1 INT4 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call"
 PEAK_HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
-KERNEL_SRC = os.path.join(ROOT, "block_wise_int4_matmulnbits_amd", "csrc", "mnb_gemv.hip")
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
-
-
-def measured_traffic(workload_name):
-    """HBM bytes per launch from the committed counter runs, if they were
-    taken on the current kernel source and this workload."""
+def measured_traffic(workload_name, m):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source, workload and row count."""
+    from block_wise_int4_matmulnbits_amd import profiling
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_src_sha256_16") != kernel_source_hash() or t.get("workload") != workload_name:
+    if (t.get("kernel_src_sha256_16") != profiling.kernel_source_hash()
+            or t.get("workload") != workload_name or t.get("m") != m):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -136,7 +131,7 @@ def main():
             raise mnb.MnbError(st, L)
 
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
-    plan = mnb.mnb_plan_default(m, w.K, w.N, cus)
+    plan = mnb.plan_for_device(m, w.K, w.N, cus)
     info = mnb.mnb_get_kernel_info(m, w.K, plan)
     log("[bench] plan %s kernel %s rotated copies %d" % (plan.as_dict(), info, R))
 
@@ -193,7 +188,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(w.name),
+            "traffic": measured_traffic(w.name, m),
         },
         "cpu_baseline": None,
     }

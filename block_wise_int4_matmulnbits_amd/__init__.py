@@ -98,7 +98,7 @@ def lib():
         L.matmul_nbits_planned.argtypes = L.matmul_nbits.argtypes + [
             ctypes.POINTER(mnb_plan)]
         L.mnb_plan_default.restype = i32
-        L.mnb_plan_default.argtypes = [i64, i64, i64, i32, ctypes.POINTER(mnb_plan)]
+        L.mnb_plan_default.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(mnb_plan)]
         L.mnb_plan_check.restype = i32
         L.mnb_plan_check.argtypes = [i64, i64, i64, ctypes.POINTER(mnb_plan)]
         L.mnb_counters_get.restype = None
@@ -207,11 +207,19 @@ def matmul_nbits_raw(A_ptr, a_dtype, m, K, N, B_ptr, scales_ptr, zp_ptr, block,
                               block, out_ptr, out_dtype, stream)
 
 
-def mnb_plan_default(m, K, N, num_cus):
+def mnb_plan_default(m, K, N, num_cus, wgs_per_cu=0):
     p = mnb_plan()
     L = lib()
-    _check(L.mnb_plan_default(m, K, N, num_cus, ctypes.byref(p)), L)
+    _check(L.mnb_plan_default(m, K, N, num_cus, wgs_per_cu, ctypes.byref(p)), L)
     return p
+
+
+def plan_for_device(m, K, N, num_cus):
+    """The plan matmul_nbits picks on the current device: the default plan,
+    re-planned with the measured occupancy of the variant it selects."""
+    p = mnb_plan_default(m, K, N, num_cus)
+    occ = mnb_get_kernel_info(m, K, p)["wgs_per_cu"]
+    return mnb_plan_default(m, K, N, num_cus, occ) if occ > 0 else p
 
 
 def mnb_plan_check(m, K, N, plan):

@@ -45,8 +45,8 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn)
     return a0 < b0 + (uintptr_t)bn && b0 < a0 + (uintptr_t)an;
 }
 
-// Target resident waves per CU when sizing the grid; the grid is then
-// clamped to what occupancy allows, so every workgroup is resident at once.
+// Nominal resident waves per CU, used to size the grid when the occupancy of
+// the chosen kernel variant is not known (host-only planning).
 constexpr int kTargetWavesPerCu = 16;
 
 int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
@@ -98,15 +98,15 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
             t_last_hip_error = e;
             return MNB_ERR_HIP;
         }
-        st = mnb_plan_default(m, K, N, cus, &plan);
+        // Plan once with a nominal occupancy to pick the kernel variant, then
+        // again with that variant's measured occupancy for the grid.
+        st = mnb_plan_default(m, K, N, cus, 0, &plan);
         if (st != MNB_OK) return st;
-        // Keep the whole grid resident: columns are split into one
-        // contiguous range per lane group, so a second wave of workgroups
-        // would only lengthen the tail.  The grid size never changes the
-        // per-column summation order.
         const int per_cu = mnb::workgroups_per_cu(m, K, plan);
-        if (per_cu > 0 && plan.workgroups > (int64_t)per_cu * cus)
-            plan.workgroups = per_cu * cus;
+        if (per_cu > 0) {
+            st = mnb_plan_default(m, K, N, cus, per_cu, &plan);
+            if (st != MNB_OK) return st;
+        }
     }
     mnb::GemvArgs args{A, Bpacked, scales, zero_points, out, m, K, N,
                        a_dtype == MNB_BF16, out_dtype == MNB_BF16};
@@ -148,7 +148,8 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     return MNB_OK;
 }
 
-int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, mnb_plan* plan)
+int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_cu,
+                     mnb_plan* plan)
 {
     if (!plan) return MNB_ERR_NULL;
     if (m < 1 || m > MNB_MAX_M) return MNB_ERR_M_RANGE;
@@ -156,42 +157,50 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, mnb_plan* pla
     if (num_cus < 1) num_cus = 1;
     const int64_t nb = K / 32;
     const int64_t bmax = max_blocks_per_lane(m);
-    const int64_t bpl_pref = bmax < 2 ? bmax : 2;
+
+    // 1. Lane split -- a function of (m, K) only, so the fp32 summation order
+    //    of a column never depends on N or on the device (column shards of
+    //    one matrix give the bits of the whole).
+    //    m = 1: two blocks per lane, so a 4096-long K is one wave per column.
+    //    m > 1: one block per lane (activation VGPRs grow with m), whole waves
+    //    per column up to 8, then K chunks.
+    const int64_t bpl_pref = m == 1 ? 2 : 1;
     int64_t lpc, bpl;
     if (ceil_div(nb, bpl_pref) <= 64) {
-        // The whole K range fits one wave at two blocks per lane.
         lpc = pow2_ceil(ceil_div(nb, bpl_pref));
         if (lpc < 16) lpc = 16;
         bpl = pow2_ceil(nb == 0 ? 1 : ceil_div(nb, lpc));
-    } else if (ceil_div(nb, bmax) <= 64) {
-        lpc = 64;
-        bpl = pow2_ceil(ceil_div(nb, 64));
     } else {
-        // Several waves share a column; beyond 8 waves, K is chunked.
-        int64_t need = ceil_div(nb, bmax);
-        lpc = 64 * ceil_div(need, 64);
+        lpc = 64 * ceil_div(ceil_div(nb, bpl_pref), 64);
         if (lpc > 512) lpc = 512;
         bpl = pow2_ceil(ceil_div(nb, lpc));
         if (bpl > bmax) bpl = bmax;
     }
-    int64_t nc_max = 8 / bpl;
-    if (nc_max * m > 32) nc_max = pow2_floor(32 / m);
+
+    // 2. Column tile: two columns per lane group in a wave, fewer rows' worth
+    //    of partial sums for wide multi-wave groups.
+    int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : (m <= 2 ? 4 : 2);
+    while (nc > 1 && (nc * bpl > 8 || nc * m > 32)) nc /= 2;
+
+    // 3. Grid: one resident generation of workgroups; two when every lane
+    //    group would otherwise walk five or more tiles (shorter tail).  Tiles
+    //    are dealt round-robin, so all groups sweep the weights as one front.
     const bool inwave = lpc <= 64;
-    // lane groups resident per CU at the target wave count
-    const int64_t groups_per_cu = inwave ? kTargetWavesPerCu * (64 / lpc)
-                                         : (kTargetWavesPerCu + lpc / 64 - 1) / (lpc / 64);
-    const int64_t target_groups = groups_per_cu * num_cus;
-    int64_t nc = pow2_floor(N / target_groups > 0 ? N / target_groups : 1);
-    if (nc > nc_max) nc = nc_max;
-    int64_t groups = ceil_div(N, nc);
-    if (groups > target_groups) groups = target_groups;
     const int64_t gpw = inwave ? 256 / lpc : 1;
-    const int64_t wgs = ceil_div(groups, gpw);
+    const int64_t waves_per_wg = inwave ? 4 : lpc / 64;
+    const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu
+                                          : (kTargetWavesPerCu + waves_per_wg - 1) / waves_per_wg;
+    const int64_t resident = per_cu * num_cus;
+    const int64_t tiles = ceil_div(N, nc);
+    int64_t wgs = resident;
+    if (inwave && tiles >= 5 * resident * gpw) wgs = 2 * resident;
+    if (wgs > ceil_div(tiles, gpw)) wgs = ceil_div(tiles, gpw);
+
     plan->lanes_per_col = (int32_t)lpc;
     plan->blocks_per_lane = (int32_t)bpl;
     plan->cols_per_tile = (int32_t)nc;
     plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
-    plan->interleave = 0;
+    plan->interleave = 1;
     return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
 }
 

@@ -113,8 +113,11 @@ typedef struct {
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`
- * compute units.  Host-only; touches no device.  Returns a status code. */
-int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus,
+ * compute units where the selected kernel variant keeps `wgs_per_cu`
+ * workgroups resident per CU (0: a nominal estimate).  The lane split
+ * (lanes_per_col, blocks_per_lane, k_chunks) depends on (m, K) only.
+ * Host-only; touches no device.  Returns a status code. */
+int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_cu,
                      mnb_plan* plan);
 
 /* Validate a plan for (m, K, N) and fill its derived fields

@@ -73,8 +73,8 @@ SHAPES = [(m, K, N) for m in range(1, 9)
 
 def test_default_plans_are_valid_and_cover_k():
     for m, K, N in SHAPES:
-        for cus in (1, 80, 256, 304):
-            p = mnb.mnb_plan_default(m, K, N, cus)
+        for cus, occ in ((1, 0), (80, 3), (256, 0), (256, 5), (304, 1)):
+            p = mnb.mnb_plan_default(m, K, N, cus, occ)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
             lpc, bpl, nc = p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile
@@ -94,7 +94,8 @@ def test_summation_order_does_not_depend_on_n_or_device():
         for K in (32, 1024, 4096, 14336, 65536):
             splits = {(p.lanes_per_col, p.blocks_per_lane, p.k_chunks)
                       for N in (1, 1000, 151936) for cus in (1, 256, 304)
-                      for p in [mnb.mnb_plan_default(m, K, N, cus)]}
+                      for occ in (0, 1, 5)
+                      for p in [mnb.mnb_plan_default(m, K, N, cus, occ)]}
             assert len(splits) == 1, (m, K, splits)
 
 
@@ -108,6 +109,19 @@ def test_plan_check_rejects(fields):
     base.update(fields)
     p = mnb.mnb_plan(**base)
     assert mnb.mnb_plan_check(1, 4096, 100, p) == 9
+
+
+def test_default_plan_shapes():
+    """The tuned plan shapes for the measured workloads."""
+    p = mnb.mnb_plan_default(1, 4096, 151936, 256, 5)
+    assert (p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile, p.interleave) == (64, 2, 2, 1)
+    assert p.workgroups == 2 * 5 * 256          # many tiles per group: two generations
+    p = mnb.mnb_plan_default(1, 4096, 28672, 256, 5)
+    assert p.workgroups == 5 * 256              # few tiles per group: one generation
+    for m in (2, 4, 8):
+        p = mnb.mnb_plan_default(m, 14336, 4096, 256, 2)
+        assert (p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (448, 1, 1)
+        assert p.workgroups == 512
 
 
 def test_plan_check_rows_limit():

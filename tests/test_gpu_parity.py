@@ -264,7 +264,7 @@ def test_non_default_stream(oracle_mod):
 
 
 def test_kernel_info():
-    plan = mnb.mnb_plan_default(1, 4096, 151936, 256)
+    plan = mnb.plan_for_device(1, 4096, 151936, 256)
     info = mnb.mnb_get_kernel_info(1, 4096, plan)
     G.log("[info] lm_head plan %s info %s" % (plan.as_dict(), info))
     assert 0 < info["vgprs"] <= 512 and info["wgs_per_cu"] >= 1
