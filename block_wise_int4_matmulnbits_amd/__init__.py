@@ -38,9 +38,12 @@ class MnbError(RuntimeError):
 
 
 class mnb_plan(ctypes.Structure):
-    _fields_ = [("lanes_per_col", ctypes.c_int32),
+    _fields_ = [("engine", ctypes.c_int32),
+                ("lanes_per_col", ctypes.c_int32),
                 ("blocks_per_lane", ctypes.c_int32),
                 ("cols_per_tile", ctypes.c_int32),
+                ("waves_per_wg", ctypes.c_int32),
+                ("chunk_blocks", ctypes.c_int32),
                 ("workgroups", ctypes.c_int32),
                 ("interleave", ctypes.c_int32),
                 ("threads_per_wg", ctypes.c_int32),

@@ -26,13 +26,6 @@ int64_t pow2_ceil(int64_t x)
     return p;
 }
 
-int64_t pow2_floor(int64_t x)
-{
-    int64_t p = 1;
-    while (p * 2 <= x) p <<= 1;
-    return p;
-}
-
 bool is_pow2_in(int64_t x, int64_t lo, int64_t hi)
 {
     return x >= lo && x <= hi && (x & (x - 1)) == 0;
@@ -127,9 +120,26 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
 
 extern "C" {
 
+// LDS for staged activations of the MFMA engine: m * chunk_blocks * 64 bytes.
+constexpr int64_t kMfmaStageBytes = 128 * 1024;
+
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
 {
     if (!plan || m < 1 || m > MNB_MAX_M || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
+    if (plan->workgroups < 1) return MNB_ERR_PLAN;
+    const int64_t nb = K / 32;
+    if (plan->engine == 1) {
+        const int64_t w = plan->waves_per_wg, kcb = plan->chunk_blocks;
+        if (w < 1 || w > 8 || kcb < 4 || kcb % 4 || m * kcb * 64 > kMfmaStageBytes)
+            return MNB_ERR_PLAN;
+        if (plan->cols_per_tile != 16) return MNB_ERR_PLAN;
+        plan->threads_per_wg = (int32_t)(64 * w);
+        const int64_t chunks = nb == 0 ? 1 : ceil_div(nb, kcb);
+        if (chunks > INT32_MAX) return MNB_ERR_PLAN;
+        plan->k_chunks = (int32_t)chunks;
+        return MNB_OK;
+    }
+    if (plan->engine != 0) return MNB_ERR_PLAN;
     const int64_t lpc = plan->lanes_per_col;
     const int64_t bpl = plan->blocks_per_lane;
     const int64_t nc = plan->cols_per_tile;
@@ -138,10 +148,8 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (!inwave && !xwave) return MNB_ERR_PLAN;
     if (!is_pow2_in(bpl, 1, 8) || m * bpl > 8) return MNB_ERR_PLAN;
     if (!is_pow2_in(nc, 1, 8) || nc * bpl > 8 || nc * m > 32) return MNB_ERR_PLAN;
-    if (plan->workgroups < 1 || (plan->interleave != 0 && plan->interleave != 1))
-        return MNB_ERR_PLAN;
+    if (plan->interleave != 0 && plan->interleave != 1) return MNB_ERR_PLAN;
     plan->threads_per_wg = inwave ? 256 : (int32_t)lpc;
-    const int64_t nb = K / 32;
     const int64_t chunks = nb == 0 ? 1 : ceil_div(nb, lpc * bpl);
     if (chunks > INT32_MAX) return MNB_ERR_PLAN;
     plan->k_chunks = (int32_t)chunks;
@@ -196,9 +204,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     if (inwave && tiles >= 5 * resident * gpw) wgs = 2 * resident;
     if (wgs > ceil_div(tiles, gpw)) wgs = ceil_div(tiles, gpw);
 
+    plan->engine = 0;
     plan->lanes_per_col = (int32_t)lpc;
     plan->blocks_per_lane = (int32_t)bpl;
     plan->cols_per_tile = (int32_t)nc;
+    plan->waves_per_wg = 0;
+    plan->chunk_blocks = 0;
     plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
     plan->interleave = 1;
     return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;

@@ -47,26 +47,11 @@
 #include <type_traits>
 
 #include "mnb.h"
+#include "mnb_device.h"
 #include "mnb_internal.h"
 
 namespace mnb {
 namespace {
-
-typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Weights, scales and zero points are read exactly once per call: stream
-// them with nontemporal loads (on gfx950 this raised a read-only probe from
-// 6.4 to 7.1 TB/s).
-#ifndef MNB_NT_LOADS
-#define MNB_NT_LOADS 1
-#endif
-template <typename T>
-__device__ __forceinline__ T stream_load(const T* p)
-{
-    if constexpr (MNB_NT_LOADS) return __builtin_nontemporal_load(p);
-    else return *p;
-}
 
 struct Params {
     const uint16_t* A;       // [m][K]
@@ -81,43 +66,6 @@ struct Params {
     int32_t a_bf16, out_bf16;
     int32_t interleave;      // tiles dealt round-robin to groups (else ranges)
 };
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t w, float c)
-{
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a),
-                                  __builtin_bit_cast(half2_t, w), c, false);
-}
-
-// bf16 bits -> fp16 bits, round to nearest even through the exact fp32 value.
-__device__ __forceinline__ uint32_t bf16_to_f16(uint32_t b)
-{
-    const _Float16 h = (_Float16)__uint_as_float(b << 16);
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v)
-{
-    return bf16_to_f16(v & 0xFFFFu) | (bf16_to_f16(v >> 16) << 16);
-}
-
-// fp16 bits -> bf16 bits: exact widening to fp32, then RNE on the bit
-// pattern; NaN becomes a quiet NaN with its sign.
-__device__ __forceinline__ uint16_t f16_to_bf16(uint16_t h)
-{
-    uint32_t u = __float_as_uint((float)__builtin_bit_cast(_Float16, h));
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// v_and_or_b32 (x & mask) | orv in one VALU op.  gfx9 VOP3 takes no literal
-// constants, so the mask comes from an SGPR and the or-value from a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv)
-{
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));
-    return r;
-}
 
 // Exact fp16 pair q - z (or 16(q - z)) from a masked nibble pair, see above.
 __device__ __forceinline__ uint32_t nib_minus_zp(uint32_t x, uint32_t mask, uint32_t magic,
@@ -165,8 +113,11 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
 // larger tiles already keep enough bytes in flight per wave.  Only for
 // wave-uniform column ranges (scalar addressing keeps the second buffer
 // cheap).
+#ifndef MNB_PREFETCH_TILE
+#define MNB_PREFETCH_TILE 2   // largest NC*BPL that gets a second tile buffer
+#endif
 template <int M, int BPL, int NC, bool UNI>
-constexpr bool kPrefetch = UNI && NC * BPL <= 2 && M <= 2;
+constexpr bool kPrefetch = UNI && NC * BPL <= MNB_PREFETCH_TILE && M <= 2;
 
 // Rough VGPR need of a variant, to ask the compiler for an occupancy it can
 // meet without spilling: activations 16*M*BPL, weights/scales/zero points
@@ -180,6 +131,9 @@ constexpr int kWavesPerEu()
     constexpr int est = 16 * M * BPL + bufs * (8 + (UNI ? 0 : 2)) * NC * BPL +
                         3 * NC * M + 2 * M + 28 + 16;
     constexpr int w = 512 / ((est + 7) / 8 * 8);
+#ifdef MNB_WPE_M1
+    if constexpr (M == 1 && UNI) return MNB_WPE_M1;
+#endif
     return w > 8 ? 8 : (w < 1 ? 1 : w);
 }
 
@@ -507,6 +461,7 @@ KernelFn lookup(int64_t m, int64_t K, const mnb_plan& plan)
 
 int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
+    if (plan.engine == 1) return launch_mfma(a, plan, stream);
     KernelFn fn = lookup(a.m, a.K, plan);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     Params p;
@@ -555,6 +510,7 @@ int current_device_cus(int* num_cus)
 
 int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
 {
+    if (plan.engine == 1) return mfma_workgroups_per_cu(m, plan);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
     int n = 0;
@@ -566,6 +522,7 @@ int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
 
 int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
 {
+    if (plan.engine == 1) return mfma_kernel_info(m, plan, info);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return -1;
     hipFuncAttributes attr;

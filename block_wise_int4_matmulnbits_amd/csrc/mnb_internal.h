@@ -19,8 +19,13 @@ struct GemvArgs {
 };
 
 // Queue one GEMV launch.  `plan` has passed mnb_plan_check.  Returns the
-// hipError_t of the launch (0 on success).
+// hipError_t of the launch (0 on success).  Dispatches on plan.engine.
 int launch_gemv(const GemvArgs& args, const mnb_plan& plan, void* stream);
+
+// The MFMA tile kernel (engine 1), mnb_gemv_mfma.hip.
+int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
+int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
+int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);

@@ -95,21 +95,31 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
                  void* out, int out_dtype, void* stream);
 
 /*
- * Launch plan: how the K range of a column is split over lanes and how
- * columns are tiled.  Every plan that mnb_plan_check() accepts computes the
- * same function; plans differ only in fp32 summation order and speed.
+ * Launch plan.  Every plan that mnb_plan_check() accepts computes the same
+ * function; plans differ only in fp32 summation order and speed.
+ *
+ * engine 0 (lane-split dot2 kernel): a group of lanes_per_col lanes shares a
+ * column; each lane owns blocks_per_lane 32-weight blocks of K per chunk and
+ * keeps their activations in VGPRs; columns are walked cols_per_tile at a
+ * time.  Dot products on v_dot2_f32_f16.
+ * engine 1 (MFMA tile kernel): a wave owns 16 columns; the waves_per_wg
+ * waves of a workgroup split K; activations are staged in LDS,
+ * chunk_blocks blocks of K per pass; dot products on
+ * v_mfma_f32_16x16x32_f16.  For 2 <= m <= 8.
  */
 typedef struct {
-    int32_t lanes_per_col;   /* 16, 32, 64 (inside one wave) or 64*W, W=2..8 */
-    int32_t blocks_per_lane; /* 1, 2, 4 or 8; lanes_per_col*blocks_per_lane
-                                blocks of K are covered per chunk            */
-    int32_t cols_per_tile;   /* 1, 2, 4 or 8 columns in flight per lane group */
-    int32_t workgroups;      /* grid size, >= 1                              */
-    int32_t interleave;      /* 0: each lane group takes one contiguous range
-                                of columns; 1: column tiles are dealt to the
-                                groups round-robin                           */
-    int32_t threads_per_wg;  /* 256 for lanes_per_col <= 64, else lanes_per_col */
-    int32_t k_chunks;        /* ceil((K/32) / (lanes_per_col*blocks_per_lane)) */
+    int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel */
+    int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
+    int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8                          */
+    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16             */
+    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K                 */
+    int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
+    int32_t workgroups;      /* grid size, >= 1                                  */
+    int32_t interleave;      /* engine 0: 0 = each lane group takes one contiguous
+                                range of columns, 1 = column tiles dealt to the
+                                groups round-robin                               */
+    int32_t threads_per_wg;  /* derived by mnb_plan_check                        */
+    int32_t k_chunks;        /* derived: passes over K                           */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`

@@ -186,6 +186,38 @@ def test_every_variant_ragged(oracle_mod):
             assert_parity(oracle_mod, d, m, "variant", plan)
 
 
+def test_mfma_engine_ragged(oracle_mod):
+    """The MFMA tile kernel for every m, ragged K and N, one to eight waves
+    per workgroup, K staged in one or several LDS chunks."""
+    cases = [
+        # m, K, N, waves, chunk_blocks, workgroups
+        (1, 4096, 1000, 4, 128, 7),
+        (2, 32 * 37, 33, 1, 4, 2),
+        (3, 32 * 37, 100, 8, 40, 3),
+        (4, 14336, 257, 8, 256, 5),
+        (5, 1024, 16, 2, 32, 1),
+        (6, 32 * 611, 70, 8, 80, 4),
+        (7, 96, 31, 3, 4, 2),
+        (8, 14336, 300, 8, 128, 9),
+        (8, 4096, 4096, 8, 128, 64),
+    ]
+    for i, (m, K, N, w, kcb, wg) in enumerate(cases):
+        d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i % 3 != 1, 0.002, 0.02, 1.0, 300 + i)
+        plan = dict(engine=1, cols_per_tile=16, waves_per_wg=w, chunk_blocks=kcb, workgroups=wg)
+        assert_parity(oracle_mod, d, m, "mfma", plan)
+
+
+def test_mfma_engine_rows_match_single_row_calls():
+    """Under one MFMA plan, row r of an m-row launch is bit-identical to a
+    one-row launch on row r."""
+    d = W.generate(8, 14336, 200, W.BF16, True, 0.001, 0.01, 0.5, 310)
+    plan = dict(engine=1, cols_per_tile=16, waves_per_wg=8, chunk_blocks=128, workgroups=13)
+    y8, _ = run(d, 8, W.BF16, plan)
+    for r in (0, 3, 7):
+        y1, _ = run(dict(d, A=d["A"][r:r + 1]), 1, W.BF16, plan)
+        assert np.array_equal(y1[0], y8[r])
+
+
 # ------------------------------------------------------------ edge shapes
 def test_k_zero_gives_zeros():
     d = W.generate(2, 0, 40, W.F16, True, 0.002, 0.02, 1.0, 30)
