@@ -190,9 +190,11 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : (m <= 2 ? 4 : 2);
     while (nc > 1 && (nc * bpl > 8 || nc * m > 32)) nc /= 2;
 
-    // 3. Grid: one resident generation of workgroups; two when every lane
-    //    group would otherwise walk five or more tiles (shorter tail).  Tiles
-    //    are dealt round-robin, so all groups sweep the weights as one front.
+    // 3. Grid.  Tiles are dealt round-robin, so all lane groups sweep the
+    //    weights as one front.  In-wave groups: about five tiles per group,
+    //    between half and twice one resident generation of workgroups
+    //    (measured best on the lm_head and gate_up shapes).  Multi-wave
+    //    groups: one resident generation.
     const bool inwave = lpc <= 64;
     const int64_t gpw = inwave ? 256 / lpc : 1;
     const int64_t waves_per_wg = inwave ? 4 : lpc / 64;
@@ -201,7 +203,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     const int64_t resident = per_cu * num_cus;
     const int64_t tiles = ceil_div(N, nc);
     int64_t wgs = resident;
-    if (inwave && tiles >= 5 * resident * gpw) wgs = 2 * resident;
+    if (inwave) {
+        wgs = ceil_div(tiles, 5 * gpw);
+        const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;
+        if (wgs < lo) wgs = lo;
+        if (wgs > 2 * resident) wgs = 2 * resident;
+    }
     if (wgs > ceil_div(tiles, gpw)) wgs = ceil_div(tiles, gpw);
 
     plan->engine = 0;

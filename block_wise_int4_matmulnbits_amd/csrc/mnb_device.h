@@ -60,4 +60,57 @@ __device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t o
     return r;
 }
 
+// Packed fp16 a + b and a * b + c (one rounding each; exact where used).
+__device__ __forceinline__ uint32_t hadd2(uint32_t a, uint32_t b)
+{
+    const half2_t r = __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint32_t hfma2(uint32_t a, uint32_t b, uint32_t c)
+{
+    const half2_t r = __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b) +
+                      __builtin_bit_cast(half2_t, c);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Nibble pairs of one dword x as exact fp16 pairs q - z.  (x & mask) lands in
+// the low mantissa bits of two fp16 numbers of exponent 2^10:
+//   mask 0x000F000F: 1024 + q  ->  + (-(1024 + z))       = q - z
+//   mask 0x00F000F0: 1024 + 16q -> * 1/16 + (-(64 + z))  = q - z
+// zneg1 = -(1024+z) and zfma = -(64+z) in both halves.
+struct ZeroPoint {
+    uint32_t zneg1, zfma;
+};
+
+__device__ __forceinline__ ZeroPoint zero_point_pairs(uint32_t z)
+{
+    const uint32_t zz = z | (z << 16);
+    return ZeroPoint{0xE400E400u | zz, 0xD400D400u | (zz << 4)};
+}
+
+__device__ __forceinline__ void unpack_dword(uint32_t x, ZeroPoint zp, uint32_t (&pr)[4])
+{
+    const uint32_t magic = 0x64006400u;      // fp16 pair (1024, 1024)
+    const uint32_t sixteenth = 0x2C002C00u;  // fp16 pair (1/16, 1/16)
+    const uint32_t y = x >> 8;
+    pr[0] = hadd2(and_or(x, 0x000F000Fu, magic), zp.zneg1);            // (q0-z, q4-z)
+    pr[1] = hfma2(and_or(x, 0x00F000F0u, magic), sixteenth, zp.zfma);  // (q1-z, q5-z)
+    pr[2] = hadd2(and_or(y, 0x000F000Fu, magic), zp.zneg1);            // (q2-z, q6-z)
+    pr[3] = hfma2(and_or(y, 0x00F000F0u, magic), sixteenth, zp.zfma);  // (q3-z, q7-z)
+}
+
+// Raw buffer resources (gfx9 layout: 48-bit base, no stride, num_records
+// bytes, word 3 = 0x00020000).  Loads at offsets >= num_records return 0,
+// which the kernels use for ragged blocks and columns past the end.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr uint32_t kOutOfRange = 0xFFFFFFF0u;
+constexpr int kNontemporal = MNB_NT_LOADS ? 2 : 0;   // cache-policy bits of the load
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint64_t bytes)
+{
+    const int n = bytes >= kOutOfRange ? (int)kOutOfRange : (int)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
 }  // namespace mnb

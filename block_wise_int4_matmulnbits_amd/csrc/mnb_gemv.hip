@@ -67,15 +67,6 @@ struct Params {
     int32_t interleave;      // tiles dealt round-robin to groups (else ranges)
 };
 
-// Exact fp16 pair q - z (or 16(q - z)) from a masked nibble pair, see above.
-__device__ __forceinline__ uint32_t nib_minus_zp(uint32_t x, uint32_t mask, uint32_t magic,
-                                                 uint32_t zneg)
-{
-    const half2_t v = __builtin_bit_cast(half2_t, and_or(x, mask, magic)) +
-                      __builtin_bit_cast(half2_t, zneg);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
 // v + (v of another lane) through a DPP lane permutation; lanes outside
 // ROW_MASK add 0 (they keep `old`).
 template <int CTRL, int ROW_MASK = 0xF>
@@ -182,7 +173,6 @@ void mnb_gemv_kernel(Params p)
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const int zshift = (lane & 1) * 4;          // block parity == lane parity (lpc even)
-    const uint32_t magic = 0x64006400u;         // fp16 pair (1024, 1024)
 
     uint32_t act[M][BPL][16];                   // permuted fp16 pairs
 
@@ -231,61 +221,80 @@ void mnb_gemv_kernel(Params p)
     // Queue the loads of columns c0 .. c0+NC-1, K chunk ch.  Tile bases are
     // scalar when the column range is wave-uniform; per-lane offsets are 32-bit.
     auto issue = [&](Tile& t, int64_t c0, int ch) {
-        const uint8_t* Bt = p.B + c0 * row_bytes;
-        const uint16_t* St = p.scales + c0 * nb;
-        const uint8_t* Zt = p.zp ? p.zp + c0 * zb : nullptr;
+        if constexpr (UNI) {
+            // Buffer resources based at the tile (scalar); per-lane offsets
+            // do not change from tile to tile.  Offsets past a resource's end
+            // (ragged blocks, columns past N) load zeros.
+            const __amdgpu_buffer_rsrc_t rB =
+                make_rsrc(p.B + c0 * row_bytes, (uint64_t)(p.N - c0) * row_bytes);
+            const __amdgpu_buffer_rsrc_t rS =
+                make_rsrc(p.scales + c0 * nb, (uint64_t)(p.N - c0) * nb * 2);
+            const __amdgpu_buffer_rsrc_t rZ =
+                make_rsrc(p.zp ? p.zp + c0 * zb : p.B, p.zp ? (uint64_t)(p.N - c0) * zb : 0);
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const bool col_ok = c0 + c < c_stop;
+            for (int c = 0; c < NC; ++c) {
 #pragma unroll
-            for (int j = 0; j < BPL; ++j) {
-                const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
-                t.w[c][j] = u32x4{0, 0, 0, 0};
-                t.sc[c][j] = 0;
-                t.zq[c][j] = 0x88;
-                if (col_ok && (EXACT_K || b < nb)) {
-                    t.w[c][j] = stream_load(reinterpret_cast<const u32x4*>(Bt + (c * row_bytes + 16 * b)));
-                    t.sc[c][j] = stream_load(St + (c * nb + b));
-                    if (Zt) t.zq[c][j] = stream_load(Zt + (c * zb + (b >> 1)));
+                for (int j = 0; j < BPL; ++j) {
+                    const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+                    const bool ok = EXACT_K || b < nb;
+                    const uint32_t ow = ok ? c * row_bytes + 16 * b : kOutOfRange;
+                    const uint32_t os = ok ? 2 * (c * nb + b) : kOutOfRange;
+                    const uint32_t oz = ok ? c * zb + (b >> 1) : kOutOfRange;
+                    t.w[c][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow, 0, kNontemporal);
+                    t.sc[c][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os, 0, kNontemporal);
+                    t.zq[c][j] = p.zp ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, oz, 0, kNontemporal)
+                                      : 0x88u;
+                }
+            }
+        } else {
+            const uint8_t* Bt = p.B + c0 * row_bytes;
+            const uint16_t* St = p.scales + c0 * nb;
+            const uint8_t* Zt = p.zp ? p.zp + c0 * zb : nullptr;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bool col_ok = c0 + c < c_stop;
+#pragma unroll
+                for (int j = 0; j < BPL; ++j) {
+                    const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+                    t.w[c][j] = u32x4{0, 0, 0, 0};
+                    t.sc[c][j] = 0;
+                    t.zq[c][j] = 0x88;
+                    if (col_ok && b < nb) {
+                        t.w[c][j] = stream_load(reinterpret_cast<const u32x4*>(Bt + (c * row_bytes + 16 * b)));
+                        t.sc[c][j] = stream_load(St + (c * nb + b));
+                        if (Zt) t.zq[c][j] = stream_load(Zt + (c * zb + (b >> 1)));
+                    }
                 }
             }
         }
     };
 
     // Unpack, subtract zero points, dot with the resident activations, scale.
+    // Every pair is an exact q - z, so one fp32 chain per block and row.
     auto compute = [&](const Tile& t, float (&acc)[NC][M]) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const uint32_t xs[4] = {t.w[c][j][0], t.w[c][j][1], t.w[c][j][2], t.w[c][j][3]};
-                const uint32_t z = (t.zq[c][j] >> zshift) & 0xFu;
-                const uint32_t zz = z | (z << 16);
-                const uint32_t zneg1 = 0xE400E400u | zz;          // -(1024 + z), both halves
-                const uint32_t zneg16 = 0xE400E400u | (zz << 4);  // -(1024 + 16z)
-                float lo[M], hi[M];
+                const ZeroPoint zp = zero_point_pairs((t.zq[c][j] >> zshift) & 0xFu);
+                float s[M];
 #pragma unroll
-                for (int r = 0; r < M; ++r) { lo[r] = 0.f; hi[r] = 0.f; }
+                for (int r = 0; r < M; ++r) s[r] = 0.f;
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const uint32_t x = xs[d];
-                    const uint32_t y = x >> 8;
-                    const uint32_t p0 = nib_minus_zp(x, 0x000F000Fu, magic, zneg1);   // (q0-z, q4-z)
-                    const uint32_t p1 = nib_minus_zp(x, 0x00F000F0u, magic, zneg16);  // 16(q1-z, q5-z)
-                    const uint32_t p2 = nib_minus_zp(y, 0x000F000Fu, magic, zneg1);   // (q2-z, q6-z)
-                    const uint32_t p3 = nib_minus_zp(y, 0x00F000F0u, magic, zneg16);  // 16(q3-z, q7-z)
+                    uint32_t pr[4];
+                    unpack_dword(t.w[c][j][d], zp, pr);
 #pragma unroll
                     for (int r = 0; r < M; ++r) {
-                        lo[r] = dot2(act[r][j][4 * d + 0], p0, lo[r]);
-                        hi[r] = dot2(act[r][j][4 * d + 1], p1, hi[r]);
-                        lo[r] = dot2(act[r][j][4 * d + 2], p2, lo[r]);
-                        hi[r] = dot2(act[r][j][4 * d + 3], p3, hi[r]);
+                        s[r] = dot2(act[r][j][4 * d + 0], pr[0], s[r]);
+                        s[r] = dot2(act[r][j][4 * d + 1], pr[1], s[r]);
+                        s[r] = dot2(act[r][j][4 * d + 2], pr[2], s[r]);
+                        s[r] = dot2(act[r][j][4 * d + 3], pr[3], s[r]);
                     }
                 }
                 const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)t.sc[c][j]);
 #pragma unroll
-                for (int r = 0; r < M; ++r)
-                    acc[c][r] = fmaf(fmaf(hi[r], 0.0625f, lo[r]), sf, acc[c][r]);
+                for (int r = 0; r < M; ++r) acc[c][r] = fmaf(s[r], sf, acc[c][r]);
             }
         }
     };
@@ -508,16 +517,49 @@ int current_device_cus(int* num_cus)
     return 0;
 }
 
+namespace {
+
+// Occupancy queries cost microseconds; they depend only on the device and the
+// (kernel, block size, dynamic LDS) triple, so cache them.
+struct OccKey {
+    int dev;
+    const void* fn;
+    int threads;
+    size_t lds;
+};
+
+int cached_occupancy(const void* fn, int threads, size_t lds)
+{
+    static std::mutex mu;
+    static OccKey keys[256];
+    static int vals[256];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    std::lock_guard<std::mutex> g(mu);
+    for (int i = 0; i < used; ++i)
+        if (keys[i].dev == dev && keys[i].fn == fn && keys[i].threads == threads &&
+            keys[i].lds == lds)
+            return vals[i];
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess) return 0;
+    if (used < 256) {
+        keys[used] = OccKey{dev, fn, threads, lds};
+        vals[used++] = n;
+    }
+    return n;
+}
+
+}  // namespace
+
+int occupancy(const void* fn, int threads, size_t lds) { return cached_occupancy(fn, threads, lds); }
+
 int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
 {
     if (plan.engine == 1) return mfma_workgroups_per_cu(m, plan);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
-                                                     plan.threads_per_wg, 0) != hipSuccess)
-        return 0;
-    return n;
+    return cached_occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, 0);
 }
 
 int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)

@@ -71,20 +71,6 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
     r[3] = s23[1];
 }
 
-// Packed fp16 fma: a * b + c on both halves (one rounding; exact here).
-__device__ __forceinline__ uint32_t hfma2(uint32_t a, uint32_t b, uint32_t c)
-{
-    const half2_t r = __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b) +
-                      __builtin_bit_cast(half2_t, c);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
-__device__ __forceinline__ uint32_t hadd2(uint32_t a, uint32_t b)
-{
-    const half2_t r = __builtin_bit_cast(half2_t, a) + __builtin_bit_cast(half2_t, b);
-    return __builtin_bit_cast(uint32_t, r);
-}
-
 // Global loads of one quad for one lane.
 struct Quad {
     u32x4 w;          // 16 bytes: block 4t+g of this lane's column
@@ -105,8 +91,6 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
     const int nb = p.nb, kcb = p.chunk_blocks;
     const int64_t ntiles = (p.N + 15) / 16;
     const uint32_t row_bytes = (uint32_t)p.K / 2;
-    const uint32_t magic = 0x64006400u;      // fp16 pair (1024, 1024)
-    const uint32_t sixteenth = 0x2C002C00u;  // fp16 pair (1/16, 1/16)
 
     // Stage rows 0..M-1, blocks b_lo .. b_lo+nbc-1 of A into LDS, converted
     // to fp16 and permuted to (a0,a4),(a1,a5),(a2,a6),(a3,a7) per 8 k.
@@ -166,16 +150,9 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
         for (int i = 0; i < 4; ++i) {
             uint4 av = make_uint4(0, 0, 0, 0);
             if (j < M && rel + i < nbc) av = a_lds[(j * kcb + rel + i) * 4 + g];
-            const uint32_t z = (q.z >> (4 * i)) & 0xFu;
-            const uint32_t zz = z | (z << 16);
-            const uint32_t zneg1 = 0xE400E400u | zz;         // -(1024 + z)
-            const uint32_t zfma = 0xD400D400u | (zz << 4);   // -(64 + z)
-            const uint32_t x = r[i], y = x >> 8;
-            // (1024+q) - (1024+z) = q - z;  (1024+16q)/16 - (64+z) = q - z
-            const uint32_t b0 = hadd2(and_or(x, 0x000F000Fu, magic), zneg1);
-            const uint32_t b1 = hfma2(and_or(x, 0x00F000F0u, magic), sixteenth, zfma);
-            const uint32_t b2 = hadd2(and_or(y, 0x000F000Fu, magic), zneg1);
-            const uint32_t b3 = hfma2(and_or(y, 0x00F000F0u, magic), sixteenth, zfma);
+            uint32_t bq[4];
+            unpack_dword(r[i], zero_point_pairs((q.z >> (4 * i)) & 0xFu), bq);
+            const uint32_t b0 = bq[0], b1 = bq[1], b2 = bq[2], b3 = bq[3];
             const u32x4 bv = {b0, b1, b2, b3};
             const u32x4 aw = {av.x, av.y, av.z, av.w};
             const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
@@ -295,12 +272,8 @@ int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan)
 {
     MfmaFn fn = lookup_mfma(m);
     if (!fn) return 0;
-    int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, reinterpret_cast<const void*>(fn),
-                                                     plan.threads_per_wg,
-                                                     mfma_lds_bytes(m, plan)) != hipSuccess)
-        return 0;
-    return n;
+    return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg,
+                     mfma_lds_bytes(m, plan));
 }
 
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)

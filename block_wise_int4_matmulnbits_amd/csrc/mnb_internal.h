@@ -2,6 +2,7 @@
 // and the HIP side (mnb_gemv.hip).  Not installed; not part of the C ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 #include "mnb.h"
@@ -30,8 +31,13 @@ int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);
 
+// Occupancy-limited workgroups per CU of kernel `fn` at a block size and
+// dynamic LDS size (0 if the query fails).  Cached per (device, kernel,
+// threads, LDS).
+int occupancy(const void* fn, int threads, size_t lds);
+
 // Occupancy-limited workgroups per CU for the kernel a plan selects
-// (0 if the query fails).  Cached per (device, variant).
+// (0 if the query fails).
 int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan);
 
 // Code-object facts of the variant (m, K and the plan select it).  Returns a hipError_t, or -1 when no

@@ -113,11 +113,11 @@ def test_plan_check_rejects(fields):
 
 def test_default_plan_shapes():
     """The tuned plan shapes for the measured workloads."""
-    p = mnb.mnb_plan_default(1, 4096, 151936, 256, 5)
+    p = mnb.mnb_plan_default(1, 4096, 151936, 256, 6)
     assert (p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile, p.interleave) == (64, 2, 2, 1)
-    assert p.workgroups == 2 * 5 * 256          # many tiles per group: two generations
-    p = mnb.mnb_plan_default(1, 4096, 28672, 256, 5)
-    assert p.workgroups == 5 * 256              # few tiles per group: one generation
+    assert p.workgroups == 2 * 6 * 256          # capped at two resident generations
+    p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
+    assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
     for m in (2, 4, 8):
         p = mnb.mnb_plan_default(m, 14336, 4096, 256, 2)
         assert (p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (448, 1, 1)
