@@ -173,29 +173,43 @@ void mnb_gemv_kernel(Params p)
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const int zshift = (lane & 1) * 4;          // block parity == lane parity (lpc even)
+    const uint32_t zdef = p.zp ? 0u : 8u;       // zero point 8 when none are given
 
     uint32_t act[M][BPL][16];                   // permuted fp16 pairs
+    typedef uint4 RawActs[M][BPL][4];           // activations as loaded
 
-    auto load_acts = [&](int ch) {
+    // This lane's activation blocks of K chunk ch (zeros past K).
+    auto fetch_acts = [&](int ch, RawActs& raw) {
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
             const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
             const bool ok = EXACT_K || b < nb;
 #pragma unroll
             for (int r = 0; r < M; ++r) {
-                uint4 v[4];
                 if (ok) {
                     const uint4* src = reinterpret_cast<const uint4*>(
                         p.A + (int64_t)r * p.K + 32 * (int64_t)b);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = src[i];
+                    for (int i = 0; i < 4; ++i) raw[r][j][i] = src[i];
                 } else {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v[i] = make_uint4(0, 0, 0, 0);
+                    for (int i = 0; i < 4; ++i) raw[r][j][i] = make_uint4(0, 0, 0, 0);
                 }
+            }
+        }
+    };
+
+    // To fp16 (bf16 rounded to nearest even), permuted into the unpack's
+    // pair order.
+    auto place_acts = [&](const RawActs& raw) {
+#pragma unroll
+        for (int j = 0; j < BPL; ++j)
+#pragma unroll
+            for (int r = 0; r < M; ++r)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uint32_t x = v[i].x, y = v[i].y, z = v[i].z, w = v[i].w;
+                    uint32_t x = raw[r][j][i].x, y = raw[r][j][i].y;
+                    uint32_t z = raw[r][j][i].z, w = raw[r][j][i].w;
                     if (p.a_bf16) {
                         x = bf16x2_to_f16x2(x);
                         y = bf16x2_to_f16x2(y);
@@ -208,42 +222,57 @@ void mnb_gemv_kernel(Params p)
                     act[r][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
                     act[r][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
                 }
-            }
-        }
+    };
+
+    auto load_acts = [&](int ch) {
+        RawActs raw;
+        fetch_acts(ch, raw);
+        place_acts(raw);
     };
 
     // Registers of one tile: NC columns x BPL blocks of this lane.
+    // Scales stay 16-bit: the fp16 -> fp32 conversion reads the low half,
+    // so no zero extension (and no wait on the load) is needed at issue.
     struct Tile {
         u32x4 w[NC][BPL];
-        uint32_t sc[NC][BPL], zq[NC][BPL];
+        uint16_t sc[NC][BPL];
+        uint32_t zq[NC][BPL];
     };
 
     // Queue the loads of columns c0 .. c0+NC-1, K chunk ch.  Tile bases are
     // scalar when the column range is wave-uniform; per-lane offsets are 32-bit.
     auto issue = [&](Tile& t, int64_t c0, int ch) {
         if constexpr (UNI) {
-            // Buffer resources based at the tile (scalar); per-lane offsets
-            // do not change from tile to tile.  Offsets past a resource's end
-            // (ragged blocks, columns past N) load zeros.
-            const __amdgpu_buffer_rsrc_t rB =
-                make_rsrc(p.B + c0 * row_bytes, (uint64_t)(p.N - c0) * row_bytes);
-            const __amdgpu_buffer_rsrc_t rS =
-                make_rsrc(p.scales + c0 * nb, (uint64_t)(p.N - c0) * nb * 2);
-            const __amdgpu_buffer_rsrc_t rZ =
-                make_rsrc(p.zp ? p.zp + c0 * zb : p.B, p.zp ? (uint64_t)(p.N - c0) * zb : 0);
+            // One buffer resource per column and array (scalar), covering
+            // exactly that column's row, so the per-lane offsets are the same
+            // for every column and every tile (BPL registers per array).
+            // Offsets past a resource's end (ragged blocks, columns past N,
+            // absent zero points) load zeros without touching memory, so
+            // every load is issued unconditionally and the compiler's wait
+            // counts stay exact across the prefetch loop.
+            uint32_t ow[BPL], os[BPL], oz[BPL];
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
+                const bool ok = EXACT_K || b < nb;
+                ow[j] = ok ? 16 * b : kOutOfRange;
+                os[j] = ok ? 2 * b : kOutOfRange;
+                oz[j] = ok ? (b >> 1) : kOutOfRange;
+            }
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
+                const int64_t col = c0 + c;
+                const bool in = col < p.N;
+                const int64_t cc = in ? col : 0;
+                const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + cc * row_bytes, in ? row_bytes : 0);
+                const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + cc * nb, in ? 2 * nb : 0);
+                const __amdgpu_buffer_rsrc_t rZ =
+                    make_rsrc(p.zp ? p.zp + cc * zb : p.B, in && p.zp ? zb : 0);
 #pragma unroll
                 for (int j = 0; j < BPL; ++j) {
-                    const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
-                    const bool ok = EXACT_K || b < nb;
-                    const uint32_t ow = ok ? c * row_bytes + 16 * b : kOutOfRange;
-                    const uint32_t os = ok ? 2 * (c * nb + b) : kOutOfRange;
-                    const uint32_t oz = ok ? c * zb + (b >> 1) : kOutOfRange;
-                    t.w[c][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow, 0, kNontemporal);
-                    t.sc[c][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os, 0, kNontemporal);
-                    t.zq[c][j] = p.zp ? (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rZ, oz, 0, kNontemporal)
-                                      : 0x88u;
+                    t.w[c][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow[j], 0, kNontemporal);
+                    t.sc[c][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os[j], 0, kNontemporal);
+                    t.zq[c][j] = __builtin_amdgcn_raw_buffer_load_b8(rZ, oz[j], 0, kNontemporal);
                 }
             }
         } else {
@@ -258,7 +287,7 @@ void mnb_gemv_kernel(Params p)
                     const uint32_t b = (uint32_t)((ch * BPL + j) * lpc + lane);
                     t.w[c][j] = u32x4{0, 0, 0, 0};
                     t.sc[c][j] = 0;
-                    t.zq[c][j] = 0x88;
+                    t.zq[c][j] = 0;
                     if (col_ok && b < nb) {
                         t.w[c][j] = stream_load(reinterpret_cast<const u32x4*>(Bt + (c * row_bytes + 16 * b)));
                         t.sc[c][j] = stream_load(St + (c * nb + b));
@@ -276,7 +305,7 @@ void mnb_gemv_kernel(Params p)
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const ZeroPoint zp = zero_point_pairs((t.zq[c][j] >> zshift) & 0xFu);
+                const ZeroPoint zp = zero_point_pairs(((t.zq[c][j] >> zshift) & 0xFu) | zdef);
                 float s[M];
 #pragma unroll
                 for (int r = 0; r < M; ++r) s[r] = 0.f;
@@ -352,40 +381,47 @@ void mnb_gemv_kernel(Params p)
         }
     };
 
-    if (EXACT_K || (p.chunks == 1 && kPrefetch<M, BPL, NC, UNI>)) {
-        // Activations stay resident; with kPrefetch the next tile's loads
-        // are in flight while the current tile is computed (two register
-        // buffers).
-        load_acts(0);
-        if constexpr (!kPrefetch<M, BPL, NC, UNI>) {
-            for (int64_t c0 = c_first; c0 < c_stop; c0 += c_step) {
-                float acc[NC][M] = {};
-                Tile t;
-                issue(t, c0, 0);
-                compute(t, acc);
-                finish(c0, acc);
-            }
-            return;
-        }
+    if (EXACT_K || (UNI && p.chunks == 1)) {
+        // Activations stay resident.  The first tiles' weight loads go out
+        // right behind the activation loads, before the activations are
+        // converted, so the conversion and the activations' own latency
+        // overlap the weights' HBM latency.  With kPrefetch the next tile's
+        // loads are in flight while the current tile is computed (two
+        // register buffers).
         Tile ta, tb;
         int64_t c0 = c_first;
-        if (c0 < c_stop) issue(ta, c0, 0);
-        while (c0 < c_stop) {
-            float acc[NC][M] = {};
-            if (c0 + c_step < c_stop) issue(tb, c0 + c_step, 0);
-            compute(ta, acc);
-            finish(c0, acc);
-            c0 += c_step;
-            if (c0 >= c_stop) break;
-            float acc2[NC][M] = {};
-            if (c0 + c_step < c_stop) issue(ta, c0 + c_step, 0);
-            compute(tb, acc2);
-            finish(c0, acc2);
-            c0 += c_step;
+        RawActs raw;
+        fetch_acts(0, raw);
+        issue(ta, c0, 0);
+        if constexpr (!kPrefetch<M, BPL, NC, UNI>) {
+            place_acts(raw);
+            while (c0 < c_stop) {
+                float acc[NC][M] = {};
+                compute(ta, acc);
+                finish(c0, acc);
+                c0 += c_step;
+                issue(ta, c0, 0);
+            }
+        } else {
+            issue(tb, c0 + c_step, 0);
+            place_acts(raw);
+            while (c0 < c_stop) {
+                float acc[NC][M] = {};
+                compute(ta, acc);
+                finish(c0, acc);
+                c0 += c_step;
+                if (c0 >= c_stop) break;
+                issue(ta, c0 + c_step, 0);
+                float acc2[NC][M] = {};
+                compute(tb, acc2);
+                finish(c0, acc2);
+                c0 += c_step;
+                issue(tb, c0 + c_step, 0);
+            }
         }
     } else if constexpr (!EXACT_K) {
-        // One tile at a time; with K longer than one pass of the group the
-        // activations are reloaded per chunk.
+        // Lane groups inside a wave, or K longer than one pass of the group
+        // (activations then reloaded per chunk): one tile at a time.
         if (p.chunks == 1) load_acts(0);
         for (int64_t c0 = c_first; c0 < c_stop; c0 += c_step) {
             float acc[NC][M] = {};
