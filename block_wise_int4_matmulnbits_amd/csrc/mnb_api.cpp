@@ -95,7 +95,7 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         // again with that variant's measured occupancy for the grid.
         st = mnb_plan_default(m, K, N, cus, 0, &plan);
         if (st != MNB_OK) return st;
-        const int per_cu = mnb::workgroups_per_cu(m, K, plan);
+        const int per_cu = mnb::workgroups_per_cu(m, K, N, plan);
         if (per_cu > 0) {
             st = mnb_plan_default(m, K, N, cus, per_cu, &plan);
             if (st != MNB_OK) return st;
@@ -117,6 +117,29 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
 }
 
 }  // namespace
+
+namespace mnb {
+
+int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap)
+{
+    *tcap = 0;
+    if (plan.engine != 0 || plan.lanes_per_col <= 64) return 0;
+    const int64_t nw = plan.lanes_per_col / 64;
+    const int64_t nv = (int64_t)plan.cols_per_tile * m;
+    const int64_t g = plan.workgroups < 1 ? 1 : plan.workgroups;
+    // Most tiles any group gets: dealt round-robin, or a contiguous range of
+    // at most ceil(N / g) columns.
+    const int64_t tiles = plan.interleave ? ceil_div(N, plan.cols_per_tile * g)
+                                          : ceil_div(ceil_div(N, g), plan.cols_per_tile);
+    const int64_t t = tiles < 1 ? 1 : tiles;
+    if (t * nw * nv * 4 <= kDeferLdsBytes) {
+        *tcap = (int32_t)t;
+        return t * nw * nv * 4;
+    }
+    return 2 * nw * nv * 4;
+}
+
+}  // namespace mnb
 
 extern "C" {
 
@@ -208,6 +231,14 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;
         if (wgs < lo) wgs = lo;
         if (wgs > 2 * resident) wgs = 2 * resident;
+    }
+    if (!inwave) {
+        // Multi-wave groups: enough workgroups that every wave's partial sums
+        // of all of a group's tiles fit the deferred-sum LDS.
+        const int64_t slot = waves_per_wg * nc * m * 4;
+        const int64_t tmax = mnb::kDeferLdsBytes / slot;
+        const int64_t need = ceil_div(tiles, tmax < 1 ? 1 : tmax);
+        if (wgs < need) wgs = need;
     }
     if (wgs > ceil_div(tiles, gpw)) wgs = ceil_div(tiles, gpw);
 

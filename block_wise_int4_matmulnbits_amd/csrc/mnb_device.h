@@ -51,13 +51,16 @@ __device__ __forceinline__ uint16_t f16_to_bf16(uint16_t h)
     return (uint16_t)(u >> 16);
 }
 
-// v_and_or_b32 (x & mask) | orv in one VALU op.  gfx9 VOP3 takes no literal
-// constants, so the mask comes from an SGPR and the or-value from a VGPR.
-__device__ __forceinline__ uint32_t and_or(uint32_t x, uint32_t mask, uint32_t orv)
+// The unpack below relies on v_and_or_b32 ((x & mask) | orv in one VALU op).
+// gfx9 VOP3 takes no literal and at most one SGPR, so the compiler forms it
+// only when orv sits in a VGPR.  A constant built from a runtime zero that
+// the compiler cannot see through (a kernel argument, always 0) stays in a
+// VGPR; no inline assembly is needed, which keeps every instruction visible
+// to the compiler's hazard checks (an MFMA still writing a register that a
+// later instruction reuses).
+__device__ __forceinline__ uint32_t vgpr_constant(uint32_t c, uint32_t zero)
 {
-    uint32_t r;
-    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(mask), "v"(orv));
-    return r;
+    return c | ((uint32_t)threadIdx.x & zero);
 }
 
 // Packed fp16 a + b and a * b + c (one rounding each; exact where used).
@@ -89,15 +92,17 @@ __device__ __forceinline__ ZeroPoint zero_point_pairs(uint32_t z)
     return ZeroPoint{0xE400E400u | zz, 0xD400D400u | (zz << 4)};
 }
 
-__device__ __forceinline__ void unpack_dword(uint32_t x, ZeroPoint zp, uint32_t (&pr)[4])
+// magic: the fp16 pair (1024, 1024), 0x64006400, held in a VGPR (see
+// vgpr_constant).
+__device__ __forceinline__ void unpack_dword(uint32_t x, ZeroPoint zp, uint32_t magic,
+                                             uint32_t (&pr)[4])
 {
-    const uint32_t magic = 0x64006400u;      // fp16 pair (1024, 1024)
     const uint32_t sixteenth = 0x2C002C00u;  // fp16 pair (1/16, 1/16)
     const uint32_t y = x >> 8;
-    pr[0] = hadd2(and_or(x, 0x000F000Fu, magic), zp.zneg1);            // (q0-z, q4-z)
-    pr[1] = hfma2(and_or(x, 0x00F000F0u, magic), sixteenth, zp.zfma);  // (q1-z, q5-z)
-    pr[2] = hadd2(and_or(y, 0x000F000Fu, magic), zp.zneg1);            // (q2-z, q6-z)
-    pr[3] = hfma2(and_or(y, 0x00F000F0u, magic), sixteenth, zp.zfma);  // (q3-z, q7-z)
+    pr[0] = hadd2((x & 0x000F000Fu) | magic, zp.zneg1);            // (q0-z, q4-z)
+    pr[1] = hfma2((x & 0x00F000F0u) | magic, sixteenth, zp.zfma);  // (q1-z, q5-z)
+    pr[2] = hadd2((y & 0x000F000Fu) | magic, zp.zneg1);            // (q2-z, q6-z)
+    pr[3] = hfma2((y & 0x00F000F0u) | magic, sixteenth, zp.zfma);  // (q3-z, q7-z)
 }
 
 // Raw buffer resources (gfx9 layout: 48-bit base, no stride, num_records

@@ -65,6 +65,9 @@ struct Params {
     int32_t chunks;          // K chunks of lpc*BPL blocks
     int32_t a_bf16, out_bf16;
     int32_t interleave;      // tiles dealt round-robin to groups (else ranges)
+    uint32_t zero;           // always 0 (see vgpr_constant)
+    int32_t tcap;            // multi-wave groups: LDS slots for deferred sums
+                             // (0: reduce across waves after every tile)
 };
 
 // v + (v of another lane) through a DPP lane permutation; lanes outside
@@ -100,54 +103,69 @@ __device__ __forceinline__ int64_t uniform64(int64_t v)
     return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Kernel modes.  LANES: groups of 16 or 32 lanes inside a wave.  WAVES:
+// one whole wave per group, so a group's column range is wave-uniform and
+// tile addresses live in SGPRs.  EXACT: WAVES with the K range covered
+// exactly once by lanes_per_col * BPL blocks (no ragged blocks, no K
+// chunks), which drops every per-lane bounds test.  WAVES_X, EXACT_X: the
+// same with a group of 2..8 waves (one workgroup) per column tile, whose
+// partial sums meet in LDS.
+enum Mode { LANES = 0, WAVES = 1, EXACT = 2, WAVES_X = 3, EXACT_X = 4 };
+
+constexpr bool uniform_mode(int mode) { return mode != LANES; }
+constexpr bool multiwave_mode(int mode) { return mode == WAVES_X || mode == EXACT_X; }
+
 // Next-tile prefetch (two register buffers) pays where a tile is small;
 // larger tiles already keep enough bytes in flight per wave.  Only for
 // wave-uniform column ranges (scalar addressing keeps the second buffer
-// cheap).
+// cheap).  Multi-wave groups (few waves per CU, long K) prefetch whenever
+// the second buffer fits a moderate register budget.
 #ifndef MNB_PREFETCH_TILE
-#define MNB_PREFETCH_TILE 2   // largest NC*BPL that gets a second tile buffer
+#define MNB_PREFETCH_TILE 2   // largest NC*BPL of a one-wave group with two tile buffers
 #endif
-template <int M, int BPL, int NC, bool UNI>
-constexpr bool kPrefetch = UNI && NC * BPL <= MNB_PREFETCH_TILE && M <= 2;
+#ifndef MNB_PREFETCH_X_VGPRS
+#define MNB_PREFETCH_X_VGPRS 128
+#endif
+template <int M, int BPL, int NC, int MODE>
+constexpr bool kPrefetch =
+    uniform_mode(MODE) &&
+    (multiwave_mode(MODE) ? 16 * M * BPL + 2 * 6 * NC * BPL <= MNB_PREFETCH_X_VGPRS
+                          : NC * BPL <= MNB_PREFETCH_TILE && M <= 2);
 
 // Rough VGPR need of a variant, to ask the compiler for an occupancy it can
 // meet without spilling: activations 16*M*BPL, weights/scales/zero points
 // 6*NC*BPL per tile buffer, sums NC*M (counted thrice: live through
 // reduction and selection), block temporaries 2*M, 64-bit per-lane
 // addresses when the column range is not wave-uniform, constants.
-template <int M, int BPL, int NC, bool UNI>
+template <int M, int BPL, int NC, int MODE>
 constexpr int kWavesPerEu()
 {
-    constexpr int bufs = kPrefetch<M, BPL, NC, UNI> ? 2 : 1;
-    constexpr int est = 16 * M * BPL + bufs * (8 + (UNI ? 0 : 2)) * NC * BPL +
+    constexpr bool uni = uniform_mode(MODE);
+    constexpr int bufs = kPrefetch<M, BPL, NC, MODE> ? 2 : 1;
+    constexpr int est = 16 * M * BPL + bufs * (8 + (uni ? 0 : 2)) * NC * BPL +
                         3 * NC * M + 2 * M + 28 + 16;
     constexpr int w = 512 / ((est + 7) / 8 * 8);
 #ifdef MNB_WPE_M1
-    if constexpr (M == 1 && UNI) return MNB_WPE_M1;
+    if constexpr (M == 1 && uni) return MNB_WPE_M1;
 #endif
     return w > 8 ? 8 : (w < 1 ? 1 : w);
 }
 
-// Kernel modes.  LANES: groups of 16 or 32 lanes inside a wave.  WAVES:
-// groups of one or more whole waves, so a group's column range is
-// wave-uniform and tile addresses live in SGPRs.  EXACT: WAVES with the K
-// range covered exactly once by lanes_per_col * BPL blocks (no ragged
-// blocks, no K chunks), which drops every per-lane bounds test.
-enum Mode { LANES = 0, WAVES = 1, EXACT = 2 };
-
 template <int M, int BPL, int NC, int MODE>
 __global__ __launch_bounds__(512)
-__attribute__((amdgpu_waves_per_eu(kWavesPerEu<M, BPL, NC, MODE != LANES>())))
+__attribute__((amdgpu_waves_per_eu(kWavesPerEu<M, BPL, NC, MODE>())))
 void mnb_gemv_kernel(Params p)
 {
-    constexpr bool UNI = MODE != LANES;
-    constexpr bool EXACT_K = MODE == EXACT;
+    constexpr bool UNI = uniform_mode(MODE);
+    constexpr bool xwave = multiwave_mode(MODE);
+    constexpr bool EXACT_K = MODE == EXACT || MODE == EXACT_X;
     constexpr int NV = NC * M;                  // partial sums per lane
-    __shared__ float red[2][8][NV];             // multi-wave groups only
+    // Multi-wave groups: per-wave partial sums, [tile][wave][NV] when
+    // deferred to the end of the kernel (tcap slots), else [2][wave][NV].
+    extern __shared__ float part[];
 
     const int tid = threadIdx.x;
     const int lpc = p.lpc;
-    const bool xwave = lpc > 64;
     const int lane = xwave ? tid : (tid & (lpc - 1));
     const int grp = xwave ? 0 : (tid / lpc);
     const int gpw = xwave ? 1 : (int)(blockDim.x / lpc);
@@ -174,6 +192,7 @@ void mnb_gemv_kernel(Params p)
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const int zshift = (lane & 1) * 4;          // block parity == lane parity (lpc even)
     const uint32_t zdef = p.zp ? 0u : 8u;       // zero point 8 when none are given
+    const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
 
     uint32_t act[M][BPL][16];                   // permuted fp16 pairs
     typedef uint4 RawActs[M][BPL][4];           // activations as loaded
@@ -312,7 +331,7 @@ void mnb_gemv_kernel(Params p)
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
                     uint32_t pr[4];
-                    unpack_dword(t.w[c][j][d], zp, pr);
+                    unpack_dword(t.w[c][j][d], zp, magic, pr);
 #pragma unroll
                     for (int r = 0; r < M; ++r) {
                         s[r] = dot2(act[r][j][4 * d + 0], pr[0], s[r]);
@@ -328,9 +347,27 @@ void mnb_gemv_kernel(Params p)
         }
     };
 
+    // fp32 -> fp16 (RNE), optionally -> bf16 (RNE), store value idx (row
+    // idx / NC, column idx % NC) of the tile at c0.
+    auto store = [&](int64_t c0, int idx, float v) {
+        const int c = idx % NC, r = idx / NC;
+        const int64_t col = c0 + c;
+        if (col < c_stop) {
+            const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
+            uint16_t bits = __builtin_bit_cast(uint16_t, h);
+            if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
+            p.out[(int64_t)r * p.N + col] = bits;
+        }
+    };
+
+    const int nw = (int)(blockDim.x >> 6);      // waves of a multi-wave group
+    const int wv = tid >> 6;
     int buf = 0;
-    // Split-K reduction, fp16 rounding, optional bf16 narrowing, store.
-    auto finish = [&](int64_t c0, float (&acc)[NC][M]) {
+    // Split-K reduction of tile k (at c0).  One-wave and in-wave groups: DPP
+    // tree, then store.  Multi-wave groups: each wave's DPP total goes to its
+    // LDS slot; with tcap > 0 the sums over waves wait for the end of the
+    // kernel (no barrier per tile), else they happen after every tile.
+    auto finish = [&](int k, int64_t c0, float (&acc)[NC][M]) {
         const int span = xwave ? 64 : lpc;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
@@ -349,33 +386,26 @@ void mnb_gemv_kernel(Params p)
                 if (idx == i) v = acc[i % NC][i / NC];
             return v;
         };
-        auto store = [&](int idx, float v) {
-            const int c = idx % NC, r = idx / NC;
-            const int64_t col = c0 + c;
-            if (col < c_stop) {
-                const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
-                uint16_t bits = __builtin_bit_cast(uint16_t, h);
-                if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
-                p.out[(int64_t)r * p.N + col] = bits;
-            }
-        };
 
         // The totals sit in the last 16-lane row of each group.
         const int first = (xwave ? 64 : lpc) - 16;
         const int wl = xwave ? (tid & 63) : lane;
-        if (!xwave) {
+        if constexpr (!xwave) {
             if (wl >= first)
-                for (int idx = wl - first; idx < NV; idx += 16) store(idx, pick(idx));
+                for (int idx = wl - first; idx < NV; idx += 16) store(c0, idx, pick(idx));
+        } else if (p.tcap > 0) {
+            if (wl >= first && k < p.tcap)
+                for (int idx = wl - first; idx < NV; idx += 16)
+                    part[(k * nw + wv) * NV + idx] = pick(idx);
         } else {
-            const int wv = tid >> 6;
             if (wl >= first)
-                for (int idx = wl - first; idx < NV; idx += 16) red[buf][wv][idx] = pick(idx);
+                for (int idx = wl - first; idx < NV; idx += 16)
+                    part[(buf * nw + wv) * NV + idx] = pick(idx);
             __syncthreads();
             if (tid < NV) {
-                const int nw = lpc >> 6;
-                float v = red[buf][0][tid];
-                for (int i = 1; i < nw; ++i) v += red[buf][i][tid];
-                store(tid, v);
+                float v = part[(buf * nw) * NV + tid];
+                for (int i = 1; i < nw; ++i) v += part[(buf * nw + i) * NV + tid];
+                store(c0, tid, v);
             }
             buf ^= 1;
         }
@@ -390,15 +420,16 @@ void mnb_gemv_kernel(Params p)
         // register buffers).
         Tile ta, tb;
         int64_t c0 = c_first;
+        int k = 0;
         RawActs raw;
         fetch_acts(0, raw);
         issue(ta, c0, 0);
-        if constexpr (!kPrefetch<M, BPL, NC, UNI>) {
+        if constexpr (!kPrefetch<M, BPL, NC, MODE>) {
             place_acts(raw);
             while (c0 < c_stop) {
                 float acc[NC][M] = {};
                 compute(ta, acc);
-                finish(c0, acc);
+                finish(k++, c0, acc);
                 c0 += c_step;
                 issue(ta, c0, 0);
             }
@@ -408,13 +439,13 @@ void mnb_gemv_kernel(Params p)
             while (c0 < c_stop) {
                 float acc[NC][M] = {};
                 compute(ta, acc);
-                finish(c0, acc);
+                finish(k++, c0, acc);
                 c0 += c_step;
                 if (c0 >= c_stop) break;
                 issue(ta, c0 + c_step, 0);
                 float acc2[NC][M] = {};
                 compute(tb, acc2);
-                finish(c0, acc2);
+                finish(k++, c0, acc2);
                 c0 += c_step;
                 issue(tb, c0 + c_step, 0);
             }
@@ -423,6 +454,7 @@ void mnb_gemv_kernel(Params p)
         // Lane groups inside a wave, or K longer than one pass of the group
         // (activations then reloaded per chunk): one tile at a time.
         if (p.chunks == 1) load_acts(0);
+        int k = 0;
         for (int64_t c0 = c_first; c0 < c_stop; c0 += c_step) {
             float acc[NC][M] = {};
             for (int ch = 0; ch < p.chunks; ++ch) {
@@ -431,7 +463,23 @@ void mnb_gemv_kernel(Params p)
                 issue(t, c0, ch);
                 compute(t, acc);
             }
-            finish(c0, acc);
+            finish(k++, c0, acc);
+        }
+    }
+
+    if constexpr (xwave) {
+        // Deferred sums over the waves of the group, in wave order, for
+        // every tile of the group.
+        if (p.tcap > 0) {
+            __syncthreads();
+            const int64_t tiles = c_first < c_stop ? (c_stop - c_first + c_step - 1) / c_step : 0;
+            const int n = (int)(tiles < p.tcap ? tiles : p.tcap) * NV;
+            for (int e = tid; e < n; e += (int)blockDim.x) {
+                const int k = e / NV, idx = e - k * NV;
+                float v = part[(k * nw) * NV + idx];
+                for (int i = 1; i < nw; ++i) v += part[(k * nw + i) * NV + idx];
+                store(c_first + k * c_step, idx, v);
+            }
         }
     }
 }
@@ -449,6 +497,8 @@ KernelFn variant_if_valid(int mode)
         case LANES: return mnb_gemv_kernel<M, BPL, NC, LANES>;
         case WAVES: return mnb_gemv_kernel<M, BPL, NC, WAVES>;
         case EXACT: return mnb_gemv_kernel<M, BPL, NC, EXACT>;
+        case WAVES_X: return mnb_gemv_kernel<M, BPL, NC, WAVES_X>;
+        case EXACT_X: return mnb_gemv_kernel<M, BPL, NC, EXACT_X>;
         }
     }
     return nullptr;
@@ -478,11 +528,14 @@ KernelFn by_bpl(int bpl, int nc, int mode)
     return nullptr;
 }
 
-// Mode for a plan: EXACT when lanes_per_col * blocks_per_lane == K/32.
+// Mode for a plan: EXACT when lanes_per_col * blocks_per_lane == K/32,
+// multi-wave when a group spans more than one wave.
 int mode_of(int64_t K, const mnb_plan& plan)
 {
     if (plan.lanes_per_col < 64) return LANES;
-    return (int64_t)plan.lanes_per_col * plan.blocks_per_lane == K / 32 ? EXACT : WAVES;
+    const bool exact = (int64_t)plan.lanes_per_col * plan.blocks_per_lane == K / 32;
+    if (plan.lanes_per_col > 64) return exact ? EXACT_X : WAVES_X;
+    return exact ? EXACT : WAVES;
 }
 
 KernelFn lookup(int64_t m, int64_t K, const mnb_plan& plan)
@@ -524,10 +577,12 @@ int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
     p.interleave = plan.interleave;
+    p.zero = 0;
+    const int64_t lds = gemv_lds_bytes(a.m, a.N, plan, &p.tcap);
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
                                    dim3((unsigned)plan.workgroups),
-                                   dim3((unsigned)plan.threads_per_wg), args, 0,
+                                   dim3((unsigned)plan.threads_per_wg), args, (size_t)lds,
                                    static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
     return (int)e;
@@ -590,12 +645,14 @@ int cached_occupancy(const void* fn, int threads, size_t lds)
 
 int occupancy(const void* fn, int threads, size_t lds) { return cached_occupancy(fn, threads, lds); }
 
-int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
+int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 {
     if (plan.engine == 1) return mfma_workgroups_per_cu(m, plan);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
-    return cached_occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, 0);
+    int32_t tcap = 0;
+    const int64_t lds = gemv_lds_bytes(m, N, plan, &tcap);
+    return cached_occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, (size_t)lds);
 }
 
 int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
@@ -608,9 +665,10 @@ int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* inf
     if (e != hipSuccess) return (int)e;
     info->vgprs = attr.numRegs;
     info->sgprs = 0;
-    info->lds_bytes = (int32_t)attr.sharedSizeBytes;
+    int32_t tcap = 0;
+    info->lds_bytes = (int32_t)(attr.sharedSizeBytes + gemv_lds_bytes(m, 1, plan, &tcap));
     info->max_threads = attr.maxThreadsPerBlock;
-    info->wgs_per_cu = workgroups_per_cu(m, K, plan);
+    info->wgs_per_cu = workgroups_per_cu(m, K, 1, plan);
     return 0;
 }
 

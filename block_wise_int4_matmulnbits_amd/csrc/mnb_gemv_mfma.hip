@@ -53,6 +53,7 @@ struct MfmaParams {
     int32_t K, nb, zb;
     int32_t chunk_blocks;    // blocks of K staged in LDS per pass (multiple of 4)
     int32_t chunks;          // passes over K
+    uint32_t zero;           // always 0 (see vgpr_constant)
     int32_t a_bf16, out_bf16;
 };
 
@@ -71,19 +72,29 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
     r[3] = s23[1];
 }
 
-// Global loads of one quad for one lane.
+// Quads of weights in flight per wave: a ring of P register sets, refilled
+// as each is consumed, so a wave keeps P*1 KB of weights (plus scales and
+// zero points) in flight instead of one quad.
+template <bool VEC>
+constexpr int kRing = VEC ? 8 : 4;
+
+// Registers of one quad for one lane.
 struct Quad {
     u32x4 w;          // 16 bytes: block 4t+g of this lane's column
-    uint32_t s[4];    // fp16 scales of blocks 4t..4t+3 of the column
-    uint32_t z;       // zero-point nibbles of blocks 4t..4t+3 (4 x 4 bits)
+    uint32_t s[4];    // fp16 scales of blocks 4t..4t+3 (VEC: two words, s[0..1])
+    uint32_t z[2];    // zero-point bytes 2t, 2t+1 (VEC: one 16-bit word, z[0])
 };
 
-template <int M>
+// VEC: scales of a quad read as one 8-byte load and its zero points as one
+// 2-byte load (K/32 a multiple of 4, scales 8-byte and zero points 2-byte
+// aligned); otherwise one load per scale and per zero-point byte.
+template <int M, bool VEC>
 __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
 {
     constexpr int RR = M < 4 ? M : 4;       // result rows 4g .. 4g+RR-1 per lane
+    constexpr int P = kRing<VEC>;
     __shared__ float red[8][RR][64];        // per-wave partial tiles
-    extern __shared__ uint4 a_lds[];        // [M][chunk_blocks][4] permuted fp16 A
+    extern __shared__ uint4 a_lds[];        // [chunk_blocks][M][4] permuted fp16 A
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6, W = (int)(blockDim.x >> 6);
@@ -91,83 +102,130 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
     const int nb = p.nb, kcb = p.chunk_blocks;
     const int64_t ntiles = (p.N + 15) / 16;
     const uint32_t row_bytes = (uint32_t)p.K / 2;
+    const uint32_t zdef = p.zp ? 0u : 8u;   // zero point 8 when none are given
+    const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
 
     // Stage rows 0..M-1, blocks b_lo .. b_lo+nbc-1 of A into LDS, converted
     // to fp16 and permuted to (a0,a4),(a1,a5),(a2,a6),(a3,a7) per 8 k.
+    // Eight 16-byte loads per thread go out before any is converted.
     auto stage = [&](int b_lo, int nbc) {
-        const int per_row = nbc * 4;
-        const int n16 = M * per_row;
-        for (int u = tid; u < n16; u += (int)blockDim.x) {
-            const int r = u / per_row;
-            const int rem = u - r * per_row;
-            const int b = rem >> 2, gg = rem & 3;
-            const uint4 v = *reinterpret_cast<const uint4*>(
-                p.A + (int64_t)r * p.K + 32 * (int64_t)(b_lo + b) + 8 * gg);
-            uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
-            if (p.a_bf16) {
-                x = bf16x2_to_f16x2(x);
-                y = bf16x2_to_f16x2(y);
-                z = bf16x2_to_f16x2(z);
-                w = bf16x2_to_f16x2(w);
+        constexpr int U = 8;
+        const int n16 = M * nbc * 4;
+        const int step = (int)blockDim.x;
+        for (int u0 = tid; u0 < n16; u0 += U * step) {
+            uint4 v[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int u = u0 + i * step;
+                v[i] = make_uint4(0, 0, 0, 0);
+                if (u < n16) {
+                    const int b = u / (4 * M);
+                    const int r = (u >> 2) - b * M, gg = u & 3;
+                    v[i] = *reinterpret_cast<const uint4*>(
+                        p.A + (int64_t)r * p.K + 32 * (int64_t)(b_lo + b) + 8 * gg);
+                }
             }
-            uint4 o;
-            o.x = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
-            o.y = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
-            o.z = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
-            o.w = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
-            a_lds[(r * kcb + b) * 4 + gg] = o;
+#pragma unroll
+            for (int i = 0; i < U; ++i) {
+                const int u = u0 + i * step;
+                if (u >= n16) break;
+                uint32_t x = v[i].x, y = v[i].y, z = v[i].z, w = v[i].w;
+                if (p.a_bf16) {
+                    x = bf16x2_to_f16x2(x);
+                    y = bf16x2_to_f16x2(y);
+                    z = bf16x2_to_f16x2(z);
+                    w = bf16x2_to_f16x2(w);
+                }
+                uint4 o;
+                o.x = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
+                o.y = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
+                o.z = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
+                o.w = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
+                a_lds[u] = o;                          // [b][r][gg]
+            }
         }
+        // Zeros after a ragged last block, up to the quad boundary, so the
+        // unconditional operand reads of the last quad stay finite.
+        const int tail = ((nbc + 3) & ~3) * M * 4;
+        for (int u = n16 + tid; u < tail; u += step) a_lds[u] = make_uint4(0, 0, 0, 0);
     };
 
-    // Queue the loads of the quad that starts at global block blk0.
-    auto issue = [&](Quad& q, int64_t col, bool col_ok, int blk0) {
-        q.w = u32x4{0, 0, 0, 0};
-        q.s[0] = q.s[1] = q.s[2] = q.s[3] = 0;
-        q.z = 0x8888u;
-        if (!col_ok) return;
-        const int bw = blk0 + g;
-        if (bw < nb)
-            q.w = stream_load(reinterpret_cast<const u32x4*>(p.B + col * row_bytes + 16 * (uint32_t)bw));
-        const uint16_t* srow = p.scales + col * nb;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (blk0 + i < nb) q.s[i] = stream_load(srow + blk0 + i);
-        if (p.zp) {
-            const uint8_t* zrow = p.zp + col * p.zb;
-            const int zi = blk0 >> 1;
-            uint32_t z0 = stream_load(zrow + zi);
-            uint32_t z1 = zi + 1 < p.zb ? (uint32_t)stream_load(zrow + zi + 1) : 0x88u;
-            q.z = z0 | (z1 << 8);
-        }
-    };
-
-    // Unpack, MFMA and scale the four blocks of a quad.  rel = quad start
-    // relative to the staged chunk, nbc = blocks in the chunk.
-    auto compute = [&](const Quad& q, int rel, int nbc, float (&acc)[RR]) {
-        uint32_t r[4] = {q.w[0], q.w[1], q.w[2], q.w[3]};
-        transpose_rows(r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint4 av = make_uint4(0, 0, 0, 0);
-            if (j < M && rel + i < nbc) av = a_lds[(j * kcb + rel + i) * 4 + g];
-            uint32_t bq[4];
-            unpack_dword(r[i], zero_point_pairs((q.z >> (4 * i)) & 0xFu), bq);
-            const uint32_t b0 = bq[0], b1 = bq[1], b2 = bq[2], b3 = bq[3];
-            const u32x4 bv = {b0, b1, b2, b3};
-            const u32x4 aw = {av.x, av.y, av.z, av.w};
-            const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                __builtin_bit_cast(half8_t, aw), __builtin_bit_cast(half8_t, bv),
-                float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)q.s[i]);
-#pragma unroll
-            for (int rr = 0; rr < RR; ++rr) acc[rr] = fmaf(d[rr], sf, acc[rr]);
-        }
-    };
-
-    bool staged = false;
     for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const int64_t col = tile * 16 + j;
+        const int64_t col0 = tile * 16;
+        const int64_t col = col0 + j;
         const bool col_ok = col < p.N;
+        const uint32_t ncols = (uint32_t)(p.N - col0 < 16 ? p.N - col0 : 16);
+        // Buffer resources over the tile's 16 column rows; loads past their
+        // end (columns past N, blocks past K, quads past this wave's range,
+        // absent zero points) return zeros without touching memory, so every
+        // load is issued unconditionally and the wait counts stay exact.
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + col0 * row_bytes, (uint64_t)ncols * row_bytes);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + col0 * nb, (uint64_t)ncols * nb * 2);
+        const __amdgpu_buffer_rsrc_t rZ =
+            make_rsrc(p.zp ? p.zp + col0 * p.zb : p.B, p.zp ? (uint64_t)ncols * p.zb : 0);
+        const uint32_t wbase = (uint32_t)j * row_bytes + 16 * (uint32_t)g;
+        const uint32_t sbase = (uint32_t)j * (uint32_t)nb * 2;
+        const uint32_t zbase = (uint32_t)j * (uint32_t)p.zb;
+
+        // Queue the loads of quad t (blocks 4t..4t+3 of K) if `live`.
+        auto issue = [&](Quad& q, int t, bool live) {
+            const uint32_t b = 4 * (uint32_t)t;
+            q.w = __builtin_amdgcn_raw_buffer_load_b128(
+                rB, live && b + g < (uint32_t)nb ? wbase + 16 * b : kOutOfRange, 0, kNontemporal);
+            if constexpr (VEC) {
+                const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(
+                    rS, live ? sbase + 2 * b : kOutOfRange, 0, kNontemporal);
+                q.s[0] = sv[0];
+                q.s[1] = sv[1];
+                q.z[0] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rZ, live ? zbase + b / 2 : kOutOfRange, 0, kNontemporal);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    q.s[i] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rS, live && b + i < (uint32_t)nb ? sbase + 2 * (b + i) : kOutOfRange, 0,
+                        kNontemporal);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    q.z[i] = __builtin_amdgcn_raw_buffer_load_b8(
+                        rZ, live && b / 2 + i < (uint32_t)p.zb ? zbase + b / 2 + i : kOutOfRange, 0,
+                        kNontemporal);
+            }
+        };
+
+        // Unpack, MFMA and scale the four blocks of a quad.  rel = quad start
+        // relative to the staged chunk.  Rows j >= M of the A operand read
+        // row 0 (their products land in result rows that are never
+        // stored), so every operand read is unconditional; the four reads,
+        // unpacks and MFMAs go out before the scaling, which waits on them.
+        const int jr = j < M ? j : 0;
+        auto compute = [&](const Quad& q, int rel, float (&acc)[RR]) {
+            uint32_t r[4] = {q.w[0], q.w[1], q.w[2], q.w[3]};
+            transpose_rows(r);
+            const uint32_t zw = VEC ? q.z[0] : ((q.z[0] & 0xFFu) | ((q.z[1] & 0xFFu) << 8));
+            uint4 av[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = a_lds[((rel + i) * M + jr) * 4 + g];
+            float4_t d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t bq[4];
+                unpack_dword(r[i], zero_point_pairs(((zw >> (4 * i)) & 0xFu) | zdef), magic, bq);
+                const u32x4 bv = {bq[0], bq[1], bq[2], bq[3]};
+                const u32x4 aw = {av[i].x, av[i].y, av[i].z, av[i].w};
+                d[i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    __builtin_bit_cast(half8_t, aw), __builtin_bit_cast(half8_t, bv),
+                    float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t sw = VEC ? (i < 2 ? q.s[0] : q.s[1]) >> (16 * (i & 1)) : q.s[i];
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
+#pragma unroll
+                for (int rr = 0; rr < RR; ++rr) acc[rr] = fmaf(d[i][rr], sf, acc[rr]);
+            }
+        };
+
         float acc[RR];
 #pragma unroll
         for (int rr = 0; rr < RR; ++rr) acc[rr] = 0.f;
@@ -177,21 +235,24 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
             const int nbc = min(kcb, nb - b_lo);
             const int nq = (nbc + 3) / 4;
             const int q0 = wv * nq / W, q1 = (wv + 1) * nq / W;
-            Quad qa, qb;
-            if (q0 < q1) issue(qa, col, col_ok, b_lo + 4 * q0);   // before the staging wait
-            if (!staged) {
+            const int T0 = b_lo / 4;         // first quad of the chunk (kcb % 4 == 0)
+            Quad ring[P];
+            // The ring fills before the staging wait.
+#pragma unroll
+            for (int s = 0; s < P; ++s) issue(ring[s], T0 + q0 + s, q0 + s < q1);
+            // Activations: staged once per workgroup when K fits one chunk,
+            // else chunk by chunk (after every wave is done with the last).
+            if (p.chunks > 1 || tile == (int64_t)blockIdx.x) {
                 __syncthreads();
                 stage(b_lo, nbc);
                 __syncthreads();
-                staged = p.chunks == 1;
             }
-            for (int t = q0; t < q1;) {
-                if (t + 1 < q1) issue(qb, col, col_ok, b_lo + 4 * (t + 1));
-                compute(qa, 4 * t, nbc, acc);
-                if (++t >= q1) break;
-                if (t + 1 < q1) issue(qa, col, col_ok, b_lo + 4 * (t + 1));
-                compute(qb, 4 * t, nbc, acc);
-                ++t;
+            for (int t = q0; t < q1; t += P) {
+#pragma unroll
+                for (int s = 0; s < P; ++s) {
+                    if (t + s < q1) compute(ring[s], 4 * (t + s), acc);
+                    issue(ring[s], T0 + t + s + P, t + s + P < q1);
+                }
             }
         }
 
@@ -219,19 +280,32 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
 
 typedef void (*MfmaFn)(MfmaParams);
 
-MfmaFn lookup_mfma(int64_t m)
+template <bool VEC>
+MfmaFn lookup_mfma_vec(int64_t m)
 {
     switch (m) {
-    case 1: return mnb_gemv_mfma_kernel<1>;
-    case 2: return mnb_gemv_mfma_kernel<2>;
-    case 3: return mnb_gemv_mfma_kernel<3>;
-    case 4: return mnb_gemv_mfma_kernel<4>;
-    case 5: return mnb_gemv_mfma_kernel<5>;
-    case 6: return mnb_gemv_mfma_kernel<6>;
-    case 7: return mnb_gemv_mfma_kernel<7>;
-    case 8: return mnb_gemv_mfma_kernel<8>;
+    case 1: return mnb_gemv_mfma_kernel<1, VEC>;
+    case 2: return mnb_gemv_mfma_kernel<2, VEC>;
+    case 3: return mnb_gemv_mfma_kernel<3, VEC>;
+    case 4: return mnb_gemv_mfma_kernel<4, VEC>;
+    case 5: return mnb_gemv_mfma_kernel<5, VEC>;
+    case 6: return mnb_gemv_mfma_kernel<6, VEC>;
+    case 7: return mnb_gemv_mfma_kernel<7, VEC>;
+    case 8: return mnb_gemv_mfma_kernel<8, VEC>;
     }
     return nullptr;
+}
+
+// The vectorised quad loads need K/32 % 4 == 0 and aligned scale and
+// zero-point rows; the kernel variant is chosen per call.
+bool mfma_vec_ok(int64_t K, const void* scales, const void* zp)
+{
+    return (K / 32) % 4 == 0 && ((uintptr_t)scales & 7) == 0 && ((uintptr_t)zp & 1) == 0;
+}
+
+MfmaFn lookup_mfma(int64_t m, bool vec)
+{
+    return vec ? lookup_mfma_vec<true>(m) : lookup_mfma_vec<false>(m);
 }
 
 size_t mfma_lds_bytes(int64_t m, const mnb_plan& plan)
@@ -243,7 +317,7 @@ size_t mfma_lds_bytes(int64_t m, const mnb_plan& plan)
 
 int launch_mfma(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    MfmaFn fn = lookup_mfma(a.m);
+    MfmaFn fn = lookup_mfma(a.m, mfma_vec_ok(a.K, a.scales, a.zp));
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     MfmaParams p;
     p.A = static_cast<const uint16_t*>(a.A);
@@ -257,6 +331,7 @@ int launch_mfma(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.zb = (p.nb + 1) / 2;
     p.chunk_blocks = plan.chunk_blocks;
     p.chunks = plan.k_chunks;
+    p.zero = 0;
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
     void* args[] = {&p};
@@ -270,7 +345,7 @@ int launch_mfma(const GemvArgs& a, const mnb_plan& plan, void* stream)
 
 int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan)
 {
-    MfmaFn fn = lookup_mfma(m);
+    MfmaFn fn = lookup_mfma(m, true);
     if (!fn) return 0;
     return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg,
                      mfma_lds_bytes(m, plan));
@@ -278,7 +353,7 @@ int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan)
 
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
 {
-    MfmaFn fn = lookup_mfma(m);
+    MfmaFn fn = lookup_mfma(m, true);
     if (!fn) return -1;
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));

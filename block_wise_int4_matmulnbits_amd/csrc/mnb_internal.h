@@ -36,9 +36,17 @@ int current_device_cus(int* num_cus);
 // threads, LDS).
 int occupancy(const void* fn, int threads, size_t lds);
 
-// Occupancy-limited workgroups per CU for the kernel a plan selects
-// (0 if the query fails).
-int workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan);
+// Occupancy-limited workgroups per CU for the kernel a plan selects, with
+// the LDS it needs for N columns (0 if the query fails).
+int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan);
+
+// Dynamic LDS of a lane-split launch (engine 0) over N columns.  Multi-wave
+// groups keep every wave's partial sums of all their tiles in LDS and sum
+// them over waves once, at the end (*tcap = tiles per group), when that
+// fits kDeferLdsBytes; otherwise they sum after each tile through two
+// slots (*tcap = 0).  One-wave and in-wave groups need none.  Host-only.
+constexpr int64_t kDeferLdsBytes = 48 * 1024;
+int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap);
 
 // Code-object facts of the variant (m, K and the plan select it).  Returns a hipError_t, or -1 when no
 // variant matches.

@@ -186,6 +186,29 @@ def test_every_variant_ragged(oracle_mod):
             assert_parity(oracle_mod, d, m, "variant", plan)
 
 
+def test_multiwave_groups_deferred_and_per_tile_sums(oracle_mod):
+    """Groups of several waves keep each wave's partial sums in LDS: summed
+    over waves once at the end of the kernel when all of a group's tiles
+    fit, else after every tile.  Both match the oracle, with K covered
+    exactly and ragged, and give the same bits for the same lane split."""
+    cases = [
+        # m, K, N, lanes_per_col, blocks_per_lane, cols_per_tile, workgroups
+        (2, 14336, 301, 448, 1, 4, 3),     # exact K, 26 tiles per group, deferred
+        (8, 14336, 2000, 448, 1, 2, 1),    # 1000 tiles in one group: per-tile sums
+        (1, 8192, 777, 128, 2, 4, 5),      # exact K, two waves per group
+        (5, 32 * 611, 150, 320, 1, 2, 2),  # ragged K in two chunks, deferred
+        (3, 4096, 5000, 128, 1, 8, 1),     # 625 tiles of 24 sums: per-tile sums
+    ]
+    for i, (m, K, N, lpc, bpl, nc, wg) in enumerate(cases):
+        d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i != 2, 0.001, 0.01, 0.5, 400 + i)
+        plan = dict(lanes_per_col=lpc, blocks_per_lane=bpl, cols_per_tile=nc, workgroups=wg)
+        y16, _, _ = assert_parity(oracle_mod, d, m, "multiwave", plan)
+        if i in (1, 4):
+            other = dict(plan, workgroups=64)   # few tiles per group: deferred
+            y2, _ = run(d, m, W.F16, other)
+            assert np.array_equal(y2, y16)
+
+
 def test_mfma_engine_ragged(oracle_mod):
     """The MFMA tile kernel for every m, ragged K and N, one to eight waves
     per workgroup, K staged in one or several LDS chunks."""
@@ -200,6 +223,8 @@ def test_mfma_engine_ragged(oracle_mod):
         (7, 96, 31, 3, 4, 2),
         (8, 14336, 300, 8, 128, 9),
         (8, 4096, 4096, 8, 128, 64),
+        (2, 14336, 100, 8, 448, 3),
+        (6, 32 * 611, 45, 8, 64, 2),
     ]
     for i, (m, K, N, w, kcb, wg) in enumerate(cases):
         d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i % 3 != 1, 0.002, 0.02, 1.0, 300 + i)
