@@ -12,8 +12,20 @@ is resident in HBM before the timed region starts.
 Prints one JSON line.  value = algorithmic bytes per call / time per call
 (GB/s); roofline.traffic comes from the committed rocprofv3 counter summary
 for the current kernel source (null if the kernel changed since).
+
+Besides the headline figure the line carries (skipped with --no-extras):
+  attainable   a read-only streaming kernel over the same bytes (the in-repo
+               probe): what one launch of this size can pull from HBM;
+  workloads    microseconds per call of the other synthetic shapes (the
+               4096x4096, gate_up and down-projection rows at m = 2, 4, 8);
+  staged_route the fp16 GEMV followed by a separate fp16 -> bf16 cast launch,
+               against the direct bf16 store (bits compared);
+  decode_step  a decode step of GEMVs (4 layers of q/k/v/o, gate_up and down,
+               then the lm_head), launched eagerly and as one captured HIP
+               graph (outputs compared).
 """
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -25,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "m=1 INT4 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call"
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_VALU_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
 
 
@@ -51,13 +64,15 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=1000)
     ap.add_argument("--workload", default="lm_head")
     ap.add_argument("--m", type=int, default=None, help="rows (default: the workload's)")
     ap.add_argument("--out-dtype", default="bf16", choices=["f16", "bf16"])
     ap.add_argument("--rotate-mb", type=int, default=512,
                     help="minimum bytes of rotated weight copies")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="headline GEMV only (profiling runs)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run torch's device copy of this many MiB "
@@ -77,6 +92,55 @@ def calib_copy(mib, reps=5):
     print(json.dumps({"calib_copy_bytes": n, "reps": reps}))
 
 
+class Resident:
+    """One workload's inputs in device memory, with rotated weight copies."""
+
+    def __init__(self, w, m, out_dtype, rotate_mb, d=None):
+        import numpy as np
+        import torch
+        from block_wise_int4_matmulnbits_amd import workloads as W
+        self.w, self.m = w, m
+        d = W.generate_workload(w, m) if d is None else d
+        self.d = d
+        dev = torch.device("cuda:0")
+        weight_bytes = d["B"].nbytes + d["scales"].nbytes + (
+            d["zp"].nbytes if d["zp"] is not None else 0)
+        self.R = max(1, math.ceil(rotate_mb * 1e6 / weight_bytes))
+        adt = torch.bfloat16 if w.a_dtype == W.BF16 else torch.float16
+        self.A = torch.from_numpy(np.ascontiguousarray(d["A"][:m]).view(np.int16)).to(dev).view(adt)
+        B0 = torch.from_numpy(d["B"]).to(dev)
+        S0 = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
+        Z0 = None if d["zp"] is None else torch.from_numpy(d["zp"]).to(dev)
+        self.copies = [(B0, S0, Z0)] + [
+            (B0.clone(), S0.clone(), None if Z0 is None else Z0.clone()) for _ in range(self.R - 1)]
+        self.out_dtype = out_dtype
+        self.out = torch.empty((m, w.N), dtype=torch.bfloat16 if out_dtype == W.BF16 else torch.float16,
+                               device=dev)
+        self.a_dt = W.BF16 if w.a_dtype == W.BF16 else W.F16
+        self.bytes_per_call = w.bytes_per_call(m)
+
+    def raw(self, stream, out=None, out_dtype=None):
+        out = self.out if out is None else out
+        out_dtype = self.out_dtype if out_dtype is None else out_dtype
+        return [(self.A.data_ptr(), self.a_dt, self.m, self.w.K, self.w.N, b.data_ptr(),
+                 s.data_ptr(), z.data_ptr() if z is not None else None, 32, out.data_ptr(),
+                 out_dtype, stream) for (b, s, z) in self.copies]
+
+
+def event_time_us(stream, fn, n):
+    """Mean microseconds per fn() over n calls, HIP events on `stream`."""
+    import torch
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(n):
+        fn(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / n * 1e3
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -90,7 +154,6 @@ def main():
         calib_copy(args.calib_copy_mib)
         return
 
-    import numpy as np
     import torch
 
     import block_wise_int4_matmulnbits_amd as mnb
@@ -101,28 +164,14 @@ def main():
     m = w.m if args.m is None else args.m
     out_dtype = W.BF16 if args.out_dtype == "bf16" else W.F16
     t0 = time.time()
-    d = W.generate_workload(w, m)
+    res = Resident(w, m, out_dtype, args.rotate_mb)
     log("[bench] generated %s inputs in %.1f s" % (w.name, time.time() - t0))
 
     dev = torch.device("cuda:0")
-    bytes_per_call = w.bytes_per_call(m)
-    weight_bytes = d["B"].nbytes + d["scales"].nbytes + (d["zp"].nbytes if d["zp"] is not None else 0)
-    R = max(1, math.ceil(args.rotate_mb * 1e6 / weight_bytes))
-    adt = torch.bfloat16 if w.a_dtype == W.BF16 else torch.float16
-    A = torch.from_numpy(np.ascontiguousarray(d["A"][:m]).view(np.int16)).to(dev).view(adt)
-    B0 = torch.from_numpy(d["B"]).to(dev)
-    S0 = torch.from_numpy(d["scales"].view(np.int16)).to(dev).view(torch.float16)
-    Z0 = None if d["zp"] is None else torch.from_numpy(d["zp"]).to(dev)
-    copies = [(B0, S0, Z0)] + [(B0.clone(), S0.clone(), None if Z0 is None else Z0.clone())
-                               for _ in range(R - 1)]
-    out = torch.empty((m, w.N), dtype=torch.bfloat16 if out_dtype == W.BF16 else torch.float16,
-                      device=dev)
     stream = torch.cuda.current_stream(dev)
     L = mnb.lib()
-    a_dt = W.BF16 if w.a_dtype == W.BF16 else W.F16
-    raw = [(A.data_ptr(), a_dt, m, w.K, w.N, b.data_ptr(), s.data_ptr(),
-            z.data_ptr() if z is not None else None, 32, out.data_ptr(), out_dtype,
-            stream.cuda_stream) for (b, s, z) in copies]
+    raw = res.raw(stream.cuda_stream)
+    R = res.R
     call = L.matmul_nbits
 
     def step(i):
@@ -135,27 +184,22 @@ def main():
     info = mnb.mnb_get_kernel_info(m, w.K, plan)
     log("[bench] plan %s kernel %s rotated copies %d" % (plan.as_dict(), info, R))
 
+    # Untimed warm-up: the first few hundred launches of a sustained run see
+    # the clocks settle; the timed region measures the steady state.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
     c0 = mnb.mnb_counters_get()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    ev1.record(stream)
-    torch.cuda.synchronize()
+    us = event_time_us(stream, step, args.steps)
     wall = time.perf_counter() - wall0
     c1 = mnb.mnb_counters_get()
     assert c1["launches"] - c0["launches"] == args.steps
     if out_dtype == W.BF16:
         assert c1["elements_bf16_direct"] - c0["elements_bf16_direct"] == args.steps * m * w.N
-    ms = ev0.elapsed_time(ev1) / args.steps
-    us = ms * 1e3
+    ms = us * 1e-3
+    bytes_per_call = res.bytes_per_call
     gbs = bytes_per_call / (ms * 1e-3) / 1e9
     log("[bench] %d steps: %.3f us/call (events), wall %.3f us/call, %.1f GB/s = %.1f%% of %.0f"
         % (args.steps, us, wall / args.steps * 1e6, gbs, 100 * gbs / PEAK_HBM_GBS, PEAK_HBM_GBS))
@@ -193,11 +237,199 @@ def main():
         "cpu_baseline": None,
     }
 
+    if not args.no_extras:
+        att = attainable(res, stream, cus)
+        if att:
+            result["roofline"]["attainable"] = att
+            result["roofline"]["frac_of_attainable"] = round(gbs / att["gbs"], 4)
+        result["workloads"] = other_workloads(args, stream, cus)
+        if w.name == "lm_head" and m == 1:
+            result["staged_route"] = staged_route(res, stream, L)
+        result["decode_step"] = decode_step(args, stream, L)
+
     if not args.no_cpu_baseline:
-        result["cpu_baseline"], parity = cpu_baseline(args, w, d, m, A, copies[0], out_dtype,
-                                                      bytes_per_call)
+        result["cpu_baseline"], parity = cpu_baseline(args, w, res.d, m, res.A, res.copies[0],
+                                                      out_dtype, bytes_per_call)
         result["parity_vs_oracle"] = parity
     print(json.dumps(result), flush=True)
+
+
+def attainable(res, stream, cus):
+    """The in-repo read-only streaming kernel over the packed weights of the
+    rotated copies (the bulk of the GEMV's bytes), best of a few launch
+    shapes: the bandwidth one launch of this size can draw."""
+    path = os.path.join(ROOT, "block_wise_int4_matmulnbits_amd", "libmnb_probe.so")
+    if not os.path.exists(path):
+        return None
+    import torch
+    P = ctypes.CDLL(path)
+    P.mnb_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    bufs = [b for (b, _, _) in res.copies]
+    n = bufs[0].numel() // 16 * 16
+    best = None
+    for unroll, per_cu in ((-1, 8), (-4, 2), (-2, 4)):
+        wg = cus * per_cu
+        sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+
+        def go(i):
+            P.mnb_probe_read(bufs[i % len(bufs)].data_ptr(), n, sink.data_ptr(), wg, unroll,
+                             stream.cuda_stream)
+        for i in range(20):
+            go(i)
+        us = event_time_us(stream, go, 200)
+        if best is None or us < best[0]:
+            best = (us, unroll, per_cu)
+    gbs = n / (best[0] * 1e-6) / 1e9
+    log("[bench] attainable read: %d B in %.2f us = %.1f GB/s" % (n, best[0], gbs))
+    return {"gbs": round(gbs, 1), "bytes": n, "us": round(best[0], 3),
+            "kernel": "read probe, unroll %d, %d workgroups/CU" % (best[1], best[2])}
+
+
+def other_workloads(args, stream, cus):
+    """Microseconds per call of the other synthetic shapes (default plans,
+    rotated copies, bf16 output)."""
+    import block_wise_int4_matmulnbits_amd as mnb
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    out = {}
+    L = mnb.lib()
+    shared = {}
+    for name, m in (("tiny_1k", 1), ("asym_4k", 1), ("gate_up_bf16", 1),
+                    ("down_rows_bf16", 2), ("down_rows_bf16", 4), ("down_rows_bf16", 8)):
+        w = W.WORKLOADS[name]
+        if name not in shared:
+            shared.clear()
+            shared[name] = W.generate_workload(w, w.m_max or w.m)
+        res = Resident(w, m, W.BF16, 0 if name == "tiny_1k" else args.rotate_mb, d=shared[name])
+        raw = res.raw(stream.cuda_stream)
+
+        def go(i):
+            L.matmul_nbits(*raw[i % len(raw)])
+        for i in range(200):
+            go(i)
+        n = max(200, int(0.1 / (res.bytes_per_call / 5e12)))
+        us = event_time_us(stream, go, n)
+        plan = mnb.plan_for_device(m, w.K, w.N, cus)
+        gbs = res.bytes_per_call / (us * 1e-6) / 1e9
+        e = {"m": m, "K": w.K, "N": w.N, "us_per_call": round(us, 3), "GB/s": round(gbs, 1),
+             "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+             "rotated_copies": res.R, "plan": {k: v for k, v in plan.as_dict().items()
+                                               if k in ("engine", "lanes_per_col", "blocks_per_lane",
+                                                        "cols_per_tile", "workgroups")}}
+        if m > 1:
+            flops = 2.0 * m * w.N * w.K
+            e["fp32_valu_floor_us"] = round(flops / (PEAK_FP32_VALU_TFLOPS * 1e12) * 1e6, 3)
+        out["%s:m%d" % (name, m)] = e
+        log("[bench] %s m=%d: %.3f us/call, %.1f GB/s" % (name, m, us, gbs))
+        del res
+    return out
+
+
+def staged_route(res, stream, L):
+    """The staged route (fp16 GEMV into a staging buffer, then a separate
+    fp16 -> bf16 cast launch) against the direct bf16 store, on the same
+    rotated inputs; both must give the same bf16 bits."""
+    import torch
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    stage = torch.empty(res.out.shape, dtype=torch.float16, device="cuda")
+    direct = torch.empty(res.out.shape, dtype=torch.bfloat16, device="cuda")
+    staged = torch.empty_like(direct)
+    raw_d = res.raw(stream.cuda_stream, direct, W.BF16)
+    raw_s = res.raw(stream.cuda_stream, stage, W.F16)
+
+    def go_direct(i):
+        L.matmul_nbits(*raw_d[i % len(raw_d)])
+
+    def go_staged(i):
+        L.matmul_nbits(*raw_s[i % len(raw_s)])
+        staged.copy_(stage)
+
+    for i in range(50):
+        go_direct(i)
+        go_staged(i)
+    n = 1000
+    us_d = event_time_us(stream, go_direct, n)
+    us_s = event_time_us(stream, go_staged, n)
+    go_direct(0)
+    go_staged(0)
+    torch.cuda.synchronize()
+    same = bool(torch.equal(direct.view(torch.int16), staged.view(torch.int16)))
+    log("[bench] staged route %.3f us/call (2 launches) vs direct %.3f us (1 launch); bits equal %s"
+        % (us_s, us_d, same))
+    return {"direct_us": round(us_d, 3), "staged_us": round(us_s, 3),
+            "saving_us": round(us_s - us_d, 3), "launches_direct": 1, "launches_staged": 2,
+            "staging_bytes": stage.numel() * 2, "bf16_bits_equal": same}
+
+
+def decode_step(args, stream, L, layers=4):
+    """One decode step of m=1 GEMVs: per layer q, k, v, o (4096 x 4096),
+    gate_up (28672 x 4096) and down (4096 x 14336), distinct weights per
+    layer, then the lm_head; eager launches against one captured HIP graph
+    replayed on the same stream.  Outputs of the graph equal the eager ones."""
+    import numpy as np
+    import torch
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    shapes = [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
+              ("gate_up", 4096, 28672), ("down", 14336, 4096)]
+    dev = torch.device("cuda:0")
+    base = {}
+    for name, K, N in shapes + [("lm_head", 4096, 151936)]:
+        if (K, N) not in base:
+            d = W.generate(1, K, N, W.F16, True, 0.001, 0.01, 1.0, 50 + len(base))
+            base[(K, N)] = (torch.from_numpy(d["B"]).to(dev),
+                            torch.from_numpy(d["scales"].view(np.int16)).to(dev),
+                            torch.from_numpy(d["zp"]).to(dev),
+                            torch.from_numpy(np.ascontiguousarray(d["A"][:1]).view(np.int16)).to(dev))
+    calls = []
+    outs = []
+    for layer in range(layers):
+        for name, K, N in shapes:
+            B, S, Z, A = base[(K, N)]
+            if layer:
+                B, S, Z = B.clone(), S.clone(), Z.clone()
+            o = torch.empty((1, N), dtype=torch.bfloat16, device=dev)
+            calls.append((A, B, S, Z, o, K, N))
+            outs.append(o)
+    B, S, Z, A = base[(4096, 151936)]
+    o = torch.empty((1, 151936), dtype=torch.bfloat16, device=dev)
+    calls.append((A, B, S, Z, o, 4096, 151936))
+    outs.append(o)
+    nbytes = sum(W.Workload("x", 1, K, N, W.F16, (W.BF16,), True, 0, 0, 0, 0).bytes_per_call()
+                 for (_, _, _, _, _, K, N) in calls)
+
+    def launch_all(s):
+        for (A, B, S, Z, o, K, N) in calls:
+            st = L.matmul_nbits(A.data_ptr(), W.F16, 1, K, N, B.data_ptr(), S.data_ptr(),
+                                Z.data_ptr(), 32, o.data_ptr(), W.BF16, s)
+            assert st == 0, st
+
+    for _ in range(10):
+        launch_all(stream.cuda_stream)
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    for o in outs:
+        o.fill_(0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        launch_all(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    same = True
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        same &= all(torch.equal(a.view(torch.int16), b.view(torch.int16)) for a, b in zip(eager, outs))
+        for o in outs:
+            o.fill_(0)
+        torch.cuda.synchronize()
+    n = 50
+    us_eager = event_time_us(stream, lambda i: launch_all(stream.cuda_stream), n)
+    us_graph = event_time_us(stream, lambda i: g.replay(), n)
+    log("[bench] decode step (%d GEMVs, %.0f MB): eager %.1f us, graph %.1f us; graph == eager %s"
+        % (len(calls), nbytes / 1e6, us_eager, us_graph, same))
+    return {"gemvs": len(calls), "layers": layers, "bytes": nbytes,
+            "eager_us": round(us_eager, 2), "graph_us": round(us_graph, 2),
+            "graph_GB/s": round(nbytes / (us_graph * 1e-6) / 1e9, 1),
+            "graph_outputs_equal_eager": bool(same)}
 
 
 def cpu_baseline(args, w, d, m, A, copy0, out_dtype, bytes_per_call):

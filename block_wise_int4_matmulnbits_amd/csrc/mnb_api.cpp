@@ -123,7 +123,9 @@ namespace mnb {
 int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap)
 {
     *tcap = 0;
-    if (plan.engine != 0 || plan.lanes_per_col <= 64) return 0;
+    if (plan.engine != 0 || plan.lanes_per_col < 64) return 0;
+    if (plan.lanes_per_col == 64)   // activations shared by the workgroup's waves
+        return plan.k_chunks == 1 ? m * plan.blocks_per_lane * 256 * 16 : 0;
     const int64_t nw = plan.lanes_per_col / 64;
     const int64_t nv = (int64_t)plan.cols_per_tile * m;
     const int64_t g = plan.workgroups < 1 ? 1 : plan.workgroups;
@@ -208,16 +210,18 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         if (bpl > bmax) bpl = bmax;
     }
 
-    // 2. Column tile: two columns per lane group in a wave, fewer rows' worth
-    //    of partial sums for wide multi-wave groups.
-    int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : (m <= 2 ? 4 : 2);
+    // 2. Column tile: two columns per lane group in a wave; multi-wave
+    //    groups one column up to four rows, two beyond (measured on the
+    //    down-projection shape).
+    int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : (m <= 4 ? 1 : 2);
     while (nc > 1 && (nc * bpl > 8 || nc * m > 32)) nc /= 2;
 
     // 3. Grid.  Tiles are dealt round-robin, so all lane groups sweep the
     //    weights as one front.  In-wave groups: about five tiles per group,
     //    between half and twice one resident generation of workgroups
     //    (measured best on the lm_head and gate_up shapes).  Multi-wave
-    //    groups: one resident generation.
+    //    groups: half a resident generation, at least one workgroup per CU
+    //    (more tiles per workgroup share its activation fetch).
     const bool inwave = lpc <= 64;
     const int64_t gpw = inwave ? 256 / lpc : 1;
     const int64_t waves_per_wg = inwave ? 4 : lpc / 64;
@@ -225,7 +229,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
                                           : (kTargetWavesPerCu + waves_per_wg - 1) / waves_per_wg;
     const int64_t resident = per_cu * num_cus;
     const int64_t tiles = ceil_div(N, nc);
-    int64_t wgs = resident;
+    int64_t wgs = resident / 2 > num_cus ? resident / 2 : num_cus;
     if (inwave) {
         wgs = ceil_div(tiles, 5 * gpw);
         const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;

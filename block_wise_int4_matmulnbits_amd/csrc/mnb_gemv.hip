@@ -218,8 +218,25 @@ void mnb_gemv_kernel(Params p)
         }
     };
 
-    // To fp16 (bf16 rounded to nearest even), permuted into the unpack's
-    // pair order.
+    // Eight activations (one uint4) to fp16 (bf16 rounded to nearest even),
+    // permuted into the unpack's pair order.
+    auto to_pairs = [&](uint4 v) {
+        uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
+        if (p.a_bf16) {
+            x = bf16x2_to_f16x2(x);
+            y = bf16x2_to_f16x2(y);
+            z = bf16x2_to_f16x2(z);
+            w = bf16x2_to_f16x2(w);
+        }
+        // halves: x=(a0,a1) y=(a2,a3) z=(a4,a5) w=(a6,a7)
+        uint4 o;
+        o.x = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
+        o.y = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
+        o.z = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
+        o.w = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
+        return o;
+    };
+
     auto place_acts = [&](const RawActs& raw) {
 #pragma unroll
         for (int j = 0; j < BPL; ++j)
@@ -227,19 +244,50 @@ void mnb_gemv_kernel(Params p)
             for (int r = 0; r < M; ++r)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    uint32_t x = raw[r][j][i].x, y = raw[r][j][i].y;
-                    uint32_t z = raw[r][j][i].z, w = raw[r][j][i].w;
-                    if (p.a_bf16) {
-                        x = bf16x2_to_f16x2(x);
-                        y = bf16x2_to_f16x2(y);
-                        z = bf16x2_to_f16x2(z);
-                        w = bf16x2_to_f16x2(w);
-                    }
-                    // halves: x=(a0,a1) y=(a2,a3) z=(a4,a5) w=(a6,a7)
-                    act[r][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
-                    act[r][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
-                    act[r][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
-                    act[r][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
+                    const uint4 o = to_pairs(raw[r][j][i]);
+                    act[r][j][4 * i + 0] = o.x;
+                    act[r][j][4 * i + 1] = o.y;
+                    act[r][j][4 * i + 2] = o.z;
+                    act[r][j][4 * i + 3] = o.w;
+                }
+    };
+
+    // One-wave groups: the four waves of a workgroup own the same blocks of
+    // K lane by lane, so the workgroup fetches and converts the activations
+    // once and each wave copies its lanes' share out of LDS (a quarter of
+    // the L2 reads and conversions of per-wave fetching).  Thread t fetches
+    // 16-byte piece i = t / 64 of lane t % 64's blocks, for every row and
+    // block of the lane; LDS holds [row][block][piece][lane].
+    constexpr bool kShareActs = UNI && !xwave;
+    constexpr int kShare = kShareActs ? M * BPL : 1;
+    uint4* const act_lds = reinterpret_cast<uint4*>(part);
+    auto fetch_shared = [&](uint4 (&sv)[kShare]) {
+        const int piece = tid >> 6, ln = tid & 63;
+#pragma unroll
+        for (int s = 0; s < kShare; ++s) {
+            const int r = s / BPL, j = s - r * BPL;
+            const uint32_t b = (uint32_t)(j * 64 + ln);
+            sv[s] = make_uint4(0, 0, 0, 0);
+            if (EXACT_K || b < nb)
+                sv[s] = *reinterpret_cast<const uint4*>(p.A + (int64_t)r * p.K + 32 * (int64_t)b + 8 * piece);
+        }
+    };
+    auto place_shared = [&](const uint4 (&sv)[kShare]) {
+#pragma unroll
+        for (int s = 0; s < kShare; ++s) act_lds[s * 256 + tid] = to_pairs(sv[s]);
+        __syncthreads();
+        const int ln = tid & 63;
+#pragma unroll
+        for (int r = 0; r < M; ++r)
+#pragma unroll
+            for (int j = 0; j < BPL; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint4 o = act_lds[((r * BPL + j) * 4 + i) * 64 + ln];
+                    act[r][j][4 * i + 0] = o.x;
+                    act[r][j][4 * i + 1] = o.y;
+                    act[r][j][4 * i + 2] = o.z;
+                    act[r][j][4 * i + 3] = o.w;
                 }
     };
 
@@ -422,10 +470,16 @@ void mnb_gemv_kernel(Params p)
         int64_t c0 = c_first;
         int k = 0;
         RawActs raw;
-        fetch_acts(0, raw);
+        uint4 sv[kShare];
+        if constexpr (kShareActs) fetch_shared(sv);
+        else fetch_acts(0, raw);
         issue(ta, c0, 0);
+        auto place = [&]() {
+            if constexpr (kShareActs) place_shared(sv);
+            else place_acts(raw);
+        };
         if constexpr (!kPrefetch<M, BPL, NC, MODE>) {
-            place_acts(raw);
+            place();
             while (c0 < c_stop) {
                 float acc[NC][M] = {};
                 compute(ta, acc);
@@ -435,7 +489,7 @@ void mnb_gemv_kernel(Params p)
             }
         } else {
             issue(tb, c0 + c_step, 0);
-            place_acts(raw);
+            place();
             while (c0 < c_stop) {
                 float acc[NC][M] = {};
                 compute(ta, acc);

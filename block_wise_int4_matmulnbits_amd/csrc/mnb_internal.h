@@ -44,7 +44,9 @@ int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan);
 // groups keep every wave's partial sums of all their tiles in LDS and sum
 // them over waves once, at the end (*tcap = tiles per group), when that
 // fits kDeferLdsBytes; otherwise they sum after each tile through two
-// slots (*tcap = 0).  One-wave and in-wave groups need none.  Host-only.
+// slots (*tcap = 0).  One-wave groups with K in one pass stage the
+// workgroup's activations (m * blocks_per_lane * 4 KB); groups inside a
+// wave need none.  Host-only.
 constexpr int64_t kDeferLdsBytes = 48 * 1024;
 int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap);
 
