@@ -210,10 +210,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         if (bpl > bmax) bpl = bmax;
     }
 
-    // 2. Column tile: two columns per lane group in a wave; multi-wave
-    //    groups one column up to four rows, two beyond (measured on the
-    //    down-projection shape).
-    int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : (m <= 4 ? 1 : 2);
+    // 2. Column tile: two columns per lane group in a wave; one column per
+    //    multi-wave group, whose waves then keep the next column's loads in
+    //    flight (measured on the down-projection shape).
+    int64_t nc = lpc <= 64 ? (bpl >= 4 ? 1 : 2) : 1;
     while (nc > 1 && (nc * bpl > 8 || nc * m > 32)) nc /= 2;
 
     // 3. Grid.  Tiles are dealt round-robin, so all lane groups sweep the

@@ -124,7 +124,7 @@ constexpr bool multiwave_mode(int mode) { return mode == WAVES_X || mode == EXAC
 #define MNB_PREFETCH_TILE 2   // largest NC*BPL of a one-wave group with two tile buffers
 #endif
 #ifndef MNB_PREFETCH_X_VGPRS
-#define MNB_PREFETCH_X_VGPRS 128
+#define MNB_PREFETCH_X_VGPRS 160
 #endif
 template <int M, int BPL, int NC, int MODE>
 constexpr bool kPrefetch =

@@ -1,7 +1,8 @@
 """Summaries of rocprofv3 CSV output for the GEMV, written under profiles/.
 
-    python -m block_wise_int4_matmulnbits_amd.profiling trace DIR OUT.md CMD
-        kernel stats and dispatch facts of a --kernel-trace --stats run
+    python -m block_wise_int4_matmulnbits_amd.profiling trace DIR OUT.md CMD [TIMED]
+        kernel stats and dispatch facts of a --kernel-trace --stats run;
+        TIMED: dispatches of the bench's timed region (the last ones)
     python -m block_wise_int4_matmulnbits_amd.profiling traffic \\
         GEMV_FETCH GEMV_WRITE COPY_FETCH COPY_WRITE COPY_BYTES WORKLOAD M \\
         OUT.json OUT.md CMD...
@@ -41,12 +42,15 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def trace_summary(trace_dir, out_md, cmd):
+def trace_summary(trace_dir, out_md, cmd, timed=0):
+    """timed: the number of dispatches of the bench's timed region (the last
+    ones traced; the warm-up dispatches come first)."""
     stats = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     with open(stats) as f:
         stats_text = f.read().strip()
     rows = [r for r in _rows(trace) if GEMV_TAG in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     r = rows[-1]
     facts = ("grid %s work-items, workgroup %s, arch VGPRs %s (as traced), SGPRs %s, "
@@ -58,8 +62,13 @@ def trace_summary(trace_dir, out_md, cmd):
                 "    %s\n\n`kernel_stats.csv`:\n\n```\n%s\n```\n\n" % (
                     r["Kernel_Name"], cmd, stats_text))
         f.write("GEMV dispatches traced: %d; median duration %.3f us "
-                "(min %.3f, max %.3f).\n\nDispatch: %s.\n" % (
-                    len(durs), med, min(durs), max(durs), facts))
+                "(min %.3f, max %.3f).\n\n" % (len(durs), med, min(durs), max(durs)))
+        if 0 < timed <= len(durs):
+            t = durs[-timed:]
+            f.write("Timed region (the last %d dispatches, after the bench's warm-up): "
+                    "mean %.3f us, median %.3f us.\n\n" % (timed, statistics.mean(t),
+                                                          statistics.median(t)))
+        f.write("Dispatch: %s.\n" % facts)
     return med
 
 
@@ -112,7 +121,7 @@ def traffic_summary(gemv_fetch, gemv_write, copy_fetch, copy_write, copy_bytes, 
 
 def main(argv):
     if argv[0] == "trace":
-        print(trace_summary(argv[1], argv[2], argv[3]))
+        print(trace_summary(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else 0))
     elif argv[0] == "traffic":
         (gf, gw, cf, cw, cb, wl, m, oj, om) = argv[1:10]
         print(json.dumps(traffic_summary(gf, gw, cf, cw, int(cb), wl, int(m), oj, om, argv[10:])))

@@ -118,7 +118,7 @@ def test_default_plan_shapes():
     assert p.workgroups == 2 * 6 * 256          # capped at two resident generations
     p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
-    for m, occ, nc, wg in ((2, 4, 1, 512), (4, 2, 1, 256), (8, 1, 2, 256)):
+    for m, occ, nc, wg in ((2, 4, 1, 512), (4, 2, 1, 256), (8, 1, 1, 256)):
         p = mnb.mnb_plan_default(m, 14336, 4096, 256, occ)
         assert (p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (448, 1, 1)
         assert (p.cols_per_tile, p.workgroups) == (nc, wg)
