@@ -218,8 +218,9 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
 
     // 3. Grid.  Tiles are dealt round-robin, so all lane groups sweep the
     //    weights as one front.  In-wave groups: about five tiles per group,
-    //    between half and twice one resident generation of workgroups
-    //    (measured best on the lm_head and gate_up shapes).  Multi-wave
+    //    in whole rounds of the CU count, between half and three times one
+    //    resident generation of workgroups (measured best on the lm_head
+    //    and gate_up shapes).  Multi-wave
     //    groups: half a resident generation, at least one workgroup per CU
     //    (more tiles per workgroup share its activation fetch).
     const bool inwave = lpc <= 64;
@@ -231,10 +232,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     const int64_t tiles = ceil_div(N, nc);
     int64_t wgs = resident / 2 > num_cus ? resident / 2 : num_cus;
     if (inwave) {
-        wgs = ceil_div(tiles, 5 * gpw);
+        wgs = num_cus * ceil_div(ceil_div(tiles, 5 * gpw), num_cus);   // whole rounds of CUs
         const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;
         if (wgs < lo) wgs = lo;
-        if (wgs > 2 * resident) wgs = 2 * resident;
+        if (wgs > 3 * resident) wgs = 3 * resident;
     }
     if (!inwave) {
         // Multi-wave groups: enough workgroups that every wave's partial sums

@@ -115,7 +115,7 @@ def test_default_plan_shapes():
     """The tuned plan shapes for the measured workloads."""
     p = mnb.mnb_plan_default(1, 4096, 151936, 256, 6)
     assert (p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile, p.interleave) == (64, 2, 2, 1)
-    assert p.workgroups == 2 * 6 * 256          # capped at two resident generations
+    assert p.workgroups == 15 * 256             # ~5 tiles per group, whole rounds of CUs
     p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
     for m, occ, nc, wg in ((2, 4, 1, 512), (4, 2, 1, 256), (8, 1, 1, 256)):
