@@ -22,7 +22,9 @@ Besides the headline figure the line carries (skipped with --no-extras):
                against the direct bf16 store (bits compared);
   decode_step  a decode step of GEMVs (4 layers of q/k/v/o, gate_up and down,
                then the lm_head), launched eagerly and as one captured HIP
-               graph (outputs compared).
+               graph (outputs compared);
+  prefill      m = 512 and 2048 rows on the gate_up and down shapes (the
+               matrix-core tile kernel), TFLOP/s against the fp16 peak.
 """
 import argparse
 import ctypes
@@ -38,6 +40,7 @@ sys.path.insert(0, ROOT)
 METRIC = "m=1 INT4 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3
+PEAK_FP16_MFMA_TFLOPS = 2500.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
 
 
@@ -246,6 +249,7 @@ def main():
         if w.name == "lm_head" and m == 1:
             result["staged_route"] = staged_route(res, stream, L)
         result["decode_step"] = decode_step(args, stream, L)
+        result["prefill"] = prefill(stream, L, cus)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], parity = cpu_baseline(args, w, res.d, m, res.A, res.copies[0],
@@ -430,6 +434,44 @@ def decode_step(args, stream, L, layers=4):
             "eager_us": round(us_eager, 2), "graph_us": round(us_graph, 2),
             "graph_GB/s": round(nbytes / (us_graph * 1e-6) / 1e9, 1),
             "graph_outputs_equal_eager": bool(same)}
+
+
+def prefill(stream, L, cus):
+    """Prefill heights (m > 8, the matrix-core tile kernel) on the gate_up
+    and down-projection shapes: microseconds per call and TFLOP/s against
+    the dense fp16 matrix-core peak."""
+    import numpy as np
+    import torch
+    import block_wise_int4_matmulnbits_amd as mnb
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    out = {}
+    dev = torch.device("cuda:0")
+    for name, K, N in (("gate_up", 4096, 28672), ("down", 14336, 4096)):
+        d = W.generate(1, K, N, W.BF16, True, 0.001, 0.01, 0.5, 90)
+        B = torch.from_numpy(d["B"]).to(dev)
+        S = torch.from_numpy(d["scales"].view(np.int16)).to(dev)
+        Z = torch.from_numpy(d["zp"]).to(dev)
+        for m in (512, 2048):
+            A = (torch.randn((m, K), device=dev) * 0.5).to(torch.bfloat16)
+            o = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+
+            def go(i):
+                st = L.matmul_nbits(A.data_ptr(), W.BF16, m, K, N, B.data_ptr(), S.data_ptr(),
+                                    Z.data_ptr(), 32, o.data_ptr(), W.BF16, stream.cuda_stream)
+                assert st == 0, st
+            for i in range(5):
+                go(i)
+            us = event_time_us(stream, go, 20)
+            tflops = 2.0 * m * N * K / (us * 1e-6) / 1e12
+            plan = mnb.plan_for_device(m, K, N, cus)
+            out["%s:m%d" % (name, m)] = {
+                "m": m, "K": K, "N": N, "us_per_call": round(us, 2), "TFLOP/s": round(tflops, 1),
+                "pct_of_fp16_mfma_peak": round(100 * tflops / PEAK_FP16_MFMA_TFLOPS, 2),
+                "plan": {k: v for k, v in plan.as_dict().items()
+                         if k in ("engine", "row_tiles", "cols_per_tile", "workgroups")}}
+            log("[bench] prefill %s m=%d: %.1f us, %.1f TFLOP/s" % (name, m, us, tflops))
+            del A, o
+    return out
 
 
 def cpu_baseline(args, w, d, m, A, copy0, out_dtype, bytes_per_call):

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(_HERE, "libmnb.so")
 
 MNB_F16 = 0
 MNB_BF16 = 1
-MNB_MAX_M = 8
+MNB_MAX_M = 8            # decode kernels; prefill up to MNB_MAX_ROWS
+MNB_MAX_ROWS = 1 << 20
 
 STATUS = {
     0: "MNB_OK", 1: "MNB_ERR_NULL", 2: "MNB_ERR_SHAPE", 3: "MNB_ERR_BLOCK",
@@ -47,7 +48,8 @@ class mnb_plan(ctypes.Structure):
                 ("workgroups", ctypes.c_int32),
                 ("interleave", ctypes.c_int32),
                 ("threads_per_wg", ctypes.c_int32),
-                ("k_chunks", ctypes.c_int32)]
+                ("k_chunks", ctypes.c_int32),
+                ("row_tiles", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -46,7 +46,7 @@ int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
              const uint8_t* Bpacked, const uint16_t* scales,
              const uint8_t* zero_points, int block, void* out, int out_dtype)
 {
-    if (m < 0 || m > MNB_MAX_M) return MNB_ERR_M_RANGE;
+    if (m < 0 || m > MNB_MAX_ROWS) return MNB_ERR_M_RANGE;
     if (K < 0 || N < 0 || K > MNB_MAX_K || N > INT32_MAX) return MNB_ERR_SHAPE;
     if (block != 32) return MNB_ERR_BLOCK;
     if (K % 32 != 0) return MNB_ERR_SHAPE;
@@ -150,9 +150,18 @@ constexpr int64_t kMfmaStageBytes = 128 * 1024;
 
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
 {
-    if (!plan || m < 1 || m > MNB_MAX_M || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
+    if (!plan || m < 1 || m > MNB_MAX_ROWS || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
     if (plan->workgroups < 1) return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
+    if (plan->engine == 2) {
+        if (!is_pow2_in(plan->row_tiles, 1, 8) || plan->cols_per_tile != 64 ||
+            plan->waves_per_wg != 4)
+            return MNB_ERR_PLAN;
+        plan->threads_per_wg = 256;
+        plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
+        return MNB_OK;
+    }
+    if (m > MNB_MAX_M) return MNB_ERR_PLAN;         // decode engines: m <= 8
     if (plan->engine == 1) {
         const int64_t w = plan->waves_per_wg, kcb = plan->chunk_blocks;
         if (w < 1 || w > 8 || kcb < 4 || kcb % 4 || m * kcb * 64 > kMfmaStageBytes)
@@ -185,9 +194,28 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
                      mnb_plan* plan)
 {
     if (!plan) return MNB_ERR_NULL;
-    if (m < 1 || m > MNB_MAX_M) return MNB_ERR_M_RANGE;
+    if (m < 1 || m > MNB_MAX_ROWS) return MNB_ERR_M_RANGE;
     if (K < 0 || K % 32 || K > MNB_MAX_K || N < 1 || N > INT32_MAX) return MNB_ERR_SHAPE;
     if (num_cus < 1) num_cus = 1;
+    *plan = mnb_plan{};
+
+    if (m > MNB_MAX_M) {
+        // Prefill: row tiles up to 8 (128 rows share each unpacked weight),
+        // one resident generation of 64-column workgroups walking the
+        // (row block, column block) tiles.
+        int64_t rt = 1;
+        while (rt < 8 && 16 * rt < m) rt *= 2;
+        const int64_t tiles = ceil_div(m, 16 * rt) * ceil_div(N, 64);
+        const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 2;
+        int64_t wgs = per_cu * num_cus;
+        if (wgs > tiles) wgs = tiles;
+        plan->engine = 2;
+        plan->row_tiles = (int32_t)rt;
+        plan->cols_per_tile = 64;
+        plan->waves_per_wg = 4;
+        plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
+        return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
+    }
     const int64_t nb = K / 32;
     const int64_t bmax = max_blocks_per_lane(m);
 
@@ -320,7 +348,7 @@ const char* mnb_status_string(int status)
     case MNB_ERR_BLOCK: return "block size must be 32";
     case MNB_ERR_DTYPE: return "dtype must be MNB_F16 or MNB_BF16";
     case MNB_ERR_ALIGN: return "A and Bpacked must be 16-byte aligned, scales and out 2-byte aligned";
-    case MNB_ERR_M_RANGE: return "m must be in [0, 8]";
+    case MNB_ERR_M_RANGE: return "m must be in [0, MNB_MAX_ROWS]";
     case MNB_ERR_HIP: return "HIP runtime error (see mnb_last_hip_error)";
     case MNB_ERR_ALIAS: return "out overlaps an input";
     case MNB_ERR_PLAN: return "launch plan not supported";

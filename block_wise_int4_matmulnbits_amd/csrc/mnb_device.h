@@ -29,16 +29,13 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t w, float c)
                                   __builtin_bit_cast(half2_t, w), c, false);
 }
 
-// bf16 bits -> fp16 bits, round to nearest even through the exact fp32 value.
-__device__ __forceinline__ uint32_t bf16_to_f16(uint32_t b)
-{
-    const _Float16 h = (_Float16)__uint_as_float(b << 16);
-    return (uint32_t)__builtin_bit_cast(uint16_t, h);
-}
-
+// Two bf16 -> two fp16, round to nearest even: the exact fp32 values of
+// both halves, then one packed RNE conversion (v_cvt_pk_f16_f32).
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v)
 {
-    return bf16_to_f16(v & 0xFFFFu) | (bf16_to_f16(v >> 16) << 16);
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t f = {__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
 }
 
 // fp16 bits -> bf16 bits: exact widening to fp32, then RNE on the bit
@@ -103,6 +100,22 @@ __device__ __forceinline__ void unpack_dword(uint32_t x, ZeroPoint zp, uint32_t 
     pr[1] = hfma2((x & 0x00F000F0u) | magic, sixteenth, zp.zfma);  // (q1-z, q5-z)
     pr[2] = hadd2((y & 0x000F000Fu) | magic, zp.zneg1);            // (q2-z, q6-z)
     pr[3] = hfma2((y & 0x00F000F0u) | magic, sixteenth, zp.zfma);  // (q3-z, q7-z)
+}
+
+// 4x4 transpose of dwords across the four 16-lane rows of a wave: before,
+// row g holds (r0..r3) = dwords 0..3 of block 4t+g; after, r_i holds dword g
+// of block 4t+i in row g (the MFMA operand layout: lane j+16g supplies
+// k = 8g..8g+7).
+__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
+{
+    const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+    const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
+    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
+    r[0] = s01[0];
+    r[1] = s01[1];
+    r[2] = s23[0];
+    r[3] = s23[1];
 }
 
 // Raw buffer resources (gfx9 layout: 48-bit base, no stride, num_records

@@ -57,21 +57,6 @@ struct MfmaParams {
     int32_t a_bf16, out_bf16;
 };
 
-// 4x4 transpose of dwords across the four 16-lane rows: before, row g holds
-// (r0..r3) = dwords 0..3 of block 4t+g; after, r_i holds dword g of block
-// 4t+i in row g.
-__device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
-{
-    const auto s02 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
-    const auto s13 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
-    const auto s01 = __builtin_amdgcn_permlane16_swap(s02[0], s13[0], false, false);
-    const auto s23 = __builtin_amdgcn_permlane16_swap(s02[1], s13[1], false, false);
-    r[0] = s01[0];
-    r[1] = s01[1];
-    r[2] = s23[0];
-    r[3] = s23[1];
-}
-
 // Quads of weights in flight per wave: a ring of P register sets, refilled
 // as each is consumed, so a wave keeps P*1 KB of weights (plus scales and
 // zero points) in flight instead of one quad.
@@ -97,7 +82,8 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma_kernel(MfmaParams p)
     extern __shared__ uint4 a_lds[];        // [chunk_blocks][M][4] permuted fp16 A
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6, W = (int)(blockDim.x >> 6);
+    const int lane = tid & 63, W = (int)(blockDim.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int j = lane & 15, g = lane >> 4;
     const int nb = p.nb, kcb = p.chunk_blocks;
     const int64_t ntiles = (p.N + 15) / 16;

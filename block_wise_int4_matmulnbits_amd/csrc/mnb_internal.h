@@ -28,6 +28,12 @@ int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
+// The prefill kernel (engine 2), mnb_gemm_mfma.hip.
+int launch_gemm(const GemvArgs& args, const mnb_plan& plan, void* stream);
+int gemm_workgroups_per_cu(const mnb_plan& plan);
+int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info);
+size_t gemm_lds_bytes(const mnb_plan& plan);
+
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);
 

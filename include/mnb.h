@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 1
+#define MNB_ABI_VERSION 2
 
 /* Element types of A and of the output. */
 typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
@@ -46,16 +46,20 @@ typedef enum {
     MNB_ERR_DTYPE = 4,    /* a_dtype or out_dtype not MNB_F16 / MNB_BF16      */
     MNB_ERR_ALIGN = 5,    /* A or Bpacked not 16-byte aligned, scales or out
                              not 2-byte aligned                              */
-    MNB_ERR_M_RANGE = 6,  /* m < 0 or m > MNB_MAX_M                           */
+    MNB_ERR_M_RANGE = 6,  /* m < 0 or m > MNB_MAX_ROWS                        */
     MNB_ERR_HIP = 7,      /* the HIP runtime reported an error; see
                              mnb_last_hip_error()                            */
     MNB_ERR_ALIAS = 8,    /* out overlaps an input buffer                    */
     MNB_ERR_PLAN = 9      /* an explicit plan is not one the library runs   */
 } mnb_status;
 
-/* Row-batched decode bound: one launch serves 1 <= m <= 8 rows (the
- * small-batch row loop of the first page, paragraph "What broke in #1549"). */
+/* Row-batched decode bound: one decode launch serves 1 <= m <= 8 rows (the
+ * small-batch row loop of the first page, paragraph "What broke in #1549").
+ * Beyond it (prefill, m up to MNB_MAX_ROWS) the same call runs a tiled
+ * matrix-core kernel with the same arithmetic and the same narrowing
+ * store (the row-batched path the first page leaves without one). */
 #define MNB_MAX_M 8
+#define MNB_MAX_ROWS (1 << 20)
 /* Largest K accepted (blocks are indexed with 32-bit integers). */
 #define MNB_MAX_K (1 << 24)
 
@@ -65,7 +69,8 @@ typedef enum {
  *   A            device, [m][K] row-major, fp16 or bf16 per a_dtype; 16-byte
  *                aligned.  Must hold finite values that are finite in fp16.
  *   a_dtype      MNB_F16 or MNB_BF16.
- *   m            rows, 0 <= m <= 8.  m == 0 or N == 0: nothing to do, MNB_OK.
+ *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
+ *                prefill kernel).  m == 0 or N == 0: nothing to do, MNB_OK.
  *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).
  *   N            output columns.
  *   Bpacked      device, [N][K/2] bytes; byte k/2 of row n holds weight k,
@@ -105,13 +110,18 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * engine 1 (MFMA tile kernel): a wave owns 16 columns; the waves_per_wg
  * waves of a workgroup split K; activations are staged in LDS,
  * chunk_blocks blocks of K per pass; dot products on
- * v_mfma_f32_16x16x32_f16.  For 2 <= m <= 8.
+ * v_mfma_f32_16x16x32_f16.  For 1 <= m <= 8.
+ * engine 2 (prefill kernel, m > 8): a workgroup of 4 waves owns a tile of
+ * 16 * row_tiles rows by 64 columns (cols_per_tile 64, waves_per_wg 4);
+ * K is walked 128 at a time through LDS; v_mfma_f32_16x16x32_f16 per
+ * block and row tile.  Also accepted for any m >= 1 as an explicit plan.
  */
 typedef struct {
-    int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel */
+    int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel;
+                                2: prefill kernel                               */
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8                          */
-    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16             */
+    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16; engine 2: 64 */
     int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K                 */
     int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
     int32_t workgroups;      /* grid size, >= 1                                  */
@@ -120,6 +130,7 @@ typedef struct {
                                 groups round-robin                               */
     int32_t threads_per_wg;  /* derived by mnb_plan_check                        */
     int32_t k_chunks;        /* derived: passes over K                           */
+    int32_t row_tiles;       /* engine 2: 16-row tiles per workgroup, 1/2/4/8    */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`
@@ -131,7 +142,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
                      mnb_plan* plan);
 
 /* Validate a plan for (m, K, N) and fill its derived fields
- * (threads_per_wg, k_chunks).  Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */
+ * (threads_per_wg, k_chunks).  The decode engines (0, 1) take m <= 8.
+ * Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan);
 
 /* matmul_nbits with an explicit plan (after mnb_plan_check); same arguments,

@@ -39,7 +39,7 @@ FAKE = 0x10000  # never dereferenced: validation fails first
 
 
 @pytest.mark.parametrize("args,status", [
-    (dict(m=9), 6), (dict(m=-1), 6), (dict(K=33), 2), (dict(K=-32), 2),
+    (dict(m=(1 << 20) + 1), 6), (dict(m=-1), 6), (dict(K=33), 2), (dict(K=-32), 2),
     (dict(N=-1), 2), (dict(block=64), 3), (dict(a_dtype=2), 4),
     (dict(out_dtype=-1), 4), (dict(A=0), 1), (dict(B=0), 1), (dict(S=0), 1),
     (dict(out=0), 1), (dict(A=FAKE + 8), 5), (dict(B=FAKE * 3 + 4), 5),
@@ -84,6 +84,44 @@ def test_default_plans_are_valid_and_cover_k():
             gpw = 256 // lpc if lpc <= 64 else 1
             groups = p.workgroups * gpw
             assert 1 <= groups <= N + gpw - 1   # no workgroup without columns
+
+
+PREFILL_SHAPES = [(m, K, N) for m in (9, 16, 17, 100, 1000, 4096, 1 << 20)
+                  for K in (0, 32, 96, 4096, 14336, 32 * 611)
+                  for N in (1, 63, 64, 4096, 151936)]
+
+
+def test_default_prefill_plans():
+    """m > 8 runs the prefill engine: 16-row tiles (up to 8 per workgroup,
+    never more than the rows need), 64 columns per workgroup, no more
+    workgroups than tiles."""
+    for m, K, N in PREFILL_SHAPES:
+        for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
+            p = mnb.mnb_plan_default(m, K, N, cus, occ)
+            assert p.engine == 2 and p.cols_per_tile == 64 and p.waves_per_wg == 4
+            q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
+            assert mnb.mnb_plan_check(m, K, N, q) == 0
+            assert q.threads_per_wg == 256 and q.k_chunks == (K // 32 + 3) // 4
+            rt = p.row_tiles
+            assert rt in (1, 2, 4, 8) and (rt == 1 or 16 * (rt // 2) < m) and (rt == 8 or 16 * rt >= m)
+            tiles = -(-m // (16 * rt)) * -(-N // 64)
+            assert 1 <= p.workgroups <= tiles
+
+
+def test_plan_check_engines_and_rows():
+    p = mnb.mnb_plan(engine=2, row_tiles=4, cols_per_tile=64, waves_per_wg=4, workgroups=3)
+    assert mnb.mnb_plan_check(3, 4096, 100, p) == 0            # engine 2 takes any m >= 1
+    assert mnb.mnb_plan_check(5000, 4096, 100, p) == 0
+    for bad in (dict(row_tiles=3), dict(row_tiles=16), dict(cols_per_tile=16),
+                dict(waves_per_wg=8), dict(workgroups=0)):
+        q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=4, cols_per_tile=64, waves_per_wg=4,
+                                     workgroups=3), **bad))
+        assert mnb.mnb_plan_check(20, 4096, 100, q) == 9
+    d = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=1, cols_per_tile=1, workgroups=1)
+    assert mnb.mnb_plan_check(8, 4096, 100, d) == 0
+    assert mnb.mnb_plan_check(9, 4096, 100, d) == 9            # decode engines: m <= 8
+    e1 = mnb.mnb_plan(engine=1, cols_per_tile=16, waves_per_wg=4, chunk_blocks=128, workgroups=1)
+    assert mnb.mnb_plan_check(9, 4096, 100, e1) == 9
 
 
 def test_summation_order_does_not_depend_on_n_or_device():

@@ -298,8 +298,8 @@ def test_errors_do_not_launch():
     st = L.matmul_nbits(A.data_ptr(), 0, 1, 256, 64, B.data_ptr(), S.data_ptr(),
                         Z.data_ptr(), 32, A.data_ptr(), 0, None)
     assert st == 8
-    st = L.matmul_nbits(A.data_ptr(), 0, 9, 256, 64, B.data_ptr(), S.data_ptr(),
-                        Z.data_ptr(), 32, base, 0, None)
+    st = L.matmul_nbits(A.data_ptr(), 0, mnb.MNB_MAX_ROWS + 1, 256, 64, B.data_ptr(),
+                        S.data_ptr(), Z.data_ptr(), 32, base, 0, None)
     assert st == 6
     torch.cuda.synchronize()
     assert np.all(G.bits(out) == 0xFFFF)
