@@ -154,10 +154,11 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->workgroups < 1) return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
-        if (!is_pow2_in(plan->row_tiles, 1, 8) || plan->cols_per_tile != 64 ||
-            plan->waves_per_wg != 4)
+        if (!is_pow2_in(plan->row_tiles, 1, 4) || !is_pow2_in(plan->cols_per_tile, 128, 256) ||
+            plan->waves_per_wg != mnb::kPrefillWaves ||
+            (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
             return MNB_ERR_PLAN;
-        plan->threads_per_wg = 256;
+        plan->threads_per_wg = 64 * mnb::kPrefillWaves;
         plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
         return MNB_OK;
     }
@@ -200,19 +201,24 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     *plan = mnb_plan{};
 
     if (m > MNB_MAX_M) {
-        // Prefill: row tiles up to 8 (128 rows share each unpacked weight),
-        // one resident generation of 64-column workgroups walking the
-        // (row block, column block) tiles.
+        // Prefill: the largest tile (rows first: every unpacked weight feeds
+        // 32 * row_tiles rows; then columns: every activation operand read
+        // feeds cols_per_tile / 128 matrix products) that still gives every
+        // compute unit a workgroup; one resident generation walking the tiles.
         int64_t rt = 1;
-        while (rt < 8 && 16 * rt < m) rt *= 2;
-        const int64_t tiles = ceil_div(m, 16 * rt) * ceil_div(N, 64);
-        const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 2;
+        while (rt < 4 && 32 * rt < m) rt *= 2;
+        while (rt > 1 && (uint64_t)64 * rt * (uint64_t)K > mnb::kPrefillRowBlockBytes) rt /= 2;
+        auto tiles = [&](int64_t r, int64_t c) { return ceil_div(m, 32 * r) * ceil_div(N, c); };
+        int64_t cols = 256;
+        while (cols > 128 && tiles(rt, cols) < num_cus) cols /= 2;
+        while (rt > 1 && tiles(rt, cols) < num_cus) rt /= 2;
+        const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
         int64_t wgs = per_cu * num_cus;
-        if (wgs > tiles) wgs = tiles;
+        if (wgs > tiles(rt, cols)) wgs = tiles(rt, cols);
         plan->engine = 2;
         plan->row_tiles = (int32_t)rt;
-        plan->cols_per_tile = 64;
-        plan->waves_per_wg = 4;
+        plan->cols_per_tile = (int32_t)cols;
+        plan->waves_per_wg = mnb::kPrefillWaves;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

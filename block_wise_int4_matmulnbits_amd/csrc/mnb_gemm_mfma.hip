@@ -1,36 +1,46 @@
 // Prefill INT4 MatMulNBits (m > 8 rows) on the matrix cores of gfx950.
 //
-//   y[r][n] = sum_k a[r][k] * (q[n][k] - z[n][k/32]) * s[n][k/32]
+//   y[r][n] = sum_k a[r][k] * w[n][k],   w[n][k] = (q[n][k] - z[n][k/32]) * s[n][k/32]
 //
-// The same operation, arithmetic and epilogue as the decode kernels
-// (onnx-genai pull request "perf(cuda): let the split-K decode GEMV store
-// bf16 directly", opening paragraphs and the paragraph on
-// matmul_nbits_store_narrowed; pull request "PORT-1 (offline
-// bias+interleave)", "Why the premise fails here", item 1): weights enter
-// the products as exact fp16 integers q - z, each 32-weight block's fp32
-// product is scaled by its fp16 scale in fp32, the fp32 sum is rounded to
-// fp16 once and, for bf16 output, narrowed to bf16 in the same kernel.
-// The first page names a row-batched path without the narrowing store as
-// the next step; this is that path with the store.
+// The operation and epilogue of the decode kernels (onnx-genai pull request
+// "perf(cuda): let the split-K decode GEMV store bf16 directly", opening
+// paragraphs and the paragraph on matmul_nbits_store_narrowed; pull request
+// "PORT-1 (offline bias+interleave)", "Why the premise fails here", item 1):
+// fp16 (or bf16 rounded to fp16) activations, fp32 accumulation, one fp16
+// rounding of the sum and, for bf16 output, the narrowing to bf16 in the
+// same kernel.  The first page names a row-batched path without the
+// narrowing store as the next step; this is that path with the store.
+//
+// Weights.  Each weight is dequantized to fp16 the way the second page's
+// GEMV holds it (a packed-half scale and zero-point subtrahend per block,
+// "Why the premise fails here", item 3): the nibble becomes the exact fp16
+// integer q - z, and one packed fp16 multiply by the block's scale rounds
+// (q - z) * s to fp16 (RNE, gradual underflow).  The matrix core then
+// multiplies exact fp16 products into fp32 accumulators that run over all of
+// K, so there is no per-block fp32 result to scale.  Against the exact
+// weights the rounding adds at most 2^-11 |a w| per product (normal fp16
+// range), inside the decode path's tolerance.
 //
 // Work decomposition.  A workgroup of four waves owns an output tile of
-// 16*RT rows by 64 columns; wave w owns columns 16w .. 16w+15 of it and all
-// RT row tiles, so each weight it unpacks feeds RT MFMAs.  K is walked one
-// quad (4 blocks, 128 k) at a time:
-//   - activations of the quad (16*RT rows x 128 k) are loaded by all 256
-//     threads, converted to fp16, permuted into the unpack's pair order and
-//     written to one of two LDS buffers ([block][row][16-byte piece], so the
-//     operand reads of a wave are 1 KB contiguous);
-//   - lane (j, g) loads block 4t+g of column j (16 bytes) with the quad's 4
-//     scales (8 bytes) and zero points (2 bytes); two v_permlane32_swap and
-//     two v_permlane16_swap put dword g of every block of the quad in row g
-//     (the B operand layout), and the nibbles become exact fp16 pairs q - z;
-//   - per block and row tile one v_mfma_f32_16x16x32_f16 (A rows from LDS,
-//     B = the unpacked block), whose fp32 result is scaled by the block's
-//     scale into the row tile's accumulators.
-// Weight loads run three quads ahead of use, activation loads two.  The
+// 32*RT rows by 128*CT columns; wave w owns columns 32*CT*w .. 32*CT*(w+1)-1
+// of it and all RT row tiles, so each weight it unpacks feeds RT matrix
+// products and each activation operand it reads from LDS feeds CT.  The
+// products are v_mfma_f32_32x32x16_f16 (on gfx950 twice the rate of the
+// 16x16x32 shape), two per 32-weight block.  K is walked one quad (4 blocks,
+// 128 k) at a time:
+//   - activations of the quad (32*RT rows x 128 k) are loaded by all 256
+//     threads, converted to fp16 (bf16 rounded to nearest even) in the
+//     unpack's pair order and written to one of two LDS buffers;
+//   - for each of its CT column tiles, lane (j, h) loads blocks 4t+h and
+//     4t+2+h of column j (16 bytes each) with the quad's 4 scales and zero
+//     points; v_permlane32_swap leaves dwords 2h, 2h+1 of every block of the
+//     quad in lane half h (the B operand layout: half h supplies k = 16h+8s
+//     .. 16h+8s+7 to product s of the block);
+//   - per block: unpack and scale the CT column tiles, then per row tile and
+//     product one LDS read and CT MFMAs into the accumulators.
+// Weight loads run two quads ahead of use, activation loads one.  The
 // summation order of an output depends only on K: equal inputs give equal
-// bits for any M, N and grid.
+// bits for any M, N, tiling and grid.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -42,7 +52,8 @@ namespace mnb {
 namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct GemmParams {
@@ -57,155 +68,252 @@ struct GemmParams {
     int32_t a_bf16, out_bf16;
 };
 
-constexpr int kGemmWaves = 4;      // waves per workgroup (64 output columns)
-constexpr int kGemmRing = 3;       // weight quads in flight per wave
+constexpr int kGemmThreads = 64 * kPrefillWaves;
+constexpr int kGemmRing = 2;             // weight quads in flight per column tile
 
 struct WQuad {
-    u32x4 w;          // 16 bytes: block 4t+g of this lane's column
+    u32x4 w[2];       // load u: 16 bytes of block 4t+2u+h of this lane's column
     uint32_t s[4];    // fp16 scales of blocks 4t..4t+3 (VEC: two words)
     uint32_t z[2];    // zero-point bytes 2t, 2t+1 (VEC: one 16-bit word)
 };
 
-template <int RT, bool VEC>
-__global__ __launch_bounds__(256) void mnb_gemm_mfma_kernel(GemmParams p)
+// Packed fp16 product (one rounding, RNE).
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b)
 {
-    constexpr int MT = 16 * RT;              // rows per workgroup tile
+    const half2_t r = __builtin_bit_cast(half2_t, a) * __builtin_bit_cast(half2_t, b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Two fp16 halves (lo from x, lo or hi per `hi`, and likewise from y) into
+// one dword: the pair (x_e, y_e) of the unpack's order.
+__device__ __forceinline__ uint32_t pair16(uint32_t x, uint32_t y, bool hi)
+{
+    return __builtin_amdgcn_perm(y, x, hi ? 0x07060302u : 0x05040100u);
+}
+
+// Two bf16 (the low or high halves of x and y) -> fp16 pair, RNE.
+__device__ __forceinline__ uint32_t pair_bf16(uint32_t x, uint32_t y, bool hi)
+{
+    const float2_t f = hi ? float2_t{__uint_as_float(x & 0xFFFF0000u), __uint_as_float(y & 0xFFFF0000u)}
+                          : float2_t{__uint_as_float(x << 16), __uint_as_float(y << 16)};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
+}
+
+// LDS slot of 16-byte piece d (k = 8d .. 8d+7) of row r: the XOR spreads
+// the 16-byte reads of 8 or 16 consecutive rows over all banks.
+__device__ __forceinline__ int a_slot(int d, int r)
+{
+    return d ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+template <int RT, int CT, bool VEC, bool ABF16>
+__global__ __launch_bounds__(kGemmThreads) void mnb_gemm_mfma_kernel(GemmParams p)
+{
+    constexpr int THREADS = kGemmThreads;
+    constexpr int MT = 32 * RT;              // rows per workgroup tile
+    constexpr int NT = 32 * CT * kPrefillWaves;   // columns per workgroup tile
     constexpr int QA = 16 * MT;              // 16-byte pieces of activations per quad
+    constexpr int SPT = QA / THREADS;        // pieces per thread
+    static_assert(QA % THREADS == 0, "whole pieces per thread");
     constexpr int P = kGemmRing;
-    extern __shared__ uint4 a_lds[];         // [2][4 blocks][MT rows][4 pieces]
+    extern __shared__ uint4 a_lds[];         // [2][4 blocks][MT rows][4 slots]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int j = lane & 15, g = lane >> 4;
+    const int j = lane & 31, h = lane >> 5;
     const int nb = p.nb;
     const int nq = (nb + 3) / 4;
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t zdef = p.zp ? 0u : 8u;    // zero point 8 when none are given
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);
     const int64_t tiles_m = (p.M + MT - 1) / MT;
-    const int64_t tiles_n = (p.N + 63) / 64;
+    const int64_t tiles_n = (p.N + NT - 1) / NT;
 
-    // Eight activations to fp16 (bf16 rounded to nearest even), permuted
-    // into the unpack's pair order.
-    auto to_pairs = [&](uint4 v) {
-        uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
-        if (p.a_bf16) {
-            x = bf16x2_to_f16x2(x);
-            y = bf16x2_to_f16x2(y);
-            z = bf16x2_to_f16x2(z);
-            w = bf16x2_to_f16x2(w);
-        }
-        uint4 o;
-        o.x = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
-        o.y = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
-        o.z = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
-        o.w = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
-        return o;
-    };
+    // Piece e of a quad's activations (e = tid + THREADS * s): block
+    // e / (4 MT), row (e / 4) % MT, piece e % 4; its LDS index and its byte
+    // offset in the row block are fixed per thread.
+    int pc_blk[SPT], pc_lds[SPT];
+    uint32_t pc_off[SPT];
+#pragma unroll
+    for (int s = 0; s < SPT; ++s) {
+        const int e = tid + THREADS * s;
+        const int br = e >> 2, d = e & 3;
+        const int blk = br / MT, row = br - blk * MT;
+        pc_blk[s] = blk;
+        pc_lds[s] = (blk * MT + row) * 4 + a_slot(d, row);
+        pc_off[s] = (uint32_t)row * (uint32_t)p.K * 2 + 64 * blk + 16 * d;
+    }
 
     for (int64_t tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
         // Consecutive workgroups share a row block (its activations stay in
         // L2) and walk the column blocks.
         const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
         const int64_t r0 = tm * MT;
-        const int64_t col0 = tn * 64 + 16 * wv;   // this wave's 16 columns
+        const int64_t col0 = tn * NT + 32 * CT * wv;   // this wave's 32*CT columns
         const int64_t left = p.N - col0;
-        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 16 ? left : 16);
+        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 32 * CT ? left : 32 * CT);
         const int64_t cb = left <= 0 ? 0 : col0;
-        // Buffer resources over the wave's 16 column rows; loads past their
-        // end (columns past N, blocks past K, quads past K, absent zero
-        // points) return zeros without touching memory.
+        // Buffer resources over the wave's column rows and the tile's
+        // activation rows; loads past their end (columns past N, rows past
+        // M, blocks past K, absent zero points) return zeros without
+        // touching memory.  The host keeps 32 * RT * K * 2 below 2^32.
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + cb * row_bytes, (uint64_t)ncols * row_bytes);
         const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + cb * nb, (uint64_t)ncols * nb * 2);
         const __amdgpu_buffer_rsrc_t rZ =
             make_rsrc(p.zp ? p.zp + cb * p.zb : p.B, p.zp ? (uint64_t)ncols * p.zb : 0);
-        const uint32_t wbase = (uint32_t)j * row_bytes + 16 * (uint32_t)g;
-        const uint32_t sbase = (uint32_t)j * (uint32_t)nb * 2;
-        const uint32_t zbase = (uint32_t)j * (uint32_t)p.zb;
+        const int64_t mrows = p.M - r0 < MT ? p.M - r0 : MT;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + r0 * p.K, (uint64_t)mrows * (uint64_t)p.K * 2);
 
-        auto issue = [&](WQuad& q, int t) {
-            const bool live = t < nq;
+        // Column tile c of the wave: columns col0 + 32c + j.
+        auto issue = [&](WQuad (&qs)[CT], int t) {
             const uint32_t b = 4 * (uint32_t)t;
-            q.w = __builtin_amdgcn_raw_buffer_load_b128(
-                rB, live && b + g < (uint32_t)nb ? wbase + 16 * b : kOutOfRange, 0, kNontemporal);
-            if constexpr (VEC) {
-                const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(
-                    rS, live ? sbase + 2 * b : kOutOfRange, 0, kNontemporal);
-                q.s[0] = sv[0];
-                q.s[1] = sv[1];
-                q.z[0] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rZ, live ? zbase + b / 2 : kOutOfRange, 0, kNontemporal);
-            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    q.s[i] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rS, live && b + i < (uint32_t)nb ? sbase + 2 * (b + i) : kOutOfRange, 0,
+            for (int c = 0; c < CT; ++c) {
+                WQuad& q = qs[c];
+                const uint32_t jc = (uint32_t)(32 * c + j);
+                const uint32_t wbase = jc * row_bytes + 16 * (uint32_t)h;
+                const uint32_t sbase = jc * (uint32_t)nb * 2;
+                const uint32_t zbase = jc * (uint32_t)p.zb;
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    q.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rB, b + 2 * u + h < (uint32_t)nb ? wbase + 16 * (b + 2 * u) : kOutOfRange, 0,
                         kNontemporal);
+                if constexpr (VEC) {
+                    const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(
+                        rS, b < (uint32_t)nb ? sbase + 2 * b : kOutOfRange, 0, kNontemporal);
+                    q.s[0] = sv[0];
+                    q.s[1] = sv[1];
+                    q.z[0] = __builtin_amdgcn_raw_buffer_load_b16(
+                        rZ, b < (uint32_t)nb ? zbase + b / 2 : kOutOfRange, 0, kNontemporal);
+                } else {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    q.z[i] = __builtin_amdgcn_raw_buffer_load_b8(
-                        rZ, live && b / 2 + i < (uint32_t)p.zb ? zbase + b / 2 + i : kOutOfRange, 0,
-                        kNontemporal);
-            }
-        };
-
-        // Activations of quad t: thread tid holds pieces tid + 256 s, piece e
-        // = (block * MT + row) * 4 + piece16 (zeros past M and past K).
-        auto fetch_a = [&](uint4 (&v)[RT], int t) {
+                    for (int i = 0; i < 4; ++i)
+                        q.s[i] = __builtin_amdgcn_raw_buffer_load_b16(
+                            rS, b + i < (uint32_t)nb ? sbase + 2 * (b + i) : kOutOfRange, 0, kNontemporal);
 #pragma unroll
-            for (int s = 0; s < RT; ++s) {
-                const int e = tid + 256 * s;
-                const int br = e >> 2, piece = e & 3;
-                const int i = br / MT, row = br - i * MT;
-                const int64_t r = r0 + row;
-                const int b = 4 * t + i;
-                v[s] = make_uint4(0, 0, 0, 0);
-                if (t < nq && r < p.M && b < nb)
-                    v[s] = *reinterpret_cast<const uint4*>(p.A + r * p.K + 32 * (int64_t)b + 8 * piece);
-            }
-        };
-        auto store_a = [&](const uint4 (&v)[RT], int buf) {
-#pragma unroll
-            for (int s = 0; s < RT; ++s) a_lds[buf * QA + tid + 256 * s] = to_pairs(v[s]);
-        };
-
-        float acc[RT][4];
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) acc[rt][rr] = 0.f;
-
-        // Unpack the quad's four blocks, one MFMA per block and row tile,
-        // scale the block products into the accumulators.
-        auto compute = [&](const WQuad& q, int buf) {
-            uint32_t r[4] = {q.w[0], q.w[1], q.w[2], q.w[3]};
-            transpose_rows(r);
-            const uint32_t zw = VEC ? q.z[0] : ((q.z[0] & 0xFFu) | ((q.z[1] & 0xFFu) << 8));
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t bq[4];
-                unpack_dword(r[i], zero_point_pairs(((zw >> (4 * i)) & 0xFu) | zdef), magic, bq);
-                const u32x4 bv = {bq[0], bq[1], bq[2], bq[3]};
-                const uint32_t sw = VEC ? (i < 2 ? q.s[0] : q.s[1]) >> (16 * (i & 1)) : q.s[i];
-                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(sw & 0xFFFFu));
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    const uint4 av = a_lds[buf * QA + ((i * MT + rt * 16 + j) * 4 + g)];
-                    const u32x4 aw = {av.x, av.y, av.z, av.w};
-                    const float4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                        __builtin_bit_cast(half8_t, aw), __builtin_bit_cast(half8_t, bv),
-                        float4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-#pragma unroll
-                    for (int rr = 0; rr < 4; ++rr) acc[rt][rr] = fmaf(d[rr], sf, acc[rt][rr]);
+                    for (int i = 0; i < 2; ++i)
+                        q.z[i] = __builtin_amdgcn_raw_buffer_load_b8(
+                            rZ, b / 2 + i < (uint32_t)p.zb ? zbase + b / 2 + i : kOutOfRange, 0, kNontemporal);
                 }
             }
         };
 
-        WQuad ring[P];
+        // Activations of quad t (zeros past M and K).
+        auto fetch_a = [&](uint4 (&v)[SPT], int t) {
+#pragma unroll
+            for (int s = 0; s < SPT; ++s) {
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+                    rA, 4 * t + pc_blk[s] < nb ? pc_off[s] + 256 * (uint32_t)t : kOutOfRange, 0, 0);
+                v[s] = make_uint4(x[0], x[1], x[2], x[3]);
+            }
+        };
+        // Eight activations to fp16 in the unpack's pair order
+        // (a0,a4) (a1,a5) (a2,a6) (a3,a7), into LDS.
+        auto store_a = [&](const uint4 (&v)[SPT], int buf) {
+#pragma unroll
+            for (int s = 0; s < SPT; ++s) {
+                const uint4 x = v[s];
+                uint4 o;
+                if constexpr (ABF16) {
+                    o.x = pair_bf16(x.x, x.z, false);
+                    o.y = pair_bf16(x.x, x.z, true);
+                    o.z = pair_bf16(x.y, x.w, false);
+                    o.w = pair_bf16(x.y, x.w, true);
+                } else {
+                    o.x = pair16(x.x, x.z, false);
+                    o.y = pair16(x.x, x.z, true);
+                    o.z = pair16(x.y, x.w, false);
+                    o.w = pair16(x.y, x.w, true);
+                }
+                a_lds[buf * QA + pc_lds[s]] = o;
+            }
+        };
+
+        float16_t acc[RT][CT];
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[rt][c][q] = 0.f;
+
+        // The A operands of block i: row tile rt, product v (k = 16h + 8v ..).
+        auto read_a = [&](half8_t (&f)[RT][2], int buf, int i) {
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    const int row = rt * 32 + j;
+                    const uint4 av = a_lds[buf * QA + (i * MT + row) * 4 + a_slot(2 * h + v, row)];
+                    f[rt][v] = __builtin_bit_cast(half8_t, u32x4{av.x, av.y, av.z, av.w});
+                }
+        };
+
+        // Unpack and scale the quad's four blocks of every column tile; two
+        // MFMAs per block, row tile and column tile.  The A operands of the
+        // next block are read from LDS while the current block multiplies.
+        auto compute = [&](const WQuad (&qs)[CT], int buf) {
+            // blk[c][i][v]: dword 2h+v of block 4t+i of column tile c.
+            uint32_t blk[CT][4][2];
+            uint32_t zw[CT];
+#pragma unroll
+            for (int c = 0; c < CT; ++c) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    // Lane half h holds block 4t+2u+h; swap so that half h
+                    // holds dwords 2h, 2h+1 of blocks 4t+2u and 4t+2u+1.
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(qs[c].w[u][0], qs[c].w[u][2], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(qs[c].w[u][1], qs[c].w[u][3], false, false);
+                    blk[c][2 * u][0] = s0[0];
+                    blk[c][2 * u][1] = s1[0];
+                    blk[c][2 * u + 1][0] = s0[1];
+                    blk[c][2 * u + 1][1] = s1[1];
+                }
+                zw[c] = VEC ? qs[c].z[0] : ((qs[c].z[0] & 0xFFu) | ((qs[c].z[1] & 0xFFu) << 8));
+            }
+            auto unpack = [&](half8_t (&bv)[CT][2], int i) {
+#pragma unroll
+                for (int c = 0; c < CT; ++c) {
+                    const ZeroPoint zp = zero_point_pairs(((zw[c] >> (4 * i)) & 0xFu) | zdef);
+                    const uint32_t sw = VEC ? (i < 2 ? qs[c].s[0] : qs[c].s[1]) : qs[c].s[i];
+                    const uint32_t s2 = __builtin_amdgcn_perm(sw, sw, (VEC && (i & 1)) ? 0x03020302u : 0x01000100u);
+#pragma unroll
+                    for (int v = 0; v < 2; ++v) {
+                        uint32_t bq[4];
+                        unpack_dword(blk[c][i][v], zp, magic, bq);
+                        const u32x4 wq = {hmul2(bq[0], s2), hmul2(bq[1], s2), hmul2(bq[2], s2), hmul2(bq[3], s2)};
+                        bv[c][v] = __builtin_bit_cast(half8_t, wq);
+                    }
+                }
+            };
+            half8_t fa[2][RT][2];
+            half8_t bv[2][CT][2];
+            read_a(fa[0], buf, 0);
+            unpack(bv[0], 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int cur = i & 1, nxt = cur ^ 1;
+                if (i < 3) read_a(fa[nxt], buf, i + 1);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int v = 0; v < 2; ++v)
+#pragma unroll
+                        for (int c = 0; c < CT; ++c)
+                            acc[rt][c] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[cur][rt][v], bv[cur][c][v],
+                                                                                acc[rt][c], 0, 0, 0);
+                if (i < 3) unpack(bv[nxt], i + 1);
+            }
+        };
+
+        // The loop body has no branches: quads past K (the odd last one of a
+        // pair, and the prefetches past the end) load zeros and add +0.
+        WQuad ring[P][CT];
 #pragma unroll
         for (int s = 0; s < P; ++s) issue(ring[s], s);
-        uint4 av[RT];
+        uint4 av[SPT];
         fetch_a(av, 0);
         __syncthreads();                  // the previous tile's readers are done
         store_a(av, 0);
@@ -214,54 +322,67 @@ __global__ __launch_bounds__(256) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
             for (int s = 0; s < P; ++s) {
                 const int t = t0 + s;
-                if (t < nq) {
-                    // Buffer t&1 is complete, and every wave is done with
-                    // buffer (t+1)&1 (it held quad t-1).
-                    __syncthreads();
-                    if (t + 1 < nq) store_a(av, (t + 1) & 1);
-                    fetch_a(av, t + 2);
-                    compute(ring[s], t & 1);
-                }
+                // Buffer t&1 is complete, and every wave is done with buffer
+                // (t+1)&1 (it held quad t-1).
+                __syncthreads();
+                store_a(av, (t + 1) & 1);
+                compute(ring[s], t & 1);
+                fetch_a(av, t + 2);
                 issue(ring[s], t + P);
             }
         }
 
         // Epilogue: fp32 -> fp16 (RNE), optionally -> bf16 (RNE), store.
-        const int64_t col = col0 + j;
-        if (col < p.N) {
+        // Accumulator element q of lane (j, h) is row (q%4) + 4h + 8(q/4),
+        // column j of its 32 x 32 tile.
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt)
+        for (int c = 0; c < CT; ++c) {
+            const int64_t col = col0 + 32 * c + j;
+            if (col < p.N) {
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const int64_t row = r0 + rt * 16 + 4 * g + rr;
-                    if (row < p.M) {
-                        const _Float16 h = (_Float16)acc[rt][rr];
-                        uint16_t bits = __builtin_bit_cast(uint16_t, h);
-                        if (p.out_bf16) bits = f16_to_bf16(bits);
-                        p.out[row * p.N + col] = bits;
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int64_t row = r0 + rt * 32 + (q & 3) + 4 * h + 8 * (q >> 2);
+                        if (row < p.M) {
+                            const _Float16 hv = (_Float16)acc[rt][c][q];
+                            uint16_t bits = __builtin_bit_cast(uint16_t, hv);
+                            if (p.out_bf16) bits = f16_to_bf16(bits);
+                            p.out[row * p.N + col] = bits;
+                        }
                     }
-                }
+            }
         }
     }
 }
 
 typedef void (*GemmFn)(GemmParams);
 
-template <bool VEC>
-GemmFn lookup_gemm_vec(int rt)
+template <int CT, bool VEC, bool ABF16>
+GemmFn lookup_gemm_ct(int rt)
 {
     switch (rt) {
-    case 1: return mnb_gemm_mfma_kernel<1, VEC>;
-    case 2: return mnb_gemm_mfma_kernel<2, VEC>;
-    case 4: return mnb_gemm_mfma_kernel<4, VEC>;
-    case 8: return mnb_gemm_mfma_kernel<8, VEC>;
+    case 1: return mnb_gemm_mfma_kernel<1, CT, VEC, ABF16>;
+    case 2: return mnb_gemm_mfma_kernel<2, CT, VEC, ABF16>;
+    case 4: return mnb_gemm_mfma_kernel<4, CT, VEC, ABF16>;
     }
     return nullptr;
 }
 
-GemmFn lookup_gemm(int rt, bool vec)
+template <bool VEC, bool ABF16>
+GemmFn lookup_gemm_cols(int rt, int cols)
 {
-    return vec ? lookup_gemm_vec<true>(rt) : lookup_gemm_vec<false>(rt);
+    switch (cols) {   // cols_per_tile = 128 CT
+    case 128: return lookup_gemm_ct<1, VEC, ABF16>(rt);
+    case 256: return lookup_gemm_ct<2, VEC, ABF16>(rt);
+    }
+    return nullptr;
+}
+
+GemmFn lookup_gemm(int rt, int cols, bool vec, bool a_bf16)
+{
+    if (vec) return a_bf16 ? lookup_gemm_cols<true, true>(rt, cols) : lookup_gemm_cols<true, false>(rt, cols);
+    return a_bf16 ? lookup_gemm_cols<false, true>(rt, cols) : lookup_gemm_cols<false, false>(rt, cols);
 }
 
 bool gemm_vec_ok(int64_t K, const void* scales, const void* zp)
@@ -273,12 +394,12 @@ bool gemm_vec_ok(int64_t K, const void* scales, const void* zp)
 
 size_t gemm_lds_bytes(const mnb_plan& plan)
 {
-    return (size_t)2 * 4 * 16 * plan.row_tiles * 4 * 16;
+    return (size_t)2 * 4 * 32 * plan.row_tiles * 4 * 16;   // two quads of 32*rt rows x 128 k, fp16
 }
 
 int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, gemm_vec_ok(a.K, a.scales, a.zp));
+    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, gemm_vec_ok(a.K, a.scales, a.zp), a.a_bf16 != 0);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     GemmParams p;
     p.A = static_cast<const uint16_t*>(a.A);
@@ -296,7 +417,7 @@ int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.out_bf16 = a.out_bf16;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
-                                   dim3((unsigned)plan.workgroups), dim3(64 * kGemmWaves), args,
+                                   dim3((unsigned)plan.workgroups), dim3(kGemmThreads), args,
                                    gemm_lds_bytes(plan), static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
     return (int)e;
@@ -304,14 +425,14 @@ int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
 
 int gemm_workgroups_per_cu(const mnb_plan& plan)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, true);
+    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, true, true);
     if (!fn) return 0;
-    return occupancy(reinterpret_cast<const void*>(fn), 64 * kGemmWaves, gemm_lds_bytes(plan));
+    return occupancy(reinterpret_cast<const void*>(fn), kGemmThreads, gemm_lds_bytes(plan));
 }
 
 int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, true);
+    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, true, true);
     if (!fn) return -1;
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));

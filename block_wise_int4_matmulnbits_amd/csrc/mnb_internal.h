@@ -28,7 +28,14 @@ int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
-// The prefill kernel (engine 2), mnb_gemm_mfma.hip.
+// The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of
+// kPrefillWaves waves owns 32 * row_tiles rows by cols_per_tile columns
+// (128 or 256: 32 or 64 per wave).
+constexpr int kPrefillWaves = 4;
+// A workgroup's activation rows (32 * row_tiles rows of K fp16) are
+// addressed with 32-bit buffer offsets: 64 * row_tiles * K must stay within
+// this many bytes.
+constexpr uint64_t kPrefillRowBlockBytes = 0xFFFFFFF0u;
 int launch_gemm(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int gemm_workgroups_per_cu(const mnb_plan& plan);
 int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info);

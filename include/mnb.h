@@ -56,8 +56,12 @@ typedef enum {
 /* Row-batched decode bound: one decode launch serves 1 <= m <= 8 rows (the
  * small-batch row loop of the first page, paragraph "What broke in #1549").
  * Beyond it (prefill, m up to MNB_MAX_ROWS) the same call runs a tiled
- * matrix-core kernel with the same arithmetic and the same narrowing
- * store (the row-batched path the first page leaves without one). */
+ * matrix-core kernel with the same narrowing store (the row-batched path the
+ * first page leaves without one).  The prefill kernel multiplies fp16
+ * weights: each (q - z) * s is rounded to fp16 (RNE) before the product, as
+ * the second page's packed-half dequant holds it ("Why the premise fails
+ * here", item 3); the decode kernels use the exact q - z and scale each
+ * block's fp32 sum. */
 #define MNB_MAX_M 8
 #define MNB_MAX_ROWS (1 << 20)
 /* Largest K accepted (blocks are indexed with 32-bit integers). */
@@ -111,18 +115,20 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * waves of a workgroup split K; activations are staged in LDS,
  * chunk_blocks blocks of K per pass; dot products on
  * v_mfma_f32_16x16x32_f16.  For 1 <= m <= 8.
- * engine 2 (prefill kernel, m > 8): a workgroup of 4 waves owns a tile of
- * 16 * row_tiles rows by 64 columns (cols_per_tile 64, waves_per_wg 4);
- * K is walked 128 at a time through LDS; v_mfma_f32_16x16x32_f16 per
- * block and row tile.  Also accepted for any m >= 1 as an explicit plan.
+ * engine 2 (prefill kernel, m > 8): a workgroup of waves_per_wg = 4 waves
+ * owns a tile of 32 * row_tiles rows by cols_per_tile = 128 or 256 columns
+ * (a quarter per wave); K is walked 128 at a time, activations through LDS;
+ * weights dequantized to fp16 and v_mfma_f32_32x32x16_f16 accumulating over
+ * all of K.  Also accepted for any m >= 1 as an explicit plan.
  */
 typedef struct {
     int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel;
                                 2: prefill kernel                               */
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8                          */
-    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16; engine 2: 64 */
-    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K                 */
+    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
+                                engine 2: 128 or 256                            */
+    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4   */
     int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
     int32_t workgroups;      /* grid size, >= 1                                  */
     int32_t interleave;      /* engine 0: 0 = each lane group takes one contiguous
@@ -130,7 +136,7 @@ typedef struct {
                                 groups round-robin                               */
     int32_t threads_per_wg;  /* derived by mnb_plan_check                        */
     int32_t k_chunks;        /* derived: passes over K                           */
-    int32_t row_tiles;       /* engine 2: 16-row tiles per workgroup, 1/2/4/8    */
+    int32_t row_tiles;       /* engine 2: 32-row tiles per workgroup, 1, 2 or 4  */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`

@@ -59,7 +59,7 @@ def _load():
         lib.mnb_oracle_matmul_nbits.argtypes = [
             u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
             u8p, u16p, u8p, i64p, ctypes.c_int64, u16p, u16p, f64p, f64p,
-            ctypes.c_int]
+            ctypes.c_int, ctypes.c_int]
         lib.mnb_oracle_f64_to_f16.restype = ctypes.c_uint16
         lib.mnb_oracle_f64_to_f16.argtypes = [ctypes.c_double]
         lib.mnb_oracle_f16_to_f64.restype = ctypes.c_double
@@ -89,13 +89,17 @@ def max_threads() -> int:
 
 
 def matmul_nbits(A_bits, a_is_bf16, B, scales, zero_points, m, K, N,
-                 cols=None, threads=0):
+                 cols=None, threads=0, weights_f16=False):
     """Run the oracle.
 
     A_bits: uint16 [m, K] (fp16 or bf16 bit patterns, per ``a_is_bf16``)
     B: uint8 [N, K/2]; scales: uint16 [N, K/32] fp16 bits;
     zero_points: uint8 [N, ceil(K/64)] or None (every zero point 8).
     cols: optional int64 column indices (a sample of the N columns).
+    weights_f16: round every dequantised weight (q - z) * s to fp16 (RNE)
+    before the dot product -- the packed-half dequant of the second page's
+    GEMV ("Why the premise fails here", item 3), which the prefill kernel
+    follows.  ``abs`` is then the sum of |a * w| over the rounded weights.
     Returns dict with ``f16`` and ``bf16`` (uint16 [m, ncols]), ``f64`` and
     ``abs`` (float64 [m, ncols]).
     """
@@ -124,7 +128,8 @@ def matmul_nbits(A_bits, a_is_bf16, B, scales, zero_points, m, K, N,
         _ptr(B, ctypes.c_uint8), _ptr(scales, ctypes.c_uint16),
         _ptr(zero_points, ctypes.c_uint8), _ptr(cols, ctypes.c_int64), ncols,
         _ptr(y16, ctypes.c_uint16), _ptr(ybf, ctypes.c_uint16),
-        _ptr(y64, ctypes.c_double), _ptr(ab, ctypes.c_double), int(threads))
+        _ptr(y64, ctypes.c_double), _ptr(ab, ctypes.c_double), int(threads),
+        int(bool(weights_f16)))
     if rc != 0:
         raise ValueError("oracle rejected its arguments")
     return {"f16": y16, "bf16": ybf, "f64": y64, "abs": ab}

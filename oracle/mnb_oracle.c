@@ -19,7 +19,10 @@
  * Steps, in order:
  *   1. activations: an fp16 input is widened exactly; a bf16 input is first
  *      rounded to fp16 (round to nearest, ties to even), then widened;
- *   2. dequantisation of every weight to fp64, which is exact;
+ *   2. dequantisation of every weight to fp64, which is exact; with
+ *      weights_f16 set, each weight is then rounded to fp16 (RNE, gradual
+ *      underflow), the packed-half dequant of the second page's GEMV ("Why
+ *      the premise fails here", item 3) that the prefill kernel follows;
  *   3. the dot product in fp64 in ascending k (every product is exact);
  *   4. one rounding of that fp64 sum to fp16 (RNE, gradual underflow,
  *      overflow to infinity);
@@ -189,6 +192,7 @@ static int zero_point(const uint8_t* zp, int64_t nblocks, int64_t n, int64_t b)
  *   y_f64       [m][ncols] unrounded fp64 sums, may be NULL
  *   abs_sum     [m][ncols] sum of |a*w| (for the tolerance), may be NULL
  *   nthreads    OpenMP threads over columns (<=0: the runtime's default)
+ *   weights_f16 nonzero: round each dequantised weight to fp16 (step 2)
  * Returns 0, or -1 for arguments it cannot use.
  */
 int mnb_oracle_matmul_nbits(const uint16_t* A_bits, int a_is_bf16,
@@ -197,7 +201,8 @@ int mnb_oracle_matmul_nbits(const uint16_t* A_bits, int a_is_bf16,
                             const uint8_t* zp,
                             const int64_t* cols, int64_t ncols,
                             uint16_t* y_f16, uint16_t* y_bf16,
-                            double* y_f64, double* abs_sum, int nthreads)
+                            double* y_f64, double* abs_sum, int nthreads,
+                            int weights_f16)
 {
     if (m < 0 || K < 0 || N < 0 || K % 32 != 0) return -1;
     if (cols == NULL) ncols = N;
@@ -226,6 +231,7 @@ int mnb_oracle_matmul_nbits(const uint16_t* A_bits, int a_is_bf16,
                 int z = zero_point(zp, nblocks, n, b);
                 int q = weight_nibble(B, K, n, k);
                 double w = (double)(q - z) * s;      /* step 2, exact */
+                if (weights_f16) w = mnb_oracle_f16_to_f64(mnb_oracle_f64_to_f16(w));
                 double p = a[r * K + k] * w;         /* exact product */
                 sum += p;                            /* step 3 */
                 asum += fabs(p);

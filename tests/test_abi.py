@@ -92,31 +92,60 @@ PREFILL_SHAPES = [(m, K, N) for m in (9, 16, 17, 100, 1000, 4096, 1 << 20)
 
 
 def test_default_prefill_plans():
-    """m > 8 runs the prefill engine: 16-row tiles (up to 8 per workgroup,
-    never more than the rows need), 64 columns per workgroup, no more
+    """m > 8 runs the prefill engine: 32-row tiles (up to 4 per workgroup,
+    never more than the rows need), 128 or 256 columns per workgroup, the
+    largest tile that still gives every compute unit a workgroup, no more
     workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
-            assert p.engine == 2 and p.cols_per_tile == 64 and p.waves_per_wg == 4
+            assert p.engine == 2 and p.cols_per_tile in (128, 256) and p.waves_per_wg == 4
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
             assert q.threads_per_wg == 256 and q.k_chunks == (K // 32 + 3) // 4
-            rt = p.row_tiles
-            assert rt in (1, 2, 4, 8) and (rt == 1 or 16 * (rt // 2) < m) and (rt == 8 or 16 * rt >= m)
-            tiles = -(-m // (16 * rt)) * -(-N // 64)
-            assert 1 <= p.workgroups <= tiles
+            rt, cols = p.row_tiles, p.cols_per_tile
+            assert rt in (1, 2, 4) and (rt == 1 or 32 * (rt // 2) < m)
+
+            def tiles(r, c):
+                return -(-m // (32 * r)) * -(-N // c)
+            cap = 1
+            while cap < 4 and 32 * cap < m:
+                cap *= 2
+            assert rt <= cap
+            # Fills the CUs unless already at the smallest tile; columns are
+            # narrowed first, rows only at 128 columns; each step down was
+            # needed.
+            assert tiles(rt, cols) >= cus or (rt, cols) == (1, 128)
+            if cols < 256:
+                assert tiles(cap, 2 * cols) < cus
+            if rt < cap:
+                assert cols == 128 and tiles(2 * rt, 128) < cus
+            assert 1 <= p.workgroups <= tiles(rt, cols)
+    # The two prefill shapes of the decode model at 512 and 2048 rows.
+    assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(2048, 4096, 28672, 256, 0)) == (4, 256)
+    assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(512, 14336, 4096, 256, 0)) == (2, 128)
 
 
 def test_plan_check_engines_and_rows():
-    p = mnb.mnb_plan(engine=2, row_tiles=4, cols_per_tile=64, waves_per_wg=4, workgroups=3)
+    p = mnb.mnb_plan(engine=2, row_tiles=4, cols_per_tile=128, waves_per_wg=4, workgroups=3)
     assert mnb.mnb_plan_check(3, 4096, 100, p) == 0            # engine 2 takes any m >= 1
     assert mnb.mnb_plan_check(5000, 4096, 100, p) == 0
-    for bad in (dict(row_tiles=3), dict(row_tiles=16), dict(cols_per_tile=16),
-                dict(waves_per_wg=8), dict(workgroups=0)):
-        q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=4, cols_per_tile=64, waves_per_wg=4,
+    for rt in (1, 2, 4):
+        for cols in (128, 256):
+            q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=4, workgroups=1)
+            assert mnb.mnb_plan_check(20, 4096, 100, q) == 0
+    for bad in (dict(row_tiles=3), dict(row_tiles=8), dict(cols_per_tile=64), dict(cols_per_tile=96),
+                dict(cols_per_tile=512), dict(waves_per_wg=2), dict(waves_per_wg=8), dict(workgroups=0)):
+        q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=4, cols_per_tile=128, waves_per_wg=4,
                                      workgroups=3), **bad))
         assert mnb.mnb_plan_check(20, 4096, 100, q) == 9
+    # 32-bit activation offsets within a workgroup's rows: 64 * row_tiles * K
+    # bytes at most 2^32 - 16.
+    big = 1 << 24
+    for rt, want in ((4, 9), (2, 0), (1, 0)):
+        q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=128, waves_per_wg=4, workgroups=1)
+        assert mnb.mnb_plan_check(1000, big, 100, q) == want
+    assert mnb.mnb_plan_default(1000, big, 100000, 256, 0).row_tiles == 2
     d = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=1, cols_per_tile=1, workgroups=1)
     assert mnb.mnb_plan_check(8, 4096, 100, d) == 0
     assert mnb.mnb_plan_check(9, 4096, 100, d) == 9            # decode engines: m <= 8

@@ -1,10 +1,15 @@
 """GPU parity of the prefill path (m > 8 rows, the matrix-core tile kernel)
 against the fp64 oracle, through the C ABI.
 
-Same acceptance as the decode path: check 1 on the fp16 output, check 2
-(bf16 output bit-identical to the narrowing of the fp16 output), counters,
-no stale element.  The summation order of an output depends only on K, so
-rows computed in launches of different heights are bit-identical.
+Same acceptance as the decode path: check 1 on the fp16 output against the
+exact weights, check 2 (bf16 output bit-identical to the narrowing of the
+fp16 output), counters, no stale element.  The prefill kernel multiplies
+weights rounded to fp16, so it is also held to a much tighter bound against
+the oracle run with the same rounded weights: the only difference left is
+fp32 accumulation, at most (K/32 + 32) roundings of 2^-24 relative to
+sum |a w| (one chained MFMA per block, 32 products each), plus one fp16 ulp
+for the output rounding.  The summation order of an output depends only on
+K, so rows computed in launches of different heights are bit-identical.
 """
 import numpy as np
 import pytest
@@ -14,6 +19,19 @@ import block_wise_int4_matmulnbits_amd as mnb
 from block_wise_int4_matmulnbits_amd import workloads as W
 from tests import gpu_util as G
 from tests.test_gpu_parity import assert_parity, run
+
+
+def assert_prefill(oracle_mod, d, m, label, plan=None):
+    y16, _, _ = assert_parity(oracle_mod, d, m, label, plan)
+    K = d["K"]
+    ref = oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"], d["scales"],
+                                  d["zp"], m, K, d["N"], weights_f16=True)
+    g = G.f16_values(y16)
+    err = np.abs(g - ref["f64"])
+    tol = (K // 32 + 32) * 2.0 ** -24 * ref["abs"] + oracle_mod.f16_ulp(ref["f16"])
+    bad = ~(err <= tol)
+    assert not bad.any(), "fp16-weight bound failed at %d of %d outputs" % (bad.sum(), bad.size)
+    G.log("[parity] %s: within %.3g of the fp16-weight bound" % (label, float(np.max(err / tol))))
 
 pytestmark = pytest.mark.gpu
 
@@ -36,25 +54,27 @@ def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
     plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
     assert plan.engine == 2
-    assert_parity(oracle_mod, d, m, "prefill", None)
+    assert_prefill(oracle_mod, d, m, "prefill", None)
 
 
-@pytest.mark.parametrize("rt", [1, 2, 4, 8])
-def test_prefill_every_row_tiling_and_small_grids(oracle_mod, rt):
-    """Every row-tile count, with fewer workgroups than tiles (each walks
-    several (row block, column block) tiles) and ragged K."""
-    m, K, N = 16 * rt + 5, 32 * 61, 200
-    d = W.generate(m, K, N, W.F16 if rt % 2 else W.BF16, rt != 2, 0.002, 0.02, 1.0, 720 + rt)
+@pytest.mark.parametrize("rt", [1, 2, 4])
+@pytest.mark.parametrize("cols", [128, 256])
+def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols):
+    """One, two or four 32-row tiles and 32 or 64 columns per wave, with
+    fewer workgroups than tiles (each walks several (row block, column
+    block) tiles), ragged rows, columns and K."""
+    m, K, N = 32 * rt + 5, 32 * 61, 300
+    d = W.generate(m, K, N, W.F16 if rt % 2 else W.BF16, rt != 2, 0.002, 0.02, 1.0, 720 + rt + cols)
     for wg in (1, 3):
-        plan = dict(engine=2, row_tiles=rt, cols_per_tile=64, waves_per_wg=4, workgroups=wg)
-        assert_parity(oracle_mod, d, m, "prefill rt=%d wg=%d" % (rt, wg), plan)
+        plan = dict(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=4, workgroups=wg)
+        assert_prefill(oracle_mod, d, m, "prefill rt=%d cols=%d wg=%d" % (rt, cols, wg), plan)
 
 
 def test_prefill_engine_for_decode_heights(oracle_mod):
     """The prefill engine also serves m <= 8 when asked for explicitly."""
     d = W.generate(3, 4096, 129, W.BF16, True, 0.001, 0.01, 0.5, 730)
-    plan = dict(engine=2, row_tiles=1, cols_per_tile=64, waves_per_wg=4, workgroups=2)
-    assert_parity(oracle_mod, d, 3, "prefill m=3", plan)
+    plan = dict(engine=2, row_tiles=1, cols_per_tile=128, waves_per_wg=4, workgroups=2)
+    assert_prefill(oracle_mod, d, 3, "prefill m=3", plan)
 
 
 def test_prefill_rows_do_not_depend_on_launch_height():
@@ -62,6 +82,32 @@ def test_prefill_rows_do_not_depend_on_launch_height():
     under different row tilings."""
     d = W.generate(40, 14336, 96, W.BF16, True, 0.001, 0.01, 0.5, 740)
     y40, _ = run(d, 40, W.BF16)
-    p17 = dict(engine=2, row_tiles=2, cols_per_tile=64, waves_per_wg=4, workgroups=5)
+    p17 = dict(engine=2, row_tiles=4, cols_per_tile=256, waves_per_wg=4, workgroups=5)
     y17, _ = run(dict(d, A=d["A"][:17]), 17, W.BF16, p17)
     assert np.array_equal(y40[:17], y17)
+
+
+@pytest.mark.parametrize("name,K,N,m", [("gate_up", 4096, 28672, 2048), ("down", 14336, 4096, 512)])
+def test_prefill_full_size_sampled(oracle_mod, name, K, N, m):
+    """The benchmarked prefill shapes at full size under the default plan:
+    check 1 and the fp16-weight bound on a sample of whole columns (every
+    row), check 2 on every output."""
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 750 + m)
+    G.log("[parity] prefill %s m=%d K=%d N=%d default plan" % (name, m, K, N))
+    y16, c16 = run(d, m, W.F16)
+    ybf, _ = run(d, m, W.BF16)
+    assert c16["launches"] == 1
+    assert not np.any(y16 == 0xFFFF) and not np.any(ybf == 0xFFFF)
+    assert G.check2(ybf, y16, oracle_mod).all()
+    rng = np.random.default_rng(751)
+    cols = np.unique(np.concatenate([[0, 127, 128, N - 1], rng.choice(N, 28, replace=False)]))
+    A = d["A"][:m]
+    ref = oracle_mod.matmul_nbits(A, True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
+    ok, max_ulps = G.check1(y16[:, cols], ref, oracle_mod)
+    assert ok.all(), "check 1 failed at %d of %d outputs" % ((~ok).sum(), ok.size)
+    ref16 = oracle_mod.matmul_nbits(A, True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols,
+                                    weights_f16=True)
+    err = np.abs(G.f16_values(y16[:, cols]) - ref16["f64"])
+    tol = (K // 32 + 32) * 2.0 ** -24 * ref16["abs"] + oracle_mod.f16_ulp(ref16["f16"])
+    assert (err <= tol).all()
+    G.log("[parity] prefill %s m=%d ok: max err %.3f fp16 ulp vs exact weights" % (name, m, max_ulps))

@@ -309,3 +309,82 @@ def test_library_matmul_agrees(oracle_mod):
     r = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
     np.testing.assert_allclose(r["f64"], y, rtol=0, atol=1e-9 * (1 + r["abs"].max()))
     assert np.array_equal(r["f16"], y.astype(np.float16).view(np.uint16))
+
+
+# ------------------------------------- fp16 weights (the prefill kernel's form)
+def test_fp16_weights_hand_tie(oracle_mod):
+    """Block 0: scale 1 + 2^-10, q - z = 3, a = +1; block 1: scale 1,
+    q - z = 3, a = -1.  Exact weights: y = 3 * 2^-10 (fp16 0x1A00).  Rounded
+    to fp16, 3 + 3 * 2^-10 sits halfway between 3 + 2^-9 (odd last bit) and
+    3 + 2^-8 (even): w = 3 + 2^-8 and y = 2^-8 (fp16 0x1C00)."""
+    K = 64
+    A = np.zeros((1, K), np.uint16)
+    A[0, 0], A[0, 32] = 0x3C00, 0xBC00
+    B = np.full((1, K // 2), 0x88, np.uint8)      # q = 8 = z: weight 0
+    B[0, 0] = B[0, 16] = 0x8B                      # k = 0 and k = 32: q = 11
+    S = np.array([[0x3C01, 0x3C00]], np.uint16)
+    exact = oracle_mod.matmul_nbits(A, False, B, S, None, 1, K, 1)
+    w16 = oracle_mod.matmul_nbits(A, False, B, S, None, 1, K, 1, weights_f16=True)
+    assert exact["f64"][0, 0] == 3 * 2.0 ** -10 and exact["f16"][0, 0] == 0x1A00
+    assert w16["f64"][0, 0] == 2.0 ** -8 and w16["f16"][0, 0] == 0x1C00
+    assert w16["bf16"][0, 0] == 0x3B80
+
+
+@pytest.mark.parametrize("m,K,N,asym,seed", [(2, 96, 7, True, 31), (1, 256, 5, False, 32),
+                                              (3, 160, 4, True, 33)])
+def test_fp16_weights_match_numpy_float16(oracle_mod, m, K, N, asym, seed):
+    """Weights rounded by numpy's float64 -> float16 conversion, products
+    exact in float64, summed in ascending k: the oracle's fp64 sums
+    bit for bit, and its fp16 results as numpy rounds those sums."""
+    from block_wise_int4_matmulnbits_amd import workloads
+    d = workloads.generate(m, K, N, workloads.F16, asym, 0.002, 0.02, 1.0, seed)
+    A = d["A"][:m]
+    r = oracle_mod.matmul_nbits(A, False, d["B"], d["scales"], d["zp"], m, K, N,
+                                weights_f16=True)
+    a = A.view(np.float16).astype(np.float64)
+    q = np.empty((N, K), np.int64)
+    q[:, 0::2] = d["B"] & 0xF
+    q[:, 1::2] = d["B"] >> 4
+    nb = K // 32
+    if d["zp"] is None:
+        z = np.full((N, nb), 8, np.int64)
+    else:
+        zb = d["zp"].astype(np.int64)
+        z = np.stack([zb & 0xF, zb >> 4], axis=2).reshape(N, -1)[:, :nb]
+    s = d["scales"].view(np.float16).astype(np.float64)
+    w = ((q - np.repeat(z, 32, axis=1)) * np.repeat(s, 32, axis=1)).astype(np.float16)
+    w = w.astype(np.float64)
+    for i in range(m):
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += a[i, k] * w[n, k]
+            assert r["f64"][i, n] == acc
+            assert r["f16"][i, n] == np.float64(acc).astype(np.float16).view(np.uint16)
+
+
+def test_fp16_weights_exact_when_representable(oracle_mod):
+    """Power-of-two scales make every (q - z) * s an fp16 number: rounding
+    the weights changes nothing."""
+    m, K, N = 2, 512, 24
+    d = _gen(m, K, N, 34)
+    e = np.random.default_rng(35).integers(-12, 3, d["scales"].shape)
+    s = (2.0 ** e).astype(np.float16).view(np.uint16)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], s, d["zp"], m, K, N)
+    r2 = oracle_mod.matmul_nbits(d["A"], False, d["B"], s, d["zp"], m, K, N, weights_f16=True)
+    for key in ("f16", "bf16", "f64", "abs"):
+        assert np.array_equal(r1[key], r2[key])
+
+
+def test_fp16_weights_within_half_ulp_per_weight(oracle_mod):
+    """Rounding each weight to fp16 moves it by at most 2^-11 |w| (normal
+    range), so the sum moves by at most 2^-11 sum |a w| (plus fp64 noise);
+    on scales that are not powers of two it does move."""
+    m, K, N = 3, 2048, 40
+    d = _gen(m, K, N, 36)
+    r1 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N)
+    r2 = oracle_mod.matmul_nbits(d["A"], False, d["B"], d["scales"], d["zp"], m, K, N,
+                                 weights_f16=True)
+    bound = 2.0 ** -11 * r1["abs"] + 2 * K * 2.0 ** -53 * r1["abs"]
+    assert np.all(np.abs(r2["f64"] - r1["f64"]) <= bound)
+    assert np.any(r2["f64"] != r1["f64"])
