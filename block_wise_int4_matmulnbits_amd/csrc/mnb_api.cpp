@@ -154,11 +154,12 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->workgroups < 1) return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
-        if (!is_pow2_in(plan->row_tiles, 1, 4) || !is_pow2_in(plan->cols_per_tile, 128, 256) ||
-            plan->waves_per_wg != mnb::kPrefillWaves ||
+        const bool shape_ok = (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
+                              (plan->waves_per_wg == 8 && plan->cols_per_tile == 256);
+        if (!is_pow2_in(plan->row_tiles, 1, 4) || !shape_ok ||
             (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
             return MNB_ERR_PLAN;
-        plan->threads_per_wg = 64 * mnb::kPrefillWaves;
+        plan->threads_per_wg = 64 * plan->waves_per_wg;
         plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
         return MNB_OK;
     }
@@ -218,7 +219,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         plan->engine = 2;
         plan->row_tiles = (int32_t)rt;
         plan->cols_per_tile = (int32_t)cols;
-        plan->waves_per_wg = mnb::kPrefillWaves;
+        plan->waves_per_wg = 4;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -68,7 +68,6 @@ struct GemmParams {
     int32_t a_bf16, out_bf16;
 };
 
-constexpr int kGemmThreads = 64 * kPrefillWaves;
 constexpr int kGemmRing = 2;             // weight quads in flight per column tile
 
 struct WQuad {
@@ -106,12 +105,12 @@ __device__ __forceinline__ int a_slot(int d, int r)
     return d ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 
-template <int RT, int CT, bool VEC, bool ABF16>
-__global__ __launch_bounds__(kGemmThreads) void mnb_gemm_mfma_kernel(GemmParams p)
+template <int RT, int CT, int W, bool VEC, bool ABF16>
+__global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 {
-    constexpr int THREADS = kGemmThreads;
+    constexpr int THREADS = 64 * W;
     constexpr int MT = 32 * RT;              // rows per workgroup tile
-    constexpr int NT = 32 * CT * kPrefillWaves;   // columns per workgroup tile
+    constexpr int NT = 32 * CT * W;          // columns per workgroup tile
     constexpr int QA = 16 * MT;              // 16-byte pieces of activations per quad
     constexpr int SPT = QA / THREADS;        // pieces per thread
     static_assert(QA % THREADS == 0, "whole pieces per thread");
@@ -358,31 +357,33 @@ __global__ __launch_bounds__(kGemmThreads) void mnb_gemm_mfma_kernel(GemmParams 
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int CT, bool VEC, bool ABF16>
+template <int CT, int W, bool VEC, bool ABF16>
 GemmFn lookup_gemm_ct(int rt)
 {
     switch (rt) {
-    case 1: return mnb_gemm_mfma_kernel<1, CT, VEC, ABF16>;
-    case 2: return mnb_gemm_mfma_kernel<2, CT, VEC, ABF16>;
-    case 4: return mnb_gemm_mfma_kernel<4, CT, VEC, ABF16>;
+    case 1: return mnb_gemm_mfma_kernel<1, CT, W, VEC, ABF16>;
+    case 2: return mnb_gemm_mfma_kernel<2, CT, W, VEC, ABF16>;
+    case 4: return mnb_gemm_mfma_kernel<4, CT, W, VEC, ABF16>;
     }
     return nullptr;
 }
 
+// Four waves with one or two 32-column tiles each (128 or 256 columns), or
+// eight waves with one (256 columns).
 template <bool VEC, bool ABF16>
-GemmFn lookup_gemm_cols(int rt, int cols)
+GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 {
-    switch (cols) {   // cols_per_tile = 128 CT
-    case 128: return lookup_gemm_ct<1, VEC, ABF16>(rt);
-    case 256: return lookup_gemm_ct<2, VEC, ABF16>(rt);
-    }
+    if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16>(rt);
+    if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16>(rt);
+    if (waves == 8 && cols == 256) return lookup_gemm_ct<1, 8, VEC, ABF16>(rt);
     return nullptr;
 }
 
-GemmFn lookup_gemm(int rt, int cols, bool vec, bool a_bf16)
+GemmFn lookup_gemm(const mnb_plan& plan, bool vec, bool a_bf16)
 {
-    if (vec) return a_bf16 ? lookup_gemm_cols<true, true>(rt, cols) : lookup_gemm_cols<true, false>(rt, cols);
-    return a_bf16 ? lookup_gemm_cols<false, true>(rt, cols) : lookup_gemm_cols<false, false>(rt, cols);
+    const int rt = plan.row_tiles, cols = plan.cols_per_tile, w = plan.waves_per_wg;
+    if (vec) return a_bf16 ? lookup_gemm_shape<true, true>(rt, cols, w) : lookup_gemm_shape<true, false>(rt, cols, w);
+    return a_bf16 ? lookup_gemm_shape<false, true>(rt, cols, w) : lookup_gemm_shape<false, false>(rt, cols, w);
 }
 
 bool gemm_vec_ok(int64_t K, const void* scales, const void* zp)
@@ -399,7 +400,7 @@ size_t gemm_lds_bytes(const mnb_plan& plan)
 
 int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, gemm_vec_ok(a.K, a.scales, a.zp), a.a_bf16 != 0);
+    GemmFn fn = lookup_gemm(plan, gemm_vec_ok(a.K, a.scales, a.zp), a.a_bf16 != 0);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     GemmParams p;
     p.A = static_cast<const uint16_t*>(a.A);
@@ -417,7 +418,7 @@ int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.out_bf16 = a.out_bf16;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
-                                   dim3((unsigned)plan.workgroups), dim3(kGemmThreads), args,
+                                   dim3((unsigned)plan.workgroups), dim3(64 * plan.waves_per_wg), args,
                                    gemm_lds_bytes(plan), static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
     return (int)e;
@@ -425,14 +426,14 @@ int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
 
 int gemm_workgroups_per_cu(const mnb_plan& plan)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, true, true);
+    GemmFn fn = lookup_gemm(plan, true, true);
     if (!fn) return 0;
-    return occupancy(reinterpret_cast<const void*>(fn), kGemmThreads, gemm_lds_bytes(plan));
+    return occupancy(reinterpret_cast<const void*>(fn), 64 * plan.waves_per_wg, gemm_lds_bytes(plan));
 }
 
 int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info)
 {
-    GemmFn fn = lookup_gemm(plan.row_tiles, plan.cols_per_tile, true, true);
+    GemmFn fn = lookup_gemm(plan, true, true);
     if (!fn) return -1;
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));

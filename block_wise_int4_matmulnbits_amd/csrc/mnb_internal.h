@@ -28,10 +28,9 @@ int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
-// The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of
-// kPrefillWaves waves owns 32 * row_tiles rows by cols_per_tile columns
-// (128 or 256: 32 or 64 per wave).
-constexpr int kPrefillWaves = 4;
+// The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of 4 or 8
+// waves owns 32 * row_tiles rows by cols_per_tile columns (4 waves: 128 or
+// 256 columns, 32 or 64 per wave; 8 waves: 256 columns, 32 per wave).
 // A workgroup's activation rows (32 * row_tiles rows of K fp16) are
 // addressed with 32-bit buffer offsets: 64 * row_tiles * K must stay within
 // this many bytes.

@@ -131,11 +131,14 @@ def test_plan_check_engines_and_rows():
     assert mnb.mnb_plan_check(3, 4096, 100, p) == 0            # engine 2 takes any m >= 1
     assert mnb.mnb_plan_check(5000, 4096, 100, p) == 0
     for rt in (1, 2, 4):
-        for cols in (128, 256):
-            q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=4, workgroups=1)
+        for cols, waves in ((128, 4), (256, 4), (256, 8)):
+            q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=1)
             assert mnb.mnb_plan_check(20, 4096, 100, q) == 0
+            assert q.threads_per_wg == 64 * waves
     for bad in (dict(row_tiles=3), dict(row_tiles=8), dict(cols_per_tile=64), dict(cols_per_tile=96),
-                dict(cols_per_tile=512), dict(waves_per_wg=2), dict(waves_per_wg=8), dict(workgroups=0)):
+                dict(cols_per_tile=512), dict(waves_per_wg=2), dict(waves_per_wg=8),
+                dict(waves_per_wg=8, cols_per_tile=512), dict(waves_per_wg=16, cols_per_tile=256),
+                dict(workgroups=0)):
         q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=4, cols_per_tile=128, waves_per_wg=4,
                                      workgroups=3), **bad))
         assert mnb.mnb_plan_check(20, 4096, 100, q) == 9

@@ -58,16 +58,18 @@ def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
 
 
 @pytest.mark.parametrize("rt", [1, 2, 4])
-@pytest.mark.parametrize("cols", [128, 256])
-def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols):
-    """One, two or four 32-row tiles and 32 or 64 columns per wave, with
-    fewer workgroups than tiles (each walks several (row block, column
-    block) tiles), ragged rows, columns and K."""
+@pytest.mark.parametrize("cols,waves", [(128, 4), (256, 4), (256, 8)])
+def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols, waves):
+    """One, two or four 32-row tiles; four waves of 32 or 64 columns or
+    eight of 32; fewer workgroups than tiles (each walks several (row block,
+    column block) tiles), ragged rows, columns and K."""
     m, K, N = 32 * rt + 5, 32 * 61, 300
-    d = W.generate(m, K, N, W.F16 if rt % 2 else W.BF16, rt != 2, 0.002, 0.02, 1.0, 720 + rt + cols)
+    d = W.generate(m, K, N, W.F16 if rt % 2 else W.BF16, rt != 2, 0.002, 0.02, 1.0,
+                   720 + rt + cols + waves)
     for wg in (1, 3):
-        plan = dict(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=4, workgroups=wg)
-        assert_prefill(oracle_mod, d, m, "prefill rt=%d cols=%d wg=%d" % (rt, cols, wg), plan)
+        plan = dict(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=wg)
+        assert_prefill(oracle_mod, d, m, "prefill rt=%d cols=%d waves=%d wg=%d" % (rt, cols, waves, wg),
+                       plan)
 
 
 def test_prefill_engine_for_decode_heights(oracle_mod):
