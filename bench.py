@@ -23,6 +23,8 @@ Besides the headline figure the line carries (skipped with --no-extras):
   decode_step  a decode step of GEMVs (4 layers of q/k/v/o, gate_up and down,
                then the lm_head), launched eagerly and as one captured HIP
                graph (outputs compared);
+  offline_layout  the natural layout against the offline odd/even nibble
+               layout (converted once by mnb_repack_weights);
   prefill      m = 512 and 2048 rows on the gate_up and down shapes (the
                matrix-core tile kernel), TFLOP/s against the fp16 peak.
 """
@@ -250,6 +252,7 @@ def main():
             result["staged_route"] = staged_route(res, stream, L)
         result["decode_step"] = decode_step(args, stream, L)
         result["prefill"] = prefill(stream, L, cus)
+        result["offline_layout"] = offline_layout(args, stream, L, cus)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"], parity = cpu_baseline(args, w, res.d, m, res.A, res.copies[0],
@@ -434,6 +437,57 @@ def decode_step(args, stream, L, layers=4):
             "eager_us": round(us_eager, 2), "graph_us": round(us_graph, 2),
             "graph_GB/s": round(nbytes / (us_graph * 1e-6) / 1e9, 1),
             "graph_outputs_equal_eager": bool(same)}
+
+
+def offline_layout(args, stream, L, cus):
+    """The second page's offline odd/even nibble interleave
+    (MNB_LAYOUT_EVEN_ODD, converted once by mnb_repack_weights) against the
+    natural layout, same plan otherwise, interleaved A/B on rotated copies.
+    With the interleave the dequant yields (k, k+1) pairs and the
+    activations skip their reorder."""
+    import ctypes
+    import torch
+    import block_wise_int4_matmulnbits_amd as mnb
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    out = {}
+    for name, m in (("lm_head", 1), ("gate_up_bf16", 1), ("down_rows_bf16", 8)):
+        w = W.WORKLOADS[name]
+        res = Resident(w, m, W.BF16, args.rotate_mb)
+        raw_n = res.raw(stream.cuda_stream)
+        eo = [torch.empty_like(b) for (b, _, _) in res.copies]
+        for (b, _, _), e in zip(res.copies, eo):
+            mnb.mnb_repack_weights(b, mnb.MNB_LAYOUT_NATURAL, e, mnb.MNB_LAYOUT_EVEN_ODD, stream=stream)
+        raw_e = [(r[0], r[1], r[2], r[3], r[4], e.data_ptr()) + tuple(r[6:]) for r, e in zip(raw_n, eo)]
+        pn = mnb.plan_for_device(m, w.K, w.N, cus)
+        pe = mnb.mnb_plan(**dict(pn.as_dict(), b_layout=mnb.MNB_LAYOUT_EVEN_ODD))
+        assert mnb.mnb_plan_check(m, w.K, w.N, pe) == 0
+        n = max(200, int(0.05 / (res.bytes_per_call / 5e12)))
+        best = {"natural": 1e30, "even_odd": 1e30}
+        for rep in range(3):
+            for key, raw, plan in (("natural", raw_n, pn), ("even_odd", raw_e, pe)):
+                pp = ctypes.byref(plan)
+
+                def go(i, raw=raw, pp=pp):
+                    L.matmul_nbits_planned(*raw[i % len(raw)], pp)
+                for i in range(100):
+                    go(i)
+                best[key] = min(best[key], event_time_us(stream, go, n))
+        b0 = res.copies[0][0]
+        scratch = torch.empty_like(b0)
+
+        def conv(i):
+            mnb.mnb_repack_weights(b0, mnb.MNB_LAYOUT_NATURAL, scratch, mnb.MNB_LAYOUT_EVEN_ODD,
+                                   stream=stream)
+        conv(0)
+        us_conv = event_time_us(stream, conv, 20)
+        out["%s:m%d" % (name, m)] = {
+            "natural_us": round(best["natural"], 3), "even_odd_us": round(best["even_odd"], 3),
+            "gain_pct": round(100 * (best["natural"] - best["even_odd"]) / best["natural"], 2),
+            "repack_us_once": round(us_conv, 2), "weight_bytes": b0.numel()}
+        log("[bench] offline layout %s m=%d: natural %.3f us, even/odd %.3f us (repack once %.1f us)"
+            % (name, m, best["natural"], best["even_odd"], us_conv))
+        del res, eo, scratch
+    return out
 
 
 def prefill(stream, L, cus):

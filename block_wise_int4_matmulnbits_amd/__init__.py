@@ -20,11 +20,13 @@ MNB_F16 = 0
 MNB_BF16 = 1
 MNB_MAX_M = 8            # decode kernels; prefill up to MNB_MAX_ROWS
 MNB_MAX_ROWS = 1 << 20
+MNB_LAYOUT_NATURAL = 0   # stored weight layouts (mnb_repack_weights)
+MNB_LAYOUT_EVEN_ODD = 1
 
 STATUS = {
     0: "MNB_OK", 1: "MNB_ERR_NULL", 2: "MNB_ERR_SHAPE", 3: "MNB_ERR_BLOCK",
     4: "MNB_ERR_DTYPE", 5: "MNB_ERR_ALIGN", 6: "MNB_ERR_M_RANGE",
-    7: "MNB_ERR_HIP", 8: "MNB_ERR_ALIAS", 9: "MNB_ERR_PLAN",
+    7: "MNB_ERR_HIP", 8: "MNB_ERR_ALIAS", 9: "MNB_ERR_PLAN", 10: "MNB_ERR_LAYOUT",
 }
 
 
@@ -49,7 +51,8 @@ class mnb_plan(ctypes.Structure):
                 ("interleave", ctypes.c_int32),
                 ("threads_per_wg", ctypes.c_int32),
                 ("k_chunks", ctypes.c_int32),
-                ("row_tiles", ctypes.c_int32)]
+                ("row_tiles", ctypes.c_int32),
+                ("b_layout", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -81,7 +84,7 @@ _lib = None
 EXPORTS = ("matmul_nbits", "matmul_nbits_planned", "mnb_plan_default",
            "mnb_plan_check", "mnb_counters_get", "mnb_counters_reset",
            "mnb_get_kernel_info", "mnb_status_string", "mnb_last_hip_error",
-           "mnb_abi_version")
+           "mnb_abi_version", "mnb_repack_weights")
 
 
 def lib():
@@ -119,6 +122,8 @@ def lib():
         L.mnb_last_hip_error.argtypes = []
         L.mnb_abi_version.restype = i32
         L.mnb_abi_version.argtypes = []
+        L.mnb_repack_weights.restype = i32
+        L.mnb_repack_weights.argtypes = [vp, i32, vp, i32, i64, i64, vp]
         _lib = L
         return L
 
@@ -210,6 +215,22 @@ def matmul_nbits_raw(A_ptr, a_dtype, m, K, N, B_ptr, scales_ptr, zp_ptr, block,
     """Direct C call with integer addresses; returns the status code."""
     return lib().matmul_nbits(A_ptr, a_dtype, m, K, N, B_ptr, scales_ptr, zp_ptr,
                               block, out_ptr, out_dtype, stream)
+
+
+def mnb_repack_weights(src, src_layout, dst, dst_layout, stream=None):
+    """Convert packed weights [N, K/2] (uint8, on the GPU) between stored
+    layouts (MNB_LAYOUT_*); ``dst`` may be ``src`` (in place).  Queued on
+    ``stream``; returns ``dst``."""
+    L = lib()
+    if src.dim() != 2 or dst.shape != src.shape or src.element_size() != 1 or dst.element_size() != 1:
+        raise ValueError("src and dst must be uint8 [N, K/2] of one shape")
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous")
+    N, K = src.shape[0], 2 * src.shape[1]
+    st = L.mnb_repack_weights(src.data_ptr(), src_layout, dst.data_ptr(), dst_layout, N, K,
+                              _stream_handle(stream, src.device))
+    _check(st, L)
+    return dst
 
 
 def mnb_plan_default(m, K, N, num_cus, wgs_per_cu=0):

@@ -1,7 +1,7 @@
 """Build libmnb.so for gfx950 in-tree.
 
 hipcc compiles the kernels (mnb_gemv.hip, mnb_gemv_mfma.hip,
-mnb_gemm_mfma.hip); the host front end
+mnb_gemm_mfma.hip, mnb_layout.hip); the host front end
 (mnb_api.cpp) is plain C++ built with g++; hipcc links both into one shared
 library next to this file.
 """
@@ -38,22 +38,24 @@ def _run(cmd, verbose):
 def build(verbose: bool = False, save_temps: bool = False) -> str:
     """Compile and link libmnb.so (always recompiles). Returns its path."""
     os.makedirs(BUILD, exist_ok=True)
-    gemv_o = os.path.join(BUILD, "mnb_gemv.o")
-    mfma_o = os.path.join(BUILD, "mnb_gemv_mfma.o")
-    gemm_o = os.path.join(BUILD, "mnb_gemm_mfma.o")
-    api_o = os.path.join(BUILD, "mnb_api.o")
     extra = ["-save-temps=obj"] if save_temps else []
-    _run(["hipcc", "-c", os.path.join(CSRC, "mnb_gemv.hip"), "-o", gemv_o]
-         + HIP_FLAGS + extra, verbose)
-    _run(["hipcc", "-c", os.path.join(CSRC, "mnb_gemv_mfma.hip"), "-o", mfma_o]
-         + HIP_FLAGS + extra, verbose)
-    _run(["hipcc", "-c", os.path.join(CSRC, "mnb_gemm_mfma.hip"), "-o", gemm_o]
-         + HIP_FLAGS + extra, verbose)
-    _run(["g++", "-c", os.path.join(CSRC, "mnb_api.cpp"), "-o", api_o] + CXX_FLAGS,
-         verbose)
+    objs = []
+    jobs = []
+    for name in ("mnb_gemv", "mnb_gemv_mfma", "mnb_gemm_mfma", "mnb_layout"):
+        obj = os.path.join(BUILD, name + ".o")
+        objs.append(obj)
+        jobs.append(["hipcc", "-c", os.path.join(CSRC, name + ".hip"), "-o", obj]
+                    + HIP_FLAGS + extra)
+    api_o = os.path.join(BUILD, "mnb_api.o")
+    objs.append(api_o)
+    jobs.append(["g++", "-c", os.path.join(CSRC, "mnb_api.cpp"), "-o", api_o] + CXX_FLAGS)
+    # The translation units are independent: compile them side by side.
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        for f in [ex.submit(_run, cmd, verbose) for cmd in jobs]:
+            f.result()
     tmp = LIB + ".tmp%d" % os.getpid()
-    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp,
-          gemv_o, mfma_o, gemm_o, api_o], verbose)
+    _run(["hipcc", "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs, verbose)
     os.replace(tmp, LIB)
     # measurement support: read-only HBM streaming probe (bench only)
     tmp = PROBE_LIB + ".tmp%d" % os.getpid()

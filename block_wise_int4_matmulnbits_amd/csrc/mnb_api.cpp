@@ -152,6 +152,9 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
 {
     if (!plan || m < 1 || m > MNB_MAX_ROWS || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
     if (plan->workgroups < 1) return MNB_ERR_PLAN;
+    if (plan->b_layout != MNB_LAYOUT_NATURAL &&
+        !(plan->b_layout == MNB_LAYOUT_EVEN_ODD && plan->engine == 0))
+        return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
         const bool shape_ok = (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
@@ -312,6 +315,26 @@ int matmul_nbits_planned(const void* A, int a_dtype, int64_t m, int64_t K, int64
                stream, plan);
 }
 
+int mnb_repack_weights(const uint8_t* src, int src_layout, uint8_t* dst, int dst_layout,
+                       int64_t N, int64_t K, void* stream)
+{
+    auto known = [](int l) { return l == MNB_LAYOUT_NATURAL || l == MNB_LAYOUT_EVEN_ODD; };
+    if (!known(src_layout) || !known(dst_layout)) return MNB_ERR_LAYOUT;
+    if (K < 0 || N < 0 || K % 32 || K > MNB_MAX_K || N > INT32_MAX) return MNB_ERR_SHAPE;
+    const int64_t bytes = N * (K / 2);
+    if (bytes == 0) return MNB_OK;
+    if (!src || !dst) return MNB_ERR_NULL;
+    if (((uintptr_t)src & 15) || ((uintptr_t)dst & 15)) return MNB_ERR_ALIGN;
+    if (dst != src && overlaps(src, bytes, dst, bytes)) return MNB_ERR_ALIAS;
+    const int e = mnb::launch_repack(src, src_layout, dst, dst_layout, bytes / 4, stream);
+    if (e != 0) {
+        t_last_hip_error = e;
+        return MNB_ERR_HIP;
+    }
+    g_launches.fetch_add(1, std::memory_order_relaxed);
+    return MNB_OK;
+}
+
 void mnb_counters_get(mnb_counters* out)
 {
     if (!out) return;
@@ -359,6 +382,7 @@ const char* mnb_status_string(int status)
     case MNB_ERR_HIP: return "HIP runtime error (see mnb_last_hip_error)";
     case MNB_ERR_ALIAS: return "out overlaps an input";
     case MNB_ERR_PLAN: return "launch plan not supported";
+    case MNB_ERR_LAYOUT: return "unknown weight layout";
     }
     return "unknown status";
 }

@@ -68,6 +68,8 @@ struct Params {
     uint32_t zero;           // always 0 (see vgpr_constant)
     int32_t tcap;            // multi-wave groups: LDS slots for deferred sums
                              // (0: reduce across waves after every tile)
+    int32_t eo_pairs;        // weights in the even/odd nibble layout: the
+                             // unpack yields (k, k+1) pairs, no reorder
 };
 
 // v + (v of another lane) through a DPP lane permutation; lanes outside
@@ -229,6 +231,7 @@ void mnb_gemv_kernel(Params p)
             w = bf16x2_to_f16x2(w);
         }
         // halves: x=(a0,a1) y=(a2,a3) z=(a4,a5) w=(a6,a7)
+        if (p.eo_pairs) return make_uint4(x, y, z, w);   // already the unpack's order
         uint4 o;
         o.x = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
         o.y = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
@@ -633,6 +636,7 @@ int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.out_bf16 = a.out_bf16;
     p.interleave = plan.interleave;
     p.zero = 0;
+    p.eo_pairs = plan.b_layout == MNB_LAYOUT_EVEN_ODD;
     const int64_t lds = gemv_lds_bytes(a.m, a.N, plan, &p.tcap);
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),

@@ -40,6 +40,11 @@ int gemm_workgroups_per_cu(const mnb_plan& plan);
 int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info);
 size_t gemm_lds_bytes(const mnb_plan& plan);
 
+// Weight-layout conversion (mnb_layout.hip): `words` 32-bit words of packed
+// weights from src_layout to dst_layout.  Returns a hipError_t.
+int launch_repack(const uint8_t* src, int src_layout, uint8_t* dst, int dst_layout, int64_t words,
+                  void* stream);
+
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);
 

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 2
+#define MNB_ABI_VERSION 3
 
 /* Element types of A and of the output. */
 typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
@@ -50,8 +50,26 @@ typedef enum {
     MNB_ERR_HIP = 7,      /* the HIP runtime reported an error; see
                              mnb_last_hip_error()                            */
     MNB_ERR_ALIAS = 8,    /* out overlaps an input buffer                    */
-    MNB_ERR_PLAN = 9      /* an explicit plan is not one the library runs   */
+    MNB_ERR_PLAN = 9,     /* an explicit plan is not one the library runs   */
+    MNB_ERR_LAYOUT = 10   /* unknown weight layout                            */
 } mnb_status;
+
+/*
+ * Stored layouts of Bpacked (versioned; see mnb_repack_weights).
+ *
+ * MNB_LAYOUT_NATURAL   byte k/2 of row n holds weight k, even k in the low
+ *                      nibble (the layout every entry point takes by default).
+ * MNB_LAYOUT_EVEN_ODD  the offline odd/even nibble interleave of the second
+ *                      page (pull request "PORT-1 (offline bias+interleave)",
+ *                      opening paragraph and "Method"): within every 32-bit
+ *                      word of a row (8 consecutive weights k0..k7, little
+ *                      endian), nibble p holds k_{2(p mod 4) + p/4}, i.e.
+ *                      k0 k2 k4 k6 in the low half-word and k1 k3 k5 k7 in
+ *                      the high one, so the dequant yields (k, k+1) pairs and
+ *                      the activations need no reorder.  Only engine 0 reads it.
+ */
+#define MNB_LAYOUT_NATURAL 0
+#define MNB_LAYOUT_EVEN_ODD 1
 
 /* Row-batched decode bound: one decode launch serves 1 <= m <= 8 rows (the
  * small-batch row loop of the first page, paragraph "What broke in #1549").
@@ -137,6 +155,8 @@ typedef struct {
     int32_t threads_per_wg;  /* derived by mnb_plan_check                        */
     int32_t k_chunks;        /* derived: passes over K                           */
     int32_t row_tiles;       /* engine 2: 32-row tiles per workgroup, 1, 2 or 4  */
+    int32_t b_layout;        /* MNB_LAYOUT_* of Bpacked; engines 1 and 2 take
+                                MNB_LAYOUT_NATURAL only                         */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`
@@ -160,6 +180,23 @@ int matmul_nbits_planned(const void* A, int a_dtype, int64_t m, int64_t K,
                          const uint16_t* scales, const uint8_t* zero_points,
                          int block, void* out, int out_dtype, void* stream,
                          const mnb_plan* plan);
+
+/*
+ * mnb_repack_weights -- convert packed weights between stored layouts, one
+ * kernel launch on `stream` (the loader of the versioned layout).
+ *
+ *   src, dst     device, [N][K/2] bytes each, 16-byte aligned; dst == src
+ *                converts in place, any other overlap is rejected.
+ *   src_layout, dst_layout   MNB_LAYOUT_NATURAL or MNB_LAYOUT_EVEN_ODD.
+ *   N, K         as for matmul_nbits (K a multiple of 32).
+ *
+ * Scales and zero points are not affected.  Asynchronous; allocates
+ * nothing.  Returns MNB_OK, MNB_ERR_NULL, MNB_ERR_SHAPE, MNB_ERR_ALIGN,
+ * MNB_ERR_ALIAS, MNB_ERR_LAYOUT or MNB_ERR_HIP; on error nothing is launched
+ * (MNB_ERR_HIP: the launch itself failed).
+ */
+int mnb_repack_weights(const uint8_t* src, int src_layout, uint8_t* dst, int dst_layout,
+                       int64_t N, int64_t K, void* stream);
 
 /*
  * Counters, updated atomically by every successful launch.  Tests assert

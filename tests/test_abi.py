@@ -199,3 +199,35 @@ def test_plan_check_rows_limit():
     assert mnb.mnb_plan_check(4, 4096, 100, p) == 0
     p = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=4, workgroups=1)
     assert mnb.mnb_plan_check(5, 4096, 100, p) == 9
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(src_layout=2), 10), (dict(dst_layout=-1), 10), (dict(K=48), 2), (dict(K=-32), 2),
+    (dict(N=-1), 2), (dict(src=0), 1), (dict(dst=0), 1), (dict(src=FAKE + 8), 5),
+    (dict(dst=FAKE * 3 + 4), 5), (dict(dst=FAKE + 64), 8), (dict(K=1 << 25), 2),
+])
+def test_repack_validation_without_gpu(args, status):
+    """mnb_repack_weights rejects bad arguments on the host and launches
+    nothing; dst == src (in place) and an empty matrix are accepted."""
+    a = dict(src=FAKE, src_layout=0, dst=FAKE * 3, dst_layout=1, N=4, K=64)
+    a.update(args)
+    L = mnb.lib()
+    c0 = mnb.mnb_counters_get()
+    st = L.mnb_repack_weights(a["src"], a["src_layout"], a["dst"], a["dst_layout"], a["N"], a["K"], 0)
+    assert st == status, mnb.mnb_status_string(st)
+    assert mnb.mnb_counters_get() == c0
+    assert mnb.mnb_status_string(st) != "unknown status"
+    assert L.mnb_repack_weights(0, 0, 0, 1, 0, 64, 0) == 0        # nothing to convert
+    assert L.mnb_repack_weights(0, 0, 0, 1, 5, 0, 0) == 0
+
+
+def test_plan_layouts():
+    """The even/odd layout is read by engine 0 only."""
+    for eng, fields in ((0, dict(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=2)),
+                        (1, dict(cols_per_tile=16, waves_per_wg=4, chunk_blocks=128)),
+                        (2, dict(row_tiles=1, cols_per_tile=128, waves_per_wg=4))):
+        for layout in (0, 1, 2):
+            q = mnb.mnb_plan(engine=eng, workgroups=1, b_layout=layout, **fields)
+            want = 0 if layout == 0 or (layout == 1 and eng == 0) else 9
+            assert mnb.mnb_plan_check(4, 4096, 100, q) == want, (eng, layout)
+    assert mnb.mnb_plan_default(1, 4096, 100, 256, 0).b_layout == mnb.MNB_LAYOUT_NATURAL
