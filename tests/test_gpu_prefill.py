@@ -113,3 +113,47 @@ def test_prefill_full_size_sampled(oracle_mod, name, K, N, m):
     tol = (K // 32 + 32) * 2.0 ** -24 * ref16["abs"] + oracle_mod.f16_ulp(ref16["f16"])
     assert (err <= tol).all()
     G.log("[parity] prefill %s m=%d ok: max err %.3f fp16 ulp vs exact weights" % (name, m, max_ulps))
+
+
+@pytest.mark.parametrize("m,K,N", [(9, 0, 5), (40, 32, 1), (33, 96, 257), (100, 32 * 3, 3)])
+def test_prefill_edge_shapes(oracle_mod, m, K, N):
+    """K = 0 (every output +0), a single column, one block, an odd block
+    count with a ragged last quad, under the default plan."""
+    d = W.generate(m, K, N, W.BF16, True, 0.002, 0.02, 1.0, 780 + m + K)
+    assert_prefill(oracle_mod, d, m, "prefill edge", None)
+    if K == 0:
+        y, _ = run(d, m, W.F16)
+        assert np.all(y == 0)
+
+
+def test_prefill_longest_rows(oracle_mod):
+    """K = 2^24 (the largest K), where a two-row-tile workgroup's 64
+    activation rows span 2^31 bytes of 32-bit buffer offsets: sampled rows
+    (the first and last of each 32-row tile) and both columns against the
+    oracle, with a four-row-tile plan rejected."""
+    m, K, N = 64, 1 << 24, 2
+    q4 = dict(engine=2, row_tiles=4, cols_per_tile=128, waves_per_wg=4, workgroups=1)
+    assert mnb.mnb_plan_check(m, K, N, mnb.mnb_plan(**q4)) == 9
+    rng = np.random.default_rng(790)
+    # Activations: a few nonzero stretches per row (at the start, in the
+    # middle and in the last block), so the sums reach every part of K.
+    A = np.zeros((m, K), np.uint16)
+    for r in range(m):
+        for start in (0, K // 2 + 32 * r, K - 32):
+            A[r, start:start + 32] = (rng.standard_normal(32) * 0.5).astype(np.float16).view(np.uint16)
+    B = rng.integers(0, 256, (N, K // 2), dtype=np.uint8)
+    S = rng.uniform(0.002, 0.02, (N, K // 32)).astype(np.float16).view(np.uint16)
+    Z = rng.integers(0, 256, (N, K // 64), dtype=np.uint8)
+    d = dict(A=A, B=B, scales=S, zp=Z, m=m, K=K, N=N, a_dtype=W.F16)
+    plan = dict(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=1)
+    y16, c16 = run(d, m, W.F16, plan)
+    ybf, _ = run(d, m, W.BF16, plan)
+    assert c16["launches"] == 1
+    assert G.check2(ybf, y16, oracle_mod).all()
+    rows = np.array([0, 1, 31, 32, 62, 63])
+    ref = oracle_mod.matmul_nbits(A[rows], False, B, S, Z, len(rows), K, N)
+    ok, max_ulps = G.check1(y16[rows], ref, oracle_mod)
+    assert ok.all(), max_ulps
+    ref16 = oracle_mod.matmul_nbits(A[rows], False, B, S, Z, len(rows), K, N, weights_f16=True)
+    err = np.abs(G.f16_values(y16[rows]) - ref16["f64"])
+    assert (err <= (K // 32 + 32) * 2.0 ** -24 * ref16["abs"] + oracle_mod.f16_ulp(ref16["f16"])).all()
