@@ -222,7 +222,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         plan->engine = 2;
         plan->row_tiles = (int32_t)rt;
         plan->cols_per_tile = (int32_t)cols;
-        plan->waves_per_wg = 4;
+        // The largest tile runs as eight waves of 32 columns (two per SIMD)
+        // rather than four of 64: faster on the gate_up shape (757 vs 831 us
+        // at m = 2048), within 5% on the down projection.
+        plan->waves_per_wg = (rt == 4 && cols == 256) ? 8 : 4;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -38,7 +38,9 @@
 //     .. 16h+8s+7 to product s of the block);
 //   - per block: unpack and scale the CT column tiles, then per row tile and
 //     product one LDS read and CT MFMAs into the accumulators.
-// Weight loads run two quads ahead of use, activation loads one.  The
+// Weight loads run four quads ahead of use (two for unaligned scale rows),
+// activation loads one; the loop walks the quads in groups of that many,
+// and the quads past K in the last group load zeros and add +0.  The
 // summation order of an output depends only on K: equal inputs give equal
 // bits for any M, N, tiling and grid.
 #include <hip/hip_runtime.h>
@@ -68,7 +70,10 @@ struct GemmParams {
     int32_t a_bf16, out_bf16;
 };
 
-constexpr int kGemmRing = 2;             // weight quads in flight per column tile
+// Weight quads in flight per column tile (the per-block loads of the
+// unaligned variant take more registers).
+template <bool VEC>
+constexpr int kGemmRing = VEC ? 4 : 2;
 
 struct WQuad {
     u32x4 w[2];       // load u: 16 bytes of block 4t+2u+h of this lane's column
@@ -114,7 +119,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
     constexpr int QA = 16 * MT;              // 16-byte pieces of activations per quad
     constexpr int SPT = QA / THREADS;        // pieces per thread
     static_assert(QA % THREADS == 0, "whole pieces per thread");
-    constexpr int P = kGemmRing;
+    constexpr int P = kGemmRing<VEC>;
     extern __shared__ uint4 a_lds[];         // [2][4 blocks][MT rows][4 slots]
 
     const int tid = threadIdx.x;
@@ -307,8 +312,9 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
             }
         };
 
-        // The loop body has no branches: quads past K (the odd last one of a
-        // pair, and the prefetches past the end) load zeros and add +0.
+        // The loop body has no branches: quads past K (those that round the
+        // last group up to P, and the prefetches past the end) load zeros
+        // and add +0.
         WQuad ring[P][CT];
 #pragma unroll
         for (int s = 0; s < P; ++s) issue(ring[s], s);

@@ -133,11 +133,12 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * waves of a workgroup split K; activations are staged in LDS,
  * chunk_blocks blocks of K per pass; dot products on
  * v_mfma_f32_16x16x32_f16.  For 1 <= m <= 8.
- * engine 2 (prefill kernel, m > 8): a workgroup of waves_per_wg = 4 waves
- * owns a tile of 32 * row_tiles rows by cols_per_tile = 128 or 256 columns
- * (a quarter per wave); K is walked 128 at a time, activations through LDS;
- * weights dequantized to fp16 and v_mfma_f32_32x32x16_f16 accumulating over
- * all of K.  Also accepted for any m >= 1 as an explicit plan.
+ * engine 2 (prefill kernel, m > 8): a workgroup owns a tile of
+ * 32 * row_tiles rows by cols_per_tile columns, split by columns over its
+ * waves: waves_per_wg = 4 with 128 or 256 columns, or 8 with 256; K is
+ * walked 128 at a time, activations through LDS; weights dequantized to
+ * fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of K.  Also
+ * accepted for any m >= 1 as an explicit plan.
  */
 typedef struct {
     int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel;
@@ -146,7 +147,7 @@ typedef struct {
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8                          */
     int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
                                 engine 2: 128 or 256                            */
-    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4   */
+    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4, 8 */
     int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
     int32_t workgroups;      /* grid size, >= 1                                  */
     int32_t interleave;      /* engine 0: 0 = each lane group takes one contiguous

@@ -99,10 +99,11 @@ def test_default_prefill_plans():
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
-            assert p.engine == 2 and p.cols_per_tile in (128, 256) and p.waves_per_wg == 4
+            assert p.engine == 2 and p.cols_per_tile in (128, 256)
+            assert p.waves_per_wg == (8 if (p.row_tiles, p.cols_per_tile) == (4, 256) else 4)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
-            assert q.threads_per_wg == 256 and q.k_chunks == (K // 32 + 3) // 4
+            assert q.threads_per_wg == 64 * p.waves_per_wg and q.k_chunks == (K // 32 + 3) // 4
             rt, cols = p.row_tiles, p.cols_per_tile
             assert rt in (1, 2, 4) and (rt == 1 or 32 * (rt // 2) < m)
 
