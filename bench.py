@@ -82,6 +82,10 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run torch's device copy of this many MiB "
                          "(reference kernel for scaling HBM counters)")
+    ap.add_argument("--prefill-only", default=None, metavar="SHAPE:M",
+                    help="only run one prefill shape (gate_up or down, M rows) "
+                         "--warmup + --steps times under its default plan "
+                         "(profiling runs)")
     return ap.parse_args()
 
 
@@ -157,6 +161,9 @@ def main():
         sys.exit(2)
     if args.calib_copy_mib:
         calib_copy(args.calib_copy_mib)
+        return
+    if args.prefill_only:
+        prefill_only(args)
         return
 
     import torch
@@ -490,6 +497,44 @@ def offline_layout(args, stream, L, cus):
     return out
 
 
+PREFILL_SHAPES = {"gate_up": (4096, 28672), "down": (14336, 4096)}
+
+
+def prefill_only(args):
+    """One prefill shape, default plan, bf16 in and out: --warmup untimed and
+    --steps timed launches (for kernel traces and counter passes)."""
+    import numpy as np
+    import torch
+    import block_wise_int4_matmulnbits_amd as mnb
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    name, m = args.prefill_only.split(":")
+    m = int(m)
+    K, N = PREFILL_SHAPES[name]
+    d = W.generate(1, K, N, W.BF16, True, 0.001, 0.01, 0.5, 90)
+    dev = torch.device("cuda:0")
+    B = torch.from_numpy(d["B"]).to(dev)
+    S = torch.from_numpy(d["scales"].view(np.int16)).to(dev)
+    Z = torch.from_numpy(d["zp"]).to(dev)
+    A = (torch.randn((m, K), device=dev) * 0.5).to(torch.bfloat16)
+    o = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    L = mnb.lib()
+
+    def go(i):
+        st = L.matmul_nbits(A.data_ptr(), W.BF16, m, K, N, B.data_ptr(), S.data_ptr(), Z.data_ptr(),
+                            32, o.data_ptr(), W.BF16, stream.cuda_stream)
+        assert st == 0, st
+    for i in range(args.warmup):
+        go(i)
+    us = event_time_us(stream, go, args.steps)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = mnb.plan_for_device(m, K, N, cus)
+    print(json.dumps({"prefill": name, "m": m, "K": K, "N": N, "steps": args.steps,
+                      "warmup": args.warmup, "us_per_call": round(us, 2),
+                      "TFLOP/s": round(2.0 * m * N * K / (us * 1e-6) / 1e12, 1),
+                      "plan": plan.as_dict()}), flush=True)
+
+
 def prefill(stream, L, cus):
     """Prefill heights (m > 8, the matrix-core tile kernel) on the gate_up
     and down-projection shapes: microseconds per call and TFLOP/s against
@@ -500,7 +545,7 @@ def prefill(stream, L, cus):
     from block_wise_int4_matmulnbits_amd import workloads as W
     out = {}
     dev = torch.device("cuda:0")
-    for name, K, N in (("gate_up", 4096, 28672), ("down", 14336, 4096)):
+    for name, (K, N) in PREFILL_SHAPES.items():
         d = W.generate(1, K, N, W.BF16, True, 0.001, 0.01, 0.5, 90)
         B = torch.from_numpy(d["B"]).to(dev)
         S = torch.from_numpy(d["scales"].view(np.int16)).to(dev)

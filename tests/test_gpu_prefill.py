@@ -66,7 +66,7 @@ def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols, waves):
     m, K, N = 32 * rt + 5, 32 * 61, 300
     d = W.generate(m, K, N, W.F16 if rt % 2 else W.BF16, rt != 2, 0.002, 0.02, 1.0,
                    720 + rt + cols + waves)
-    for wg in (1, 3):
+    for wg in (1, 3, 13):
         plan = dict(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=wg)
         assert_prefill(oracle_mod, d, m, "prefill rt=%d cols=%d waves=%d wg=%d" % (rt, cols, waves, wg),
                        plan)
