@@ -18,6 +18,7 @@ import torch
 import block_wise_int4_matmulnbits_amd as mnb
 from block_wise_int4_matmulnbits_amd import workloads as W
 from tests import gpu_util as G
+from tests.hand_cases import build_case, load_cases
 from tests.test_gpu_parity import assert_parity, run
 
 
@@ -157,3 +158,24 @@ def test_prefill_longest_rows(oracle_mod):
     ref16 = oracle_mod.matmul_nbits(A[rows], False, B, S, Z, len(rows), K, N, weights_f16=True)
     err = np.abs(G.f16_values(y16[rows]) - ref16["f64"])
     assert (err <= (K // 32 + 32) * 2.0 ** -24 * ref16["abs"] + oracle_mod.f16_ulp(ref16["f16"])).all()
+
+
+HAND = load_cases()
+
+
+@pytest.mark.parametrize("case", HAND, ids=[c["name"] for c in HAND])
+def test_hand_case_through_prefill_engine(case):
+    """Every hand case's weights are fp16 numbers, so the prefill kernel's
+    fp16 dequant changes nothing and the golden bits must hold exactly: the
+    case's rows alone, and repeated to 40 rows (two row tiles of 32)."""
+    c = build_case(case)
+    for reps in (1, -(-40 // c["m"])):
+        A = np.tile(c["A"], (reps, 1))
+        m = A.shape[0]
+        d = dict(A=A, B=c["B"], scales=c["scales"], zp=c["zp"], m=m, K=c["K"], N=c["N"],
+                 a_dtype=W.BF16 if c["a_is_bf16"] else W.F16)
+        plan = dict(engine=2, row_tiles=1, cols_per_tile=128, waves_per_wg=4, workgroups=1)
+        y16, _ = run(d, m, W.F16, plan)
+        ybf, _ = run(d, m, W.BF16, plan)
+        assert np.array_equal(y16, np.tile(c["f16"], (reps, 1))), [hex(v) for v in y16[:c["m"]].ravel()]
+        assert np.array_equal(ybf, np.tile(c["bf16"], (reps, 1))), [hex(v) for v in ybf[:c["m"]].ravel()]
