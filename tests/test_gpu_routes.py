@@ -6,7 +6,8 @@ fp16 -> bf16 cast) is what the direct store replaces (onnx-genai pull
 request "perf(cuda): let the split-K decode GEMV store bf16 directly",
 opening paragraphs); both must give the same bf16 bits.  The graph test
 replays a captured decode-style sequence several times, with eager work in
-between, and compares every replay with the eager outputs bit for bit.
+between, and compares every replay with the eager outputs bit for bit.  The
+last test calls the library from several host threads at once.
 """
 import numpy as np
 import pytest
@@ -76,3 +77,46 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for e, c in zip(eager, calls):
             assert np.array_equal(e, G.bits(c[4]))
+
+
+def test_concurrent_host_threads():
+    """Several host threads call the library at once, each on its own stream
+    (the header allows it): every output equals the same call made alone,
+    and the counters account for every launch."""
+    import threading
+    shapes = [(1, 4096, 4096, W.F16), (3, 14336, 777, W.BF16), (40, 4096, 1000, W.BF16),
+              (8, 4096, 2048, W.F16)]
+    jobs = []
+    for i, (m, K, N, a_dtype) in enumerate(shapes):
+        d = W.generate(m, K, N, a_dtype, True, 0.001, 0.01, 0.5, 650 + i)
+        A, B, S, Z = G.to_dev(d, m)
+        jobs.append((A, B, S, Z, G.new_out(m, N, W.BF16), G.new_out(m, N, W.BF16)))
+    for (A, B, S, Z, alone, _) in jobs:
+        mnb.matmul_nbits(A, B, S, Z, alone)
+    torch.cuda.synchronize()
+    c0 = mnb.mnb_counters_get()
+    reps = 20
+    errors = []
+
+    def worker(job):
+        try:
+            A, B, S, Z, _, out = job
+            stream = torch.cuda.Stream()
+            for _ in range(reps):
+                mnb.matmul_nbits(A, B, S, Z, out, stream=stream)
+            stream.synchronize()
+        except Exception as e:   # reported by the main thread
+            errors.append(e)
+
+    threads = [threading.Thread(target=worker, args=(j,)) for j in jobs]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (_, _, _, _, alone, out) in jobs:
+        assert np.array_equal(G.bits(alone), G.bits(out))
+    c1 = mnb.mnb_counters_get()
+    assert c1["launches"] - c0["launches"] == reps * len(jobs)
+    assert c1["calls"] - c0["calls"] == reps * len(jobs)
