@@ -270,6 +270,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu
                                           : (kTargetWavesPerCu + waves_per_wg - 1) / waves_per_wg;
     const int64_t resident = per_cu * num_cus;
+    // Too few columns to give half a resident generation one tile per lane
+    // group: one column per tile doubles the groups at work (the 4096-column
+    // shape: 4.56 -> 4.36 us).
+    while (inwave && nc > 1 && ceil_div(ceil_div(N, nc), gpw) < resident / 2) nc /= 2;
     const int64_t tiles = ceil_div(N, nc);
     int64_t wgs = resident / 2 > num_cus ? resident / 2 : num_cus;
     if (inwave) {
@@ -277,6 +281,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;
         if (wgs < lo) wgs = lo;
         if (wgs > 3 * resident) wgs = 3 * resident;
+        // One tile per lane group fits in one resident generation: take it.
+        if (ceil_div(tiles, gpw) <= resident) wgs = ceil_div(tiles, gpw);
     }
     if (!inwave) {
         // Multi-wave groups: enough workgroups that every wave's partial sums
