@@ -270,7 +270,8 @@ def test_empty_outputs_are_noops():
 @pytest.mark.parametrize("m,K,N", [(1, 32, 1), (8, 32, 3), (1, 96, 257),
                                    (5, 32 * 129, 65), (8, 65536, 33),
                                    (1, 262144, 20), (2, 1024, 131071),
-                                   (8, 512, 70000)])   # 16-lane groups holding 32 sums each
+                                   (8, 512, 70000),    # 16-lane groups holding 32 sums each
+                                   (1, 1 << 24, 2), (8, 1 << 24, 2)])   # the largest K
 def test_edge_shapes(oracle_mod, m, K, N):
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 1.0, 40 + m)
     assert_parity(oracle_mod, d, m, "edge")
