@@ -157,9 +157,11 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
         return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
-        const bool shape_ok = (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
-                              (plan->waves_per_wg == 8 && plan->cols_per_tile == 256);
-        if (!is_pow2_in(plan->row_tiles, 1, 4) || !shape_ok ||
+        const bool shape_ok =
+            plan->row_tiles == 8 ? (plan->waves_per_wg == 8 && plan->cols_per_tile == 256)
+                                 : ((plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
+                                    (plan->waves_per_wg == 8 && plan->cols_per_tile == 256));
+        if (!is_pow2_in(plan->row_tiles, 1, 8) || !shape_ok ||
             (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
             return MNB_ERR_PLAN;
         plan->threads_per_wg = 64 * plan->waves_per_wg;
@@ -216,16 +218,26 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         int64_t cols = 256;
         while (cols > 128 && tiles(rt, cols) < num_cus) cols /= 2;
         while (rt > 1 && tiles(rt, cols) < num_cus) rt /= 2;
+        // 256 x 256 tiles with the weights staged through LDS when they give
+        // at least 85% of the CUs a tile (gate_up, interleaved A/B against
+        // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
+        // m = 2048 787 vs 773).
+        const int64_t t8 = ceil_div(m, 256) * ceil_div(N, 256);
+        if (m > 128 && 100 * t8 >= 85 * (int64_t)num_cus &&
+            (uint64_t)64 * 8 * (uint64_t)K <= mnb::kPrefillRowBlockBytes) {
+            rt = 8;
+            cols = 256;
+        }
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
         int64_t wgs = per_cu * num_cus;
         if (wgs > tiles(rt, cols)) wgs = tiles(rt, cols);
         plan->engine = 2;
         plan->row_tiles = (int32_t)rt;
         plan->cols_per_tile = (int32_t)cols;
-        // The largest tile runs as eight waves of 32 columns (two per SIMD)
-        // rather than four of 64: faster on the gate_up shape (757 vs 831 us
-        // at m = 2048), within 5% on the down projection.
-        plan->waves_per_wg = (rt == 4 && cols == 256) ? 8 : 4;
+        // The largest tiles run as eight waves of 32 (or 2 x 4 waves of 64)
+        // columns rather than four of 64: faster on the gate_up shape (757 vs
+        // 831 us at m = 2048), within 5% on the down projection.
+        plan->waves_per_wg = (rt >= 4 && cols == 256) ? 8 : 4;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -361,6 +361,210 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
     }
 }
 
+// 256 x 256 tiles with the weights staged through LDS.  Eight waves in a
+// 2 x 4 arrangement: wave (wr, wc) owns rows 128 wr .. 128 wr + 127 (four
+// row tiles) and columns 64 wc .. 64 wc + 63 (two column tiles) of the
+// workgroup tile, 128 accumulators per lane.  K is walked in stages of two
+// blocks (64 k).  Per stage every thread converts 4 pieces of activations
+// and dequantizes one 32-weight block of one column (thread t: column t/2,
+// block t%2 of the stage) into LDS, both in the MFMA operand layout
+// ([block][row or column][16-byte slot], XOR-swizzled), so each weight is
+// unpacked once per workgroup and feeds 256 rows.  The arithmetic is that
+// of the kernel above (fp16 weights (q - z) * s, fp32 accumulation over all
+// of K in the matrix core, the same narrowing store).
+constexpr int kLdsTileRows = 256, kLdsTileCols = 256, kLdsRing = 2;
+
+template <bool ABF16>
+__global__ __launch_bounds__(512) void mnb_gemm_lds_kernel(GemmParams p)
+{
+    constexpr int THREADS = 512;
+    constexpr int RTW = 4, CTW = 2;          // row and column tiles per wave
+    constexpr int MT = kLdsTileRows, NT = kLdsTileCols;
+    constexpr int SB = 2;                    // blocks per stage
+    constexpr int QA = MT * SB * 4;          // 16-byte pieces of activations per stage
+    constexpr int QB = NT * SB * 4;          // 16-byte pieces of weights per stage
+    constexpr int APT = QA / THREADS;        // pieces per thread
+    constexpr int P = kLdsRing;              // weight stages in flight
+    static_assert(QA % THREADS == 0 && QB == 4 * THREADS, "one block of one column per thread");
+    extern __shared__ uint4 lds[];
+    uint4* const a_lds = lds;                // [2][SB][MT][4]
+    uint4* const b_lds = lds + 2 * QA;       // [2][SB][NT][4]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wr = wv >> 2, wc = wv & 3;
+    const int j = lane & 31, h = lane >> 5;
+    const int nb = p.nb;
+    const int ns = (nb + SB - 1) / SB;       // stages
+    const uint32_t row_bytes = (uint32_t)p.K / 2;
+    const uint32_t zdef = p.zp ? 0u : 8u;
+    const uint32_t magic = vgpr_constant(0x64006400u, p.zero);
+    const int64_t tiles_m = (p.M + MT - 1) / MT;
+    const int64_t tiles_n = (p.N + NT - 1) / NT;
+
+    // Activation piece e = tid + THREADS * s of a stage: block e / (4 MT)
+    // = s / 2, row (e / 4) % MT = tid / 4 + 128 (s % 2), piece tid % 4.
+    // The swizzle does not see the +128, so only the base is per lane.
+    static_assert(APT == 4 && 4 * MT == 2 * THREADS, "piece mapping");
+    const int a_row = tid >> 2, a_d = tid & 3;
+    const int a_lds0 = a_row * 4 + a_slot(a_d, a_row);
+    const uint32_t a_off0 = (uint32_t)a_row * (uint32_t)p.K * 2 + 16 * (uint32_t)a_d;
+    const uint32_t half_rows = 128u * (uint32_t)p.K * 2;   // bytes of 128 rows
+    // This thread's weights: column bc, block bu of each stage.
+    const int bc = tid >> 1, bu = tid & 1;
+
+    for (int64_t tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
+        const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
+        const int64_t r0 = tm * MT, c0 = tn * NT;
+        const int64_t left = p.N - c0;
+        const uint32_t ncols = (uint32_t)(left < NT ? left : NT);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + c0 * row_bytes, (uint64_t)ncols * row_bytes);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + c0 * nb, (uint64_t)ncols * nb * 2);
+        const __amdgpu_buffer_rsrc_t rZ =
+            make_rsrc(p.zp ? p.zp + c0 * p.zb : p.B, p.zp ? (uint64_t)ncols * p.zb : 0);
+        const int64_t mrows = p.M - r0 < MT ? p.M - r0 : MT;
+        const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + r0 * p.K, (uint64_t)mrows * (uint64_t)p.K * 2);
+
+        struct WStage {
+            u32x4 w;
+            uint32_t s, z;
+        };
+        auto issue = [&](WStage& q, int st) {
+            const uint32_t b = (uint32_t)(SB * st + bu);
+            const bool ok = b < (uint32_t)nb;
+            q.w = __builtin_amdgcn_raw_buffer_load_b128(
+                rB, ok ? (uint32_t)bc * row_bytes + 16 * b : kOutOfRange, 0, kNontemporal);
+            q.s = __builtin_amdgcn_raw_buffer_load_b16(
+                rS, ok ? ((uint32_t)bc * (uint32_t)nb + b) * 2 : kOutOfRange, 0, kNontemporal);
+            q.z = __builtin_amdgcn_raw_buffer_load_b8(
+                rZ, ok ? (uint32_t)bc * (uint32_t)p.zb + b / 2 : kOutOfRange, 0, kNontemporal);
+        };
+        auto fetch_a = [&](uint4 (&v)[APT], int st) {
+#pragma unroll
+            for (int s = 0; s < APT; ++s) {
+                const uint32_t off = a_off0 + (s & 1) * half_rows + 64 * (s >> 1) + 128 * (uint32_t)st;
+                const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
+                    rA, SB * st + (s >> 1) < nb ? off : kOutOfRange, 0, 0);
+                v[s] = make_uint4(x[0], x[1], x[2], x[3]);
+            }
+        };
+        // Activations to fp16 in the unpack's pair order; weights dequantized
+        // to fp16 (q - z) * s in the same order; both into buffer buf.
+        auto store = [&](const uint4 (&v)[APT], const WStage& q, int buf) {
+#pragma unroll
+            for (int s = 0; s < APT; ++s) {
+                const uint4 x = v[s];
+                uint4 o;
+                if constexpr (ABF16) {
+                    o.x = pair_bf16(x.x, x.z, false);
+                    o.y = pair_bf16(x.x, x.z, true);
+                    o.z = pair_bf16(x.y, x.w, false);
+                    o.w = pair_bf16(x.y, x.w, true);
+                } else {
+                    o.x = pair16(x.x, x.z, false);
+                    o.y = pair16(x.x, x.z, true);
+                    o.z = pair16(x.y, x.w, false);
+                    o.w = pair16(x.y, x.w, true);
+                }
+                a_lds[buf * QA + a_lds0 + ((s >> 1) * MT + 128 * (s & 1)) * 4] = o;
+            }
+            // Block SB*st + bu has parity bu (SB is even): its zero point is
+            // nibble bu of the byte.
+            const uint32_t zn = ((q.z >> (4 * bu)) & 0xFu) | zdef;
+            const ZeroPoint zp = zero_point_pairs(zn);
+            const uint32_t s2 = __builtin_amdgcn_perm(q.s, q.s, 0x01000100u);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t bq[4];
+                unpack_dword(q.w[d], zp, magic, bq);
+                b_lds[buf * QB + (bu * NT + bc) * 4 + a_slot(d, bc)] =
+                    make_uint4(hmul2(bq[0], s2), hmul2(bq[1], s2), hmul2(bq[2], s2), hmul2(bq[3], s2));
+            }
+        };
+
+        float16_t acc[RTW][CTW];
+#pragma unroll
+        for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+            for (int ct = 0; ct < CTW; ++ct)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) acc[rt][ct][q] = 0.f;
+
+        auto compute = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < SB; ++i)
+#pragma unroll
+                for (int v = 0; v < 2; ++v) {
+                    half8_t fa[RTW], fb[CTW];
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt) {
+                        const int row = wr * 128 + rt * 32 + j;
+                        const uint4 x = a_lds[buf * QA + (i * MT + row) * 4 + a_slot(2 * h + v, row)];
+                        fa[rt] = __builtin_bit_cast(half8_t, u32x4{x.x, x.y, x.z, x.w});
+                    }
+#pragma unroll
+                    for (int ct = 0; ct < CTW; ++ct) {
+                        const int col = wc * 64 + ct * 32 + j;
+                        const uint4 x = b_lds[buf * QB + (i * NT + col) * 4 + a_slot(2 * h + v, col)];
+                        fb[ct] = __builtin_bit_cast(half8_t, u32x4{x.x, x.y, x.z, x.w});
+                    }
+#pragma unroll
+                    for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                        for (int ct = 0; ct < CTW; ++ct)
+                            acc[rt][ct] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[rt], fb[ct], acc[rt][ct],
+                                                                                 0, 0, 0);
+                }
+        };
+
+        // Weight stages P ahead, activations one ahead, both stored into
+        // LDS one stage ahead of use; one barrier per stage.  Stages past K
+        // load zeros and add +0.
+        WStage ring[P];
+#pragma unroll
+        for (int s = 0; s < P; ++s) issue(ring[s], s);
+        uint4 av[APT];
+        fetch_a(av, 0);
+        __syncthreads();                  // the previous tile's readers are done
+        store(av, ring[0], 0);
+        issue(ring[0], P);
+        fetch_a(av, 1);
+        for (int s0 = 0; s0 < ns; s0 += P) {
+#pragma unroll
+            for (int s = 0; s < P; ++s) {
+                const int st = s0 + s;
+                __syncthreads();
+                store(av, ring[(s + 1) % P], (st + 1) & 1);
+                issue(ring[(s + 1) % P], st + 1 + P);
+                compute(st & 1);
+                fetch_a(av, st + 2);
+            }
+        }
+
+        // Epilogue: accumulator element q of lane (j, h) of tile (rt, ct) is
+        // row 128 wr + 32 rt + (q%4) + 4h + 8(q/4), column 64 wc + 32 ct + j.
+#pragma unroll
+        for (int ct = 0; ct < CTW; ++ct) {
+            const int64_t col = c0 + wc * 64 + ct * 32 + j;
+            if (col < p.N) {
+#pragma unroll
+                for (int rt = 0; rt < RTW; ++rt)
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) {
+                        const int64_t row = r0 + wr * 128 + rt * 32 + (q & 3) + 4 * h + 8 * (q >> 2);
+                        if (row < p.M) {
+                            const _Float16 hv = (_Float16)acc[rt][ct][q];
+                            uint16_t bits = __builtin_bit_cast(uint16_t, hv);
+                            if (p.out_bf16) bits = f16_to_bf16(bits);
+                            p.out[row * p.N + col] = bits;
+                        }
+                    }
+            }
+        }
+    }
+}
+
 typedef void (*GemmFn)(GemmParams);
 
 template <int CT, int W, bool VEC, bool ABF16>
@@ -388,6 +592,9 @@ GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 GemmFn lookup_gemm(const mnb_plan& plan, bool vec, bool a_bf16)
 {
     const int rt = plan.row_tiles, cols = plan.cols_per_tile, w = plan.waves_per_wg;
+    if (rt == 8)   // 256 x 256, weights through LDS (any scale alignment)
+        return cols == kLdsTileCols && w == 8 ? (a_bf16 ? mnb_gemm_lds_kernel<true> : mnb_gemm_lds_kernel<false>)
+                                              : nullptr;
     if (vec) return a_bf16 ? lookup_gemm_shape<true, true>(rt, cols, w) : lookup_gemm_shape<true, false>(rt, cols, w);
     return a_bf16 ? lookup_gemm_shape<false, true>(rt, cols, w) : lookup_gemm_shape<false, false>(rt, cols, w);
 }
@@ -401,6 +608,8 @@ bool gemm_vec_ok(int64_t K, const void* scales, const void* zp)
 
 size_t gemm_lds_bytes(const mnb_plan& plan)
 {
+    if (plan.row_tiles == 8)   // two stages of activations and weights
+        return (size_t)2 * (kLdsTileRows + kLdsTileCols) * 2 * 4 * 16;
     return (size_t)2 * 4 * 32 * plan.row_tiles * 4 * 16;   // two quads of 32*rt rows x 128 k, fp16
 }
 

@@ -100,10 +100,16 @@ def test_default_prefill_plans():
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
             assert p.engine == 2 and p.cols_per_tile in (128, 256)
-            assert p.waves_per_wg == (8 if (p.row_tiles, p.cols_per_tile) == (4, 256) else 4)
+            assert p.waves_per_wg == (8 if p.row_tiles >= 4 and p.cols_per_tile == 256 else 4)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
             assert q.threads_per_wg == 64 * p.waves_per_wg and q.k_chunks == (K // 32 + 3) // 4
+            t8 = -(-m // 256) * -(-N // 256)
+            if p.row_tiles == 8:     # 256 x 256 tiles: when they give 85% of the CUs a tile
+                assert p.cols_per_tile == 256 and m > 128 and 0.85 * cus <= t8
+                assert 1 <= p.workgroups <= t8
+                continue
+            assert not (m > 128 and 0.85 * cus <= t8 and 512 * K <= 0xFFFFFFF0)
             rt, cols = p.row_tiles, p.cols_per_tile
             assert rt in (1, 2, 4) and (rt == 1 or 32 * (rt // 2) < m)
 
@@ -123,7 +129,8 @@ def test_default_prefill_plans():
                 assert cols == 128 and tiles(2 * rt, 128) < cus
             assert 1 <= p.workgroups <= tiles(rt, cols)
     # The two prefill shapes of the decode model at 512 and 2048 rows.
-    assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(2048, 4096, 28672, 256, 0)) == (4, 256)
+    for m in (512, 1024, 2048):
+        assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(m, 4096, 28672, 256, 0)) == (8, 256)
     assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(512, 14336, 4096, 256, 0)) == (2, 128)
 
 
@@ -136,7 +143,10 @@ def test_plan_check_engines_and_rows():
             q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=1)
             assert mnb.mnb_plan_check(20, 4096, 100, q) == 0
             assert q.threads_per_wg == 64 * waves
-    for bad in (dict(row_tiles=3), dict(row_tiles=8), dict(cols_per_tile=64), dict(cols_per_tile=96),
+    q8 = mnb.mnb_plan(engine=2, row_tiles=8, cols_per_tile=256, waves_per_wg=8, workgroups=1)
+    assert mnb.mnb_plan_check(20, 4096, 100, q8) == 0              # 256 x 256, weights through LDS
+    for bad in (dict(row_tiles=3), dict(row_tiles=16), dict(row_tiles=8, waves_per_wg=4),
+                dict(row_tiles=8, cols_per_tile=128, waves_per_wg=8), dict(cols_per_tile=64), dict(cols_per_tile=96),
                 dict(cols_per_tile=512), dict(waves_per_wg=2), dict(waves_per_wg=8),
                 dict(waves_per_wg=8, cols_per_tile=512), dict(waves_per_wg=16, cols_per_tile=256),
                 dict(workgroups=0)):

@@ -73,6 +73,20 @@ def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols, waves):
                        plan)
 
 
+@pytest.mark.parametrize("m,K,N,a_dtype,asym", [
+    (261, 32 * 61, 300, W.BF16, True),     # ragged rows, columns, odd block count
+    (40, 4096, 513, W.F16, False),         # one partial row block, zero point 8
+    (512, 14336, 260, W.BF16, True),       # two row blocks, long K
+])
+def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
+    """256 x 256 tiles with the weights dequantized once per workgroup into
+    LDS (row_tiles 8, eight waves), with 1, 3 and 13 workgroups."""
+    d = W.generate(m, K, N, a_dtype, asym, 0.002, 0.02, 1.0, 800 + m)
+    for wg in (1, 3, 13):
+        plan = dict(engine=2, row_tiles=8, cols_per_tile=256, waves_per_wg=8, workgroups=wg)
+        assert_prefill(oracle_mod, d, m, "prefill lds-staged wg=%d" % wg, plan)
+
+
 def test_prefill_engine_for_decode_heights(oracle_mod):
     """The prefill engine also serves m <= 8 when asked for explicitly."""
     d = W.generate(3, 4096, 129, W.BF16, True, 0.001, 0.01, 0.5, 730)
@@ -90,7 +104,8 @@ def test_prefill_rows_do_not_depend_on_launch_height():
     assert np.array_equal(y40[:17], y17)
 
 
-@pytest.mark.parametrize("name,K,N,m", [("gate_up", 4096, 28672, 2048), ("down", 14336, 4096, 512)])
+@pytest.mark.parametrize("name,K,N,m", [("gate_up", 4096, 28672, 2048), ("gate_up", 4096, 28672, 512),
+                                        ("down", 14336, 4096, 512)])
 def test_prefill_full_size_sampled(oracle_mod, name, K, N, m):
     """The benchmarked prefill shapes at full size under the default plan:
     check 1 and the fp16-weight bound on a sample of whole columns (every
