@@ -77,6 +77,8 @@ def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols, waves):
     (261, 32 * 61, 300, W.BF16, True),     # ragged rows, columns, odd block count
     (40, 4096, 513, W.F16, False),         # one partial row block, zero point 8
     (512, 14336, 260, W.BF16, True),       # two row blocks, long K
+    (300, 0, 600, W.BF16, True),           # K = 0: every output +0
+    (300, 32, 600, W.F16, True),           # one block: half of the only stage
 ])
 def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
     """256 x 256 tiles with the weights dequantized once per workgroup into
