@@ -440,10 +440,36 @@ def decode_step(args, stream, L, layers=4):
     us_graph = event_time_us(stream, lambda i: g.replay(), n)
     log("[bench] decode step (%d GEMVs, %.0f MB): eager %.1f us, graph %.1f us; graph == eager %s"
         % (len(calls), nbytes / 1e6, us_eager, us_graph, same))
+
+    # Launch cost at the small end: a chain of 64 GEMVs of the 1024 x 1024
+    # shape (cache-resident weights), eager against one replayed graph.
+    d = W.generate(1, 1024, 1024, W.F16, False, 0.002, 0.02, 1.0, 70)
+    sB = torch.from_numpy(d["B"]).to(dev)
+    sS = torch.from_numpy(d["scales"].view(np.int16)).to(dev)
+    sA = torch.from_numpy(np.ascontiguousarray(d["A"][:1]).view(np.int16)).to(dev)
+    souts = [torch.empty((1, 1024), dtype=torch.float16, device=dev) for _ in range(64)]
+
+    def chain(s):
+        for o in souts:
+            st = L.matmul_nbits(sA.data_ptr(), W.F16, 1, 1024, 1024, sB.data_ptr(), sS.data_ptr(),
+                                None, 32, o.data_ptr(), W.F16, s)
+            assert st == 0, st
+    for _ in range(10):
+        chain(stream.cuda_stream)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        chain(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    us_ce = event_time_us(stream, lambda i: chain(stream.cuda_stream), 20) / len(souts)
+    us_cg = event_time_us(stream, lambda i: g2.replay(), 20) / len(souts)
+    log("[bench] 64 small GEMVs (1024 x 1024): eager %.2f us each, graph %.2f us each" % (us_ce, us_cg))
     return {"gemvs": len(calls), "layers": layers, "bytes": nbytes,
             "eager_us": round(us_eager, 2), "graph_us": round(us_graph, 2),
             "graph_GB/s": round(nbytes / (us_graph * 1e-6) / 1e9, 1),
-            "graph_outputs_equal_eager": bool(same)}
+            "graph_outputs_equal_eager": bool(same),
+            "small_chain": {"gemvs": len(souts), "K": 1024, "N": 1024,
+                            "eager_us_per_gemv": round(us_ce, 3), "graph_us_per_gemv": round(us_cg, 3)}}
 
 
 def offline_layout(args, stream, L, cus):
