@@ -539,6 +539,15 @@ __global__ __launch_bounds__(512) void mnb_gemm_lds_kernel(GemmParams p)
                 issue(ring[(s + 1) % P], st + 1 + P);
                 compute(st & 1);
                 fetch_a(av, st + 2);
+                // The two waves of a SIMD reach each barrier together, so the
+                // conversions of a stage only overlap the matrix core if they
+                // sit between its MFMAs: four VALU instructions after each of
+                // the stage's 32 (2, 3 and 6 were slower).
+#pragma unroll
+                for (int g = 0; g < 32; ++g) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);   // VALU
+                }
             }
         }
 
