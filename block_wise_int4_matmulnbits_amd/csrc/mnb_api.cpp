@@ -180,6 +180,19 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
         plan->k_chunks = (int32_t)chunks;
         return MNB_OK;
     }
+    if (plan->engine == 3) {
+        // 4x4x4 MFMA kernel: the workgroup's 16 * waves lane groups cover K
+        // in one pass, blocks_per_lane blocks each; 4 or 8 columns per tile.
+        const int64_t w = plan->waves_per_wg, bpl = plan->blocks_per_lane;
+        if (w < 1 || w > 8 || !is_pow2_in(bpl, 1, 4) ||
+            (plan->cols_per_tile != 4 && plan->cols_per_tile != 8))
+            return MNB_ERR_PLAN;
+        if (16 * w * bpl < nb) return MNB_ERR_PLAN;
+        if (m > 4 && bpl * (plan->cols_per_tile / 4) > 4) return MNB_ERR_PLAN;   // registers
+        plan->threads_per_wg = (int32_t)(64 * w);
+        plan->k_chunks = 1;
+        return MNB_OK;
+    }
     if (plan->engine != 0) return MNB_ERR_PLAN;
     const int64_t lpc = plan->lanes_per_col;
     const int64_t bpl = plan->blocks_per_lane;
@@ -243,6 +256,29 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     }
     const int64_t nb = K / 32;
     const int64_t bmax = max_blocks_per_lane(m);
+
+    // Four or more rows with K within one pass of a workgroup (8 waves x 16
+    // lane groups x 4 blocks): the 4x4x4 MFMA kernel, whose dot products do
+    // not grow the VALU work with m (measured against the lane split below:
+    // gate_up m = 8 70.4 -> 26.5 us, m = 4 26.5 -> 21.4; down m = 8 26.1 ->
+    // 20.0, m = 4 17.3 -> 15.0; the 6144-column shape m = 8 20.0 -> 12.6).
+    // Its lane split (waves, blocks per lane) depends on K only; one
+    // resident generation of workgroups.
+    if (m >= 4 && nb >= 1 && nb <= 512) {
+        const int64_t bpl3 = nb <= 256 ? 2 : 4;
+        const int64_t w3 = ceil_div(nb, 16 * bpl3);
+        const int64_t cols3 = (m <= 4 && bpl3 <= 2) ? 8 : 4;
+        const int64_t tiles3 = ceil_div(N, cols3);
+        const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
+        int64_t wgs3 = per_cu3 * num_cus;
+        if (wgs3 > tiles3) wgs3 = tiles3;
+        plan->engine = 3;
+        plan->waves_per_wg = (int32_t)w3;
+        plan->blocks_per_lane = (int32_t)bpl3;
+        plan->cols_per_tile = (int32_t)cols3;
+        plan->workgroups = (int32_t)(wgs3 < 1 ? 1 : wgs3);
+        return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
+    }
 
     // 1. Lane split -- a function of (m, K) only, so the fp32 summation order
     //    of a column never depends on N or on the device (column shards of

@@ -1,0 +1,339 @@
+// Row-batched INT4 MatMulNBits GEMV (a few rows) on the 4x4x4 matrix
+// product of gfx950, v_mfma_f32_4x4x4_16b_f16.
+//
+//   y[r][n] = sum_k a[r][k] * (q[n][k] - z[n][k/32]) * s[n][k/32]
+//
+// The operation, arithmetic and epilogue are those of the lane-split kernel
+// (onnx-genai pull request "perf(cuda): let the split-K decode GEMV store
+// bf16 directly", opening paragraphs and the paragraph on
+// matmul_nbits_store_narrowed; pull request "PORT-1 (offline
+// bias+interleave)", "Why the premise fails here", item 1): fp16 (or bf16
+// rounded to fp16) activations, exact products a * (q - z) summed in fp32
+// per 32-weight block, the block's fp16 scale applied by one fp32 FMA, one
+// fp16 rounding of the total and, for bf16 output, the narrowing to bf16.
+//
+// Why this shape.  With several rows the lane-split kernel spends four
+// v_dot2 per eight weights per row; one v_mfma_f32_4x4x4_16b_f16 does the
+// work of eight of them in about two of their issue slots.  The instruction
+// is sixteen independent 4x4x4 products, one per group of four lanes: lane
+// 4b+i supplies row i of block b's A operand (four k) and column i of its B
+// operand, and receives column i of the 4x4 result (register r = row r).
+//
+// Work decomposition.  A workgroup of W waves owns a contiguous range of
+// column quads and walks it NC quads at a time.  Lane (g, i) of a wave (group
+// g = lane / 4) holds column 4n + i of each quad n and, as the A side, rows i
+// and 4 + i of the activations; group gg = 16 * wave + g owns K blocks
+// gg, gg + 16W, ..., BPL of them, which together cover all of K in one pass.
+// The lane's activations are loaded once, converted to fp16, permuted into
+// the unpack's pair order and kept in VGPRs.  Per block and column the lane
+// loads its 16 bytes of weights (the four lanes of a group read four
+// columns, the sixteen groups of a wave 256 contiguous bytes of each),
+// unpacks them to the exact fp16 integers q - z, and per row quad eight
+// chained MFMAs give the block's exact 4 x 4 product, which one FMA per row
+// scales into the lane's fp32 accumulators.  Partial sums meet through a
+// fixed xor-shuffle tree inside the wave and a wave-ordered sum in LDS, so
+// the summation order depends only on (K, W, BPL).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mnb.h"
+#include "mnb_device.h"
+#include "mnb_internal.h"
+
+namespace mnb {
+namespace {
+
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+struct Mfma4Params {
+    const uint16_t* A;       // [m][K]
+    const uint8_t* B;        // [N][K/2]
+    const uint16_t* scales;  // [N][nb]
+    const uint8_t* zp;       // [N][zb] or null
+    uint16_t* out;           // [m][N]
+    int64_t N;
+    int32_t m, K, nb, zb;
+    uint32_t zero;           // always 0 (see vgpr_constant)
+    int32_t a_bf16, out_bf16;
+};
+
+__device__ __forceinline__ half4_t as_half4(uint32_t lo, uint32_t hi)
+{
+    return __builtin_bit_cast(half4_t, (uint32_t __attribute__((ext_vector_type(2)))){lo, hi});
+}
+
+// RQ row quads (m <= 4 * RQ), BPL blocks per group, NC column quads per tile.
+template <int RQ, int BPL, int NC>
+__global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
+{
+    constexpr int NV = 16 * NC * RQ;        // results of one tile (columns x rows)
+    __shared__ float part[2][8][NV];        // per-wave tile totals, two tiles deep
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int W = (int)(blockDim.x >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int qi = lane & 3, g = lane >> 2;
+    const uint32_t gg = (uint32_t)(wv * 16 + g);
+    const uint32_t GT = (uint32_t)(16 * W);
+    const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
+    const uint32_t row_bytes = (uint32_t)p.K / 2;
+    const int zshift = (g & 1) * 4;         // block parity == group parity (GT even)
+    const uint32_t zdef = p.zp ? 0u : 8u;   // zero point 8 when none are given
+    const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
+
+    // Column quads [q_first, q_stop) of this workgroup.
+    const int64_t nq = (p.N + 3) / 4;
+    const int64_t q_first = nq * blockIdx.x / gridDim.x;
+    const int64_t q_stop = nq * (blockIdx.x + 1) / gridDim.x;
+    const int64_t c_stop = 4 * q_stop < p.N ? 4 * q_stop : p.N;
+
+    // Activations: rows qi and 4 + qi of this group's blocks; rows past m and
+    // blocks past K load zeros.
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)p.m * (uint64_t)p.K * 2);
+    u32x4 raw[RQ][BPL][4];
+#pragma unroll
+    for (int rq = 0; rq < RQ; ++rq)
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            const uint32_t b = (uint32_t)j * GT + gg;
+            const uint32_t base = (uint32_t)(4 * rq + qi) * (uint32_t)p.K * 2 + 64 * b;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                raw[rq][j][i] = __builtin_amdgcn_raw_buffer_load_b128(rA, b < nb ? base + 16 * i : kOutOfRange, 0, 0);
+        }
+
+    struct Tile {
+        u32x4 w[NC][BPL];
+        uint32_t sc[NC][BPL];
+        uint32_t zq[NC][BPL];
+    };
+    // Loads of column quads qs .. qs + NC - 1 (zeros past this workgroup's
+    // columns and past K: every load is issued, none touches memory there).
+    auto issue = [&](Tile& t, int64_t qs) {
+        const int64_t c0 = 4 * qs;
+        const bool live = qs < q_stop;
+        const int64_t left = c_stop - c0;
+        const uint32_t ncols = live ? (uint32_t)(left < 4 * NC ? left : 4 * NC) : 0u;
+        const int64_t cb = live ? c0 : 0;
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + cb * row_bytes, (uint64_t)ncols * row_bytes);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + cb * nb, (uint64_t)ncols * nb * 2);
+        const __amdgpu_buffer_rsrc_t rZ =
+            make_rsrc(p.zp ? p.zp + cb * zb : p.B, p.zp ? (uint64_t)ncols * zb : 0);
+#pragma unroll
+        for (int n = 0; n < NC; ++n) {
+            const uint32_t col = (uint32_t)(4 * n + qi);
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t b = (uint32_t)j * GT + gg;
+                const bool ok = b < nb;
+                t.w[n][j] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rB, ok ? col * row_bytes + 16 * b : kOutOfRange, 0, kNontemporal);
+                t.sc[n][j] = __builtin_amdgcn_raw_buffer_load_b16(
+                    rS, ok ? (col * nb + b) * 2 : kOutOfRange, 0, kNontemporal);
+                t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(
+                    rZ, ok ? col * zb + (b >> 1) : kOutOfRange, 0, kNontemporal);
+            }
+        }
+    };
+
+    Tile ta, tb;
+    issue(ta, q_first);
+    issue(tb, q_first + NC);
+
+    // fp16 (bf16 rounded to nearest even), pairs (a_e, a_e+4) per 8 k: the
+    // order in which the unpack yields the weights.
+    uint32_t act[RQ][BPL][16];
+#pragma unroll
+    for (int rq = 0; rq < RQ; ++rq)
+#pragma unroll
+        for (int j = 0; j < BPL; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t x = raw[rq][j][i][0], y = raw[rq][j][i][1], z = raw[rq][j][i][2], w = raw[rq][j][i][3];
+                if (p.a_bf16) {
+                    x = bf16x2_to_f16x2(x);
+                    y = bf16x2_to_f16x2(y);
+                    z = bf16x2_to_f16x2(z);
+                    w = bf16x2_to_f16x2(w);
+                }
+                act[rq][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
+                act[rq][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
+                act[rq][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
+                act[rq][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
+            }
+
+    // Per block: the exact products of each row quad in one 4x4 result
+    // (eight chained MFMAs over the block's 32 k), then acc += D * s.
+    auto compute = [&](const Tile& t, float4_t (&acc)[NC][RQ]) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) {
+                const ZeroPoint zp = zero_point_pairs(((t.zq[n][j] >> zshift) & 0xFu) | zdef);
+                uint32_t pr[4][4];
+#pragma unroll
+                for (int d = 0; d < 4; ++d) unpack_dword(t.w[n][j][d], zp, magic, pr[d]);
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(t.sc[n][j] & 0xFFFFu));
+#pragma unroll
+                for (int rq = 0; rq < RQ; ++rq) {
+                    float4_t dsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        dsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                            as_half4(act[rq][j][4 * d + 0], act[rq][j][4 * d + 1]),
+                            as_half4(pr[d][0], pr[d][1]), dsum, 0, 0, 0);
+                        dsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                            as_half4(act[rq][j][4 * d + 2], act[rq][j][4 * d + 3]),
+                            as_half4(pr[d][2], pr[d][3]), dsum, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[n][rq][r] = fmaf(dsum[r], sf, acc[n][rq][r]);
+                }
+            }
+    };
+
+    // Sum over the 64 groups' partials (same column lane i in every group),
+    // then over the waves in wave order; one barrier per tile, two LDS slots.
+    int buf = 0;
+    auto finish = [&](float4_t (&acc)[NC][RQ], int64_t qs) {
+#pragma unroll
+        for (int n = 0; n < NC; ++n)
+#pragma unroll
+            for (int rq = 0; rq < RQ; ++rq)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = acc[n][rq][r];
+                    v += __shfl_xor(v, 4);
+                    v += __shfl_xor(v, 8);
+                    v += __shfl_xor(v, 16);
+                    v += __shfl_xor(v, 32);
+                    acc[n][rq][r] = v;
+                }
+        if (g == 0) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n)
+#pragma unroll
+                for (int rq = 0; rq < RQ; ++rq)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        part[buf][wv][((4 * n + qi) * RQ + rq) * 4 + r] = acc[n][rq][r];
+        }
+        __syncthreads();
+        if (tid < NV) {
+            float v = part[buf][0][tid];
+            for (int w = 1; w < W; ++w) v += part[buf][w][tid];
+            const int64_t col = 4 * qs + tid / (4 * RQ);
+            const int row = tid % (4 * RQ);
+            if (row < p.m && col < c_stop) {
+                const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
+                uint16_t bits = __builtin_bit_cast(uint16_t, h);
+                if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
+                p.out[(int64_t)row * p.N + col] = bits;
+            }
+        }
+        buf ^= 1;
+    };
+
+    for (int64_t qs = q_first; qs < q_stop;) {
+        {
+            float4_t acc[NC][RQ] = {};
+            compute(ta, acc);
+            issue(ta, qs + 2 * NC);
+            finish(acc, qs);
+            qs += NC;
+        }
+        if (qs >= q_stop) break;
+        {
+            float4_t acc[NC][RQ] = {};
+            compute(tb, acc);
+            issue(tb, qs + 2 * NC);
+            finish(acc, qs);
+            qs += NC;
+        }
+    }
+}
+
+typedef void (*Mfma4Fn)(Mfma4Params);
+
+template <int RQ, int BPL>
+Mfma4Fn by_nc(int nc)
+{
+    switch (nc) {
+    case 1: return mnb_gemv_mfma4_kernel<RQ, BPL, 1>;
+    case 2: return mnb_gemv_mfma4_kernel<RQ, BPL, 2>;
+    }
+    return nullptr;
+}
+
+template <int RQ>
+Mfma4Fn by_bpl(int bpl, int nc)
+{
+    switch (bpl) {
+    case 1: return by_nc<RQ, 1>(nc);
+    case 2: return by_nc<RQ, 2>(nc);
+    case 4: return by_nc<RQ, 4>(nc);
+    }
+    return nullptr;
+}
+
+Mfma4Fn lookup_mfma4(int64_t m, const mnb_plan& plan)
+{
+    const int nc = plan.cols_per_tile / 4;
+    if (m >= 1 && m <= 4) return by_bpl<1>(plan.blocks_per_lane, nc);
+    if (m >= 5 && m <= 8) return by_bpl<2>(plan.blocks_per_lane, nc);
+    return nullptr;
+}
+
+}  // namespace
+
+int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
+{
+    Mfma4Fn fn = lookup_mfma4(a.m, plan);
+    if (!fn) return (int)hipErrorInvalidDeviceFunction;
+    Mfma4Params p;
+    p.A = static_cast<const uint16_t*>(a.A);
+    p.B = a.B;
+    p.scales = a.scales;
+    p.zp = a.zp;
+    p.out = static_cast<uint16_t*>(a.out);
+    p.N = a.N;
+    p.m = (int32_t)a.m;
+    p.K = (int32_t)a.K;
+    p.nb = (int32_t)(a.K / 32);
+    p.zb = (p.nb + 1) / 2;
+    p.zero = 0;
+    p.a_bf16 = a.a_bf16;
+    p.out_bf16 = a.out_bf16;
+    void* args[] = {&p};
+    hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)plan.workgroups),
+                                   dim3((unsigned)plan.threads_per_wg), args, 0,
+                                   static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+    return (int)e;
+}
+
+int mfma4_workgroups_per_cu(int64_t m, const mnb_plan& plan)
+{
+    Mfma4Fn fn = lookup_mfma4(m, plan);
+    if (!fn) return 0;
+    return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, 0);
+}
+
+int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
+{
+    Mfma4Fn fn = lookup_mfma4(m, plan);
+    if (!fn) return -1;
+    hipFuncAttributes attr;
+    hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
+    if (e != hipSuccess) return (int)e;
+    info->vgprs = attr.numRegs;
+    info->sgprs = 0;
+    info->lds_bytes = (int32_t)attr.sharedSizeBytes;
+    info->max_threads = attr.maxThreadsPerBlock;
+    info->wgs_per_cu = mfma4_workgroups_per_cu(m, plan);
+    return 0;
+}
+
+}  // namespace mnb

@@ -28,6 +28,13 @@ int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
 int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
+// The 4x4x4 MFMA kernel (engine 3), mnb_gemv_mfma4.hip: W waves per
+// workgroup whose 16 W lane groups cover K in one pass (16 W * blocks_per_lane
+// >= K/32), cols_per_tile = 4 or 8.  No dynamic LDS.
+int launch_mfma4(const GemvArgs& args, const mnb_plan& plan, void* stream);
+int mfma4_workgroups_per_cu(int64_t m, const mnb_plan& plan);
+int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
+
 // The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of 4 or 8
 // waves owns 32 * row_tiles rows by cols_per_tile columns (4 waves: 128 or
 // 256 columns, 32 or 64 per wave; 8 waves: 256 columns, 32 per wave).

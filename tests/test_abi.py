@@ -72,11 +72,26 @@ SHAPES = [(m, K, N) for m in range(1, 9)
 
 
 def test_default_plans_are_valid_and_cover_k():
+    split3 = {}
     for m, K, N in SHAPES:
         for cus, occ in ((1, 0), (80, 3), (256, 0), (256, 5), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
+            nb = K // 32
+            if p.engine == 3:
+                # The 4x4x4 MFMA kernel: four or more rows, K in one pass of
+                # the workgroup's 16 * waves lane groups; its lane split
+                # depends on K only.
+                assert 4 <= m <= 8 and 1 <= nb <= 512
+                w, bpl = p.waves_per_wg, p.blocks_per_lane
+                assert 1 <= w <= 8 and bpl in (1, 2, 4) and 16 * w * bpl >= nb > 16 * (w - 1) * bpl
+                assert split3.setdefault(K, (w, bpl)) == (w, bpl)
+                assert q.k_chunks == 1 and q.threads_per_wg == 64 * w
+                assert p.cols_per_tile in (4, 8) and not (m > 4 and bpl * p.cols_per_tile // 4 > 4)
+                assert 1 <= p.workgroups <= -(-N // p.cols_per_tile)
+                continue
+            assert p.engine == 0 and not (m >= 4 and 1 <= nb <= 512)
             lpc, bpl, nc = p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile
             assert lpc * bpl * p.k_chunks >= K // 32
             assert m * bpl <= 8 and nc * bpl <= 8 and nc * m <= 32
@@ -199,10 +214,16 @@ def test_default_plan_shapes():
     assert p.workgroups == 15 * 256             # ~5 tiles per group, whole rounds of CUs
     p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
-    for m, occ, nc, wg in ((2, 4, 1, 512), (4, 2, 1, 256), (8, 1, 1, 256)):
-        p = mnb.mnb_plan_default(m, 14336, 4096, 256, occ)
-        assert (p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (448, 1, 1)
-        assert (p.cols_per_tile, p.workgroups) == (nc, wg)
+    p = mnb.mnb_plan_default(2, 14336, 4096, 256, 4)
+    assert (p.engine, p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (0, 448, 1, 1)
+    assert (p.cols_per_tile, p.workgroups) == (1, 512)
+    # Four or more rows: the 4x4x4 MFMA kernel, seven waves of four blocks per
+    # lane group for the 14336-long K, four waves of two for 4096.
+    for m, K, N, occ, shape in ((4, 14336, 4096, 1, (7, 4, 4, 256)), (8, 14336, 4096, 1, (7, 4, 4, 256)),
+                                (4, 4096, 28672, 3, (4, 2, 8, 768)), (8, 4096, 28672, 2, (4, 2, 4, 512))):
+        p = mnb.mnb_plan_default(m, K, N, 256, occ)
+        assert p.engine == 3
+        assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape
 
 
 def test_plan_check_rows_limit():

@@ -326,3 +326,67 @@ def test_kernel_info():
     info = mnb.mnb_get_kernel_info(1, 4096, plan)
     G.log("[info] lm_head plan %s info %s" % (plan.as_dict(), info))
     assert 0 < info["vgprs"] <= 512 and info["wgs_per_cu"] >= 1
+
+
+# ------------------------------------------------- 4x4x4 MFMA kernel (engine 3)
+def test_mfma4_engine_every_variant_ragged(oracle_mod):
+    """The 4x4x4 MFMA kernel for every m, every (blocks per lane, column
+    quads per tile) variant, ragged N (not a multiple of 4) and K (a ragged
+    last pass of the lane groups), one to eight waves, more or fewer
+    workgroups than column tiles."""
+    rng = np.random.default_rng(3)
+    i = 0
+    for m in range(1, 9):
+        for bpl in (1, 2, 4):
+            for cols in (4, 8):
+                if m > 4 and bpl * cols // 4 > 4:
+                    continue
+                w = int(rng.integers(1, 9))
+                nb = int(rng.integers(max(1, 16 * (w - 1) * bpl + 1), 16 * w * bpl + 1))
+                K, N = 32 * nb, int(rng.integers(1, 70))
+                d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i % 3 != 1, 0.002, 0.02, 1.0, 400 + i)
+                plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols,
+                            workgroups=int(rng.integers(1, 25)))
+                assert_parity(oracle_mod, d, m, "mfma4", plan)
+                i += 1
+
+
+def test_mfma4_engine_shapes(oracle_mod):
+    """Decode shapes through the 4x4x4 MFMA kernel: the largest K of one
+    pass (8 waves x 16 groups x 4 blocks), the 14336-long K in seven waves,
+    a single column, columns spread over more workgroups than tiles."""
+    cases = [
+        # m, K, N, waves, blocks per lane, cols, workgroups
+        (8, 16384, 37, 8, 4, 4, 5),
+        (5, 14336, 301, 7, 4, 4, 3),
+        (4, 4096, 1, 4, 2, 8, 3),
+        (7, 4096, 130, 4, 2, 8, 200),
+        (1, 2048, 99, 2, 2, 8, 4),
+    ]
+    for i, (m, K, N, w, bpl, cols, wg) in enumerate(cases):
+        d = W.generate(m, K, N, W.BF16, i % 2 == 0, 0.001, 0.01, 0.5, 430 + i)
+        plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols, workgroups=wg)
+        assert_parity(oracle_mod, d, m, "mfma4", plan)
+
+
+def test_mfma4_engine_rows_and_columns_match():
+    """Under one 4x4x4 MFMA plan, row r of an m-row launch is bit-identical
+    to a one-row launch on row r, and a column shard gives the bits of the
+    whole (the lane split fixes the summation order of every column)."""
+    d = W.generate(8, 14336, 203, W.BF16, True, 0.001, 0.01, 0.5, 440)
+    plan = dict(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=4, workgroups=9)
+    y8, _ = run(d, 8, W.BF16, plan)
+    for r in (0, 3, 5, 7):
+        y1, _ = run(dict(d, A=d["A"][r:r + 1]), 1, W.BF16, plan)
+        assert np.array_equal(y1[0], y8[r])
+    lo, hi = 41, 150
+    shard = dict(d, B=d["B"][lo:hi], scales=d["scales"][lo:hi], zp=d["zp"][lo:hi], N=hi - lo)
+    ys, _ = run(shard, 8, W.BF16, dict(plan, workgroups=4))
+    assert np.array_equal(ys, y8[:, lo:hi])
+
+
+def test_mfma4_engine_k_zero():
+    d = W.generate(6, 0, 23, W.BF16, True, 0.002, 0.02, 1.0, 450)
+    d["zp"] = np.zeros((23, 0), np.uint8)
+    y, cnt = run(d, 6, W.F16, dict(engine=3, waves_per_wg=1, blocks_per_lane=1, cols_per_tile=4, workgroups=2))
+    assert np.all(y == 0) and cnt["elements_f16"] == 6 * 23
