@@ -136,6 +136,15 @@ class Resident:
                  out_dtype, stream) for (b, s, z) in self.copies]
 
 
+def plan_fields(plan):
+    """The fields of a decode plan that its engine reads."""
+    keys = {0: ("lanes_per_col", "blocks_per_lane", "cols_per_tile", "workgroups"),
+            1: ("waves_per_wg", "chunk_blocks", "cols_per_tile", "workgroups"),
+            3: ("waves_per_wg", "blocks_per_lane", "cols_per_tile", "workgroups")}
+    d = plan.as_dict()
+    return dict({"engine": d["engine"]}, **{k: d[k] for k in keys.get(d["engine"], ())})
+
+
 def event_time_us(stream, fn, n):
     """Mean microseconds per fn() over n calls, HIP events on `stream`."""
     import torch
@@ -327,9 +336,7 @@ def other_workloads(args, stream, cus):
         gbs = res.bytes_per_call / (us * 1e-6) / 1e9
         e = {"m": m, "K": w.K, "N": w.N, "us_per_call": round(us, 3), "GB/s": round(gbs, 1),
              "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-             "rotated_copies": res.R, "plan": {k: v for k, v in plan.as_dict().items()
-                                               if k in ("engine", "lanes_per_col", "blocks_per_lane",
-                                                        "cols_per_tile", "workgroups")}}
+             "rotated_copies": res.R, "plan": plan_fields(plan)}
         if m > 1:
             flops = 2.0 * m * w.N * w.K
             e["fp32_valu_floor_us"] = round(flops / (PEAK_FP32_VALU_TFLOPS * 1e12) * 1e6, 3)

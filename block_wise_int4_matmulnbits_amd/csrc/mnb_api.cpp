@@ -153,7 +153,7 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (!plan || m < 1 || m > MNB_MAX_ROWS || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
     if (plan->workgroups < 1) return MNB_ERR_PLAN;
     if (plan->b_layout != MNB_LAYOUT_NATURAL &&
-        !(plan->b_layout == MNB_LAYOUT_EVEN_ODD && plan->engine == 0))
+        !(plan->b_layout == MNB_LAYOUT_EVEN_ODD && (plan->engine == 0 || plan->engine == 3)))
         return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
@@ -257,25 +257,28 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     const int64_t nb = K / 32;
     const int64_t bmax = max_blocks_per_lane(m);
 
-    // Four or more rows with K within one pass of a workgroup (8 waves x 16
+    // Two or more rows with K within one pass of a workgroup (8 waves x 16
     // lane groups x 4 blocks): the 4x4x4 MFMA kernel, whose dot products do
-    // not grow the VALU work with m (measured against the lane split below:
-    // gate_up m = 8 70.4 -> 26.5 us, m = 4 26.5 -> 21.4; down m = 8 26.1 ->
-    // 20.0, m = 4 17.3 -> 15.0; the 6144-column shape m = 8 20.0 -> 12.6).
-    // Its lane split (waves, blocks per lane) depends on K only; one
-    // resident generation of workgroups.
-    if (m >= 4 && nb >= 1 && nb <= 512) {
-        const int64_t bpl3 = nb <= 256 ? 2 : 4;
+    // not grow the VALU work with m (against the lane split below, bf16:
+    // lm_head m = 2 82.9 -> 69.7 us, m = 8 104 -> 90.6; gate_up m = 8 70.4 ->
+    // 26.9, m = 3 25.4 -> 20.0; down m = 8 26.1 -> 18.5, m = 3 15.6 -> 12.9;
+    // the 6144-column shape gains at m = 8 and loses up to 1 us at m <= 3).
+    // Lane split, a function of K only: the fewest blocks per lane group that
+    // cover K with at most four waves (else eight).  Four columns per tile.
+    // One resident generation of workgroups, but at least two tiles each
+    // (the tile loop runs in pairs).
+    if (m >= 2 && nb >= 1 && nb <= 512) {
+        int64_t bpl3 = 1;
+        while (bpl3 < 4 && ceil_div(nb, 16 * bpl3) > 4) bpl3 *= 2;
         const int64_t w3 = ceil_div(nb, 16 * bpl3);
-        const int64_t cols3 = (m <= 4 && bpl3 <= 2) ? 8 : 4;
-        const int64_t tiles3 = ceil_div(N, cols3);
+        const int64_t tiles3 = ceil_div(N, 4);
         const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
         int64_t wgs3 = per_cu3 * num_cus;
-        if (wgs3 > tiles3) wgs3 = tiles3;
+        if (wgs3 > ceil_div(tiles3, 2)) wgs3 = ceil_div(tiles3, 2);
         plan->engine = 3;
         plan->waves_per_wg = (int32_t)w3;
         plan->blocks_per_lane = (int32_t)bpl3;
-        plan->cols_per_tile = (int32_t)cols3;
+        plan->cols_per_tile = 4;
         plan->workgroups = (int32_t)(wgs3 < 1 ? 1 : wgs3);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -709,7 +709,7 @@ int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 {
     if (plan.engine == 1) return mfma_workgroups_per_cu(m, plan);
     if (plan.engine == 2) return gemm_workgroups_per_cu(plan);
-    if (plan.engine == 3) return mfma4_workgroups_per_cu(m, plan);
+    if (plan.engine == 3) return mfma4_workgroups_per_cu(m, N, plan);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
     int32_t tcap = 0;

@@ -31,7 +31,8 @@
 // unpacks them to the exact fp16 integers q - z, and per row quad eight
 // chained MFMAs give the block's exact 4 x 4 product, which one FMA per row
 // scales into the lane's fp32 accumulators.  Partial sums meet through a
-// fixed xor-shuffle tree inside the wave and a wave-ordered sum in LDS, so
+// fixed tree inside the wave (two DPP row rotations, then the rows swapped by
+// v_permlane32_swap and v_permlane16_swap) and a wave-ordered sum in LDS, so
 // the summation order depends only on (K, W, BPL).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -56,19 +57,48 @@ struct Mfma4Params {
     int32_t m, K, nb, zb;
     uint32_t zero;           // always 0 (see vgpr_constant)
     int32_t a_bf16, out_bf16;
+    int32_t eo_pairs;        // weights in the even/odd nibble layout: the unpack
+                             // yields (k, k+1) pairs, activations keep their order
 };
+
+// v plus the value of lane (i - 4n) mod 16 of its 16-lane row (n = 1, 2):
+// lanes that share i mod 4 (one column) stay together.
+template <int CTRL>
+__device__ __forceinline__ float row_ror_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lane groups of a wave of the value held by lane (g, i):
+// two rotations inside each 16-lane row, then the rows exchanged with
+// v_permlane32_swap and v_permlane16_swap.  Lane (0, i) ends with the total
+// of column lane i, in an order that depends only on g.
+__device__ __forceinline__ float column_sum(float v)
+{
+    v = row_ror_add<0x124>(v);   // row_ror:4
+    v = row_ror_add<0x128>(v);   // row_ror:8
+    const uint32_t u = __float_as_uint(v);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);   // (rows 0-1, rows 2-3) per lane
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const uint32_t w = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);   // (even row, odd row) per lane
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ half4_t as_half4(uint32_t lo, uint32_t hi)
 {
     return __builtin_bit_cast(half4_t, (uint32_t __attribute__((ext_vector_type(2)))){lo, hi});
 }
 
-// RQ row quads (m <= 4 * RQ), BPL blocks per group, NC column quads per tile.
+// RQ row quads (m <= 4 * RQ), BPL blocks per group, NC column quads per
+// tile.  The tile loop is straight-line code, two tiles per pass: each wave
+// leaves its totals of the pass's two tiles in LDS, and one barrier, the
+// sums over waves and another barrier close the pass.
 template <int RQ, int BPL, int NC>
 __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 {
     constexpr int NV = 16 * NC * RQ;        // results of one tile (columns x rows)
-    __shared__ float part[2][8][NV];        // per-wave tile totals, two tiles deep
+    __shared__ float part[2][8][NV];        // per-wave totals of a pass's two tiles
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,11 +136,27 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 
     struct Tile {
         u32x4 w[NC][BPL];
-        uint32_t sc[NC][BPL];
+        uint32_t sc[NC][BPL];   // fp16 scale in the low half (the load zero-extends)
         uint32_t zq[NC][BPL];
     };
+    // Per-lane offsets of this lane's blocks within a tile's column rows,
+    // fixed for the kernel (the tile moves the buffer base): out of range
+    // past K, so every load below is issued unconditionally.
+    uint32_t ow[NC][BPL], os[NC][BPL], oz[NC][BPL];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const uint32_t col = (uint32_t)(4 * n + qi);
+#pragma unroll
+        for (int j = 0; j < BPL; ++j) {
+            const uint32_t b = (uint32_t)j * GT + gg;
+            const bool ok = b < nb;
+            ow[n][j] = ok ? col * row_bytes + 16 * b : kOutOfRange;
+            os[n][j] = ok ? (col * nb + b) * 2 : kOutOfRange;
+            oz[n][j] = ok ? col * zb + (b >> 1) : kOutOfRange;
+        }
+    }
     // Loads of column quads qs .. qs + NC - 1 (zeros past this workgroup's
-    // columns and past K: every load is issued, none touches memory there).
+    // columns: the resources end there; none touches memory past them).
     auto issue = [&](Tile& t, int64_t qs) {
         const int64_t c0 = 4 * qs;
         const bool live = qs < q_stop;
@@ -122,28 +168,22 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         const __amdgpu_buffer_rsrc_t rZ =
             make_rsrc(p.zp ? p.zp + cb * zb : p.B, p.zp ? (uint64_t)ncols * zb : 0);
 #pragma unroll
-        for (int n = 0; n < NC; ++n) {
-            const uint32_t col = (uint32_t)(4 * n + qi);
+        for (int n = 0; n < NC; ++n)
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const uint32_t b = (uint32_t)j * GT + gg;
-                const bool ok = b < nb;
-                t.w[n][j] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rB, ok ? col * row_bytes + 16 * b : kOutOfRange, 0, kNontemporal);
-                t.sc[n][j] = __builtin_amdgcn_raw_buffer_load_b16(
-                    rS, ok ? (col * nb + b) * 2 : kOutOfRange, 0, kNontemporal);
-                t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(
-                    rZ, ok ? col * zb + (b >> 1) : kOutOfRange, 0, kNontemporal);
+                t.w[n][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow[n][j], 0, kNontemporal);
+                t.sc[n][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os[n][j], 0, kNontemporal);
+                t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(rZ, oz[n][j], 0, kNontemporal);
             }
-        }
     };
 
-    Tile ta, tb;
-    issue(ta, q_first);
-    issue(tb, q_first + NC);
+    Tile ring[2];
+    issue(ring[0], q_first);
+    issue(ring[1], q_first + NC);
 
-    // fp16 (bf16 rounded to nearest even), pairs (a_e, a_e+4) per 8 k: the
-    // order in which the unpack yields the weights.
+    // fp16 (bf16 rounded to nearest even), in the order in which the unpack
+    // yields the weights: pairs (a_e, a_e+4) per 8 k, or (a_2e, a_2e+1) for
+    // even/odd weights.
     uint32_t act[RQ][BPL][16];
 #pragma unroll
     for (int rq = 0; rq < RQ; ++rq)
@@ -158,10 +198,17 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
                     z = bf16x2_to_f16x2(z);
                     w = bf16x2_to_f16x2(w);
                 }
-                act[rq][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
-                act[rq][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
-                act[rq][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
-                act[rq][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
+                if (p.eo_pairs) {
+                    act[rq][j][4 * i + 0] = x;
+                    act[rq][j][4 * i + 1] = y;
+                    act[rq][j][4 * i + 2] = z;
+                    act[rq][j][4 * i + 3] = w;
+                } else {
+                    act[rq][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
+                    act[rq][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
+                    act[rq][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
+                    act[rq][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
+                }
             }
 
     // Per block: the exact products of each row quad in one 4x4 result
@@ -175,7 +222,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
                 uint32_t pr[4][4];
 #pragma unroll
                 for (int d = 0; d < 4; ++d) unpack_dword(t.w[n][j][d], zp, magic, pr[d]);
-                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)(t.sc[n][j] & 0xFFFFu));
+                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)t.sc[n][j]);
 #pragma unroll
                 for (int rq = 0; rq < RQ; ++rq) {
                     float4_t dsum = {0.f, 0.f, 0.f, 0.f};
@@ -194,64 +241,59 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
             }
     };
 
-    // Sum over the 64 groups' partials (same column lane i in every group),
-    // then over the waves in wave order; one barrier per tile, two LDS slots.
-    int buf = 0;
-    auto finish = [&](float4_t (&acc)[NC][RQ], int64_t qs) {
+    // Totals of the tile at quad qs: the column sums inside the wave into LDS
+    // slot k of the chunk; after the chunk, the sums over the waves in wave
+    // order.
+    const int W_ = W;
+    auto store = [&](int64_t qs, int idx, float v) {
+        const int64_t col = 4 * qs + idx / (4 * RQ);
+        const int row = idx % (4 * RQ);
+        if (row < p.m && col < c_stop) {
+            const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
+            uint16_t bits = __builtin_bit_cast(uint16_t, h);
+            if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
+            p.out[(int64_t)row * p.N + col] = bits;
+        }
+    };
+    auto finish = [&](float4_t (&acc)[NC][RQ], int k) {
 #pragma unroll
         for (int n = 0; n < NC; ++n)
 #pragma unroll
             for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    float v = acc[n][rq][r];
-                    v += __shfl_xor(v, 4);
-                    v += __shfl_xor(v, 8);
-                    v += __shfl_xor(v, 16);
-                    v += __shfl_xor(v, 32);
-                    acc[n][rq][r] = v;
+                    const float v = column_sum(acc[n][rq][r]);
+                    if (g == 0) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + r] = v;
                 }
-        if (g == 0) {
+    };
+
+    // Two tiles per pass; an odd last tile is followed by one past the
+    // workgroup's columns (zeros, never stored).  The tile's scaled sums are
+    // pinned (an empty asm operand) and the scheduler fenced before its
+    // reloads, so the last uses of the tile's registers precede the loads
+    // that refill them: no copies, and no waits on those loads, at the loop
+    // edge.  The pass ends with the sums over waves of its two tiles.
+    for (int64_t qs = q_first; qs < q_stop; qs += 2 * NC) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            float4_t acc[NC][RQ] = {};
+            compute(ring[u], acc);
 #pragma unroll
             for (int n = 0; n < NC; ++n)
 #pragma unroll
-                for (int rq = 0; rq < RQ; ++rq)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        part[buf][wv][((4 * n + qi) * RQ + rq) * 4 + r] = acc[n][rq][r];
+                for (int rq = 0; rq < RQ; ++rq) asm volatile("" : "+v"(acc[n][rq]));
+            __builtin_amdgcn_sched_barrier(0);
+            issue(ring[u], qs + (2 + u) * NC);
+            finish(acc, u);
         }
         __syncthreads();
-        if (tid < NV) {
-            float v = part[buf][0][tid];
-            for (int w = 1; w < W; ++w) v += part[buf][w][tid];
-            const int64_t col = 4 * qs + tid / (4 * RQ);
-            const int row = tid % (4 * RQ);
-            if (row < p.m && col < c_stop) {
-                const _Float16 h = (_Float16)v;               // fp32 -> fp16, RNE
-                uint16_t bits = __builtin_bit_cast(uint16_t, h);
-                if (p.out_bf16) bits = f16_to_bf16(bits);     // fp16 -> bf16, RNE
-                p.out[(int64_t)row * p.N + col] = bits;
-            }
+        for (int e = tid; e < 2 * NV; e += (int)blockDim.x) {   // 2 NV can exceed one wave
+            const int t = e / NV, idx = e - t * NV;
+            float v = part[t][0][idx];
+            for (int w = 1; w < W_; ++w) v += part[t][w][idx];
+            store(qs + (int64_t)t * NC, idx, v);
         }
-        buf ^= 1;
-    };
-
-    for (int64_t qs = q_first; qs < q_stop;) {
-        {
-            float4_t acc[NC][RQ] = {};
-            compute(ta, acc);
-            issue(ta, qs + 2 * NC);
-            finish(acc, qs);
-            qs += NC;
-        }
-        if (qs >= q_stop) break;
-        {
-            float4_t acc[NC][RQ] = {};
-            compute(tb, acc);
-            issue(tb, qs + 2 * NC);
-            finish(acc, qs);
-            qs += NC;
-        }
+        __syncthreads();   // the slots are refilled by the next pass
     }
 }
 
@@ -306,6 +348,7 @@ int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.zero = 0;
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
+    p.eo_pairs = plan.b_layout == MNB_LAYOUT_EVEN_ODD;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)plan.workgroups),
                                    dim3((unsigned)plan.threads_per_wg), args, 0,
@@ -314,10 +357,11 @@ int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
     return (int)e;
 }
 
-int mfma4_workgroups_per_cu(int64_t m, const mnb_plan& plan)
+int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan)
 {
     Mfma4Fn fn = lookup_mfma4(m, plan);
     if (!fn) return 0;
+    (void)N;
     return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, 0);
 }
 
@@ -332,7 +376,7 @@ int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
     info->sgprs = 0;
     info->lds_bytes = (int32_t)attr.sharedSizeBytes;
     info->max_threads = attr.maxThreadsPerBlock;
-    info->wgs_per_cu = mfma4_workgroups_per_cu(m, plan);
+    info->wgs_per_cu = mfma4_workgroups_per_cu(m, 1, plan);
     return 0;
 }
 

@@ -32,7 +32,7 @@ int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 // workgroup whose 16 W lane groups cover K in one pass (16 W * blocks_per_lane
 // >= K/32), cols_per_tile = 4 or 8.  No dynamic LDS.
 int launch_mfma4(const GemvArgs& args, const mnb_plan& plan, void* stream);
-int mfma4_workgroups_per_cu(int64_t m, const mnb_plan& plan);
+int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan);
 int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 
 // The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of 4 or 8

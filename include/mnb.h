@@ -66,7 +66,7 @@ typedef enum {
  *                      endian), nibble p holds k_{2(p mod 4) + p/4}, i.e.
  *                      k0 k2 k4 k6 in the low half-word and k1 k3 k5 k7 in
  *                      the high one, so the dequant yields (k, k+1) pairs and
- *                      the activations need no reorder.  Only engine 0 reads it.
+ *                      the activations need no reorder.  Engines 0 and 3 read it.
  */
 #define MNB_LAYOUT_NATURAL 0
 #define MNB_LAYOUT_EVEN_ODD 1
@@ -139,15 +139,25 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * walked 128 at a time, activations through LDS; weights dequantized to
  * fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of K.  Also
  * accepted for any m >= 1 as an explicit plan.
+ * engine 3 (4x4x4 MFMA kernel, m <= 8): a workgroup of waves_per_wg waves
+ * walks its columns cols_per_tile (4 or 8) at a time; lane i of each group
+ * of four lanes holds column i of a quad and rows i and 4 + i of the
+ * activations (in VGPRs); the 16 * waves_per_wg lane groups own
+ * blocks_per_lane blocks each and together cover K in one pass; per block
+ * the exact products come from v_mfma_f32_4x4x4_16b_f16 and the block scale
+ * is applied in fp32, as in engine 0.  Needs 16 * waves_per_wg *
+ * blocks_per_lane >= K/32 (so K <= 16384).
  */
 typedef struct {
     int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel;
-                                2: prefill kernel                               */
+                                2: prefill kernel; 3: 4x4x4 MFMA kernel         */
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
-    int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8                          */
+    int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8; engine 3: 1, 2 or 4     */
     int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
-                                engine 2: 128 or 256                            */
-    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4, 8 */
+                                engine 2: 128 or 256; engine 3: 4 or 8 (4 with
+                                blocks_per_lane 4 when m > 4)                   */
+    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4, 8;
+                                engine 3: 1..8                                  */
     int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
     int32_t workgroups;      /* grid size, >= 1                                  */
     int32_t interleave;      /* engine 0: 0 = each lane group takes one contiguous
@@ -163,13 +173,14 @@ typedef struct {
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`
  * compute units where the selected kernel variant keeps `wgs_per_cu`
  * workgroups resident per CU (0: a nominal estimate).  The lane split
- * (lanes_per_col, blocks_per_lane, k_chunks) depends on (m, K) only.
+ * (engine 0: lanes_per_col, blocks_per_lane, k_chunks; engine 3:
+ * waves_per_wg, blocks_per_lane) depends on (m, K) only.
  * Host-only; touches no device.  Returns a status code. */
 int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_cu,
                      mnb_plan* plan);
 
 /* Validate a plan for (m, K, N) and fill its derived fields
- * (threads_per_wg, k_chunks).  The decode engines (0, 1) take m <= 8.
+ * (threads_per_wg, k_chunks).  The decode engines (0, 1, 3) take m <= 8.
  * Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan);
 

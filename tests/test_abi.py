@@ -83,15 +83,18 @@ def test_default_plans_are_valid_and_cover_k():
                 # The 4x4x4 MFMA kernel: four or more rows, K in one pass of
                 # the workgroup's 16 * waves lane groups; its lane split
                 # depends on K only.
-                assert 4 <= m <= 8 and 1 <= nb <= 512
+                assert 2 <= m <= 8 and 1 <= nb <= 512
                 w, bpl = p.waves_per_wg, p.blocks_per_lane
                 assert 1 <= w <= 8 and bpl in (1, 2, 4) and 16 * w * bpl >= nb > 16 * (w - 1) * bpl
+                assert bpl == 1 or 16 * 4 * (bpl // 2) < nb      # fewest blocks for <= 4 waves
+                assert p.cols_per_tile == 4
                 assert split3.setdefault(K, (w, bpl)) == (w, bpl)
                 assert q.k_chunks == 1 and q.threads_per_wg == 64 * w
                 assert p.cols_per_tile in (4, 8) and not (m > 4 and bpl * p.cols_per_tile // 4 > 4)
-                assert 1 <= p.workgroups <= -(-N // p.cols_per_tile)
+                tiles = -(-(-(-N // 4)) // (p.cols_per_tile // 4))
+                assert 1 <= p.workgroups <= max(1, -(-tiles // 2))   # two tiles per workgroup
                 continue
-            assert p.engine == 0 and not (m >= 4 and 1 <= nb <= 512)
+            assert p.engine == 0 and not (m >= 2 and 1 <= nb <= 512)
             lpc, bpl, nc = p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile
             assert lpc * bpl * p.k_chunks >= K // 32
             assert m * bpl <= 8 and nc * bpl <= 8 and nc * m <= 32
@@ -214,13 +217,12 @@ def test_default_plan_shapes():
     assert p.workgroups == 15 * 256             # ~5 tiles per group, whole rounds of CUs
     p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
-    p = mnb.mnb_plan_default(2, 14336, 4096, 256, 4)
-    assert (p.engine, p.lanes_per_col, p.blocks_per_lane, p.k_chunks) == (0, 448, 1, 1)
-    assert (p.cols_per_tile, p.workgroups) == (1, 512)
-    # Four or more rows: the 4x4x4 MFMA kernel, seven waves of four blocks per
-    # lane group for the 14336-long K, four waves of two for 4096.
-    for m, K, N, occ, shape in ((4, 14336, 4096, 1, (7, 4, 4, 256)), (8, 14336, 4096, 1, (7, 4, 4, 256)),
-                                (4, 4096, 28672, 3, (4, 2, 8, 768)), (8, 4096, 28672, 2, (4, 2, 4, 512))):
+    # Two or more rows: the 4x4x4 MFMA kernel, seven waves of four blocks per
+    # lane group for the 14336-long K, four waves of two for 4096; four
+    # columns per tile, at least two tiles per workgroup.
+    for m, K, N, occ, shape in ((2, 14336, 4096, 1, (7, 4, 4, 256)), (8, 14336, 4096, 1, (7, 4, 4, 256)),
+                                (4, 4096, 28672, 4, (4, 2, 4, 1024)), (8, 4096, 151936, 4, (4, 2, 4, 1024)),
+                                (8, 4096, 6144, 4, (4, 2, 4, 768))):
         p = mnb.mnb_plan_default(m, K, N, 256, occ)
         assert p.engine == 3
         assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape
@@ -254,12 +256,13 @@ def test_repack_validation_without_gpu(args, status):
 
 
 def test_plan_layouts():
-    """The even/odd layout is read by engine 0 only."""
+    """The even/odd layout is read by engines 0 and 3 only."""
     for eng, fields in ((0, dict(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=2)),
                         (1, dict(cols_per_tile=16, waves_per_wg=4, chunk_blocks=128)),
-                        (2, dict(row_tiles=1, cols_per_tile=128, waves_per_wg=4))):
+                        (2, dict(row_tiles=1, cols_per_tile=128, waves_per_wg=4)),
+                        (3, dict(waves_per_wg=4, blocks_per_lane=2, cols_per_tile=4))):
         for layout in (0, 1, 2):
             q = mnb.mnb_plan(engine=eng, workgroups=1, b_layout=layout, **fields)
-            want = 0 if layout == 0 or (layout == 1 and eng == 0) else 9
+            want = 0 if layout == 0 or (layout == 1 and eng in (0, 3)) else 9
             assert mnb.mnb_plan_check(4, 4096, 100, q) == want, (eng, layout)
     assert mnb.mnb_plan_default(1, 4096, 100, 256, 0).b_layout == mnb.MNB_LAYOUT_NATURAL

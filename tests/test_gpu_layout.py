@@ -96,6 +96,20 @@ def test_even_odd_layout_every_mode(oracle_mod, lpc, bpl, nc):
                                               m, K, N))
 
 
+def test_even_odd_layout_mfma4_engine(oracle_mod):
+    """The 4x4x4 MFMA kernel on even/odd weights: ragged K and N, one and
+    two row quads, one and two column quads per tile."""
+    for i, (m, K, N, w, bpl, cols) in enumerate(((2, 32 * 61, 77, 4, 1, 4), (7, 32 * 61, 45, 2, 2, 4),
+                                                  (4, 4096, 130, 4, 2, 8), (8, 14336, 33, 7, 4, 4))):
+        d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i != 2, 0.002, 0.02, 1.0, 780 + i)
+        de = dict(d, B=even_odd(d["B"]))
+        plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols, workgroups=3,
+                    b_layout=mnb.MNB_LAYOUT_EVEN_ODD)
+        assert_parity(oracle_mod, de, m, "even/odd mfma4", plan,
+                      ref=oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"], d["scales"],
+                                                  d["zp"], m, K, N))
+
+
 CASES = load_cases()
 
 
