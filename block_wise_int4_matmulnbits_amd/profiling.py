@@ -49,14 +49,15 @@ def _rows(path):
         return list(csv.DictReader(f))
 
 
-def trace_summary(trace_dir, out_md, cmd, timed=0):
+def trace_summary(trace_dir, out_md, cmd, timed=0, tag=GEMV_TAG):
     """timed: the number of dispatches of the bench's timed region (the last
-    ones traced; the warm-up dispatches come first)."""
+    ones traced; the warm-up dispatches come first).  tag: a substring of the
+    kernel's name."""
     stats = _one(os.path.join(trace_dir, "**", "*kernel_stats.csv"))
     trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     with open(stats) as f:
         stats_text = f.read().strip()
-    rows = [r for r in _rows(trace) if GEMV_TAG in r["Kernel_Name"]]
+    rows = [r for r in _rows(trace) if tag in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     r = rows[-1]
@@ -189,7 +190,8 @@ def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs
 
 def main(argv):
     if argv[0] == "trace":
-        print(trace_summary(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else 0))
+        print(trace_summary(argv[1], argv[2], argv[3], int(argv[4]) if len(argv) > 4 else 0,
+                            argv[5] if len(argv) > 5 else GEMV_TAG))
     elif argv[0] == "counters":
         tag, tdir, out_md, flops, cmd_t, cmd_p = argv[1:7]
         print(counters_summary(tag, tdir, out_md, float(flops), cmd_t, cmd_p, argv[7:]))
