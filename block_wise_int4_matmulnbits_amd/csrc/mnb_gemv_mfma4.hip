@@ -215,30 +215,42 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     // (eight chained MFMAs over the block's 32 k), then acc += D * s.
     auto compute = [&](const Tile& t, float4_t (&acc)[NC][RQ]) {
 #pragma unroll
-        for (int n = 0; n < NC; ++n)
+        for (int n = 0; n < NC; ++n) {
+            ZeroPoint zp[BPL];
+#pragma unroll
+            for (int j = 0; j < BPL; ++j) zp[j] = zero_point_pairs(((t.zq[n][j] >> zshift) & 0xFu) | zdef);
+            float4_t dsum[BPL][RQ];
+#pragma unroll
+            for (int j = 0; j < BPL; ++j)
+#pragma unroll
+                for (int rq = 0; rq < RQ; ++rq) dsum[j][rq] = float4_t{0.f, 0.f, 0.f, 0.f};
+            // Dword d of every block, then one MFMA per (block, row quad):
+            // consecutive MFMAs are independent, each block's chain keeps its
+            // order over k.
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                uint32_t pr[BPL][4];
+#pragma unroll
+                for (int j = 0; j < BPL; ++j) unpack_dword(t.w[n][j][d], zp[j], magic, pr[j]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int j = 0; j < BPL; ++j)
+#pragma unroll
+                        for (int rq = 0; rq < RQ; ++rq)
+                            dsum[j][rq] = __builtin_amdgcn_mfma_f32_4x4x4f16(
+                                as_half4(act[rq][j][4 * d + 2 * h], act[rq][j][4 * d + 2 * h + 1]),
+                                as_half4(pr[j][2 * h], pr[j][2 * h + 1]), dsum[j][rq], 0, 0, 0);
+            }
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const ZeroPoint zp = zero_point_pairs(((t.zq[n][j] >> zshift) & 0xFu) | zdef);
-                uint32_t pr[4][4];
-#pragma unroll
-                for (int d = 0; d < 4; ++d) unpack_dword(t.w[n][j][d], zp, magic, pr[d]);
                 const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)t.sc[n][j]);
 #pragma unroll
-                for (int rq = 0; rq < RQ; ++rq) {
-                    float4_t dsum = {0.f, 0.f, 0.f, 0.f};
+                for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) {
-                        dsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
-                            as_half4(act[rq][j][4 * d + 0], act[rq][j][4 * d + 1]),
-                            as_half4(pr[d][0], pr[d][1]), dsum, 0, 0, 0);
-                        dsum = __builtin_amdgcn_mfma_f32_4x4x4f16(
-                            as_half4(act[rq][j][4 * d + 2], act[rq][j][4 * d + 3]),
-                            as_half4(pr[d][2], pr[d][3]), dsum, 0, 0, 0);
-                    }
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[n][rq][r] = fmaf(dsum[r], sf, acc[n][rq][r]);
-                }
+                    for (int r = 0; r < 4; ++r) acc[n][rq][r] = fmaf(dsum[j][rq][r], sf, acc[n][rq][r]);
             }
+        }
     };
 
     // Totals of the tile at quad qs: the column sums inside the wave into LDS
