@@ -157,16 +157,18 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     }
     // Loads of column quads qs .. qs + NC - 1 (zeros past this workgroup's
     // columns: the resources end there; none touches memory past them).
-    auto issue = [&](Tile& t, int64_t qs) {
-        const int64_t c0 = 4 * qs;
-        const bool live = qs < q_stop;
-        const int64_t left = c_stop - c0;
-        const uint32_t ncols = live ? (uint32_t)(left < 4 * NC ? left : 4 * NC) : 0u;
-        const int64_t cb = live ? c0 : 0;
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + cb * row_bytes, (uint64_t)ncols * row_bytes);
-        const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + cb * nb, (uint64_t)ncols * nb * 2);
-        const __amdgpu_buffer_rsrc_t rZ =
-            make_rsrc(p.zp ? p.zp + cb * zb : p.B, p.zp ? (uint64_t)ncols * zb : 0);
+    // Tiles are issued in column order, NC quads apart, so the bases of the
+    // three buffer resources advance by fixed strides and the columns left
+    // count down; a tile at or past q_stop gets empty resources.
+    const uint8_t* nb_B = p.B + 4 * q_first * (int64_t)row_bytes;
+    const uint16_t* nb_S = p.scales + 4 * q_first * (int64_t)nb;
+    const uint8_t* nb_Z = p.zp ? p.zp + 4 * q_first * (int64_t)zb : p.B;
+    int64_t left = c_stop - 4 * q_first;
+    auto issue = [&](Tile& t) {
+        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 4 * NC ? left : 4 * NC);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(nb_B, (uint64_t)ncols * row_bytes);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(nb_S, (uint64_t)ncols * nb * 2);
+        const __amdgpu_buffer_rsrc_t rZ = make_rsrc(nb_Z, p.zp ? (uint64_t)ncols * zb : 0);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
 #pragma unroll
@@ -175,11 +177,17 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
                 t.sc[n][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os[n][j], 0, kNontemporal);
                 t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(rZ, oz[n][j], 0, kNontemporal);
             }
+        if (left > 0) {   // uniform; past the end the bases stay put
+            nb_B += 4 * NC * (int64_t)row_bytes;
+            nb_S += 4 * NC * (int64_t)nb;
+            if (p.zp) nb_Z += 4 * NC * (int64_t)zb;
+        }
+        left -= 4 * NC;
     };
 
     Tile ring[2];
-    issue(ring[0], q_first);
-    issue(ring[1], q_first + NC);
+    issue(ring[0]);
+    issue(ring[1]);
 
     // fp16 (bf16 rounded to nearest even), in the order in which the unpack
     // yields the weights: pairs (a_e, a_e+4) per 8 k, or (a_2e, a_2e+1) for
@@ -273,10 +281,15 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 #pragma unroll
             for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float v = column_sum(acc[n][rq][r]);
-                    if (g == 0) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + r] = v;
-                }
+                for (int r = 0; r < 4; ++r) acc[n][rq][r] = column_sum(acc[n][rq][r]);
+        if (g == 0) {
+#pragma unroll
+            for (int n = 0; n < NC; ++n)
+#pragma unroll
+                for (int rq = 0; rq < RQ; ++rq)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + r] = acc[n][rq][r];
+        }
     };
 
     // Two tiles per pass; an odd last tile is followed by one past the
@@ -295,7 +308,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 #pragma unroll
                 for (int rq = 0; rq < RQ; ++rq) asm volatile("" : "+v"(acc[n][rq]));
             __builtin_amdgcn_sched_barrier(0);
-            issue(ring[u], qs + (2 + u) * NC);
+            issue(ring[u]);   // the tile two ahead: qs + (2 + u) NC
             finish(acc, u);
         }
         __syncthreads();
