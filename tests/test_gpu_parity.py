@@ -390,3 +390,31 @@ def test_mfma4_engine_k_zero():
     d["zp"] = np.zeros((23, 0), np.uint8)
     y, cnt = run(d, 6, W.F16, dict(engine=3, waves_per_wg=1, blocks_per_lane=1, cols_per_tile=4, workgroups=2))
     assert np.all(y == 0) and cnt["elements_f16"] == 6 * 23
+
+
+@pytest.mark.parametrize("m", [2, 5, 8])
+def test_mfma4_engine_lm_head_full_size_sampled(oracle_mod, m):
+    """The lm_head shape (K = 4096, N = 151936) with several rows under the
+    default plan (the 4x4x4 MFMA kernel, hundreds of two-tile passes per
+    workgroup): check 1 on a sample of whole columns (the first and last
+    tiles, both ends of a workgroup's range, random ones), check 2 on every
+    output."""
+    K, N = 4096, 151936
+    d = W.generate(m, K, N, W.F16, True, 0.001, 0.01, 0.5, 460 + m)
+    plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.engine == 3
+    G.log("[parity] mfma4 lm_head m=%d default plan %s" % (m, plan.as_dict()))
+    y16, c16 = run(d, m, W.F16)
+    ybf, _ = run(d, m, W.BF16)
+    assert c16["launches"] == 1
+    assert not np.any(y16 == 0xFFFF) and not np.any(ybf == 0xFFFF)
+    assert G.check2(ybf, y16, oracle_mod).all()
+    nq, g = (N + 3) // 4, plan.workgroups
+    edges = [4 * (nq * b // g) for b in (1, g // 2, g - 1)]
+    rng = np.random.default_rng(461)
+    cols = np.unique(np.concatenate([[0, 1, 2, 3, 4, N - 1], edges, [e - 1 for e in edges],
+                                     rng.choice(N, 24, replace=False)]))
+    ref = oracle_mod.matmul_nbits(d["A"][:m], False, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
+    ok, max_ulps = G.check1(y16[:, cols], ref, oracle_mod)
+    assert ok.all(), "check 1 failed at %d of %d outputs" % ((~ok).sum(), ok.size)
+    G.log("[parity] mfma4 lm_head m=%d ok: max err %.3f fp16 ulp" % (m, max_ulps))
