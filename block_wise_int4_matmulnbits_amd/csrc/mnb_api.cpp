@@ -2,6 +2,7 @@
 // and status strings.  Plain C++ (no HIP headers): everything here runs, and
 // is tested, without a GPU.  The kernels and their launch live in
 // mnb_gemv.hip.
+#include <algorithm>
 #include <atomic>
 #include <stdint.h>
 
@@ -95,24 +96,36 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         // again with that variant's measured occupancy for the grid.
         st = mnb_plan_default(m, K, N, cus, 0, &plan);
         if (st != MNB_OK) return st;
-        const int per_cu = mnb::workgroups_per_cu(m, K, N, plan);
+        const int per_cu = mnb::workgroups_per_cu(plan.engine == 2 ? m : std::min<int64_t>(m, MNB_MAX_M), K, N, plan);
         if (per_cu > 0) {
             st = mnb_plan_default(m, K, N, cus, per_cu, &plan);
             if (st != MNB_OK) return st;
         }
     }
-    mnb::GemvArgs args{A, Bpacked, scales, zero_points, out, m, K, N,
-                       a_dtype == MNB_BF16, out_dtype == MNB_BF16};
-    int e = mnb::launch_gemv(args, plan, stream);
-    if (e != 0) {
-        t_last_hip_error = e;
-        return MNB_ERR_HIP;
+    // One launch, or for a decode plan with more than MNB_MAX_M rows one
+    // launch per MNB_MAX_M rows (rows are independent in those kernels).
+    const int64_t step = plan.engine == 2 ? m : MNB_MAX_M;
+    const size_t a_row = (size_t)K * 2, out_row = (size_t)N * 2;
+    int64_t launched = 0, batched = 0;
+    for (int64_t r0 = 0; r0 < m; r0 += step) {
+        const int64_t mc = std::min<int64_t>(step, m - r0);
+        mnb::GemvArgs args{static_cast<const uint8_t*>(A) + r0 * a_row, Bpacked, scales, zero_points,
+                           static_cast<uint8_t*>(out) + r0 * out_row, mc, K, N,
+                           a_dtype == MNB_BF16, out_dtype == MNB_BF16};
+        int e = mnb::launch_gemv(args, plan, stream);
+        if (e != 0) {
+            t_last_hip_error = e;
+            g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
+            return MNB_ERR_HIP;
+        }
+        ++launched;
+        if (mc > 1) ++batched;
     }
     g_calls.fetch_add(1, std::memory_order_relaxed);
-    g_launches.fetch_add(1, std::memory_order_relaxed);
+    g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
     if (out_dtype == MNB_BF16) g_bf16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
     else g_f16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
-    if (m > 1) g_rows.fetch_add(1, std::memory_order_relaxed);
+    g_rows.fetch_add((uint64_t)batched, std::memory_order_relaxed);
     return MNB_OK;
 }
 
@@ -168,7 +181,10 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
         plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
         return MNB_OK;
     }
-    if (m > MNB_MAX_M) return MNB_ERR_PLAN;         // decode engines: m <= 8
+    // Decode engines: a launch serves at most MNB_MAX_M rows; more rows run
+    // as launches of MNB_MAX_M rows (the last one fewer) under this plan, so
+    // the plan must fit MNB_MAX_M rows.
+    if (m > MNB_MAX_M) m = MNB_MAX_M;
     if (plan->engine == 1) {
         const int64_t w = plan->waves_per_wg, kcb = plan->chunk_blocks;
         if (w < 1 || w > 8 || kcb < 4 || kcb % 4 || m * kcb * 64 > kMfmaStageBytes)
@@ -241,6 +257,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
             rt = 8;
             cols = 256;
         }
+        // A few rows on few columns (the down projection's 4096 at m = 9:
+        // 32 tiles for 256 CUs, 139 us against 19 us for 8 rows): the decode
+        // kernels in launches of 8 rows, while at most six such launches and
+        // the tiles would leave more than half of the CUs idle.
+        if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 6 * MNB_MAX_M)
+            return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
         int64_t wgs = per_cu * num_cus;
         if (wgs > tiles(rt, cols)) wgs = tiles(rt, cols);
@@ -420,7 +442,7 @@ int mnb_get_kernel_info(int64_t m, int64_t K, const mnb_plan* plan, mnb_kernel_i
     mnb_plan p = *plan;
     if (p.workgroups < 1) p.workgroups = 1;
     if (mnb_plan_check(m, K, 1, &p) != MNB_OK) return MNB_ERR_PLAN;
-    int e = mnb::kernel_info(m, K, p, info);
+    int e = mnb::kernel_info(p.engine == 2 ? m : std::min<int64_t>(m, MNB_MAX_M), K, p, info);
     if (e == -1) return MNB_ERR_PLAN;
     if (e != 0) {
         t_last_hip_error = e;

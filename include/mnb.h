@@ -86,13 +86,17 @@ typedef enum {
 #define MNB_MAX_K (1 << 24)
 
 /*
- * matmul_nbits -- y = A * dequant(B)^T, one kernel launch on `stream`.
+ * matmul_nbits -- y = A * dequant(B)^T, kernel launches on `stream`: one,
+ * or for a decode plan with m > 8 one per 8 rows.
  *
  *   A            device, [m][K] row-major, fp16 or bf16 per a_dtype; 16-byte
  *                aligned.  Must hold finite values that are finite in fp16.
  *   a_dtype      MNB_F16 or MNB_BF16.
  *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
- *                prefill kernel).  m == 0 or N == 0: nothing to do, MNB_OK.
+ *                prefill kernel, except that up to 48 rows whose prefill
+ *                tiles would leave more than half of the compute units idle
+ *                run the decode kernels in launches of 8 rows).  m == 0 or
+ *                N == 0: nothing to do, MNB_OK.
  *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).
  *   N            output columns.
  *   Bpacked      device, [N][K/2] bytes; byte k/2 of row n holds weight k,
@@ -103,8 +107,8 @@ typedef enum {
  *   block        must be 32.
  *   out          device, [m][N] row-major, fp16 or bf16 per out_dtype;
  *                2-byte aligned; must not overlap any input.  Every one of
- *                the m*N elements is overwritten (no accumulation), by this
- *                one launch.
+ *                the m*N elements is overwritten (no accumulation) by this
+ *                call's launches, each of which writes all of its rows.
  *   out_dtype    MNB_F16 (fp32 -> fp16 RNE) or MNB_BF16 (fp32 -> fp16 RNE
  *                -> bf16 RNE).
  *   stream       hipStream_t, or NULL for the default stream.
@@ -180,7 +184,9 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
                      mnb_plan* plan);
 
 /* Validate a plan for (m, K, N) and fill its derived fields
- * (threads_per_wg, k_chunks).  The decode engines (0, 1, 3) take m <= 8.
+ * (threads_per_wg, k_chunks).  A decode plan (engines 0, 1, 3) must fit 8
+ * rows; with m > 8 the call runs it once per 8 rows (the last launch
+ * fewer).
  * Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan);
 

@@ -117,6 +117,18 @@ def test_default_prefill_plans():
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
+            if p.engine != 2:
+                # A few rows on few columns: the 8-row decode plan, launched
+                # per 8 rows, when the prefill tiles would leave more than half
+                # of the CUs idle.
+                assert m <= 48 and p.as_dict() == mnb.mnb_plan_default(8, K, N, cus, occ).as_dict()
+                rt = 1
+                while rt < 4 and 32 * rt < m:
+                    rt *= 2
+                while rt > 1 and 64 * rt * K > 0xFFFFFFF0:
+                    rt //= 2
+                assert 2 * -(-m // (32 * rt)) * -(-N // 128) < cus
+                continue
             assert p.engine == 2 and p.cols_per_tile in (128, 256)
             assert p.waves_per_wg == (8 if p.row_tiles >= 4 and p.cols_per_tile == 256 else 4)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
@@ -178,11 +190,18 @@ def test_plan_check_engines_and_rows():
         q = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=128, waves_per_wg=4, workgroups=1)
         assert mnb.mnb_plan_check(1000, big, 100, q) == want
     assert mnb.mnb_plan_default(1000, big, 100000, 256, 0).row_tiles == 2
+    # Decode plans take any m (launches of 8 rows) when they fit 8 rows.
     d = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=1, cols_per_tile=1, workgroups=1)
     assert mnb.mnb_plan_check(8, 4096, 100, d) == 0
-    assert mnb.mnb_plan_check(9, 4096, 100, d) == 9            # decode engines: m <= 8
+    assert mnb.mnb_plan_check(9, 4096, 100, d) == 0
+    d2 = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=4, workgroups=1)
+    assert mnb.mnb_plan_check(4, 4096, 100, d2) == 0
+    assert mnb.mnb_plan_check(9, 4096, 100, d2) == 9           # 8 rows x 2 blocks > 8
     e1 = mnb.mnb_plan(engine=1, cols_per_tile=16, waves_per_wg=4, chunk_blocks=128, workgroups=1)
-    assert mnb.mnb_plan_check(9, 4096, 100, e1) == 9
+    assert mnb.mnb_plan_check(9, 4096, 100, e1) == 0
+    e3 = mnb.mnb_plan(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=8, workgroups=1)
+    assert mnb.mnb_plan_check(4, 14336, 100, e3) == 0
+    assert mnb.mnb_plan_check(40, 14336, 100, e3) == 9         # 8 rows: registers
 
 
 def test_summation_order_does_not_depend_on_n_or_device():

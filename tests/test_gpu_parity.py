@@ -47,6 +47,22 @@ def run(d, m, out_dtype, plan=None, stream=None):
     return G.bits(out), {k: c1[k] - c0[k] for k in c0}
 
 
+def effective_plan(m, K, N, plan=None):
+    """The plan a call runs: the given one, or the device's default."""
+    if plan is not None:
+        return plan if isinstance(plan, dict) else plan.as_dict()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return mnb.plan_for_device(m, K, N, cus).as_dict()
+
+
+def launch_rows(m, K, N, plan=None):
+    """Rows per launch of a call: decode plans (engines 0, 1, 3) serve at
+    most 8 rows per launch."""
+    if effective_plan(m, K, N, plan).get("engine", 0) == 2 or m <= 8:
+        return [m]
+    return [min(8, m - r) for r in range(0, m, 8)]
+
+
 def oracle_ref(oracle_mod, d, m):
     return oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"],
                                    d["scales"], d["zp"], m, d["K"], d["N"])
@@ -66,9 +82,10 @@ def assert_parity(oracle_mod, d, m, label, plan=None, ref=None):
     ok2 = G.check2(ybf, y16, oracle_mod)
     assert ok2.all(), "check 2 failed at %d of %d outputs" % ((~ok2).sum(), ok2.size)
     n = m * d["N"]
-    assert c16["launches"] == 1 and c16["elements_f16"] == n and c16["elements_bf16_direct"] == 0
-    assert cbf["launches"] == 1 and cbf["elements_bf16_direct"] == n and cbf["elements_f16"] == 0
-    assert c16["row_batched_launches"] == (1 if m > 1 else 0)
+    chunks = launch_rows(m, d["K"], d["N"], plan)
+    assert c16["launches"] == len(chunks) and c16["elements_f16"] == n and c16["elements_bf16_direct"] == 0
+    assert cbf["launches"] == len(chunks) and cbf["elements_bf16_direct"] == n and cbf["elements_f16"] == 0
+    assert c16["row_batched_launches"] == sum(1 for r in chunks if r > 1)
     exact = np.mean(y16 == ref["f16"])
     G.log("[parity] %s ok: max err %.3f fp16 ulp, %.4f%% bit-equal to the oracle"
           % (label, max_ulps, 100 * exact))

@@ -19,11 +19,15 @@ import block_wise_int4_matmulnbits_amd as mnb
 from block_wise_int4_matmulnbits_amd import workloads as W
 from tests import gpu_util as G
 from tests.hand_cases import build_case, load_cases
-from tests.test_gpu_parity import assert_parity, run
+from tests.test_gpu_parity import assert_parity, effective_plan, run
 
 
 def assert_prefill(oracle_mod, d, m, label, plan=None):
+    """Checks 1 and 2; when the call runs the prefill kernel, also the bound
+    of its fp16-weight reading."""
     y16, _, _ = assert_parity(oracle_mod, d, m, label, plan)
+    if effective_plan(m, d["K"], d["N"], plan).get("engine") != 2:
+        return y16
     K = d["K"]
     ref = oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"], d["scales"],
                                   d["zp"], m, K, d["N"], weights_f16=True)
@@ -54,7 +58,7 @@ def _gpu():
 def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
     plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert plan.engine == 2
+    assert plan.engine == 2 or m <= 48     # few tiles: the decode kernels per 8 rows
     assert_prefill(oracle_mod, d, m, "prefill", None)
 
 
@@ -89,6 +93,34 @@ def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
         assert_prefill(oracle_mod, d, m, "prefill lds-staged wg=%d" % wg, plan)
 
 
+@pytest.mark.parametrize("m", [9, 16, 23, 48])
+def test_few_tiles_run_decode_kernels_per_8_rows(oracle_mod, m):
+    """The down projection (N = 4096) with 9..48 rows gives the prefill
+    kernel 32 tiles for 256 CUs, so the default plan runs the decode kernels
+    in launches of 8 rows: against the oracle (sampled columns for the
+    larger heights), and each block of 8 rows bit-equal to its own launch."""
+    K, N = 14336, 4096
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 860 + m)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = mnb.plan_for_device(m, K, N, cus)
+    assert plan.engine != 2 and plan.as_dict() == mnb.plan_for_device(8, K, N, cus).as_dict()
+    if m <= 16:
+        y16 = assert_prefill(oracle_mod, d, m, "decode per 8 rows", None)
+    else:
+        y16, c = run(d, m, W.F16)
+        assert c["launches"] == -(-m // 8)
+        ybf, _ = run(d, m, W.BF16)
+        assert G.check2(ybf, y16, oracle_mod).all()
+        cols = np.unique(np.concatenate([[0, 1, N - 1], np.random.default_rng(861).choice(N, 20, replace=False)]))
+        ref = oracle_mod.matmul_nbits(d["A"][:m], True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
+        ok, _ = G.check1(y16[:, cols], ref, oracle_mod)
+        assert ok.all()
+    for r0 in range(0, m, 8):
+        mc = min(8, m - r0)
+        y, _ = run(dict(d, A=d["A"][r0:r0 + mc]), mc, W.F16, plan.as_dict())
+        assert np.array_equal(y, y16[r0:r0 + mc])
+
+
 def test_prefill_engine_for_decode_heights(oracle_mod):
     """The prefill engine also serves m <= 8 when asked for explicitly."""
     d = W.generate(3, 4096, 129, W.BF16, True, 0.001, 0.01, 0.5, 730)
@@ -100,7 +132,7 @@ def test_prefill_rows_do_not_depend_on_launch_height():
     """Rows 0..16 of a 40-row launch equal a 17-row launch of the same rows,
     under different row tilings."""
     d = W.generate(40, 14336, 96, W.BF16, True, 0.001, 0.01, 0.5, 740)
-    y40, _ = run(d, 40, W.BF16)
+    y40, _ = run(d, 40, W.BF16, dict(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=1))
     p17 = dict(engine=2, row_tiles=4, cols_per_tile=256, waves_per_wg=4, workgroups=5)
     y17, _ = run(dict(d, A=d["A"][:17]), 17, W.BF16, p17)
     assert np.array_equal(y40[:17], y17)
