@@ -155,20 +155,20 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
             oz[n][j] = ok ? col * zb + (b >> 1) : kOutOfRange;
         }
     }
-    // Loads of column quads qs .. qs + NC - 1 (zeros past this workgroup's
-    // columns: the resources end there; none touches memory past them).
-    // Tiles are issued in column order, NC quads apart, so the bases of the
-    // three buffer resources advance by fixed strides and the columns left
-    // count down; a tile at or past q_stop gets empty resources.
-    const uint8_t* nb_B = p.B + 4 * q_first * (int64_t)row_bytes;
-    const uint16_t* nb_S = p.scales + 4 * q_first * (int64_t)nb;
-    const uint8_t* nb_Z = p.zp ? p.zp + 4 * q_first * (int64_t)zb : p.B;
+    // Loads of the next tile of this workgroup (NC column quads).  Tiles are
+    // issued in column order, so the bases of the three buffer resources
+    // advance by fixed strides and the columns left count down; the
+    // resources end at the workgroup's last column (zeros past it, without
+    // touching memory), and a tile past q_stop gets empty ones.
+    const uint8_t* next_B = p.B + 4 * q_first * (int64_t)row_bytes;
+    const uint16_t* next_S = p.scales + 4 * q_first * (int64_t)nb;
+    const uint8_t* next_Z = p.zp ? p.zp + 4 * q_first * (int64_t)zb : p.B;
     int64_t left = c_stop - 4 * q_first;
     auto issue = [&](Tile& t) {
         const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 4 * NC ? left : 4 * NC);
-        const __amdgpu_buffer_rsrc_t rB = make_rsrc(nb_B, (uint64_t)ncols * row_bytes);
-        const __amdgpu_buffer_rsrc_t rS = make_rsrc(nb_S, (uint64_t)ncols * nb * 2);
-        const __amdgpu_buffer_rsrc_t rZ = make_rsrc(nb_Z, p.zp ? (uint64_t)ncols * zb : 0);
+        const __amdgpu_buffer_rsrc_t rB = make_rsrc(next_B, (uint64_t)ncols * row_bytes);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(next_S, (uint64_t)ncols * nb * 2);
+        const __amdgpu_buffer_rsrc_t rZ = make_rsrc(next_Z, p.zp ? (uint64_t)ncols * zb : 0);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
 #pragma unroll
@@ -178,9 +178,9 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
                 t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(rZ, oz[n][j], 0, kNontemporal);
             }
         if (left > 0) {   // uniform; past the end the bases stay put
-            nb_B += 4 * NC * (int64_t)row_bytes;
-            nb_S += 4 * NC * (int64_t)nb;
-            if (p.zp) nb_Z += 4 * NC * (int64_t)zb;
+            next_B += 4 * NC * (int64_t)row_bytes;
+            next_S += 4 * NC * (int64_t)nb;
+            if (p.zp) next_Z += 4 * NC * (int64_t)zb;
         }
         left -= 4 * NC;
     };
@@ -261,10 +261,9 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         }
     };
 
-    // Totals of the tile at quad qs: the column sums inside the wave into LDS
-    // slot k of the chunk; after the chunk, the sums over the waves in wave
-    // order.
-    const int W_ = W;
+    // Totals of a tile: the column sums inside the wave go to LDS slot k (the
+    // tile's place in its pass); after the pass, the sums over the waves in
+    // wave order are stored.
     auto store = [&](int64_t qs, int idx, float v) {
         const int64_t col = 4 * qs + idx / (4 * RQ);
         const int row = idx % (4 * RQ);
@@ -315,7 +314,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         for (int e = tid; e < 2 * NV; e += (int)blockDim.x) {   // 2 NV can exceed one wave
             const int t = e / NV, idx = e - t * NV;
             float v = part[t][0][idx];
-            for (int w = 1; w < W_; ++w) v += part[t][w][idx];
+            for (int w = 1; w < W; ++w) v += part[t][w][idx];
             store(qs + (int64_t)t * NC, idx, v);
         }
         __syncthreads();   // the slots are refilled by the next pass
