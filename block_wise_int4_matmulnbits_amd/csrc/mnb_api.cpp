@@ -172,7 +172,8 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->engine == 2) {
         const bool shape_ok =
             plan->row_tiles == 8 ? (plan->waves_per_wg == 8 && plan->cols_per_tile == 256)
-                                 : ((plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
+                                 : ((plan->waves_per_wg == 2 && plan->cols_per_tile == 64) ||
+                                    (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
                                     (plan->waves_per_wg == 8 && plan->cols_per_tile == 256));
         if (!is_pow2_in(plan->row_tiles, 1, 8) || !shape_ok ||
             (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
@@ -244,9 +245,21 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         while (rt < 4 && 32 * rt < m) rt *= 2;
         while (rt > 1 && (uint64_t)64 * rt * (uint64_t)K > mnb::kPrefillRowBlockBytes) rt /= 2;
         auto tiles = [&](int64_t r, int64_t c) { return ceil_div(m, 32 * r) * ceil_div(N, c); };
+        // Narrow the columns, then the rows, only while the tiles would give
+        // fewer than 85% of the CUs one: a last round with a few idle CUs
+        // costs less than halving every tile's rows (gate_up, µs: m = 64
+        // 84.2 -> 57.5, m = 96 106.9 -> 74.2, m = 128 113.7 -> 78.1, m = 256
+        // 154.4 -> 111.4).
+        auto fills = [&](int64_t r, int64_t c) { return 100 * tiles(r, c) >= 85 * (int64_t)num_cus; };
         int64_t cols = 256;
-        while (cols > 128 && tiles(rt, cols) < num_cus) cols /= 2;
-        while (rt > 1 && tiles(rt, cols) < num_cus) rt /= 2;
+        while (cols > 128 && !fills(rt, cols)) cols /= 2;
+        while (rt > 1 && !fills(rt, cols)) rt /= 2;
+        // Tiles for at most half of the CUs even at one row block: 64
+        // columns on two waves double them (down projection m = 64: 134 ->
+        // 109 us, m = 128: 134.5 -> 112.5).  With more tiles than that, 128
+        // columns stay ahead, since the narrower tiles convert each
+        // activation for half as many columns (gate_up m = 16: 45.8 vs 49.3).
+        if (cols == 128 && 2 * tiles(rt, cols) <= (int64_t)num_cus) cols = 64;
         // 256 x 256 tiles with the weights staged through LDS when they give
         // at least 85% of the CUs a tile (gate_up, interleaved A/B against
         // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
@@ -272,7 +285,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // The largest tiles run as eight waves of 32 (or 2 x 4 waves of 64)
         // columns rather than four of 64: faster on the gate_up shape (757 vs
         // 831 us at m = 2048), within 5% on the down projection.
-        plan->waves_per_wg = (rt >= 4 && cols == 256) ? 8 : 4;
+        plan->waves_per_wg = cols == 64 ? 2 : (rt >= 4 && cols == 256) ? 8 : 4;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

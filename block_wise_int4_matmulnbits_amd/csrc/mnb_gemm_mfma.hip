@@ -587,11 +587,12 @@ GemmFn lookup_gemm_ct(int rt)
     return nullptr;
 }
 
-// Four waves with one or two 32-column tiles each (128 or 256 columns), or
-// eight waves with one (256 columns).
+// Two waves with one 32-column tile each (64 columns), four waves with one
+// or two (128 or 256 columns), or eight waves with one (256 columns).
 template <bool VEC, bool ABF16>
 GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 {
+    if (waves == 2 && cols == 64) return lookup_gemm_ct<1, 2, VEC, ABF16>(rt);
     if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16>(rt);
     if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16>(rt);
     if (waves == 8 && cols == 256) return lookup_gemm_ct<1, 8, VEC, ABF16>(rt);

@@ -139,7 +139,8 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * v_mfma_f32_16x16x32_f16.  For 1 <= m <= 8.
  * engine 2 (prefill kernel, m > 8): a workgroup owns a tile of
  * 32 * row_tiles rows by cols_per_tile columns, split by columns over its
- * waves: waves_per_wg = 4 with 128 or 256 columns, or 8 with 256; K is
+ * waves: waves_per_wg = 2 with 64 columns, 4 with 128 or 256, or 8 with
+ * 256; K is
  * walked 128 at a time, activations through LDS; weights dequantized to
  * fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of K.  Also
  * accepted for any m >= 1 as an explicit plan.
@@ -158,9 +159,9 @@ typedef struct {
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8; engine 3: 1, 2 or 4     */
     int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
-                                engine 2: 128 or 256; engine 3: 4 or 8 (4 with
+                                engine 2: 64, 128 or 256; engine 3: 4 or 8 (4 with
                                 blocks_per_lane 4 when m > 4)                   */
-    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 4, 8;
+    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 2, 4, 8;
                                 engine 3: 1..8                                  */
     int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
     int32_t workgroups;      /* grid size, >= 1                                  */

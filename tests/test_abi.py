@@ -109,59 +109,67 @@ PREFILL_SHAPES = [(m, K, N) for m in (9, 16, 17, 100, 1000, 4096, 1 << 20)
                   for N in (1, 63, 64, 4096, 151936)]
 
 
+def _prefill_rule(m, K, N, cus):
+    """The prefill planner's rules, restated: (row_tiles, cols, waves), or
+    "decode" for the 8-row decode plan run per 8 rows."""
+    def tiles(r, c):
+        return -(-m // (32 * r)) * -(-N // c)
+    rt = 1
+    while rt < 4 and 32 * rt < m:
+        rt *= 2
+    while rt > 1 and 64 * rt * K > 0xFFFFFFF0:
+        rt //= 2
+    def fills(r, c):
+        return 100 * tiles(r, c) >= 85 * cus
+    cols = 256
+    while cols > 128 and not fills(rt, cols):
+        cols //= 2
+    while rt > 1 and not fills(rt, cols):
+        rt //= 2
+    if cols == 128 and 2 * tiles(rt, cols) <= cus:
+        cols = 64                     # two waves, twice the tiles
+    t8 = -(-m // 256) * -(-N // 256)
+    if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
+        rt, cols = 8, 256
+    if 2 * tiles(rt, cols) < cus and m <= 48:
+        return "decode"
+    return rt, cols, 2 if cols == 64 else (8 if rt >= 4 and cols == 256 else 4)
+
+
 def test_default_prefill_plans():
     """m > 8 runs the prefill engine: 32-row tiles (up to 4 per workgroup,
-    never more than the rows need), 128 or 256 columns per workgroup, the
-    largest tile that still gives every compute unit a workgroup, no more
-    workgroups than tiles."""
+    never more than the rows need), 256 columns, narrowed to 128 and then
+    to fewer rows while the tiles would give fewer than 85% of the compute
+    units one; 64 columns on two waves when the tiles would leave at least
+    half of the CUs idle; 256 x 256 LDS-staged tiles when they give 85% of
+    the CUs a tile; with up to 48 rows and tiles for less than half of the
+    CUs, the 8-row decode plan per 8 rows.  No more workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
-            if p.engine != 2:
-                # A few rows on few columns: the 8-row decode plan, launched
-                # per 8 rows, when the prefill tiles would leave more than half
-                # of the CUs idle.
-                assert m <= 48 and p.as_dict() == mnb.mnb_plan_default(8, K, N, cus, occ).as_dict()
-                rt = 1
-                while rt < 4 and 32 * rt < m:
-                    rt *= 2
-                while rt > 1 and 64 * rt * K > 0xFFFFFFF0:
-                    rt //= 2
-                assert 2 * -(-m // (32 * rt)) * -(-N // 128) < cus
+            want = _prefill_rule(m, K, N, cus)
+            if want == "decode":
+                assert p.engine != 2
+                assert p.as_dict() == mnb.mnb_plan_default(8, K, N, cus, occ).as_dict()
                 continue
-            assert p.engine == 2 and p.cols_per_tile in (128, 256)
-            assert p.waves_per_wg == (8 if p.row_tiles >= 4 and p.cols_per_tile == 256 else 4)
+            assert p.engine == 2 and (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N, cus)
             q = mnb.mnb_plan(**{f: getattr(p, f) for f, _ in mnb.mnb_plan._fields_})
             assert mnb.mnb_plan_check(m, K, N, q) == 0
             assert q.threads_per_wg == 64 * p.waves_per_wg and q.k_chunks == (K // 32 + 3) // 4
-            t8 = -(-m // 256) * -(-N // 256)
-            if p.row_tiles == 8:     # 256 x 256 tiles: when they give 85% of the CUs a tile
-                assert p.cols_per_tile == 256 and m > 128 and 0.85 * cus <= t8
-                assert 1 <= p.workgroups <= t8
-                continue
-            assert not (m > 128 and 0.85 * cus <= t8 and 512 * K <= 0xFFFFFFF0)
-            rt, cols = p.row_tiles, p.cols_per_tile
-            assert rt in (1, 2, 4) and (rt == 1 or 32 * (rt // 2) < m)
-
-            def tiles(r, c):
-                return -(-m // (32 * r)) * -(-N // c)
-            cap = 1
-            while cap < 4 and 32 * cap < m:
-                cap *= 2
-            assert rt <= cap
-            # Fills the CUs unless already at the smallest tile; columns are
-            # narrowed first, rows only at 128 columns; each step down was
-            # needed.
-            assert tiles(rt, cols) >= cus or (rt, cols) == (1, 128)
-            if cols < 256:
-                assert tiles(cap, 2 * cols) < cus
-            if rt < cap:
-                assert cols == 128 and tiles(2 * rt, 128) < cus
-            assert 1 <= p.workgroups <= tiles(rt, cols)
+            rows = 256 if p.row_tiles == 8 else 32 * p.row_tiles
+            assert 1 <= p.workgroups <= -(-m // rows) * -(-N // p.cols_per_tile)
+            assert p.row_tiles == 1 or 32 * (p.row_tiles // 2) < m
     # The two prefill shapes of the decode model at 512 and 2048 rows.
     for m in (512, 1024, 2048):
         assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(m, 4096, 28672, 256, 0)) == (8, 256)
     assert (lambda p: (p.row_tiles, p.cols_per_tile))(mnb.mnb_plan_default(512, 14336, 4096, 256, 0)) == (2, 128)
+    # Measured choices at small and middle heights.
+    for m, K, N, want in ((64, 4096, 28672, (2, 128, 4)), (128, 4096, 28672, (4, 128, 4)),
+                          (256, 4096, 28672, (4, 256, 8)), (16, 4096, 28672, (1, 128, 4)),
+                          (64, 14336, 4096, (1, 64, 2)), (128, 14336, 4096, (1, 64, 2)),
+                          (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
+        p = mnb.mnb_plan_default(m, K, N, 256, 0)
+        assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
 
 
 def test_plan_check_engines_and_rows():

@@ -63,7 +63,7 @@ def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
 
 
 @pytest.mark.parametrize("rt", [1, 2, 4])
-@pytest.mark.parametrize("cols,waves", [(128, 4), (256, 4), (256, 8)])
+@pytest.mark.parametrize("cols,waves", [(64, 2), (128, 4), (256, 4), (256, 8)])
 def test_prefill_every_tiling_and_small_grids(oracle_mod, rt, cols, waves):
     """One, two or four 32-row tiles; four waves of 32 or 64 columns or
     eight of 32; fewer workgroups than tiles (each walks several (row block,
@@ -93,12 +93,13 @@ def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
         assert_prefill(oracle_mod, d, m, "prefill lds-staged wg=%d" % wg, plan)
 
 
-@pytest.mark.parametrize("m", [9, 16, 23, 48])
+@pytest.mark.parametrize("m", [9, 16, 23, 32])
 def test_few_tiles_run_decode_kernels_per_8_rows(oracle_mod, m):
-    """The down projection (N = 4096) with 9..48 rows gives the prefill
-    kernel 32 tiles for 256 CUs, so the default plan runs the decode kernels
-    in launches of 8 rows: against the oracle (sampled columns for the
-    larger heights), and each block of 8 rows bit-equal to its own launch."""
+    """The down projection (N = 4096) with 9..32 rows gives the prefill
+    kernel 64 tiles for 256 CUs even at 64 columns, so the default plan runs
+    the decode kernels in launches of 8 rows: against the oracle (sampled
+    columns for the larger heights), and each block of 8 rows bit-equal to
+    its own launch."""
     K, N = 14336, 4096
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 860 + m)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
