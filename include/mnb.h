@@ -136,14 +136,13 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * engine 1 (MFMA tile kernel): a wave owns 16 columns; the waves_per_wg
  * waves of a workgroup split K; activations are staged in LDS,
  * chunk_blocks blocks of K per pass; dot products on
- * v_mfma_f32_16x16x32_f16.  For 1 <= m <= 8.
+ * v_mfma_f32_16x16x32_f16.  Up to 8 rows per launch.
  * engine 2 (prefill kernel, m > 8): a workgroup owns a tile of
  * 32 * row_tiles rows by cols_per_tile columns, split by columns over its
  * waves: waves_per_wg = 2 with 64 columns, 4 with 128 or 256, or 8 with
- * 256; K is
- * walked 128 at a time, activations through LDS; weights dequantized to
- * fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of K.  Also
- * accepted for any m >= 1 as an explicit plan.
+ * 256; K is walked 128 at a time, activations through LDS; weights
+ * dequantized to fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of
+ * K.  Also accepted for any m >= 1 as an explicit plan.
  * engine 3 (4x4x4 MFMA kernel, m <= 8): a workgroup of waves_per_wg waves
  * walks its columns cols_per_tile (4 or 8) at a time; lane i of each group
  * of four lanes holds column i of a quad and rows i and 4 + i of the
