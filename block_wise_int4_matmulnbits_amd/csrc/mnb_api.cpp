@@ -276,6 +276,20 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // the tiles would leave more than half of the CUs idle.
         if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 6 * MNB_MAX_M)
             return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
+        // Up to 16 rows over at least 768 Ki weights per CU: below 32 rows
+        // the tiles' cost is their dequantization whatever m, and two 8-row
+        // launches of the 4x4x4 MFMA kernel, which scales whole blocks'
+        // sums instead of every weight, cost less (us, prefill -> decode:
+        // 151936 x 4096 m = 9 242 -> 158, m = 16 247 -> 179; 57344 x 4096
+        // m = 16 90 -> 79; 28672 x 8192 m = 16 103 -> 79; kept at 28672 x
+        // 4096, m = 12 45 vs 47).
+        if (m <= 2 * MNB_MAX_M && (uint64_t)N * (uint64_t)K >= (uint64_t)786432 * (uint64_t)num_cus) {
+            mnb_plan p8;
+            if (mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, &p8) == MNB_OK && p8.engine == 3) {
+                *plan = p8;
+                return MNB_OK;
+            }
+        }
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
         int64_t wgs = per_cu * num_cus;
         if (wgs > tiles(rt, cols)) wgs = tiles(rt, cols);

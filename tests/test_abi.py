@@ -133,6 +133,8 @@ def _prefill_rule(m, K, N, cus):
         rt, cols = 8, 256
     if 2 * tiles(rt, cols) < cus and m <= 48:
         return "decode"
+    if m <= 16 and N * K >= 786432 * cus and mnb.mnb_plan_default(8, K, N, cus, 0).engine == 3:
+        return "decode"
     return rt, cols, 2 if cols == 64 else (8 if rt >= 4 and cols == 256 else 4)
 
 
@@ -143,7 +145,9 @@ def test_default_prefill_plans():
     units one; 64 columns on two waves when the tiles would leave at least
     half of the CUs idle; 256 x 256 LDS-staged tiles when they give 85% of
     the CUs a tile; with up to 48 rows and tiles for less than half of the
-    CUs, the 8-row decode plan per 8 rows.  No more workgroups than tiles."""
+    CUs, or up to 16 rows over at least 768 Ki weights per CU when the 8-row
+    plan is the 4x4x4 MFMA kernel, the 8-row decode plan per 8 rows.  No
+    more workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
@@ -170,6 +174,12 @@ def test_default_prefill_plans():
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
+    # Up to 16 rows over large weights: 8-row launches of the 4x4x4 MFMA
+    # kernel; 17 rows, K past 16384 or smaller weights stay on the tiles.
+    for m, K, N, engine in ((9, 4096, 151936, 3), (16, 4096, 151936, 3), (16, 4096, 57344, 3),
+                            (12, 8192, 28672, 3), (17, 4096, 151936, 2), (16, 4096, 28672, 2),
+                            (16, 2048, 57344, 2), (16, 32 * 600, 57344, 2)):
+        assert mnb.mnb_plan_default(m, K, N, 256, 0).engine == engine, (m, K, N)
 
 
 def test_plan_check_engines_and_rows():

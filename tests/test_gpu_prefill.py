@@ -122,6 +122,33 @@ def test_few_tiles_run_decode_kernels_per_8_rows(oracle_mod, m):
         assert np.array_equal(y, y16[r0:r0 + mc])
 
 
+@pytest.mark.parametrize("m", [9, 16])
+def test_large_weights_run_decode_kernels_per_8_rows(oracle_mod, m):
+    """The lm_head shape (K = 4096, N = 151936) with 9 and 16 rows: the
+    default plan is the 8-row 4x4x4 MFMA plan, run twice; check 1 on sampled
+    columns, check 2 on every output, and each block of 8 rows bit-equal to
+    its own launch."""
+    K, N = 4096, 151936
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 880 + m)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = mnb.plan_for_device(m, K, N, cus)
+    assert plan.engine == 3 and plan.as_dict() == mnb.plan_for_device(8, K, N, cus).as_dict()
+    G.log("[parity] lm_head m=%d per 8 rows, plan %s" % (m, plan.as_dict()))
+    y16, c = run(d, m, W.F16)
+    assert c["launches"] == 2
+    ybf, _ = run(d, m, W.BF16)
+    assert not np.any(y16 == 0xFFFF)
+    assert G.check2(ybf, y16, oracle_mod).all()
+    cols = np.unique(np.concatenate([[0, 1, 2, 3, N - 1], np.random.default_rng(881).choice(N, 24, replace=False)]))
+    ref = oracle_mod.matmul_nbits(d["A"][:m], True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
+    ok, _ = G.check1(y16[:, cols], ref, oracle_mod)
+    assert ok.all()
+    for r0 in range(0, m, 8):
+        mc = min(8, m - r0)
+        y, _ = run(dict(d, A=d["A"][r0:r0 + mc]), mc, W.F16, plan.as_dict())
+        assert np.array_equal(y, y16[r0:r0 + mc])
+
+
 def test_prefill_engine_for_decode_heights(oracle_mod):
     """The prefill engine also serves m <= 8 when asked for explicitly."""
     d = W.generate(3, 4096, 129, W.BF16, True, 0.001, 0.01, 0.5, 730)
