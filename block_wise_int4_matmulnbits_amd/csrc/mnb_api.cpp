@@ -172,7 +172,8 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->engine == 2) {
         const bool shape_ok =
             plan->row_tiles == 8 ? (plan->waves_per_wg == 8 && plan->cols_per_tile == 256)
-                                 : ((plan->waves_per_wg == 2 && plan->cols_per_tile == 64) ||
+                                 : ((plan->waves_per_wg == 4 && plan->cols_per_tile == 32 && plan->row_tiles == 1) ||
+                                    (plan->waves_per_wg == 2 && plan->cols_per_tile == 64) ||
                                     (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
                                     (plan->waves_per_wg == 8 && plan->cols_per_tile == 256));
         if (!is_pow2_in(plan->row_tiles, 1, 8) || !shape_ok ||
@@ -270,12 +271,21 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
             rt = 8;
             cols = 256;
         }
-        // A few rows on few columns (the down projection's 4096 at m = 9:
-        // 32 tiles for 256 CUs, 139 us against 19 us for 8 rows): the decode
-        // kernels in launches of 8 rows, while at most six such launches and
-        // the tiles would leave more than half of the CUs idle.
-        if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 6 * MNB_MAX_M)
+        // Few columns: 32-row, 32-column tiles whose K four waves split,
+        // while there are at most two such tiles per CU and more than 16
+        // rows (us, before -> after: down projection m = 24 57.5 -> 47.2, m =
+        // 48 101 -> 46.1, m = 64 103 -> 48.3, m = 128 105 -> 92.4; 4096 x 6144
+        // m = 32 46.7 -> 17.9; at three tiles per CU, down m = 192, 131.5 vs
+        // 135.6, the wider tiles stay).  Otherwise, with up to 16 rows whose
+        // tiles would leave more than half of the CUs idle (the down
+        // projection at m = 9: 32 tiles for 256 CUs), the decode kernels in
+        // launches of 8 rows (m = 9 139 -> 30.7 us, against 42.7 split).
+        if (m > 2 * MNB_MAX_M && ceil_div(m, 32) * ceil_div(N, 32) <= 2 * (int64_t)num_cus) {
+            rt = 1;
+            cols = 32;
+        } else if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 2 * MNB_MAX_M) {
             return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
+        }
         // Up to 16 rows over at least 768 Ki weights per CU: below 32 rows
         // the tiles' cost is their dequantization whatever m, and two 8-row
         // launches of the 4x4x4 MFMA kernel, which scales whole blocks'
@@ -299,7 +309,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // The largest tiles run as eight waves of 32 (or 2 x 4 waves of 64)
         // columns rather than four of 64: faster on the gate_up shape (757 vs
         // 831 us at m = 2048), within 5% on the down projection.
-        plan->waves_per_wg = cols == 64 ? 2 : (rt >= 4 && cols == 256) ? 8 : 4;
+        plan->waves_per_wg = cols == 64 ? 2 : (rt >= 4 && cols == 256) ? 8 : 4;   // 32 columns: 4
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

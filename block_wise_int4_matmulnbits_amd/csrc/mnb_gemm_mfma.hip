@@ -110,14 +110,24 @@ __device__ __forceinline__ int a_slot(int d, int r)
     return d ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 
-template <int RT, int CT, int W, bool VEC, bool ABF16>
+// KS > 1 splits K over the waves: KS slices of W / KS waves, slice s
+// walking quads s, s + KS, s + 2 KS, ... of the same columns; at the end the
+// slices' accumulators meet in LDS and slice 0 adds them in slice order and
+// stores.  More waves then walk a tile's K at once where the tiles are too
+// few to fill the chip (the down projection's 4096 columns).
+template <int RT, int CT, int W, bool VEC, bool ABF16, int KS>
 __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 {
     constexpr int THREADS = 64 * W;
+    constexpr int WC = W / KS;               // waves per K slice
+    static_assert(WC * KS == W, "whole slices");
     constexpr int MT = 32 * RT;              // rows per workgroup tile
-    constexpr int NT = 32 * CT * W;          // columns per workgroup tile
-    constexpr int QA = 16 * MT;              // 16-byte pieces of activations per quad
+    constexpr int NT = 32 * CT * WC;         // columns per workgroup tile
+    constexpr int QAQ = 16 * MT;             // 16-byte pieces of activations per quad
+    constexpr int QA = KS * QAQ;             // per step: one quad per slice
     constexpr int SPT = QA / THREADS;        // pieces per thread
+    static_assert(KS == 1 || (KS - 1) * WC * RT * CT * 16 * 64 * 4 <= 2 * QA * 16,
+                  "the partial sums fit the activation stages");
     static_assert(QA % THREADS == 0, "whole pieces per thread");
     constexpr int P = kGemmRing<VEC>;
     extern __shared__ uint4 a_lds[];         // [2][4 blocks][MT rows][4 slots]
@@ -125,28 +135,32 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int slice = wv / WC, wcol = wv - slice * WC;
     const int j = lane & 31, h = lane >> 5;
     const int nb = p.nb;
     const int nq = (nb + 3) / 4;
+    const int nsteps = (nq + KS - 1) / KS;   // steps of KS quads
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t zdef = p.zp ? 0u : 8u;    // zero point 8 when none are given
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);
     const int64_t tiles_m = (p.M + MT - 1) / MT;
     const int64_t tiles_n = (p.N + NT - 1) / NT;
 
-    // Piece e of a quad's activations (e = tid + THREADS * s): block
-    // e / (4 MT), row (e / 4) % MT, piece e % 4; its LDS index and its byte
-    // offset in the row block are fixed per thread.
+    // Piece e0 = tid + THREADS * s of a step's activations: quad e0 / QAQ
+    // of the step, and within it (e = e0 % QAQ) block e / (4 MT), row
+    // (e / 4) % MT, piece e % 4; its LDS index, block and byte offset in the
+    // row block are fixed per thread.
     int pc_blk[SPT], pc_lds[SPT];
     uint32_t pc_off[SPT];
 #pragma unroll
     for (int s = 0; s < SPT; ++s) {
-        const int e = tid + THREADS * s;
+        const int e0 = tid + THREADS * s;
+        const int qo = e0 / QAQ, e = e0 - qo * QAQ;
         const int br = e >> 2, d = e & 3;
         const int blk = br / MT, row = br - blk * MT;
-        pc_blk[s] = blk;
-        pc_lds[s] = (blk * MT + row) * 4 + a_slot(d, row);
-        pc_off[s] = (uint32_t)row * (uint32_t)p.K * 2 + 64 * blk + 16 * d;
+        pc_blk[s] = 4 * qo + blk;
+        pc_lds[s] = qo * QAQ + (blk * MT + row) * 4 + a_slot(d, row);
+        pc_off[s] = (uint32_t)row * (uint32_t)p.K * 2 + 256 * qo + 64 * blk + 16 * d;
     }
 
     for (int64_t tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         // L2) and walk the column blocks.
         const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
         const int64_t r0 = tm * MT;
-        const int64_t col0 = tn * NT + 32 * CT * wv;   // this wave's 32*CT columns
+        const int64_t col0 = tn * NT + 32 * CT * wcol;   // this wave's 32*CT columns
         const int64_t left = p.N - col0;
         const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 32 * CT ? left : 32 * CT);
         const int64_t cb = left <= 0 ? 0 : col0;
@@ -169,9 +183,10 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         const int64_t mrows = p.M - r0 < MT ? p.M - r0 : MT;
         const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A + r0 * p.K, (uint64_t)mrows * (uint64_t)p.K * 2);
 
-        // Column tile c of the wave: columns col0 + 32c + j.
+        // Column tile c of the wave: columns col0 + 32c + j; step t of
+        // the slice is quad KS t + slice.
         auto issue = [&](WQuad (&qs)[CT], int t) {
-            const uint32_t b = 4 * (uint32_t)t;
+            const uint32_t b = 4 * (uint32_t)(KS * t + slice);
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
                 WQuad& q = qs[c];
@@ -204,12 +219,13 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
             }
         };
 
-        // Activations of quad t (zeros past M and K).
+        // Activations of step t: quads KS t .. KS t + KS - 1 (zeros past M
+        // and K).
         auto fetch_a = [&](uint4 (&v)[SPT], int t) {
 #pragma unroll
             for (int s = 0; s < SPT; ++s) {
                 const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-                    rA, 4 * t + pc_blk[s] < nb ? pc_off[s] + 256 * (uint32_t)t : kOutOfRange, 0, 0);
+                    rA, 4 * KS * t + pc_blk[s] < nb ? pc_off[s] + 256 * KS * (uint32_t)t : kOutOfRange, 0, 0);
                 v[s] = make_uint4(x[0], x[1], x[2], x[3]);
             }
         };
@@ -250,7 +266,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                 for (int v = 0; v < 2; ++v) {
                     const int row = rt * 32 + j;
-                    const uint4 av = a_lds[buf * QA + (i * MT + row) * 4 + a_slot(2 * h + v, row)];
+                    const uint4 av = a_lds[buf * QA + slice * QAQ + (i * MT + row) * 4 + a_slot(2 * h + v, row)];
                     f[rt][v] = __builtin_bit_cast(half8_t, u32x4{av.x, av.y, av.z, av.w});
                 }
         };
@@ -323,7 +339,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         __syncthreads();                  // the previous tile's readers are done
         store_a(av, 0);
         fetch_a(av, 1);
-        for (int t0 = 0; t0 < nq; t0 += P) {
+        for (int t0 = 0; t0 < nsteps; t0 += P) {
 #pragma unroll
             for (int s = 0; s < P; ++s) {
                 const int t = t0 + s;
@@ -341,6 +357,33 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
             }
         }
 
+        if constexpr (KS > 1) {
+            // Slices 1 .. KS-1 leave their sums in the (now idle) stages,
+            // lane-contiguous; slice 0 adds them in slice order.
+            float* const part = reinterpret_cast<float*>(a_lds);
+            auto at = [&](int k, int rt, int c, int q) {
+                return ((((k - 1) * WC + wcol) * RT + rt) * CT * 16 + c * 16 + q) * 64 + lane;
+            };
+            __syncthreads();              // every slice is done with the stages
+            if (slice > 0) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) part[at(slice, rt, c, q)] = acc[rt][c][q];
+            }
+            __syncthreads();
+            if (slice > 0) continue;      // wave-uniform; the next tile's barriers are the same
+#pragma unroll
+            for (int k = 1; k < KS; ++k)
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int c = 0; c < CT; ++c)
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) acc[rt][c][q] += part[at(k, rt, c, q)];
+        }
         // Epilogue: fp32 -> fp16 (RNE), optionally -> bf16 (RNE), store.
         // Accumulator element q of lane (j, h) is row (q%4) + 4h + 8(q/4),
         // column j of its 32 x 32 tile.
@@ -588,18 +631,20 @@ template <int CT, int W, bool VEC, bool ABF16>
 GemmFn lookup_gemm_ct(int rt)
 {
     switch (rt) {
-    case 1: return mnb_gemm_mfma_kernel<1, CT, W, VEC, ABF16>;
-    case 2: return mnb_gemm_mfma_kernel<2, CT, W, VEC, ABF16>;
-    case 4: return mnb_gemm_mfma_kernel<4, CT, W, VEC, ABF16>;
+    case 1: return mnb_gemm_mfma_kernel<1, CT, W, VEC, ABF16, 1>;
+    case 2: return mnb_gemm_mfma_kernel<2, CT, W, VEC, ABF16, 1>;
+    case 4: return mnb_gemm_mfma_kernel<4, CT, W, VEC, ABF16, 1>;
     }
     return nullptr;
 }
 
 // Two waves with one 32-column tile each (64 columns), four waves with one
-// or two (128 or 256 columns), or eight waves with one (256 columns).
+// or two (128 or 256 columns), or eight waves with one (256 columns); or
+// one 32-row, 32-column tile whose K four waves split.
 template <bool VEC, bool ABF16>
 GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 {
+    if (waves == 4 && cols == 32) return rt == 1 ? mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4> : nullptr;
     if (waves == 2 && cols == 64) return lookup_gemm_ct<1, 2, VEC, ABF16>(rt);
     if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16>(rt);
     if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16>(rt);
@@ -628,7 +673,9 @@ size_t gemm_lds_bytes(const mnb_plan& plan)
 {
     if (plan.row_tiles == 8)   // two stages of activations and weights
         return (size_t)2 * (kLdsTileRows + kLdsTileCols) * 2 * 4 * 16;
-    return (size_t)2 * 4 * 32 * plan.row_tiles * 4 * 16;   // two quads of 32*rt rows x 128 k, fp16
+    // Two steps of 32*rt rows x 128 k (one quad per K slice), fp16.
+    const size_t slices = plan.cols_per_tile == 32 ? 4 : 1;
+    return (size_t)2 * slices * 4 * 32 * plan.row_tiles * 4 * 16;
 }
 
 int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)

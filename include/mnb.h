@@ -93,7 +93,7 @@ typedef enum {
  *                aligned.  Must hold finite values that are finite in fp16.
  *   a_dtype      MNB_F16 or MNB_BF16.
  *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
- *                prefill kernel, except that up to 48 rows whose prefill
+ *                prefill kernel, except that up to 16 rows whose prefill
  *                tiles would leave more than half of the compute units idle,
  *                and up to 16 rows over at least 768 Ki weights per compute
  *                unit with K <= 16384, run the decode kernels in launches of
@@ -144,7 +144,10 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * waves: waves_per_wg = 2 with 64 columns, 4 with 128 or 256, or 8 with
  * 256; K is walked 128 at a time, activations through LDS; weights
  * dequantized to fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of
- * K.  Also accepted for any m >= 1 as an explicit plan.
+ * K.  With 32 columns (row_tiles 1, waves_per_wg 4) the four waves split K
+ * instead (wave s takes the 128-wide steps s, s + 4, ...) and their fp32
+ * sums are added in wave order at the end.  Also accepted for any m >= 1
+ * as an explicit plan.
  * engine 3 (4x4x4 MFMA kernel, m <= 8): a workgroup of waves_per_wg waves
  * walks its columns cols_per_tile (4 or 8) at a time; lane i of each group
  * of four lanes holds column i of a quad and rows i and 4 + i of the
@@ -160,7 +163,7 @@ typedef struct {
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8; engine 3: 1, 2 or 4     */
     int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
-                                engine 2: 64, 128 or 256; engine 3: 4 or 8 (4 with
+                                engine 2: 32, 64, 128 or 256; engine 3: 4 or 8 (4 with
                                 blocks_per_lane 4 when m > 4)                   */
     int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 2, 4, 8;
                                 engine 3: 1..8                                  */

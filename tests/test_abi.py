@@ -131,7 +131,9 @@ def _prefill_rule(m, K, N, cus):
     t8 = -(-m // 256) * -(-N // 256)
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
-    if 2 * tiles(rt, cols) < cus and m <= 48:
+    if m > 16 and -(-m // 32) * -(-N // 32) <= 2 * cus:
+        return 1, 32, 4                 # K split over four waves
+    if 2 * tiles(rt, cols) < cus and m <= 16:
         return "decode"
     if m <= 16 and N * K >= 786432 * cus and mnb.mnb_plan_default(8, K, N, cus, 0).engine == 3:
         return "decode"
@@ -144,8 +146,9 @@ def test_default_prefill_plans():
     to fewer rows while the tiles would give fewer than 85% of the compute
     units one; 64 columns on two waves when the tiles would leave at least
     half of the CUs idle; 256 x 256 LDS-staged tiles when they give 85% of
-    the CUs a tile; with up to 48 rows and tiles for less than half of the
-    CUs, or up to 16 rows over at least 768 Ki weights per CU when the 8-row
+    the CUs a tile; with more than 16 rows and at most two 32 x 32 tiles per
+    CU, those tiles with K split over four waves; otherwise with up to 16
+    rows and tiles for less than half of the CUs, or up to 16 rows over at least 768 Ki weights per CU when the 8-row
     plan is the 4x4x4 MFMA kernel, the 8-row decode plan per 8 rows.  No
     more workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
@@ -170,7 +173,9 @@ def test_default_prefill_plans():
     # Measured choices at small and middle heights.
     for m, K, N, want in ((64, 4096, 28672, (2, 128, 4)), (128, 4096, 28672, (4, 128, 4)),
                           (256, 4096, 28672, (4, 256, 8)), (16, 4096, 28672, (1, 128, 4)),
-                          (64, 14336, 4096, (1, 64, 2)), (128, 14336, 4096, (1, 64, 2)),
+                          (64, 14336, 4096, (1, 32, 4)), (128, 14336, 4096, (1, 32, 4)),
+                          (24, 14336, 4096, (1, 32, 4)), (32, 4096, 6144, (1, 32, 4)),
+                          (128, 4096, 6144, (1, 128, 4)), (192, 14336, 4096, (1, 128, 4)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)

@@ -8,8 +8,11 @@ weights rounded to fp16, so it is also held to a much tighter bound against
 the oracle run with the same rounded weights: the only difference left is
 fp32 accumulation, at most (K/32 + 32) roundings of 2^-24 relative to
 sum |a w| (one chained MFMA per block, 32 products each), plus one fp16 ulp
-for the output rounding.  The summation order of an output depends only on
-K, so rows computed in launches of different heights are bit-identical.
+for the output rounding (the tiles that split K over four waves add the
+slices' fp32 sums at the end: fewer roundings in a chain, not more).  The
+summation order of an output depends only on K and on whether the plan
+splits K, so rows computed in launches of different heights under tilings
+that do not split K are bit-identical.
 """
 import numpy as np
 import pytest
@@ -58,7 +61,7 @@ def _gpu():
 def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
     plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert plan.engine == 2 or m <= 48     # few tiles: the decode kernels per 8 rows
+    assert plan.engine == 2 or m <= 16     # few tiles: the decode kernels per 8 rows
     assert_prefill(oracle_mod, d, m, "prefill", None)
 
 
@@ -93,29 +96,52 @@ def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
         assert_prefill(oracle_mod, d, m, "prefill lds-staged wg=%d" % wg, plan)
 
 
-@pytest.mark.parametrize("m", [9, 16, 23, 32])
+@pytest.mark.parametrize("m,K,N", [(5, 32 * 61, 300), (37, 32 * 61, 300), (100, 32 * 61, 300),
+                                   (40, 32, 77), (33, 0, 64), (64, 4096, 1000)])
+def test_prefill_k_split_tiles(oracle_mod, m, K, N):
+    """32-row, 32-column tiles whose K four waves split (slice s takes
+    quads s, s + 4, ...; an odd quad count, a single block, K = 0), with 1,
+    3 and 13 workgroups and the default grid; ragged rows and columns."""
+    d = W.generate(m, K, N, W.BF16 if m % 2 else W.F16, m != 40, 0.002, 0.02, 1.0, 900 + m)
+    for wg in (1, 3, 13, -(-m // 32) * -(-N // 32)):
+        plan = dict(engine=2, row_tiles=1, cols_per_tile=32, waves_per_wg=4, workgroups=wg)
+        assert_prefill(oracle_mod, d, m, "prefill k-split wg=%d" % wg, plan)
+
+
+@pytest.mark.parametrize("m", [23, 32, 48, 64])
+def test_down_projection_k_split_default(oracle_mod, m):
+    """The down projection (K = 14336, N = 4096) with 17..128 rows: the
+    default plan splits K over four waves of 32-column tiles; check 1 on
+    sampled columns, check 2 on every output."""
+    K, N = 14336, 4096
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 920 + m)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = mnb.plan_for_device(m, K, N, cus)
+    assert (plan.engine, plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) == (2, 1, 32, 4)
+    G.log("[parity] down m=%d k-split, plan %s" % (m, plan.as_dict()))
+    y16, c = run(d, m, W.F16)
+    assert c["launches"] == 1
+    ybf, _ = run(d, m, W.BF16)
+    assert not np.any(y16 == 0xFFFF)
+    assert G.check2(ybf, y16, oracle_mod).all()
+    cols = np.unique(np.concatenate([[0, 1, 31, 32, N - 1], np.random.default_rng(921).choice(N, 20, replace=False)]))
+    ref = oracle_mod.matmul_nbits(d["A"][:m], True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
+    ok, _ = G.check1(y16[:, cols], ref, oracle_mod)
+    assert ok.all()
+
+
+@pytest.mark.parametrize("m", [9, 16])
 def test_few_tiles_run_decode_kernels_per_8_rows(oracle_mod, m):
-    """The down projection (N = 4096) with 9..32 rows gives the prefill
-    kernel 64 tiles for 256 CUs even at 64 columns, so the default plan runs
-    the decode kernels in launches of 8 rows: against the oracle (sampled
-    columns for the larger heights), and each block of 8 rows bit-equal to
-    its own launch."""
+    """The down projection (N = 4096) with 9..16 rows gives the prefill
+    kernel 32 tiles for 256 CUs even at 64 columns, so the default plan runs
+    the decode kernels in launches of 8 rows: against the oracle, and each
+    block of 8 rows bit-equal to its own launch."""
     K, N = 14336, 4096
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 860 + m)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = mnb.plan_for_device(m, K, N, cus)
     assert plan.engine != 2 and plan.as_dict() == mnb.plan_for_device(8, K, N, cus).as_dict()
-    if m <= 16:
-        y16 = assert_prefill(oracle_mod, d, m, "decode per 8 rows", None)
-    else:
-        y16, c = run(d, m, W.F16)
-        assert c["launches"] == -(-m // 8)
-        ybf, _ = run(d, m, W.BF16)
-        assert G.check2(ybf, y16, oracle_mod).all()
-        cols = np.unique(np.concatenate([[0, 1, N - 1], np.random.default_rng(861).choice(N, 20, replace=False)]))
-        ref = oracle_mod.matmul_nbits(d["A"][:m], True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols)
-        ok, _ = G.check1(y16[:, cols], ref, oracle_mod)
-        assert ok.all()
+    y16 = assert_prefill(oracle_mod, d, m, "decode per 8 rows", None)
     for r0 in range(0, m, 8):
         mc = min(8, m - r0)
         y, _ = run(dict(d, A=d["A"][r0:r0 + mc]), mc, W.F16, plan.as_dict())
