@@ -261,6 +261,13 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // columns stay ahead, since the narrower tiles convert each
         // activation for half as many columns (gate_up m = 16: 45.8 vs 49.3).
         if (cols == 128 && 2 * tiles(rt, cols) <= (int64_t)num_cus) cols = 64;
+        // One or two row tiles with more than two full-width tiles per CU:
+        // 128 columns, whose finer tiles end the last round sooner (lm_head
+        // 4096 x 151936, us: m = 24 252 -> 217, m = 64 292 -> 258; 2048 x
+        // 151936 m = 64 143 -> 120).  With at most two per CU the 256
+        // columns stay, on eight waves (4096 x 65536 m = 32: 88.3 against
+        // 94.3 at 128 columns and 96.2 on four waves of 64).
+        if (rt <= 2 && cols == 256 && tiles(rt, cols) > 2 * (int64_t)num_cus) cols = 128;
         // 256 x 256 tiles with the weights staged through LDS when they give
         // at least 85% of the CUs a tile (gate_up, interleaved A/B against
         // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
@@ -306,10 +313,11 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         plan->engine = 2;
         plan->row_tiles = (int32_t)rt;
         plan->cols_per_tile = (int32_t)cols;
-        // The largest tiles run as eight waves of 32 (or 2 x 4 waves of 64)
-        // columns rather than four of 64: faster on the gate_up shape (757 vs
-        // 831 us at m = 2048), within 5% on the down projection.
-        plan->waves_per_wg = cols == 64 ? 2 : (rt >= 4 && cols == 256) ? 8 : 4;   // 32 columns: 4
+        // 256-column tiles run as eight waves of 32 columns rather than four
+        // of 64: faster on the gate_up shape (757 vs 831 us at m = 2048),
+        // within 5% on the down projection, 0-8% faster at one or two row
+        // tiles.  64 columns run on two waves, 32 (K split) and 128 on four.
+        plan->waves_per_wg = cols == 64 ? 2 : cols == 256 ? 8 : 4;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -128,6 +128,8 @@ def _prefill_rule(m, K, N, cus):
         rt //= 2
     if cols == 128 and 2 * tiles(rt, cols) <= cus:
         cols = 64                     # two waves, twice the tiles
+    if rt <= 2 and cols == 256 and tiles(rt, cols) > 2 * cus:
+        cols = 128                    # finer tiles for the last round
     t8 = -(-m // 256) * -(-N // 256)
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
@@ -137,7 +139,7 @@ def _prefill_rule(m, K, N, cus):
         return "decode"
     if m <= 16 and N * K >= 786432 * cus and mnb.mnb_plan_default(8, K, N, cus, 0).engine == 3:
         return "decode"
-    return rt, cols, 2 if cols == 64 else (8 if rt >= 4 and cols == 256 else 4)
+    return rt, cols, 2 if cols == 64 else (8 if cols == 256 else 4)
 
 
 def test_default_prefill_plans():
@@ -145,12 +147,14 @@ def test_default_prefill_plans():
     never more than the rows need), 256 columns, narrowed to 128 and then
     to fewer rows while the tiles would give fewer than 85% of the compute
     units one; 64 columns on two waves when the tiles would leave at least
-    half of the CUs idle; 256 x 256 LDS-staged tiles when they give 85% of
-    the CUs a tile; with more than 16 rows and at most two 32 x 32 tiles per
-    CU, those tiles with K split over four waves; otherwise with up to 16
-    rows and tiles for less than half of the CUs, or up to 16 rows over at least 768 Ki weights per CU when the 8-row
-    plan is the 4x4x4 MFMA kernel, the 8-row decode plan per 8 rows.  No
-    more workgroups than tiles."""
+    half of the CUs idle; 128 columns at one or two row tiles with more than
+    two 256-column tiles per CU; 256 columns on eight waves; 256 x 256
+    LDS-staged tiles when they give 85% of the CUs a tile; with more than
+    16 rows and at most two 32 x 32 tiles per CU, those tiles with K split
+    over four waves; otherwise with up to 16 rows and tiles for less than
+    half of the CUs, or up to 16 rows over at least 768 Ki weights per CU
+    when the 8-row plan is the 4x4x4 MFMA kernel, the 8-row decode plan per
+    8 rows.  No more workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
@@ -176,6 +180,8 @@ def test_default_prefill_plans():
                           (64, 14336, 4096, (1, 32, 4)), (128, 14336, 4096, (1, 32, 4)),
                           (24, 14336, 4096, (1, 32, 4)), (32, 4096, 6144, (1, 32, 4)),
                           (128, 4096, 6144, (1, 128, 4)), (192, 14336, 4096, (1, 128, 4)),
+                          (24, 4096, 151936, (1, 128, 4)), (64, 4096, 151936, (2, 128, 4)),
+                          (32, 4096, 65536, (1, 256, 8)), (128, 4096, 151936, (4, 256, 8)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
