@@ -267,7 +267,7 @@ def main():
         if w.name == "lm_head" and m == 1:
             result["staged_route"] = staged_route(res, stream, L)
         result["decode_step"] = decode_step(args, stream, L)
-        result["prefill"] = prefill(stream, L, cus)
+        result["prefill"] = prefill(stream, L, cus, args.rotate_mb)
         result["offline_layout"] = offline_layout(args, stream, L, cus)
 
     if not args.no_cpu_baseline:
@@ -568,10 +568,15 @@ def prefill_only(args):
                       "plan": plan.as_dict()}), flush=True)
 
 
-def prefill(stream, L, cus):
-    """Prefill heights (m > 8, the matrix-core tile kernel) on the gate_up
-    and down-projection shapes: microseconds per call and TFLOP/s against
-    the dense fp16 matrix-core peak."""
+PREFILL_HEIGHTS = {"gate_up": (512, 2048), "down": (16, 64, 512, 2048)}
+
+
+def prefill(stream, L, cus, rotate_mb):
+    """Prefill heights (m > 8) on the gate_up and down-projection shapes:
+    microseconds per call and TFLOP/s against the dense fp16 matrix-core
+    peak.  The large heights reuse one weight copy (they are bound by the
+    matrix core); the small ones, bound by the weight read, rotate over
+    enough copies that none is still cached."""
     import numpy as np
     import torch
     import block_wise_int4_matmulnbits_amd as mnb
@@ -583,26 +588,32 @@ def prefill(stream, L, cus):
         B = torch.from_numpy(d["B"]).to(dev)
         S = torch.from_numpy(d["scales"].view(np.int16)).to(dev)
         Z = torch.from_numpy(d["zp"]).to(dev)
-        for m in (512, 2048):
+        wbytes = B.numel() + 2 * S.numel() + Z.numel()
+        for m in PREFILL_HEIGHTS[name]:
             A = (torch.randn((m, K), device=dev) * 0.5).to(torch.bfloat16)
             o = torch.empty((m, N), dtype=torch.bfloat16, device=dev)
+            copies = [(B, S, Z)]
+            if m <= 64:
+                copies += [(B.clone(), S.clone(), Z.clone()) for _ in range(math.ceil(rotate_mb * 1e6 / wbytes) - 1)]
 
             def go(i):
-                st = L.matmul_nbits(A.data_ptr(), W.BF16, m, K, N, B.data_ptr(), S.data_ptr(),
-                                    Z.data_ptr(), 32, o.data_ptr(), W.BF16, stream.cuda_stream)
+                b, sc, z = copies[i % len(copies)]
+                st = L.matmul_nbits(A.data_ptr(), W.BF16, m, K, N, b.data_ptr(), sc.data_ptr(),
+                                    z.data_ptr(), 32, o.data_ptr(), W.BF16, stream.cuda_stream)
                 assert st == 0, st
             for i in range(5):
                 go(i)
-            us = event_time_us(stream, go, 20)
+            us = event_time_us(stream, go, max(20, 2 * len(copies)))
             tflops = 2.0 * m * N * K / (us * 1e-6) / 1e12
             plan = mnb.plan_for_device(m, K, N, cus)
             out["%s:m%d" % (name, m)] = {
                 "m": m, "K": K, "N": N, "us_per_call": round(us, 2), "TFLOP/s": round(tflops, 1),
                 "pct_of_fp16_mfma_peak": round(100 * tflops / PEAK_FP16_MFMA_TFLOPS, 2),
+                "weight_GB/s": round(wbytes / (us * 1e3), 1), "rotated_copies": len(copies),
                 "plan": {k: v for k, v in plan.as_dict().items()
-                         if k in ("engine", "row_tiles", "cols_per_tile", "workgroups")}}
+                         if k in ("engine", "row_tiles", "cols_per_tile", "waves_per_wg", "workgroups")}}
             log("[bench] prefill %s m=%d: %.1f us, %.1f TFLOP/s" % (name, m, us, tflops))
-            del A, o
+            del A, o, copies
     return out
 
 
