@@ -93,9 +93,9 @@ typedef enum {
  *                aligned.  Must hold finite values that are finite in fp16.
  *   a_dtype      MNB_F16 or MNB_BF16.
  *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
- *                prefill kernel, except that up to 16 rows whose prefill
- *                tiles would leave more than half of the compute units idle,
- *                and up to 16 rows over at least 768 Ki weights per compute
+ *                prefill kernel, except that up to 16 rows whose 32-column
+ *                prefill tiles would leave at least half of the compute
+ *                units idle, and up to 16 rows over at least 768 Ki weights per compute
  *                unit with K <= 16384, run the decode kernels in launches of
  *                8 rows).  m == 0 or
  *                N == 0: nothing to do, MNB_OK.

@@ -133,7 +133,8 @@ def _prefill_rule(m, K, N, cus):
     t8 = -(-m // 256) * -(-N // 256)
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
-    if m > 16 and -(-m // 32) * -(-N // 32) <= 2 * cus:
+    t32 = -(-m // 32) * -(-N // 32)
+    if (m > 16 or 2 * t32 > cus) and t32 <= 2 * cus:
         return 1, 32, 4                 # K split over four waves
     if 2 * tiles(rt, cols) < cus and m <= 16:
         return "decode"
@@ -149,9 +150,10 @@ def test_default_prefill_plans():
     units one; 64 columns on two waves when the tiles would leave at least
     half of the CUs idle; 128 columns at one or two row tiles with more than
     two 256-column tiles per CU; 256 columns on eight waves; 256 x 256
-    LDS-staged tiles when they give 85% of the CUs a tile; with more than
-    16 rows and at most two 32 x 32 tiles per CU, those tiles with K split
-    over four waves; otherwise with up to 16 rows and tiles for less than
+    LDS-staged tiles when they give 85% of the CUs a tile; with at most two
+    32 x 32 tiles per CU and either more than 16 rows or more than half of
+    the CUs given one, those tiles with K split over four waves; otherwise
+    with up to 16 rows and tiles for less than
     half of the CUs, or up to 16 rows over at least 768 Ki weights per CU
     when the 8-row plan is the 4x4x4 MFMA kernel, the 8-row decode plan per
     8 rows.  No more workgroups than tiles."""
@@ -181,6 +183,7 @@ def test_default_prefill_plans():
                           (24, 14336, 4096, (1, 32, 4)), (32, 4096, 6144, (1, 32, 4)),
                           (128, 4096, 6144, (1, 128, 4)), (192, 14336, 4096, (1, 128, 4)),
                           (24, 4096, 151936, (1, 128, 4)), (64, 4096, 151936, (2, 128, 4)),
+                          (12, 4096, 6144, (1, 32, 4)), (9, 2048, 8192, (1, 32, 4)), (16, 14336, 8192, (1, 32, 4)),
                           (32, 4096, 65536, (1, 256, 8)), (128, 4096, 151936, (4, 256, 8)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
@@ -188,6 +191,7 @@ def test_default_prefill_plans():
     # Up to 16 rows over large weights: 8-row launches of the 4x4x4 MFMA
     # kernel; 17 rows, K past 16384 or smaller weights stay on the tiles.
     for m, K, N, engine in ((9, 4096, 151936, 3), (16, 4096, 151936, 3), (16, 4096, 57344, 3),
+                            (16, 14336, 4096, 3), (12, 4096, 4096, 3), (9, 8192, 2048, 3),
                             (12, 8192, 28672, 3), (17, 4096, 151936, 2), (16, 4096, 28672, 2),
                             (16, 2048, 57344, 2), (16, 32 * 600, 57344, 2)):
         assert mnb.mnb_plan_default(m, K, N, 256, 0).engine == engine, (m, K, N)

@@ -54,6 +54,8 @@ def _gpu():
     (9, 4096, 1000, W.F16, True),       # smallest prefill height, one 16-row tile
     (16, 4096, 64, W.BF16, True),       # exactly one tile
     (17, 1024, 130, W.F16, False),      # ragged rows and columns, zero point 8
+    (12, 4096, 6144, W.BF16, True),     # K split over four waves at 12 rows
+    (9, 2048, 8200, W.F16, False),      # the same at 9 rows, ragged columns
     (100, 32 * 37, 77, W.BF16, True),   # K not a whole number of 128-wide steps
     (130, 14336, 300, W.BF16, True),    # down-projection K, row tail of 2
     (256, 4096, 1024, W.F16, True),     # several row and column blocks
