@@ -280,36 +280,23 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         }
         // Few columns: 32-row, 32-column tiles whose K four waves split,
         // while there are at most two such tiles per CU, and either more
-        // than 16 rows or more than half of the CUs get one (us, before ->
+        // than 16 rows or at least half of the CUs get one (us, before ->
         // after: down projection m = 24 57.5 -> 47.2, m = 48 101 -> 46.1, m =
         // 64 103 -> 48.3, m = 128 105 -> 92.4; 4096 x 6144 m = 32 46.7 ->
         // 17.9, m = 12 20.4 -> 16.9; 8192 x 8192 m = 12 61.0 -> 29.6; at three
-        // tiles per CU, down m = 192, 131.5 vs 135.6, the wider tiles stay).
+        // tiles per CU, down m = 192, 131.5 vs 135.6, the wider tiles stay;
+        // 8192 x 4096 m = 12 27.9 -> 22.5, 14336 x 4096 m = 16 38.8 -> 36.5).
         // Otherwise, with up to 16 rows whose tiles would leave more than
-        // half of the CUs idle (the down projection at m = 9: 32 tiles for
-        // 256 CUs), the decode kernels in launches of 8 rows (m = 9 139 ->
-        // 30.7 us, against 42.7 split).
+        // half of the CUs idle (2048 columns: 64 tiles for 256 CUs), the
+        // decode kernels in launches of 8 rows (14336 x 2048 m = 9: 24.1
+        // against 34.8 split).
         const int64_t t32 = ceil_div(m, 32) * ceil_div(N, 32);
-        const bool split = (m > 2 * MNB_MAX_M || 2 * t32 > (int64_t)num_cus) && t32 <= 2 * (int64_t)num_cus;
+        const bool split = (m > 2 * MNB_MAX_M || 2 * t32 >= (int64_t)num_cus) && t32 <= 2 * (int64_t)num_cus;
         if (split) {
             rt = 1;
             cols = 32;
         } else if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 2 * MNB_MAX_M) {
             return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
-        }
-        // Up to 16 rows over at least 768 Ki weights per CU: below 32 rows
-        // the tiles' cost is their dequantization whatever m, and two 8-row
-        // launches of the 4x4x4 MFMA kernel, which scales whole blocks'
-        // sums instead of every weight, cost less (us, prefill -> decode:
-        // 151936 x 4096 m = 9 242 -> 158, m = 16 247 -> 179; 57344 x 4096
-        // m = 16 90 -> 79; 28672 x 8192 m = 16 103 -> 79; kept at 28672 x
-        // 4096, m = 12 45 vs 47).
-        if (!split && m <= 2 * MNB_MAX_M && (uint64_t)N * (uint64_t)K >= (uint64_t)786432 * (uint64_t)num_cus) {
-            mnb_plan p8;
-            if (mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, &p8) == MNB_OK && p8.engine == 3) {
-                *plan = p8;
-                return MNB_OK;
-            }
         }
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
         int64_t wgs = per_cu * num_cus;

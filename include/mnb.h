@@ -94,9 +94,8 @@ typedef enum {
  *   a_dtype      MNB_F16 or MNB_BF16.
  *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
  *                prefill kernel, except that up to 16 rows whose 32-column
- *                prefill tiles would leave at least half of the compute
- *                units idle, and up to 16 rows over at least 768 Ki weights per compute
- *                unit with K <= 16384, run the decode kernels in launches of
+ *                prefill tiles would leave more than half of the compute
+ *                units idle run the decode kernels in launches of
  *                8 rows).  m == 0 or
  *                N == 0: nothing to do, MNB_OK.
  *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).

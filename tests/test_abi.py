@@ -134,11 +134,9 @@ def _prefill_rule(m, K, N, cus):
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
     t32 = -(-m // 32) * -(-N // 32)
-    if (m > 16 or 2 * t32 > cus) and t32 <= 2 * cus:
+    if (m > 16 or 2 * t32 >= cus) and t32 <= 2 * cus:
         return 1, 32, 4                 # K split over four waves
     if 2 * tiles(rt, cols) < cus and m <= 16:
-        return "decode"
-    if m <= 16 and N * K >= 786432 * cus and mnb.mnb_plan_default(8, K, N, cus, 0).engine == 3:
         return "decode"
     return rt, cols, 2 if cols == 64 else (8 if cols == 256 else 4)
 
@@ -151,12 +149,10 @@ def test_default_prefill_plans():
     half of the CUs idle; 128 columns at one or two row tiles with more than
     two 256-column tiles per CU; 256 columns on eight waves; 256 x 256
     LDS-staged tiles when they give 85% of the CUs a tile; with at most two
-    32 x 32 tiles per CU and either more than 16 rows or more than half of
+    32 x 32 tiles per CU and either more than 16 rows or at least half of
     the CUs given one, those tiles with K split over four waves; otherwise
-    with up to 16 rows and tiles for less than
-    half of the CUs, or up to 16 rows over at least 768 Ki weights per CU
-    when the 8-row plan is the 4x4x4 MFMA kernel, the 8-row decode plan per
-    8 rows.  No more workgroups than tiles."""
+    with up to 16 rows and tiles for less than half of the CUs, the 8-row
+    decode plan per 8 rows.  No more workgroups than tiles."""
     for m, K, N in PREFILL_SHAPES:
         for cus, occ in ((1, 0), (256, 0), (256, 2), (304, 1)):
             p = mnb.mnb_plan_default(m, K, N, cus, occ)
@@ -188,12 +184,12 @@ def test_default_prefill_plans():
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
-    # Up to 16 rows over large weights: 8-row launches of the 4x4x4 MFMA
-    # kernel; 17 rows, K past 16384 or smaller weights stay on the tiles.
-    for m, K, N, engine in ((9, 4096, 151936, 3), (16, 4096, 151936, 3), (16, 4096, 57344, 3),
-                            (16, 14336, 4096, 3), (12, 4096, 4096, 3), (9, 8192, 2048, 3),
-                            (12, 8192, 28672, 3), (17, 4096, 151936, 2), (16, 4096, 28672, 2),
-                            (16, 2048, 57344, 2), (16, 32 * 600, 57344, 2)):
+    # Up to 16 rows: 8-row launches of the decode kernels only where the
+    # 32-column tiles would leave more than half of the CUs idle.
+    for m, K, N, engine in ((9, 4096, 151936, 2), (16, 4096, 151936, 2), (16, 4096, 57344, 2),
+                            (16, 14336, 4096, 2), (12, 4096, 4096, 2), (9, 8192, 2048, 3),
+                            (16, 14336, 2048, 3), (12, 8192, 28672, 2), (17, 4096, 151936, 2),
+                            (16, 4096, 28672, 2), (16, 2048, 57344, 2), (16, 32 * 600, 57344, 2)):
         assert mnb.mnb_plan_default(m, K, N, 256, 0).engine == engine, (m, K, N)
 
 
