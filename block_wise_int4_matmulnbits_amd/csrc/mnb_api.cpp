@@ -261,13 +261,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // columns stay ahead, since the narrower tiles convert each
         // activation for half as many columns (gate_up m = 16: 45.8 vs 49.3).
         if (cols == 128 && 2 * tiles(rt, cols) <= (int64_t)num_cus) cols = 64;
-        // One or two row tiles with more than two full-width tiles per CU:
-        // 128 columns, whose finer tiles end the last round sooner (lm_head
-        // 4096 x 151936, us: m = 24 252 -> 217, m = 64 292 -> 258; 2048 x
-        // 151936 m = 64 143 -> 120).  With at most two per CU the 256
-        // columns stay, on eight waves (4096 x 65536 m = 32: 88.3 against
-        // 94.3 at 128 columns and 96.2 on four waves of 64).
-        if (rt <= 2 && cols == 256 && tiles(rt, cols) > 2 * (int64_t)num_cus) cols = 128;
+        // One or two row tiles: 128 columns on four waves rather than 256 on
+        // eight; the finer tiles end the last round sooner (K = 4096, m =
+        // 24, us: 65536 columns 64.6 -> 58.7, 81920 110.3 -> 80.7, 131072
+        // 122.9 -> 106.5, 151936 166.4 -> 131.1; level at 57344 and at
+        // 8192 x 100000).
+        if (rt <= 2 && cols == 256) cols = 128;
         // 256 x 256 tiles with the weights staged through LDS when they give
         // at least 85% of the CUs a tile (gate_up, interleaved A/B against
         // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
