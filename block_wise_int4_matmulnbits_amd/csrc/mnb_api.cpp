@@ -267,6 +267,14 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // 122.9 -> 106.5, 151936 166.4 -> 131.1; level at 57344 and at
         // 8192 x 100000).
         if (rt <= 2 && cols == 256) cols = 128;
+        // One row tile whose tiles overflow one round where two row tiles
+        // fit in it: two, since a tile's cost is mostly its dequantization
+        // (us, one -> two row tiles: down projection m = 384 154.6 -> 99.6;
+        // 4096 x 6144 m = 192 44.7 -> 32.1, m = 256 46.0 -> 32.9).  Not four:
+        // those tiles cost more (4096 x 6144 m = 384 57.7 against 51.0).
+        if (rt == 1 && m > 32 && tiles(1, cols) > (int64_t)num_cus && tiles(2, cols) <= (int64_t)num_cus &&
+            (uint64_t)64 * 2 * (uint64_t)K <= mnb::kPrefillRowBlockBytes)
+            rt = 2;
         // 256 x 256 tiles with the weights staged through LDS when they give
         // at least 85% of the CUs a tile (gate_up, interleaved A/B against
         // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
