@@ -132,6 +132,8 @@ def _prefill_rule(m, K, N, cus):
         cols = 128                    # finer tiles for the last round
     if rt == 1 and m > 32 and tiles(1, cols) > cus and tiles(2, cols) <= cus and 128 * K <= 0xFFFFFFF0:
         rt = 2                        # one round of taller tiles
+    if rt == 4 and cols == 128 and tiles(4, 128) > cus and tiles(4, 256) <= cus:
+        cols = 256                    # one round of wider tiles
     t8 = -(-m // 256) * -(-N // 256)
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
@@ -150,7 +152,8 @@ def test_default_prefill_plans():
     units one; 64 columns on two waves when the tiles would leave at least
     half of the CUs idle; 128 columns at one or two row tiles; two row
     tiles where one would overflow a round and two fit in it; 256 columns
-    on eight waves; 256 x 256
+    at four row tiles where 128 would overflow a round and 256 fit in it;
+    256 columns on eight waves; 256 x 256
     LDS-staged tiles when they give 85% of the CUs a tile; with at most two
     32 x 32 tiles per CU and either more than 16 rows or at least half of
     the CUs given one, those tiles with K split over four waves; otherwise
@@ -184,7 +187,9 @@ def test_default_prefill_plans():
                           (24, 4096, 151936, (1, 128, 4)), (64, 4096, 151936, (2, 128, 4)),
                           (12, 4096, 6144, (1, 32, 4)), (9, 2048, 8192, (1, 32, 4)), (16, 14336, 8192, (1, 32, 4)),
                           (32, 4096, 65536, (1, 128, 4)), (384, 14336, 4096, (2, 128, 4)),
-                          (192, 4096, 6144, (2, 128, 4)), (256, 4096, 6144, (2, 128, 4)), (128, 4096, 151936, (4, 256, 8)),
+                          (192, 4096, 6144, (2, 128, 4)), (256, 4096, 6144, (2, 128, 4)),
+                          (1152, 4096, 4096, (4, 256, 8)), (768, 4096, 6144, (4, 256, 8)),
+                          (320, 14336, 14336, (4, 256, 8)), (384, 4096, 6144, (2, 128, 4)), (128, 4096, 151936, (4, 256, 8)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
