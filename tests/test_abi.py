@@ -137,6 +137,8 @@ def _prefill_rule(m, K, N, cus):
     t8 = -(-m // 256) * -(-N // 256)
     if m > 128 and 100 * t8 >= 85 * cus and 512 * K <= 0xFFFFFFF0:
         rt, cols = 8, 256
+    elif m > 128 and rt == 4 and cols == 256 and tiles(4, 256) > cus and t8 <= cus and 512 * K <= 0xFFFFFFF0:
+        rt = 8                        # one round of 256 x 256 tiles
     t32 = -(-m // 32) * -(-N // 32)
     if (m > 16 or 2 * t32 >= cus) and t32 <= 2 * cus:
         return 1, 32, 4                 # K split over four waves
@@ -153,7 +155,8 @@ def test_default_prefill_plans():
     half of the CUs idle; 128 columns at one or two row tiles; two row
     tiles where one would overflow a round and two fit in it; 256 columns
     at four row tiles where 128 would overflow a round and 256 fit in it;
-    256 columns on eight waves; 256 x 256
+    256 columns on eight waves; 256 x 256 tiles where 128 x 256 tiles would
+    overflow a round and they fit in it; 256 x 256
     LDS-staged tiles when they give 85% of the CUs a tile; with at most two
     32 x 32 tiles per CU and either more than 16 rows or at least half of
     the CUs given one, those tiles with K split over four waves; otherwise
@@ -189,7 +192,9 @@ def test_default_prefill_plans():
                           (32, 4096, 65536, (1, 128, 4)), (384, 14336, 4096, (2, 128, 4)),
                           (192, 4096, 6144, (2, 128, 4)), (256, 4096, 6144, (2, 128, 4)),
                           (1152, 4096, 4096, (4, 256, 8)), (768, 4096, 6144, (4, 256, 8)),
-                          (320, 14336, 14336, (4, 256, 8)), (384, 4096, 6144, (2, 128, 4)), (128, 4096, 151936, (4, 256, 8)),
+                          (320, 14336, 14336, (4, 256, 8)), (384, 4096, 6144, (2, 128, 4)),
+                          (2176, 14336, 4096, (8, 256, 8)), (2048, 14336, 4096, (4, 256, 8)),
+                          (1536, 4096, 6144, (8, 256, 8)), (640, 4096, 14336, (8, 256, 8)), (128, 4096, 151936, (4, 256, 8)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
