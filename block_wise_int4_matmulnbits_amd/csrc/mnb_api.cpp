@@ -302,6 +302,17 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
             // 152.7 -> 113.8; 26 of 26 such shapes 17-25% faster).
             rt = 8;
         }
+        // 256 x 256 tiles against 128 x 256 ones by rounds of tiles over the
+        // CUs: a 256 x 256 tile holds a CU for one unit, a 128 x 256 tile
+        // (two per CU) for 0.625 (half the rows, 25% less efficient per
+        // row).  This picks the faster of the two on each of 26 shapes where
+        // the last 256-row block wastes at least 10% of its rows (us: 4096 x
+        // 14336 m = 1152 253.9 -> 178.7; lm_head 4096 x 151936 m = 384 722.1
+        // -> 624.0; kept at m = 640, 1064.7 against 1076.2), and on every
+        // earlier tall measurement (gate_up m = 384, 1024, 2048 and 4096 stay
+        // on 256 x 256).
+        if (rt == 8 && 5 * ceil_div(ceil_div(m, 128) * ceil_div(N, 256), num_cus) < 8 * ceil_div(t8, num_cus))
+            rt = 4;
         // Few columns: 32-row, 32-column tiles whose K four waves split,
         // while there are at most two such tiles per CU, and either more
         // than 16 rows or at least half of the CUs get one (us, before ->

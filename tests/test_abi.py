@@ -139,6 +139,8 @@ def _prefill_rule(m, K, N, cus):
         rt, cols = 8, 256
     elif m > 128 and rt == 4 and cols == 256 and tiles(4, 256) > cus and t8 <= cus and 512 * K <= 0xFFFFFFF0:
         rt = 8                        # one round of 256 x 256 tiles
+    if rt == 8 and 5 * -(-(-(-m // 128) * -(-N // 256)) // cus) < 8 * -(-t8 // cus):
+        rt = 4                        # fewer rounds of 128 x 256 tiles
     t32 = -(-m // 32) * -(-N // 32)
     if (m > 16 or 2 * t32 >= cus) and t32 <= 2 * cus:
         return 1, 32, 4                 # K split over four waves
@@ -156,7 +158,8 @@ def test_default_prefill_plans():
     tiles where one would overflow a round and two fit in it; 256 columns
     at four row tiles where 128 would overflow a round and 256 fit in it;
     256 columns on eight waves; 256 x 256 tiles where 128 x 256 tiles would
-    overflow a round and they fit in it; 256 x 256
+    overflow a round and they fit in it, and 128 x 256 tiles where they take
+    fewer rounds at 0.625 of a 256 x 256 tile each; 256 x 256
     LDS-staged tiles when they give 85% of the CUs a tile; with at most two
     32 x 32 tiles per CU and either more than 16 rows or at least half of
     the CUs given one, those tiles with K split over four waves; otherwise
@@ -194,7 +197,9 @@ def test_default_prefill_plans():
                           (1152, 4096, 4096, (4, 256, 8)), (768, 4096, 6144, (4, 256, 8)),
                           (320, 14336, 14336, (4, 256, 8)), (384, 4096, 6144, (2, 128, 4)),
                           (2176, 14336, 4096, (8, 256, 8)), (2048, 14336, 4096, (4, 256, 8)),
-                          (1536, 4096, 6144, (8, 256, 8)), (640, 4096, 14336, (8, 256, 8)), (128, 4096, 151936, (4, 256, 8)),
+                          (1536, 4096, 6144, (8, 256, 8)), (640, 4096, 14336, (8, 256, 8)),
+                          (384, 4096, 151936, (4, 256, 8)), (640, 4096, 151936, (8, 256, 8)),
+                          (1152, 4096, 14336, (4, 256, 8)), (1024, 4096, 28672, (8, 256, 8)), (128, 4096, 151936, (4, 256, 8)),
                           (256, 14336, 4096, (1, 128, 4)), (1024, 14336, 4096, (4, 128, 4))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)

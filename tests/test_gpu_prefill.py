@@ -63,6 +63,7 @@ def _gpu():
     (40, 4096, 65536, W.F16, True),     # 128-column tiles at two row tiles, many rounds
     (1152, 1024, 4096, W.BF16, True),   # 256 columns kept at four row tiles: one round
     (640, 512, 14336, W.F16, True),     # one round of 256 x 256 tiles, not two of 128 x 256
+    (1152, 512, 14336, W.BF16, True),   # 128 x 256 tiles: two rounds where 256 x 256 take two of more work
 ])
 def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
