@@ -10,10 +10,21 @@ follows the definition on the onnx-genai pages "perf(cuda): let the split-K
 decode GEMV store bf16 directly" and "PORT-1 (offline bias+interleave)").
 This module only builds that file with gcc and marshals numpy arrays.
 
-Every function here is pinned by ``tests/test_oracle_pins.py``: hand-derived
-closed forms (``tests/golden/hand_cases.json``), exhaustive checks of the
-rounding routines against numpy/torch, an exact-integer recomputation of the
-sums, and invariants.  No function is "parity unpinned".
+Every output is pinned by ``tests/test_oracle_pins.py`` against something
+other than the oracle itself:
+  * ``f16``/``bf16``/``f64``: hand-derived closed forms
+    (``tests/golden/hand_cases.json``), exhaustive checks of the rounding
+    routines against numpy/torch, an exact-integer recomputation of the sums,
+    brute force with a closed form, and invariants;
+  * ``abs`` (the sum of |a*w|, which scales the first acceptance check):
+    hand-derived values, the exact-integer sum of |a|*|q-z|*|s|, and the
+    brute-force closed form;
+  * ``f16_ulp`` (the other term of that check): every one of the 65,536 fp16
+    patterns against the gap to the next pattern of larger magnitude and
+    against numpy's spacing, plus a hand table.
+``tests/test_oracle_mutations.py`` plants 21 plausible mistakes in a copy of
+this package, one at a time, and checks that each fails a pin.  No function
+is "parity unpinned".
 """
 from __future__ import annotations
 

@@ -15,6 +15,15 @@ def pytest_configure(config):
 
 @pytest.fixture(scope="session")
 def oracle_mod():
+    # MNB_ORACLE_ROOT names a directory holding another copy of the oracle
+    # package (the mutation test plants one mistake in such a copy and runs
+    # the pins against it).
+    alt = os.environ.get("MNB_ORACLE_ROOT")
+    if alt:
+        sys.path.insert(0, alt)
     import oracle
+    if alt:
+        assert os.path.dirname(os.path.dirname(os.path.abspath(oracle.__file__))) == \
+            os.path.abspath(alt), oracle.__file__
     oracle.build(force=False)
     return oracle

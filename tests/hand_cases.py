@@ -62,6 +62,7 @@ def build_case(c):
     scales = sh.view(np.uint16).reshape(N, nb)
     exp16 = np.array([[_int(v) for v in row] for row in c["expected_f16"]], np.uint16)
     expbf = np.array([[_int(v) for v in row] for row in c["expected_bf16"]], np.uint16)
+    absum = np.array(c["abs"], np.float64) if "abs" in c else None
     return dict(m=m, K=K, N=N, A=A, a_is_bf16=a_is_bf16, B=B, scales=scales,
                 zp=zp, value=np.array(c["value"], np.float64), f16=exp16,
-                bf16=expbf)
+                bf16=expbf, abs=absum)

@@ -33,6 +33,8 @@ def test_hand_case(oracle_mod, case):
     assert np.array_equal(r["f64"], c["value"]), (r["f64"], c["value"])
     assert np.array_equal(r["f16"], c["f16"]), [hex(x) for x in r["f16"].ravel()]
     assert np.array_equal(r["bf16"], c["bf16"]), [hex(x) for x in r["bf16"].ravel()]
+    if c["abs"] is not None:
+        assert np.array_equal(r["abs"], c["abs"]), r["abs"]
 
 
 # ------------------------------------------------------ rounding, exhaustive
@@ -125,9 +127,10 @@ def test_exact_rounding_helper_matches_numpy():
         assert _exact_f16_bits(S, 53 - int(e)) == np.float16(v).view(np.uint16)
 
 
-def _exact_sums(A_bits, a_is_bf16, B, scales, zp, m, K, N, oracle_mod):
+def _exact_sums(A_bits, a_is_bf16, B, scales, zp, m, K, N, oracle_mod, magnitudes=False):
     """Exact sums as Python ints in units of 2^-48.  fp16 values are integer
-    multiples of 2^-24, so a*(q-z)*s is an integer multiple of 2^-48."""
+    multiples of 2^-24, so a*(q-z)*s is an integer multiple of 2^-48.  With
+    ``magnitudes`` the sums of |a*(q-z)*s| instead."""
     nb = K // 32
     if a_is_bf16:
         # activations: bf16 -> fp16 by numpy (float32 widening then RNE)
@@ -147,6 +150,8 @@ def _exact_sums(A_bits, a_is_bf16, B, scales, zp, m, K, N, oracle_mod):
         z[:, 1::2] = zp >> 4
         z = z[:, :nb]
     d = (q.reshape(N, nb, 32) - z[:, :, None])                       # q - z
+    if magnitudes:
+        a_int, d, s_int = np.abs(a_int), np.abs(d), np.abs(s_int)
     inner = np.einsum("rbk,nbk->rnb", a_int.reshape(m, nb, 32), d)   # < 2^50
     out = np.empty((m, N), dtype=object)
     for r in range(m):
@@ -178,6 +183,74 @@ def test_oracle_equals_exact_rounding(oracle_mod, m, K, N, bf16, asym, seed):
     assert np.all(np.abs(r["f64"] - exact) <= K * 2.0 ** -53 * r["abs"] + 1e-300)
 
 
+# ------------------------------------------ the two inputs of check 1's bound
+# Check 1 accepts |y_gpu - y_oracle| <= 1e-3 * sum_k |a_k w_k| + 1 fp16 ulp of
+# y_oracle.  Both terms of the bound come from the oracle, so both are pinned
+# here against statements that do not go through it.
+
+def test_f16_ulp_every_pattern(oracle_mod):
+    """One fp16 ulp at y (2^(max(floor(log2|y|), -14) - 10)) is the gap from
+    |y| to the next fp16 number of larger magnitude, read off the bit
+    patterns (consecutive patterns of one sign are consecutive numbers).  The
+    largest finite value, whose successor is infinity, takes the gap below it
+    (same binade).  Non-finite values get an infinite ulp."""
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = oracle_mod.f16_ulp(h)
+    mag = h & np.uint16(0x7FFF)
+    finite = mag < 0x7C00
+    val = lambda b: b.astype(np.uint16).view(np.float16).astype(np.float64)
+    up = mag < 0x7BFF
+    want = np.full(h.shape, np.inf)
+    want[up] = val(mag[up] + 1) - val(mag[up])
+    top = mag == 0x7BFF
+    want[top] = val(mag[top]) - val(mag[top] - 1)
+    assert np.array_equal(got[finite], want[finite])
+    assert np.all(np.isinf(got[~finite]))
+    # numpy's spacing of |y| (the distance to the next larger fp16) agrees
+    with np.errstate(over="ignore"):
+        sp = np.spacing(np.abs(h[up].view(np.float16))).astype(np.float64)
+    assert np.array_equal(got[up], sp)
+
+
+@pytest.mark.parametrize("bits,ulp", [
+    (0x0000, 2.0 ** -24), (0x8000, 2.0 ** -24), (0x0001, 2.0 ** -24),
+    (0x03FF, 2.0 ** -24), (0x0400, 2.0 ** -24), (0x07FF, 2.0 ** -24),
+    (0x0800, 2.0 ** -23), (0x3BFF, 2.0 ** -11), (0x3C00, 2.0 ** -10),
+    (0xBC00, 2.0 ** -10), (0x3C01, 2.0 ** -10), (0x4000, 2.0 ** -9),
+    (0x5B80, 0.125), (0x7BFF, 32.0), (0x7C00, np.inf), (0xFC00, np.inf),
+    (0x7E00, np.inf)])
+def test_f16_ulp_hand_table(oracle_mod, bits, ulp):
+    """By hand: subnormals and the first binade share 2^-24; 1.0 and its
+    neighbours above 2^-10, just below 1.0 2^-11; 240 (0x5B80) lies in
+    [128, 256), ulp 2^(7-10); 65504 lies in [32768, 65536), ulp 32."""
+    assert oracle_mod.f16_ulp(np.array([bits], np.uint16))[0] == ulp
+
+
+@pytest.mark.parametrize("m,K,N,bf16,asym,seed", [
+    (1, 1024, 48, False, False, 0),
+    (2, 2048, 40, False, True, 1),
+    (3, 96, 33, True, True, 2),
+    (8, 4096, 8, True, True, 3),
+])
+def test_oracle_abs_equals_exact_magnitudes(oracle_mod, m, K, N, bf16, asym, seed):
+    """The oracle's sum of |a*w| against the exact integer sum of
+    |a|*|q-z|*|s| (units of 2^-48): every term is positive, so the fp64 sum
+    is within (K-1) u of it, and the exact value rounded to fp64 within u."""
+    from block_wise_int4_matmulnbits_amd import workloads
+    d = workloads.generate(m, K, N, workloads.BF16 if bf16 else workloads.F16,
+                           asym, 0.002, 0.02, 1.0, seed)
+    A = d["A"][:m]
+    r = oracle_mod.matmul_nbits(A, bf16, d["B"], d["scales"], d["zp"], m, K, N)
+    ex = _exact_sums(A, bf16, d["B"], d["scales"], d["zp"], m, K, N, oracle_mod,
+                     magnitudes=True)
+    exact = np.array([[float(ex[i, j]) * 2.0 ** -48 for j in range(N)]
+                      for i in range(m)])
+    assert np.all(exact > 0)
+    assert np.all(np.abs(r["abs"] - exact) <= (K + 1) * 2.0 ** -53 * exact)
+    # and never below |y|, with equality only when all products share a sign
+    assert np.all(r["abs"] >= np.abs(r["f64"]))
+
+
 # ------------------------------------------------------- structured brute force
 def test_brute_force_uniform_blocks(oracle_mod):
     """K=64, N<=4, each (column, block) holds one nibble value from {0, 15},
@@ -203,6 +276,10 @@ def test_brute_force_uniform_blocks(oracle_mod):
         blocksum = a.reshape(nb, 32).sum(axis=1)
         want = ((qv - zv) * sv * blocksum[None, :]).sum(axis=1)
         assert np.array_equal(r["f64"][0], want)
+        # sum of |a w| in closed form: |q - z| s per block times sum |a|
+        magsum = np.abs(a).reshape(nb, 32).sum(axis=1)
+        want_abs = (np.abs(qv - zv) * sv * magsum[None, :]).sum(axis=1)
+        assert np.array_equal(r["abs"][0], want_abs)
         assert np.array_equal(r["f16"][0], want.astype(np.float16).view(np.uint16))
 
 
@@ -356,10 +433,12 @@ def test_fp16_weights_match_numpy_float16(oracle_mod, m, K, N, asym, seed):
     w = w.astype(np.float64)
     for i in range(m):
         for n in range(N):
-            acc = 0.0
+            acc = mag = 0.0
             for k in range(K):
                 acc += a[i, k] * w[n, k]
+                mag += abs(a[i, k] * w[n, k])
             assert r["f64"][i, n] == acc
+            assert r["abs"][i, n] == mag
             assert r["f16"][i, n] == np.float64(acc).astype(np.float16).view(np.uint16)
 
 
