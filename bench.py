@@ -139,7 +139,6 @@ class Resident:
 def plan_fields(plan):
     """The fields of a decode plan that its engine reads."""
     keys = {0: ("lanes_per_col", "blocks_per_lane", "cols_per_tile", "workgroups"),
-            1: ("waves_per_wg", "chunk_blocks", "cols_per_tile", "workgroups"),
             3: ("waves_per_wg", "blocks_per_lane", "cols_per_tile", "workgroups")}
     d = plan.as_dict()
     return dict({"engine": d["engine"]}, **{k: d[k] for k in keys.get(d["engine"], ())})

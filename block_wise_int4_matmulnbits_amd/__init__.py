@@ -46,7 +46,6 @@ class mnb_plan(ctypes.Structure):
                 ("blocks_per_lane", ctypes.c_int32),
                 ("cols_per_tile", ctypes.c_int32),
                 ("waves_per_wg", ctypes.c_int32),
-                ("chunk_blocks", ctypes.c_int32),
                 ("workgroups", ctypes.c_int32),
                 ("interleave", ctypes.c_int32),
                 ("threads_per_wg", ctypes.c_int32),

@@ -1,7 +1,7 @@
 """Build libmnb.so for gfx950 in-tree.
 
-hipcc compiles the kernels (mnb_gemv.hip, mnb_gemv_mfma.hip,
-mnb_gemv_mfma4.hip, mnb_gemm_mfma.hip, mnb_layout.hip); the host front end
+hipcc compiles the kernels (mnb_gemv.hip, mnb_gemv_mfma4.hip,
+mnb_gemm_mfma.hip, mnb_layout.hip); the host front end
 (mnb_api.cpp) is plain C++ built with g++; hipcc links both into one shared
 library next to this file.
 """
@@ -41,7 +41,7 @@ def build(verbose: bool = False, save_temps: bool = False) -> str:
     extra = ["-save-temps=obj"] if save_temps else []
     objs = []
     jobs = []
-    for name in ("mnb_gemv", "mnb_gemv_mfma", "mnb_gemv_mfma4", "mnb_gemm_mfma", "mnb_layout"):
+    for name in ("mnb_gemv", "mnb_gemv_mfma4", "mnb_gemm_mfma", "mnb_layout"):
         obj = os.path.join(BUILD, name + ".o")
         objs.append(obj)
         jobs.append(["hipcc", "-c", os.path.join(CSRC, name + ".hip"), "-o", obj]

@@ -158,9 +158,6 @@ int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap
 
 extern "C" {
 
-// LDS for staged activations of the MFMA engine: m * chunk_blocks * 64 bytes.
-constexpr int64_t kMfmaStageBytes = 128 * 1024;
-
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
 {
     if (!plan || m < 1 || m > MNB_MAX_ROWS || K < 0 || K % 32 || N < 0) return MNB_ERR_PLAN;
@@ -187,17 +184,6 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     // as launches of MNB_MAX_M rows (the last one fewer) under this plan, so
     // the plan must fit MNB_MAX_M rows.
     if (m > MNB_MAX_M) m = MNB_MAX_M;
-    if (plan->engine == 1) {
-        const int64_t w = plan->waves_per_wg, kcb = plan->chunk_blocks;
-        if (w < 1 || w > 8 || kcb < 4 || kcb % 4 || m * kcb * 64 > kMfmaStageBytes)
-            return MNB_ERR_PLAN;
-        if (plan->cols_per_tile != 16) return MNB_ERR_PLAN;
-        plan->threads_per_wg = (int32_t)(64 * w);
-        const int64_t chunks = nb == 0 ? 1 : ceil_div(nb, kcb);
-        if (chunks > INT32_MAX) return MNB_ERR_PLAN;
-        plan->k_chunks = (int32_t)chunks;
-        return MNB_OK;
-    }
     if (plan->engine == 3) {
         // 4x4x4 MFMA kernel: the workgroup's 16 * waves lane groups cover K
         // in one pass, blocks_per_lane blocks each; 4 or 8 columns per tile.
@@ -443,7 +429,6 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     plan->blocks_per_lane = (int32_t)bpl;
     plan->cols_per_tile = (int32_t)nc;
     plan->waves_per_wg = 0;
-    plan->chunk_blocks = 0;
     plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
     plan->interleave = 1;
     return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;

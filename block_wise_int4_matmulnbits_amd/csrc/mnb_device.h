@@ -1,5 +1,5 @@
-// Device helpers shared by the gfx950 GEMV kernels (lane-split dot2 kernel
-// and MFMA tile kernel).  Internal header: HIP device code only.
+// Device helpers shared by the gfx950 GEMV kernels.  Internal header: HIP
+// device code only.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -8,6 +8,8 @@
 namespace mnb {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Weights, scales and zero points are read exactly once per call: stream
@@ -116,6 +118,65 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
     r[1] = s01[1];
     r[2] = s23[0];
     r[3] = s23[1];
+}
+
+// Activations of one 32-weight block (four 16-byte pieces of fp16 or bf16,
+// k = 0..31) as fp16 pairs in the order the unpack yields the weights:
+// (a_e, a_e+4) per 8 k for natural weights, (a_2e, a_2e+1) for the even/odd
+// layout.  bf16 is rounded to fp16 (RNE).
+__device__ __forceinline__ void activation_pairs(const u32x4 (&raw)[4], int a_bf16, int eo_pairs,
+                                                 uint32_t (&act)[16])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t x = raw[i][0], y = raw[i][1], z = raw[i][2], w = raw[i][3];
+        if (a_bf16) {
+            x = bf16x2_to_f16x2(x);
+            y = bf16x2_to_f16x2(y);
+            z = bf16x2_to_f16x2(z);
+            w = bf16x2_to_f16x2(w);
+        }
+        if (eo_pairs) {
+            act[4 * i + 0] = x;
+            act[4 * i + 1] = y;
+            act[4 * i + 2] = z;
+            act[4 * i + 3] = w;
+        } else {
+            act[4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
+            act[4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
+            act[4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
+            act[4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
+        }
+    }
+}
+
+// v plus the value of lane (i - 4n) mod 16 of its 16-lane row (n = 1, 2):
+// lanes that share i mod 4 (one column of a 4x4x4 product) stay together.
+template <int CTRL>
+__device__ __forceinline__ float row_ror_add(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lane groups (of four lanes) of a wave of the value held by
+// lane (g, i): two rotations inside each 16-lane row, then the rows exchanged
+// with v_permlane32_swap and v_permlane16_swap.  Every lane ends with the
+// total of its column lane i, in an order that depends only on g.
+__device__ __forceinline__ float column_sum(float v)
+{
+    v = row_ror_add<0x124>(v);   // row_ror:4
+    v = row_ror_add<0x128>(v);   // row_ror:8
+    const uint32_t u = __float_as_uint(v);
+    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);   // (rows 0-1, rows 2-3) per lane
+    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const uint32_t w = __float_as_uint(v);
+    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);   // (even row, odd row) per lane
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ half4_t as_half4(uint32_t lo, uint32_t hi)
+{
+    return __builtin_bit_cast(half4_t, (uint32_t __attribute__((ext_vector_type(2)))){lo, hi});
 }
 
 // Raw buffer resources (gfx9 layout: 48-bit base, no stride, num_records

@@ -616,7 +616,6 @@ KernelFn lookup(int64_t m, int64_t K, const mnb_plan& plan)
 
 int launch_gemv(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    if (plan.engine == 1) return launch_mfma(a, plan, stream);
     if (plan.engine == 2) return launch_gemm(a, plan, stream);
     if (plan.engine == 3) return launch_mfma4(a, plan, stream);
     KernelFn fn = lookup(a.m, a.K, plan);
@@ -707,7 +706,6 @@ int occupancy(const void* fn, int threads, size_t lds) { return cached_occupancy
 
 int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 {
-    if (plan.engine == 1) return mfma_workgroups_per_cu(m, plan);
     if (plan.engine == 2) return gemm_workgroups_per_cu(plan);
     if (plan.engine == 3) return mfma4_workgroups_per_cu(m, N, plan);
     KernelFn fn = lookup(m, K, plan);
@@ -719,7 +717,6 @@ int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 
 int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
 {
-    if (plan.engine == 1) return mfma_kernel_info(m, plan, info);
     if (plan.engine == 2) return gemm_kernel_info(plan, info);
     if (plan.engine == 3) return mfma4_kernel_info(m, plan, info);
     KernelFn fn = lookup(m, K, plan);

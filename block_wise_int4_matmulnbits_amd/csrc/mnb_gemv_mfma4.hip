@@ -22,15 +22,20 @@
 // Work decomposition.  A workgroup of W waves owns a contiguous range of
 // column quads and walks it NC quads at a time.  Lane (g, i) of a wave (group
 // g = lane / 4) holds column 4n + i of each quad n and, as the A side, rows i
-// and 4 + i of the activations; group gg = 16 * wave + g owns K blocks
-// gg, gg + 16W, ..., BPL of them, which together cover all of K in one pass.
-// The lane's activations are loaded once, converted to fp16, permuted into
-// the unpack's pair order and kept in VGPRs.  Per block and column the lane
-// loads its 16 bytes of weights (the four lanes of a group read four
-// columns, the sixteen groups of a wave 256 contiguous bytes of each),
-// unpacks them to the exact fp16 integers q - z, and per row quad eight
-// chained MFMAs give the block's exact 4 x 4 product, which one FMA per row
-// scales into the lane's fp32 accumulators.  Partial sums meet through a
+// and 4 + i of the activations.  Wave w owns the 16 BPL consecutive K blocks
+// from 16 BPL w, and its group g the blocks 16 BPL w + 16 j + g (j < BPL);
+// together the waves cover all of K in one pass.  The lane's activations are
+// loaded once, converted to fp16, permuted into the unpack's pair order and
+// kept in VGPRs.  Per block and column the lane loads its 16 bytes of
+// weights (the four lanes of a group read four columns, the sixteen groups
+// of a wave 256 contiguous bytes of each).  A wave's scales and zero points
+// of a column are one contiguous run, read as whole dwords (full lines, any
+// alignment of the arrays) and handed to the lanes through a small
+// wave-private LDS stage: one 2- and one 1-byte load per lane and block had
+// cost a load-only copy of this kernel 1.9 us on the down projection.  The
+// lane unpacks its weights to the exact fp16 integers q - z, and per row
+// quad eight chained MFMAs give the block's exact 4 x 4 product, which one
+// FMA per row scales into the lane's fp32 accumulators.  Partial sums meet through a
 // fixed tree inside the wave (two DPP row rotations, then the rows swapped by
 // v_permlane32_swap and v_permlane16_swap) and a wave-ordered sum in LDS, so
 // the summation order depends only on (K, W, BPL).
@@ -43,9 +48,6 @@
 
 namespace mnb {
 namespace {
-
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 struct Mfma4Params {
     const uint16_t* A;       // [m][K]
@@ -61,36 +63,7 @@ struct Mfma4Params {
                              // yields (k, k+1) pairs, activations keep their order
 };
 
-// v plus the value of lane (i - 4n) mod 16 of its 16-lane row (n = 1, 2):
-// lanes that share i mod 4 (one column) stay together.
-template <int CTRL>
-__device__ __forceinline__ float row_ror_add(float v)
-{
-    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lane groups of a wave of the value held by lane (g, i):
-// two rotations inside each 16-lane row, then the rows exchanged with
-// v_permlane32_swap and v_permlane16_swap.  Lane (0, i) ends with the total
-// of column lane i, in an order that depends only on g.
-__device__ __forceinline__ float column_sum(float v)
-{
-    v = row_ror_add<0x124>(v);   // row_ror:4
-    v = row_ror_add<0x128>(v);   // row_ror:8
-    const uint32_t u = __float_as_uint(v);
-    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);   // (rows 0-1, rows 2-3) per lane
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const uint32_t w = __float_as_uint(v);
-    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);   // (even row, odd row) per lane
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-__device__ __forceinline__ half4_t as_half4(uint32_t lo, uint32_t hi)
-{
-    return __builtin_bit_cast(half4_t, (uint32_t __attribute__((ext_vector_type(2)))){lo, hi});
-}
-
-// RQ row quads (m <= 4 * RQ), BPL blocks per group, NC column quads per
+// RQ row quads (m <= 4 * RQ), BPL blocks per lane group, NC column quads per
 // tile.  The tile loop is straight-line code, two tiles per pass: each wave
 // leaves its totals of the pass's two tiles in LDS, and one barrier, the
 // sums over waves and another barrier close the pass.
@@ -98,18 +71,27 @@ template <int RQ, int BPL, int NC>
 __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 {
     constexpr int NV = 16 * NC * RQ;        // results of one tile (columns x rows)
+    constexpr int NCOL = 4 * NC;            // columns of a tile
+    constexpr int DS = 8 * BPL + 1;         // dwords covering a wave's 16 BPL scales of a column
+    constexpr int DZ = 2 * BPL + 1;         // dwords covering its 16 BPL zero-point nibbles
+    constexpr int SD = (NCOL * DS + 63) / 64;   // scale dwords loaded per lane and tile
+    constexpr int ZD = (NCOL * DZ + 63) / 64;   // zero-point dwords loaded per lane and tile
     __shared__ float part[2][8][NV];        // per-wave totals of a pass's two tiles
+    __shared__ uint32_t stage[8][64 * (SD + ZD)];   // a wave's scales and zero points of one tile
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int W = (int)(blockDim.x >> 6);
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int W = (int)(blockDim.x >> 6);
     const int qi = lane & 3, g = lane >> 2;
-    const uint32_t gg = (uint32_t)(wv * 16 + g);
-    const uint32_t GT = (uint32_t)(16 * W);
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const uint32_t row_bytes = (uint32_t)p.K / 2;
-    const int zshift = (g & 1) * 4;         // block parity == group parity (GT even)
+    // Wave wv owns the 16 BPL consecutive blocks from B0; lane group g takes
+    // blocks B0 + 16 j + g (j < BPL), so each load instruction of a wave reads
+    // 256 contiguous bytes of each of four columns, and a wave's scales (and
+    // zero points) of a column are one contiguous run.
+    const uint32_t B0 = (uint32_t)(16 * BPL * wv);
+    const int zshift = (g & 1) * 4;         // block parity == group parity (B0 even)
     const uint32_t zdef = p.zp ? 0u : 8u;   // zero point 8 when none are given
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
 
@@ -127,7 +109,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
-            const uint32_t b = (uint32_t)j * GT + gg;
+            const uint32_t b = B0 + 16 * (uint32_t)j + (uint32_t)g;
             const uint32_t base = (uint32_t)(4 * rq + qi) * (uint32_t)p.K * 2 + 64 * b;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -136,53 +118,75 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 
     struct Tile {
         u32x4 w[NC][BPL];
-        uint32_t sc[NC][BPL];   // fp16 scale in the low half (the load zero-extends)
-        uint32_t zq[NC][BPL];
+        uint32_t sd[SD];   // whole dwords covering the wave's scales of the tile's columns
+        uint32_t zd[ZD];   // and its zero points
     };
-    // Per-lane offsets of this lane's blocks within a tile's column rows,
-    // fixed for the kernel (the tile moves the buffer base): out of range
-    // past K, so every load below is issued unconditionally.
-    uint32_t ow[NC][BPL], os[NC][BPL], oz[NC][BPL];
+    // Scales and zero points are read as whole dwords from 4-byte-aligned
+    // resource bases (ms, mz: how far the arrays start past such a boundary;
+    // tiles advance the bases by multiples of 4 bytes, so these stay fixed).
+    // Lane L loads dword L % D of column L / D of the tile's runs (D = DS or
+    // DZ), in full lines rather than one 2- or 1-byte load per block.
+    const uint32_t ms = (uint32_t)((uintptr_t)p.scales & 3);
+    const uint32_t mz = p.zp ? (uint32_t)((uintptr_t)p.zp & 3) : 0u;
+    uint32_t ow[NC][BPL], osd[SD], ozd[ZD];
 #pragma unroll
     for (int n = 0; n < NC; ++n) {
         const uint32_t col = (uint32_t)(4 * n + qi);
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
-            const uint32_t b = (uint32_t)j * GT + gg;
-            const bool ok = b < nb;
-            ow[n][j] = ok ? col * row_bytes + 16 * b : kOutOfRange;
-            os[n][j] = ok ? (col * nb + b) * 2 : kOutOfRange;
-            oz[n][j] = ok ? col * zb + (b >> 1) : kOutOfRange;
+            const uint32_t b = B0 + 16 * (uint32_t)j + (uint32_t)g;
+            ow[n][j] = b < nb ? col * row_bytes + 16 * b : kOutOfRange;
         }
     }
+#pragma unroll
+    for (int k = 0; k < SD; ++k) {
+        const uint32_t item = 64 * (uint32_t)k + (uint32_t)lane, c = item / DS, kk = item % DS;
+        osd[k] = c < NCOL ? ((ms + c * nb * 2 + B0 * 2) & ~3u) + 4 * kk : kOutOfRange;
+    }
+#pragma unroll
+    for (int k = 0; k < ZD; ++k) {
+        const uint32_t item = 64 * (uint32_t)k + (uint32_t)lane, c = item / DZ, kk = item % DZ;
+        ozd[k] = c < NCOL ? ((mz + c * zb + B0 / 2) & ~3u) + 4 * kk : kOutOfRange;
+    }
+    // Where this lane finds its own scale and zero point of column 4n + qi,
+    // block B0 + 16 j + g, in the wave's stage (bytes; + 32 j and + 8 j).
+    uint32_t sread[NC], zread[NC];
+#pragma unroll
+    for (int n = 0; n < NC; ++n) {
+        const uint32_t c = (uint32_t)(4 * n + qi);
+        sread[n] = 4 * c * DS + ((ms + c * nb * 2 + B0 * 2) & 3u) + 2 * (uint32_t)g;
+        zread[n] = 4 * (64 * SD + c * DZ) + ((mz + c * zb + B0 / 2) & 3u) + (uint32_t)g / 2;
+    }
+
     // Loads of the next tile of this workgroup (NC column quads).  Tiles are
     // issued in column order, so the bases of the three buffer resources
     // advance by fixed strides and the columns left count down; the
     // resources end at the workgroup's last column (zeros past it, without
     // touching memory), and a tile past q_stop gets empty ones.
     const uint8_t* next_B = p.B + 4 * q_first * (int64_t)row_bytes;
-    const uint16_t* next_S = p.scales + 4 * q_first * (int64_t)nb;
-    const uint8_t* next_Z = p.zp ? p.zp + 4 * q_first * (int64_t)zb : p.B;
+    const uint8_t* next_S = reinterpret_cast<const uint8_t*>(p.scales + 4 * q_first * (int64_t)nb) - ms;
+    const uint8_t* next_Z = p.zp ? p.zp + 4 * q_first * (int64_t)zb - mz : p.B;
     int64_t left = c_stop - 4 * q_first;
     auto issue = [&](Tile& t) {
-        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 4 * NC ? left : 4 * NC);
+        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < NCOL ? left : NCOL);
         const __amdgpu_buffer_rsrc_t rB = make_rsrc(next_B, (uint64_t)ncols * row_bytes);
-        const __amdgpu_buffer_rsrc_t rS = make_rsrc(next_S, (uint64_t)ncols * nb * 2);
-        const __amdgpu_buffer_rsrc_t rZ = make_rsrc(next_Z, p.zp ? (uint64_t)ncols * zb : 0);
+        const __amdgpu_buffer_rsrc_t rS = make_rsrc(next_S, ncols ? (ms + (uint64_t)ncols * nb * 2 + 3) & ~3ull : 0);
+        const __amdgpu_buffer_rsrc_t rZ = make_rsrc(next_Z, p.zp && ncols ? (mz + (uint64_t)ncols * zb + 3) & ~3ull : 0);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
 #pragma unroll
-            for (int j = 0; j < BPL; ++j) {
+            for (int j = 0; j < BPL; ++j)
                 t.w[n][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow[n][j], 0, kNontemporal);
-                t.sc[n][j] = __builtin_amdgcn_raw_buffer_load_b16(rS, os[n][j], 0, kNontemporal);
-                t.zq[n][j] = __builtin_amdgcn_raw_buffer_load_b8(rZ, oz[n][j], 0, kNontemporal);
-            }
+#pragma unroll
+        for (int k = 0; k < SD; ++k) t.sd[k] = __builtin_amdgcn_raw_buffer_load_b32(rS, osd[k], 0, kNontemporal);
+#pragma unroll
+        for (int k = 0; k < ZD; ++k) t.zd[k] = __builtin_amdgcn_raw_buffer_load_b32(rZ, ozd[k], 0, kNontemporal);
         if (left > 0) {   // uniform; past the end the bases stay put
-            next_B += 4 * NC * (int64_t)row_bytes;
-            next_S += 4 * NC * (int64_t)nb;
-            if (p.zp) next_Z += 4 * NC * (int64_t)zb;
+            next_B += NCOL * (int64_t)row_bytes;
+            next_S += NCOL * (int64_t)nb * 2;
+            if (p.zp) next_Z += NCOL * (int64_t)zb;
         }
-        left -= 4 * NC;
+        left -= NCOL;
     };
 
     Tile ring[2];
@@ -196,37 +200,29 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 #pragma unroll
     for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-        for (int j = 0; j < BPL; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t x = raw[rq][j][i][0], y = raw[rq][j][i][1], z = raw[rq][j][i][2], w = raw[rq][j][i][3];
-                if (p.a_bf16) {
-                    x = bf16x2_to_f16x2(x);
-                    y = bf16x2_to_f16x2(y);
-                    z = bf16x2_to_f16x2(z);
-                    w = bf16x2_to_f16x2(w);
-                }
-                if (p.eo_pairs) {
-                    act[rq][j][4 * i + 0] = x;
-                    act[rq][j][4 * i + 1] = y;
-                    act[rq][j][4 * i + 2] = z;
-                    act[rq][j][4 * i + 3] = w;
-                } else {
-                    act[rq][j][4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
-                    act[rq][j][4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
-                    act[rq][j][4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
-                    act[rq][j][4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
-                }
-            }
+        for (int j = 0; j < BPL; ++j) activation_pairs(raw[rq][j], p.a_bf16, p.eo_pairs, act[rq][j]);
 
     // Per block: the exact products of each row quad in one 4x4 result
     // (eight chained MFMAs over the block's 32 k), then acc += D * s.
     auto compute = [&](const Tile& t, float4_t (&acc)[NC][RQ]) {
+        // The tile's scale and zero-point dwords into the wave's stage, then
+        // each lane's own (the wave's DS operations run in order).
+        uint32_t* st = stage[wv];
+#pragma unroll
+        for (int k = 0; k < SD; ++k) st[64 * k + lane] = t.sd[k];
+#pragma unroll
+        for (int k = 0; k < ZD; ++k) st[64 * (SD + k) + lane] = t.zd[k];
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(st);
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
             ZeroPoint zp[BPL];
+            float sf[BPL];
 #pragma unroll
-            for (int j = 0; j < BPL; ++j) zp[j] = zero_point_pairs(((t.zq[n][j] >> zshift) & 0xFu) | zdef);
+            for (int j = 0; j < BPL; ++j) {
+                const uint32_t zq = sb[zread[n] + 8 * j];
+                zp[j] = zero_point_pairs(((zq >> zshift) & 0xFu) | zdef);
+                sf[j] = (float)*reinterpret_cast<const _Float16*>(sb + sread[n] + 32 * j);
+            }
             float4_t dsum[BPL][RQ];
 #pragma unroll
             for (int j = 0; j < BPL; ++j)
@@ -251,13 +247,11 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
                                 as_half4(pr[j][2 * h], pr[j][2 * h + 1]), dsum[j][rq], 0, 0, 0);
             }
 #pragma unroll
-            for (int j = 0; j < BPL; ++j) {
-                const float sf = (float)__builtin_bit_cast(_Float16, (uint16_t)t.sc[n][j]);
+            for (int j = 0; j < BPL; ++j)
 #pragma unroll
                 for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[n][rq][r] = fmaf(dsum[j][rq][r], sf, acc[n][rq][r]);
-            }
+                    for (int r = 0; r < 4; ++r) acc[n][rq][r] = fmaf(dsum[j][rq][r], sf[j], acc[n][rq][r]);
         }
     };
 

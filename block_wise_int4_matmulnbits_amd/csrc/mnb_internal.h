@@ -23,11 +23,6 @@ struct GemvArgs {
 // hipError_t of the launch (0 on success).  Dispatches on plan.engine.
 int launch_gemv(const GemvArgs& args, const mnb_plan& plan, void* stream);
 
-// The MFMA tile kernel (engine 1), mnb_gemv_mfma.hip.
-int launch_mfma(const GemvArgs& args, const mnb_plan& plan, void* stream);
-int mfma_workgroups_per_cu(int64_t m, const mnb_plan& plan);
-int mfma_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
-
 // The 4x4x4 MFMA kernel (engine 3), mnb_gemv_mfma4.hip: W waves per
 // workgroup whose 16 W lane groups cover K in one pass (16 W * blocks_per_lane
 // >= K/32), cols_per_tile = 4 or 8.  No dynamic LDS.

@@ -31,7 +31,7 @@
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 3
+#define MNB_ABI_VERSION 4
 
 /* Element types of A and of the output. */
 typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
@@ -134,10 +134,6 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * column; each lane owns blocks_per_lane 32-weight blocks of K per chunk and
  * keeps their activations in VGPRs; columns are walked cols_per_tile at a
  * time.  Dot products on v_dot2_f32_f16.
- * engine 1 (MFMA tile kernel): a wave owns 16 columns; the waves_per_wg
- * waves of a workgroup split K; activations are staged in LDS,
- * chunk_blocks blocks of K per pass; dot products on
- * v_mfma_f32_16x16x32_f16.  Up to 8 rows per launch.
  * engine 2 (prefill kernel, m > 8): a workgroup owns a tile of
  * 32 * row_tiles rows by cols_per_tile columns, split by columns over its
  * waves: waves_per_wg = 2 with 64 columns, 4 with 128 or 256, or 8 with
@@ -157,16 +153,14 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * blocks_per_lane >= K/32 (so K <= 16384).
  */
 typedef struct {
-    int32_t engine;          /* 0: lane-split dot2 kernel; 1: MFMA tile kernel;
-                                2: prefill kernel; 3: 4x4x4 MFMA kernel         */
+    int32_t engine;          /* 0: lane-split dot2 kernel; 2: prefill kernel;
+                                3: 4x4x4 MFMA kernel                            */
     int32_t lanes_per_col;   /* engine 0: 16, 32, 64 (one wave) or 64*W, W=2..8 */
     int32_t blocks_per_lane; /* engine 0: 1, 2, 4 or 8; engine 3: 1, 2 or 4     */
-    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 1: 16;
-                                engine 2: 32, 64, 128 or 256; engine 3: 4 or 8 (4 with
-                                blocks_per_lane 4 when m > 4)                   */
-    int32_t waves_per_wg;    /* engine 1: 1..8 waves splitting K; engine 2: 2, 4, 8;
-                                engine 3: 1..8                                  */
-    int32_t chunk_blocks;    /* engine 1: K blocks staged per pass, multiple of 4 */
+    int32_t cols_per_tile;   /* engine 0: 1, 2, 4 or 8; engine 2: 32, 64, 128 or
+                                256; engine 3: 4 or 8 (4 with blocks_per_lane 4
+                                when m > 4)                                     */
+    int32_t waves_per_wg;    /* engine 2: 2, 4, 8; engine 3: 1..8               */
     int32_t workgroups;      /* grid size, >= 1                                  */
     int32_t interleave;      /* engine 0: 0 = each lane group takes one contiguous
                                 range of columns, 1 = column tiles dealt to the
@@ -174,7 +168,7 @@ typedef struct {
     int32_t threads_per_wg;  /* derived by mnb_plan_check                        */
     int32_t k_chunks;        /* derived: passes over K                           */
     int32_t row_tiles;       /* engine 2: 32-row tiles per workgroup, 1, 2 or 4  */
-    int32_t b_layout;        /* MNB_LAYOUT_* of Bpacked; engines 1 and 2 take
+    int32_t b_layout;        /* MNB_LAYOUT_* of Bpacked; engine 2 takes
                                 MNB_LAYOUT_NATURAL only                         */
 } mnb_plan;
 
@@ -188,7 +182,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
                      mnb_plan* plan);
 
 /* Validate a plan for (m, K, N) and fill its derived fields
- * (threads_per_wg, k_chunks).  A decode plan (engines 0, 1, 3) must fit 8
+ * (threads_per_wg, k_chunks).  A decode plan (engines 0 and 3) must fit 8
  * rows; with m > 8 the call runs it once per 8 rows (the last launch
  * fewer).
  * Host-only.  Returns MNB_OK or MNB_ERR_PLAN. */

@@ -251,8 +251,8 @@ def test_plan_check_engines_and_rows():
     d2 = mnb.mnb_plan(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=4, workgroups=1)
     assert mnb.mnb_plan_check(4, 4096, 100, d2) == 0
     assert mnb.mnb_plan_check(9, 4096, 100, d2) == 9           # 8 rows x 2 blocks > 8
-    e1 = mnb.mnb_plan(engine=1, cols_per_tile=16, waves_per_wg=4, chunk_blocks=128, workgroups=1)
-    assert mnb.mnb_plan_check(9, 4096, 100, e1) == 0
+    e1 = mnb.mnb_plan(engine=1, cols_per_tile=16, waves_per_wg=4, workgroups=1)
+    assert mnb.mnb_plan_check(4, 4096, 100, e1) == 9            # no engine 1
     e3 = mnb.mnb_plan(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=8, workgroups=1)
     assert mnb.mnb_plan_check(4, 14336, 100, e3) == 0
     assert mnb.mnb_plan_check(40, 14336, 100, e3) == 9         # 8 rows: registers
@@ -331,7 +331,6 @@ def test_repack_validation_without_gpu(args, status):
 def test_plan_layouts():
     """The even/odd layout is read by engines 0 and 3 only."""
     for eng, fields in ((0, dict(lanes_per_col=64, blocks_per_lane=2, cols_per_tile=2)),
-                        (1, dict(cols_per_tile=16, waves_per_wg=4, chunk_blocks=128)),
                         (2, dict(row_tiles=1, cols_per_tile=128, waves_per_wg=4)),
                         (3, dict(waves_per_wg=4, blocks_per_lane=2, cols_per_tile=4))):
         for layout in (0, 1, 2):

@@ -56,7 +56,7 @@ def effective_plan(m, K, N, plan=None):
 
 
 def launch_rows(m, K, N, plan=None):
-    """Rows per launch of a call: decode plans (engines 0, 1, 3) serve at
+    """Rows per launch of a call: decode plans (engines 0 and 3) serve at
     most 8 rows per launch."""
     if effective_plan(m, K, N, plan).get("engine", 0) == 2 or m <= 8:
         return [m]
@@ -226,40 +226,6 @@ def test_multiwave_groups_deferred_and_per_tile_sums(oracle_mod):
             assert np.array_equal(y2, y16)
 
 
-def test_mfma_engine_ragged(oracle_mod):
-    """The MFMA tile kernel for every m, ragged K and N, one to eight waves
-    per workgroup, K staged in one or several LDS chunks."""
-    cases = [
-        # m, K, N, waves, chunk_blocks, workgroups
-        (1, 4096, 1000, 4, 128, 7),
-        (2, 32 * 37, 33, 1, 4, 2),
-        (3, 32 * 37, 100, 8, 40, 3),
-        (4, 14336, 257, 8, 256, 5),
-        (5, 1024, 16, 2, 32, 1),
-        (6, 32 * 611, 70, 8, 80, 4),
-        (7, 96, 31, 3, 4, 2),
-        (8, 14336, 300, 8, 128, 9),
-        (8, 4096, 4096, 8, 128, 64),
-        (2, 14336, 100, 8, 448, 3),
-        (6, 32 * 611, 45, 8, 64, 2),
-    ]
-    for i, (m, K, N, w, kcb, wg) in enumerate(cases):
-        d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i % 3 != 1, 0.002, 0.02, 1.0, 300 + i)
-        plan = dict(engine=1, cols_per_tile=16, waves_per_wg=w, chunk_blocks=kcb, workgroups=wg)
-        assert_parity(oracle_mod, d, m, "mfma", plan)
-
-
-def test_mfma_engine_rows_match_single_row_calls():
-    """Under one MFMA plan, row r of an m-row launch is bit-identical to a
-    one-row launch on row r."""
-    d = W.generate(8, 14336, 200, W.BF16, True, 0.001, 0.01, 0.5, 310)
-    plan = dict(engine=1, cols_per_tile=16, waves_per_wg=8, chunk_blocks=128, workgroups=13)
-    y8, _ = run(d, 8, W.BF16, plan)
-    for r in (0, 3, 7):
-        y1, _ = run(dict(d, A=d["A"][r:r + 1]), 1, W.BF16, plan)
-        assert np.array_equal(y1[0], y8[r])
-
-
 # ------------------------------------------------------------ edge shapes
 def test_k_zero_gives_zeros():
     d = W.generate(2, 0, 40, W.F16, True, 0.002, 0.02, 1.0, 30)
@@ -400,6 +366,31 @@ def test_mfma4_engine_rows_and_columns_match():
     shard = dict(d, B=d["B"][lo:hi], scales=d["scales"][lo:hi], zp=d["zp"][lo:hi], N=hi - lo)
     ys, _ = run(shard, 8, W.BF16, dict(plan, workgroups=4))
     assert np.array_equal(ys, y8[:, lo:hi])
+
+
+def test_mfma4_engine_any_scale_and_zero_point_alignment():
+    """Scales and zero points are read as whole dwords from 4-byte-aligned
+    bases: arrays starting 2 bytes (scales) or 1 to 3 bytes (zero points)
+    past a 4-byte boundary give the bits of aligned ones, on a ragged K
+    (an odd number of blocks per column) and ragged N."""
+    m, K, N = 5, 32 * 299, 37
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 455)
+    plan = dict(engine=3, waves_per_wg=5, blocks_per_lane=4, cols_per_tile=4, workgroups=3)
+    A, B, S, Z = G.to_dev(d, m)
+    ref = G.new_out(m, N, W.BF16)
+    mnb.matmul_nbits_planned(A, B, S, Z, ref, plan)
+    for ms, mz in ((2, 0), (0, 1), (2, 2), (0, 3), (2, 3)):
+        sbuf = torch.zeros(S.numel() + 4, dtype=torch.float16, device="cuda")
+        zbuf = torch.zeros(Z.numel() + 4, dtype=torch.uint8, device="cuda")
+        S2 = sbuf[ms // 2: ms // 2 + S.numel()].view(S.shape)
+        Z2 = zbuf[mz: mz + Z.numel()].view(Z.shape)
+        S2.copy_(S)
+        Z2.copy_(Z)
+        assert S2.data_ptr() % 4 == ms and Z2.data_ptr() % 4 == mz
+        out = G.new_out(m, N, W.BF16)
+        mnb.matmul_nbits_planned(A, B, S2, Z2, out, plan)
+        torch.cuda.synchronize()
+        assert np.array_equal(G.bits(out), G.bits(ref)), (ms, mz)
 
 
 def test_mfma4_engine_k_zero():
