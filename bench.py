@@ -11,13 +11,17 @@ is resident in HBM before the timed region starts.
 
 Prints one JSON line.  value = algorithmic bytes per call / time per call
 (GB/s); roofline.traffic comes from the committed rocprofv3 counter summary
-for the current kernel source (null if the kernel changed since).
+(profiles/hbm_traffic.json) for the current kernel sources (null if any of
+them changed since).
 
 Besides the headline figure the line carries (skipped with --no-extras):
   attainable   a read-only streaming kernel over the same bytes (the in-repo
                probe): what one launch of this size can pull from HBM;
-  workloads    microseconds per call of the other synthetic shapes (the
-               4096x4096, gate_up and down-projection rows at m = 2, 4, 8);
+  configs      every synthetic configuration in its own output type(s):
+               microseconds per call (median and range of 5 timed passes),
+               algorithmic GB/s and fraction of 8 TB/s, the plan, VGPRs and
+               occupancy, and the rocprofv3 kernel time and FETCH_SIZE
+               fraction of the committed profile;
   staged_route the fp16 GEMV followed by a separate fp16 -> bf16 cast launch,
                against the direct bf16 store (bits compared);
   decode_step  a decode step of GEMVs (4 layers of q/k/v/o, gate_up and down,
@@ -43,26 +47,37 @@ METRIC = "m=1 INT4 GEMV achieved HBM GB/s (% of MI355X peak) and µs/call"
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_VALU_TFLOPS = 157.3
 PEAK_FP16_MFMA_TFLOPS = 2500.0
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lm_head_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+# The synthetic configurations: workload, rows, output types.
+CONFIGS = [("tiny_1k", 1, ("f16",)), ("asym_4k", 1, ("f16",)), ("gate_up_bf16", 1, ("bf16",)),
+           ("down_rows_bf16", 2, ("bf16",)), ("down_rows_bf16", 4, ("bf16",)),
+           ("down_rows_bf16", 8, ("bf16",)), ("lm_head", 1, ("f16", "bf16"))]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def measured_traffic(workload_name, m):
-    """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel source, workload and row count."""
+def measured_profile(workload_name, m, out_dtype):
+    """The committed rocprofv3 record of one configuration (kernel time,
+    FETCH_SIZE and WRITE_SIZE bytes per launch), if it was taken on the
+    current kernel sources; else None."""
     from block_wise_int4_matmulnbits_amd import profiling
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if (t.get("kernel_src_sha256_16") != profiling.kernel_source_hash()
-            or t.get("workload") != workload_name or t.get("m") != m):
+    if t.get("kernel_src_sha256_16") != profiling.kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    return t.get("configs", {}).get("%s:%d:%s" % (workload_name, m, out_dtype))
+
+
+def measured_traffic(workload_name, m, out_dtype="bf16"):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, copy-calibrated) of a
+    configuration from the committed profile, or None."""
+    e = measured_profile(workload_name, m, out_dtype)
+    return None if e is None else e["fetch_bytes"] + e["write_bytes"]
 
 
 def parse():
@@ -78,7 +93,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="headline GEMV only (profiling runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="seconds of whole oracle calls on every usable core")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="only run torch's device copy of this many MiB "
                          "(reference kernel for scaling HBM counters)")
@@ -252,7 +268,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
             "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-            "traffic": measured_traffic(w.name, m),
+            "traffic": measured_traffic(w.name, m, args.out_dtype),
         },
         "cpu_baseline": None,
     }
@@ -262,7 +278,7 @@ def main():
         if att:
             result["roofline"]["attainable"] = att
             result["roofline"]["frac_of_attainable"] = round(gbs / att["gbs"], 4)
-        result["workloads"] = other_workloads(args, stream, cus)
+        result["configs"] = decode_configs(args, stream, cus)
         if w.name == "lm_head" and m == 1:
             result["staged_route"] = staged_route(res, stream, L)
         result["decode_step"] = decode_step(args, stream, L)
@@ -308,40 +324,63 @@ def attainable(res, stream, cus):
             "kernel": "read probe, unroll %d, %d workgroups/CU" % (best[1], best[2])}
 
 
-def other_workloads(args, stream, cus):
-    """Microseconds per call of the other synthetic shapes (default plans,
-    rotated copies, bf16 output)."""
+def decode_configs(args, stream, cus, passes=5):
+    """Every synthetic configuration in its own output type(s), default
+    plan, rotated weight copies (the 1024 x 1024 one stays cache-resident):
+    microseconds per call as the median and range of `passes` timed passes,
+    algorithmic GB/s, the plan, VGPRs and occupancy, and the committed
+    rocprofv3 kernel time and FETCH_SIZE fraction when they were taken on
+    the current sources."""
     import block_wise_int4_matmulnbits_amd as mnb
     from block_wise_int4_matmulnbits_amd import workloads as W
     out = {}
     L = mnb.lib()
     shared = {}
-    for name, m in (("tiny_1k", 1), ("asym_4k", 1), ("gate_up_bf16", 1),
-                    ("down_rows_bf16", 2), ("down_rows_bf16", 4), ("down_rows_bf16", 8)):
+    for name, m, odts in CONFIGS:
         w = W.WORKLOADS[name]
         if name not in shared:
             shared.clear()
-            shared[name] = W.generate_workload(w, w.m_max or w.m)
-        res = Resident(w, m, W.BF16, 0 if name == "tiny_1k" else args.rotate_mb, d=shared[name])
-        raw = res.raw(stream.cuda_stream)
+            shared[name] = W.generate_workload(w, max(w.m_max, 8) if name == "down_rows_bf16" else w.m)
+        for odt in odts:
+            res = Resident(w, m, W.BF16 if odt == "bf16" else W.F16,
+                           0 if name == "tiny_1k" else args.rotate_mb, d=shared[name])
+            raw = res.raw(stream.cuda_stream)
 
-        def go(i):
-            L.matmul_nbits(*raw[i % len(raw)])
-        for i in range(200):
-            go(i)
-        n = max(200, int(0.1 / (res.bytes_per_call / 5e12)))
-        us = event_time_us(stream, go, n)
-        plan = mnb.plan_for_device(m, w.K, w.N, cus)
-        gbs = res.bytes_per_call / (us * 1e-6) / 1e9
-        e = {"m": m, "K": w.K, "N": w.N, "us_per_call": round(us, 3), "GB/s": round(gbs, 1),
-             "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
-             "rotated_copies": res.R, "plan": plan_fields(plan)}
-        if m > 1:
-            flops = 2.0 * m * w.N * w.K
-            e["fp32_valu_floor_us"] = round(flops / (PEAK_FP32_VALU_TFLOPS * 1e12) * 1e6, 3)
-        out["%s:m%d" % (name, m)] = e
-        log("[bench] %s m=%d: %.3f us/call, %.1f GB/s" % (name, m, us, gbs))
-        del res
+            def go(i):
+                st = L.matmul_nbits(*raw[i % len(raw)])
+                if st != 0:
+                    raise mnb.MnbError(st, L)
+            for i in range(200):
+                go(i)
+            n = max(200, int(0.05 / (res.bytes_per_call / 5e12)))
+            samples = sorted(event_time_us(stream, go, n) for _ in range(passes))
+            us = samples[len(samples) // 2]
+            plan = mnb.plan_for_device(m, w.K, w.N, cus)
+            info = mnb.mnb_get_kernel_info(m, w.K, plan)
+            gbs = res.bytes_per_call / (us * 1e-6) / 1e9
+            e = {"m": m, "K": w.K, "N": w.N, "out_dtype": odt, "bytes_per_call": res.bytes_per_call,
+                 "us_per_call": round(us, 3), "us_min": round(samples[0], 3), "us_max": round(samples[-1], 3),
+                 "passes": passes, "calls_per_pass": n,
+                 "GB/s": round(gbs, 1), "frac_of_8TBs": round(gbs / PEAK_HBM_GBS, 4),
+                 "rotated_copies": res.R, "plan": plan_fields(plan),
+                 "vgprs": info["vgprs"], "wgs_per_cu": info["wgs_per_cu"],
+                 "waves_per_cu": info["wgs_per_cu"] * plan.threads_per_wg // 64,
+                 "lds_bytes": info["lds_bytes"]}
+            if m > 1:
+                flops = 2.0 * m * w.N * w.K
+                e["fp32_valu_floor_us"] = round(flops / (PEAK_FP32_VALU_TFLOPS * 1e12) * 1e6, 3)
+            prof = measured_profile(name, m, odt)
+            if prof is not None:
+                e["rocprof"] = {k: prof[k] for k in ("kernel_mean_us", "fetch_bytes", "write_bytes",
+                                                     "fetch_over_alg", "alg_frac_of_8TBs",
+                                                     "fetch_frac_of_8TBs")}
+            else:
+                e["rocprof"] = None
+            out["%s:m%d:%s" % (name, m, odt)] = e
+            log("[bench] %s m=%d %s: %.3f us/call (%.3f-%.3f), %.1f GB/s = %.1f%% of 8 TB/s, %s, %d VGPRs, "
+                "%d waves/CU" % (name, m, odt, us, samples[0], samples[-1], gbs, 100 * gbs / PEAK_HBM_GBS,
+                                 plan_fields(plan), info["vgprs"], e["waves_per_cu"]))
+            del res
     return out
 
 
@@ -616,10 +655,20 @@ def prefill(stream, L, cus, rotate_mb):
     return out
 
 
+def oracle_threads():
+    """Host cores the oracle may use: the process's CPU affinity, capped by
+    OMP_NUM_THREADS where the environment sets it (the GPU machine gives each
+    GPU a 16-core share and sets it so)."""
+    cores = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    return (min(cores, int(cap)) if cap.isdigit() and int(cap) > 0 else cores), cores
+
+
 def cpu_baseline(args, w, d, m, A, copy0, out_dtype, bytes_per_call):
-    """The oracle, as it stands, timed on the host cores over whole calls of
-    the same workload for about --cpu-seconds; also checks copy 0 of the GPU
-    output against it."""
+    """The oracle, as it stands, timed on the host over whole calls of the
+    same workload: on every usable core for about --cpu-seconds, and on one
+    thread for three calls; the median call time of each.  Also checks
+    copy 0 of the GPU output against it."""
     import numpy as np
     import torch
 
@@ -627,17 +676,25 @@ def cpu_baseline(args, w, d, m, A, copy0, out_dtype, bytes_per_call):
     import oracle
     from block_wise_int4_matmulnbits_amd import workloads as W
 
-    threads = oracle.max_threads()
-    n, t0 = 0, time.perf_counter()
-    while True:
-        ref = oracle.matmul_nbits(d["A"][:m], w.a_dtype == W.BF16, d["B"], d["scales"],
-                                  d["zp"], m, w.K, w.N, threads=threads)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= args.cpu_seconds:
-            break
-    cpu_gbs = n * bytes_per_call / el / 1e9
-    log("[bench] oracle: %d calls in %.1f s on %d threads = %.3f GB/s" % (n, el, threads, cpu_gbs))
+    threads, affinity = oracle_threads()
+
+    def timed_calls(nthreads, seconds, min_calls):
+        times, ref = [], None
+        t_start = time.perf_counter()
+        while len(times) < min_calls or time.perf_counter() - t_start < seconds:
+            t0 = time.perf_counter()
+            ref = oracle.matmul_nbits(d["A"][:m], w.a_dtype == W.BF16, d["B"], d["scales"],
+                                      d["zp"], m, w.K, w.N, threads=nthreads)
+            times.append(time.perf_counter() - t0)
+        return sorted(times), ref
+
+    t_all, ref = timed_calls(threads, args.cpu_seconds, 3)
+    t_one, _ = timed_calls(1, 0.0, 3)
+    med_all, med_one = t_all[len(t_all) // 2], t_one[len(t_one) // 2]
+    gbs_all, gbs_one = bytes_per_call / med_all / 1e9, bytes_per_call / med_one / 1e9
+    log("[bench] oracle: %d calls on %d threads, median %.1f ms = %.3f GB/s; 1 thread: median %.1f ms "
+        "= %.4f GB/s (%d cores in the affinity mask)"
+        % (len(t_all), threads, med_all * 1e3, gbs_all, med_one * 1e3, gbs_one, affinity))
     # parity of the timed configuration's output (copy 0)
     B, S, Z = copy0
     y16 = torch.empty((m, w.N), dtype=torch.float16, device=A.device)
@@ -650,16 +707,37 @@ def cpu_baseline(args, w, d, m, A, copy0, out_dtype, bytes_per_call):
     g = g16.view(np.float16).astype(np.float64)
     o = ref["f16"].view(np.float16).astype(np.float64)
     ulp = oracle.f16_ulp(ref["f16"])
-    ok1 = bool(np.all(np.abs(g - o) <= 1e-3 * ref["abs"] + ulp))
+    err = np.abs(g - o)
+    ok1 = bool(np.all(err <= 1e-3 * ref["abs"] + ulp))
     ok2 = bool(np.array_equal(gbf, oracle.f16_to_bf16(g16.ravel()).reshape(g16.shape)))
+    ulps = err / ulp
+    worst = np.unravel_index(int(np.argmax(ulps)), ulps.shape)
+    # Outputs off by more than one fp16 ulp are sums with heavy cancellation:
+    # |y| is a small fraction of sum |a w|, so the fp32 accumulation error
+    # (relative to sum |a w|) is many ulps of y, still far inside check 1.
+    off = ulps > 1
     parity = {"check1": ok1, "check2_bf16_bit_exact": ok2,
-              "max_err_fp16_ulp": float(np.max(np.abs(g - o) / ulp)),
-              "bit_equal_frac": float(np.mean(g16 == ref["f16"]))}
+              "max_err_fp16_ulp": float(ulps.max()),
+              "bit_equal_frac": float(np.mean(g16 == ref["f16"])),
+              "outputs_over_1_ulp": int(off.sum()),
+              "worst": {"row": int(worst[0]), "col": int(worst[1]), "y": float(o[worst]),
+                        "sum_abs_aw": float(ref["abs"][worst]),
+                        "y_over_sum_abs": float(abs(o[worst]) / ref["abs"][worst]),
+                        "err_over_check1_bound": float(err[worst] / (1e-3 * ref["abs"][worst] + ulp[worst]))},
+              "median_y_over_sum_abs_where_over_1_ulp":
+                  float(np.median(np.abs(o[off]) / ref["abs"][off])) if off.any() else None,
+              "median_y_over_sum_abs_all": float(np.median(np.abs(o) / ref["abs"]))}
     log("[bench] parity vs oracle: %s" % parity)
-    base = {"value": round(cpu_gbs, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": "%d whole %s calls (m=%d, K=%d, N=%d) in %.1f s, fp64 C oracle, "
-                      "OpenMP over columns" % (n, w.name, m, w.K, w.N, el),
-            "ms_per_call": round(el / n * 1e3, 2)}
+    base = {"value": round(gbs_all, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": "whole %s calls (m=%d, K=%d, N=%d), fp64 C oracle with OpenMP over columns: "
+                      "%d calls on %d threads (median), and 3 calls on 1 thread; %d cores in the "
+                      "affinity mask" % (w.name, m, w.K, w.N, len(t_all), threads, affinity),
+            "ms_per_call": round(med_all * 1e3, 2),
+            "ms_per_call_range": [round(t_all[0] * 1e3, 2), round(t_all[-1] * 1e3, 2)],
+            "single_thread": {"value": round(gbs_one, 5), "unit": "GB/s", "cores": 1,
+                              "ms_per_call": round(med_one * 1e3, 1),
+                              "ms_per_call_range": [round(t_one[0] * 1e3, 1), round(t_one[-1] * 1e3, 1)]},
+            "affinity_cores": affinity}
     return base, parity
 
 

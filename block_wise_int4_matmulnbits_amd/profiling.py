@@ -9,12 +9,19 @@
         HBM bytes per GEMV launch from FETCH_SIZE and WRITE_SIZE passes
         (KiB per dispatch), each scaled by what the same counter reads for a
         device copy of COPY_BYTES, next to the algorithmic bytes.
+    python -m block_wise_int4_matmulnbits_amd.profiling decode PROFROOT OUT.json OUT.md
+        every decode configuration profiled under PROFROOT/<config>/{trace,
+        fetch,write} (a --kernel-trace --stats run and FETCH_SIZE and
+        WRITE_SIZE passes of bench.py on that configuration; each directory
+        holds cmd.txt, the command that made it) and the device-copy
+        calibration under PROFROOT/copy_{fetch,write}: kernel time, HBM bytes
+        per launch and their fractions of 8 TB/s, per configuration.
     python -m block_wise_int4_matmulnbits_amd.profiling counters TAG TRACE_DIR \
         OUT.md FLOPS CMD_TRACE CMD_PMC PMC_DIR...
         duration statistics of the kernels whose name contains TAG in a
         --kernel-trace --stats run, and the per-dispatch mean of every counter
-        of the --pmc runs in PMC_DIR... (FETCH_SIZE scaled by the factor of
-        profiles/lm_head_traffic.json), with the shader clock (GRBM_GUI_ACTIVE
+        of the --pmc runs in PMC_DIR... (FETCH_SIZE scaled by the device-copy
+        factor of profiles/hbm_traffic.json), with the shader clock (GRBM_GUI_ACTIVE
         over the 8 XCDs) and the MFMA-busy share where counted.
 
 Reads CSV only; runs nothing on the GPU.
@@ -28,13 +35,28 @@ import statistics
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SRC = os.path.join(HERE, "csrc", "mnb_gemv.hip")
 GEMV_TAG = "mnb_gemv_kernel"
+DECODE_TAG = "::mnb_ge"          # every GEMV/GEMM kernel of the library
+PEAK_HBM_BYTES_PER_S = 8e12
+
+
+def source_files():
+    """Every source the kernels and the launch planner are built from."""
+    root = os.path.dirname(HERE)
+    files = sorted(glob.glob(os.path.join(HERE, "csrc", "*")))
+    files.append(os.path.join(root, "include", "mnb.h"))
+    return [f for f in files if os.path.isfile(f)]
 
 
 def kernel_source_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """sha256[:16] over the kernel, device-helper, planner and header sources:
+    a counter figure taken on other sources is stale."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def _one(pattern):
@@ -87,46 +109,6 @@ def _per_dispatch(d, counter, tag=None):
     return vals
 
 
-def traffic_summary(gemv_fetch, gemv_write, copy_fetch, copy_write, copy_bytes, workload, m,
-                    out_json, out_md, cmd):
-    sys.path.insert(0, os.path.dirname(HERE))
-    from block_wise_int4_matmulnbits_amd import workloads as W
-    w = W.WORKLOADS[workload]
-    alg = w.bytes_per_call(m)
-    kib = 1024.0
-    gf = statistics.median(_per_dispatch(gemv_fetch, "FETCH_SIZE", GEMV_TAG)) * kib
-    gw = statistics.median(_per_dispatch(gemv_write, "WRITE_SIZE", GEMV_TAG)) * kib
-    # the copy: largest dispatch of the run is the copy of copy_bytes
-    cf = max(_per_dispatch(copy_fetch, "FETCH_SIZE")) * kib
-    cw = max(_per_dispatch(copy_write, "WRITE_SIZE")) * kib
-    f_scale = copy_bytes / cf
-    w_scale = copy_bytes / cw
-    fetch = gf * f_scale
-    write = gw * w_scale
-    out = {"workload": workload, "m": m, "kernel_src_sha256_16": kernel_source_hash(),
-           "fetch_bytes_per_launch": round(fetch), "write_bytes_per_launch": round(write),
-           "hbm_bytes_per_launch": round(fetch + write), "algorithmic_bytes_per_launch": alg,
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "raw_fetch_kib": gf / kib, "raw_write_kib": gw / kib,
-           "copy_bytes": copy_bytes, "copy_fetch_kib": cf / kib, "copy_write_kib": cw / kib}
-    with open(out_json, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    with open(out_md, "w") as f:
-        f.write("# HBM traffic of one GEMV launch, %s (m=%d, K=%d, N=%d)\n\n" % (
-            workload, m, w.K, w.N))
-        f.write("Commands (repository root, one MI355X):\n\n%s\n\n" % "\n".join(
-            "    " + c for c in cmd))
-        f.write("| | raw counter (KiB/dispatch) | scale (copy of %d B) | bytes |\n|---|---|---|---|\n"
-                % copy_bytes)
-        f.write("| FETCH_SIZE | %.1f | %.4f | %d |\n" % (gf / kib, f_scale, fetch))
-        f.write("| WRITE_SIZE | %.1f | %.4f | %d |\n" % (gw / kib, w_scale, write))
-        f.write("\nAlgorithmic bytes per launch: %d.  Measured / algorithmic: fetch %.4f, "
-                "total %.4f.  Kernel source sha256[:16] %s.\n" % (
-                    alg, fetch / alg, (fetch + write) / alg, out["kernel_src_sha256_16"]))
-    return out
-
-
 def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs):
     trace = _one(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
     rows = [r for r in _rows(trace) if tag in r["Kernel_Name"]]
@@ -149,7 +131,7 @@ def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs
             if c == "GRBM_GUI_ACTIVE" and c in vals:
                 continue
             vals[c] = statistics.mean(v[c] for v in disp.values() if c in v)
-    with open(os.path.join(os.path.dirname(HERE), "profiles", "lm_head_traffic.json")) as f:
+    with open(os.path.join(os.path.dirname(HERE), "profiles", "hbm_traffic.json")) as f:
         fetch_scale = json.load(f)["fetch_scale"]
     pmc_mean = statistics.mean(pmc_durs) if pmc_durs else float("nan")
     with open(out_md, "w") as f:
@@ -181,11 +163,116 @@ def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs
                     % ((vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"]))
         if "FETCH_SIZE" in vals:
             f.write("- HBM fetch: %.1f MB per call (FETCH_SIZE KiB x 1024 x %.4f, the device-copy "
-                    "factor of profiles/lm_head_traffic.json)\n"
+                    "factor of profiles/hbm_traffic.json)\n"
                     % (vals["FETCH_SIZE"] * 1024 * fetch_scale / 1e6, fetch_scale))
         if "WRITE_SIZE" in vals:
             f.write("- HBM write: %.1f MB per call\n" % (vals["WRITE_SIZE"] * 1024 / 1e6))
     return mean
+
+
+def _cmd(d):
+    try:
+        with open(os.path.join(d, "cmd.txt")) as f:
+            return f.read().strip()
+    except OSError:
+        return "(command not recorded)"
+
+
+def _durations(trace_dir, tag):
+    rows = [r for r in _rows(_one(os.path.join(trace_dir, "**", "*kernel_trace.csv")))
+            if tag in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    return rows, [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+
+
+def kernel_short_name(full):
+    """'mnb_gemv_kernel<1, 2, 2, 1>' from a demangled rocprofv3 kernel name."""
+    import re
+    m = re.search(r"(mnb_\w+)(<[^>]*>)?\(", full)
+    return (m.group(1) + (m.group(2) or "")) if m else full
+
+
+def decode_summary(root, out_json, out_md, timed=500):
+    """Per decode configuration (a subdirectory of root named
+    workload:m:out_dtype): the mean kernel time of the last `timed`
+    dispatches of the trace run, FETCH_SIZE and WRITE_SIZE per dispatch
+    (median) scaled by the device-copy factors, and the fractions of
+    8 TB/s they make."""
+    sys.path.insert(0, os.path.dirname(HERE))
+    from block_wise_int4_matmulnbits_amd import workloads as W
+    kib = 1024.0
+    copy = {}
+    for kind, counter in (("fetch", "FETCH_SIZE"), ("write", "WRITE_SIZE")):
+        d = os.path.join(root, "copy_" + kind)
+        with open(os.path.join(d, "bytes.txt")) as f:
+            nbytes = int(f.read())
+        copy[kind] = {"scale": nbytes / (max(_per_dispatch(d, counter)) * kib),
+                      "bytes": nbytes, "cmd": _cmd(d)}
+    out = {"kernel_src_sha256_16": kernel_source_hash(),
+           "fetch_scale": copy["fetch"]["scale"], "write_scale": copy["write"]["scale"],
+           "copy_bytes": copy["fetch"]["bytes"], "configs": {}}
+    lines = []
+    for key in sorted(os.listdir(root)):
+        d = os.path.join(root, key)
+        if key.startswith("copy_") or not os.path.isdir(d):
+            continue
+        name, m, odt = key.split(":")
+        m = int(m)
+        w = W.WORKLOADS[name]
+        alg = w.bytes_per_call(m)
+        rows, durs = _durations(os.path.join(d, "trace"), DECODE_TAG)
+        t = durs[-timed:] if len(durs) >= timed else durs
+        mean_us = statistics.mean(t)
+        fetch = statistics.median(_per_dispatch(os.path.join(d, "fetch"), "FETCH_SIZE", DECODE_TAG)) \
+            * kib * copy["fetch"]["scale"]
+        write = statistics.median(_per_dispatch(os.path.join(d, "write"), "WRITE_SIZE", DECODE_TAG)) \
+            * kib * copy["write"]["scale"]
+        r = rows[-1]
+        e = {"workload": name, "m": m, "out_dtype": odt, "K": w.K, "N": w.N,
+             "kernel": kernel_short_name(r["Kernel_Name"]),
+             "dispatches_traced": len(durs), "timed_dispatches": len(t),
+             "kernel_mean_us": round(mean_us, 3), "kernel_median_us": round(statistics.median(t), 3),
+             "algorithmic_bytes": alg, "fetch_bytes": round(fetch), "write_bytes": round(write),
+             "alg_frac_of_8TBs": round(alg / (mean_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
+             "fetch_frac_of_8TBs": round(fetch / (mean_us * 1e-6) / PEAK_HBM_BYTES_PER_S, 4),
+             "fetch_over_alg": round(fetch / alg, 4),
+             # rocprofv3 decodes the descriptor's VGPR blocks with a granule of
+             # 4 where gfx950 allocates wave64 VGPRs in 8s: twice the traced
+             # figure is the allocation (75 registers -> 80 -> 40 traced).
+             "vgprs_traced": int(r["VGPR_Count"]), "vgprs_allocated": 2 * int(r["VGPR_Count"]),
+             "accum_vgprs_traced": int(r.get("Accum_VGPR_Count") or 0),
+             "grid": int(r["Grid_Size_X"]), "workgroup": int(r["Workgroup_Size_X"]),
+             "lds_bytes": int(r["LDS_Block_Size"]),
+             "cmd_trace": _cmd(os.path.join(d, "trace")), "cmd_fetch": _cmd(os.path.join(d, "fetch")),
+             "cmd_write": _cmd(os.path.join(d, "write"))}
+        out["configs"][key] = e
+        lines.append("| %s | %d | %s | `%s` | %.2f | %.2f | %d | %.4f | %.1f%% | %.1f%% | %d (%d) | %d x %d |" % (
+            name, m, odt, e["kernel"], e["kernel_mean_us"], e["kernel_median_us"], alg,
+            e["fetch_over_alg"], 100 * e["alg_frac_of_8TBs"], 100 * e["fetch_frac_of_8TBs"],
+            e["vgprs_traced"], e["vgprs_allocated"], e["grid"] // e["workgroup"], e["workgroup"]))
+    with open(out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    with open(out_md, "w") as f:
+        f.write("# Decode configurations: rocprofv3 kernel time and HBM traffic\n\n")
+        f.write("One MI355X; kernel sources sha256[:16] %s.  Per configuration, a `--kernel-trace "
+                "--stats` run of bench.py on it (mean of the last %d dispatches, the timed region), then "
+                "a `--pmc FETCH_SIZE` and a `--pmc WRITE_SIZE` run (median KiB per dispatch), each "
+                "scaled by what the same counter reads for a device copy of %d bytes (fetch factor "
+                "%.4f, write factor %.4f).  Fractions are of 8 TB/s.  VGPRs: as traced (rocprofv3 "
+                "decodes the descriptor with a granule of 4; gfx950 allocates wave64 VGPRs in 8s, so the "
+                "allocation, in brackets, is twice the traced figure).\n\n"
+                % (out["kernel_src_sha256_16"], timed, out["copy_bytes"], out["fetch_scale"],
+                   out["write_scale"]))
+        f.write("| workload | m | out | kernel | mean us | median us | algorithmic B | fetch / alg "
+                "| alg GB/s frac | FETCH frac | VGPRs traced (allocated) | grid x wg |\n"
+                "|---|---|---|---|---|---|---|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n\nCommands (repository root; `$REPO` is its path):\n\n")
+        for key, e in out["configs"].items():
+            f.write("- %s:\n    - `%s`\n    - `%s`\n    - `%s`\n" % (key, e["cmd_trace"], e["cmd_fetch"],
+                                                               e["cmd_write"]))
+        f.write("- copy calibration:\n    - `%s`\n    - `%s`\n" % (copy["fetch"]["cmd"], copy["write"]["cmd"]))
+    return out
 
 
 def main(argv):
@@ -195,9 +282,8 @@ def main(argv):
     elif argv[0] == "counters":
         tag, tdir, out_md, flops, cmd_t, cmd_p = argv[1:7]
         print(counters_summary(tag, tdir, out_md, float(flops), cmd_t, cmd_p, argv[7:]))
-    elif argv[0] == "traffic":
-        (gf, gw, cf, cw, cb, wl, m, oj, om) = argv[1:10]
-        print(json.dumps(traffic_summary(gf, gw, cf, cw, int(cb), wl, int(m), oj, om, argv[10:])))
+    elif argv[0] == "decode":
+        print(json.dumps(decode_summary(argv[1], argv[2], argv[3]), indent=1))
     else:
         raise SystemExit(__doc__)
 
