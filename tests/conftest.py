@@ -11,6 +11,13 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line(
         "markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+    # MNB_HOST_LIB names a host-only build of the library (the sanitizer
+    # test builds the front end with stand-ins for the HIP side); the ABI
+    # tests then load it in place of libmnb.so.
+    host_lib = os.environ.get("MNB_HOST_LIB")
+    if host_lib:
+        import block_wise_int4_matmulnbits_amd as mnb
+        mnb.LIB_PATH = host_lib
 
 
 @pytest.fixture(scope="session")
