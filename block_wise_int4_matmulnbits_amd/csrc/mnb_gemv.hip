@@ -24,13 +24,14 @@
 //   (x & 0x00F000F0)        | 0x64006400 -> (1024+16q1, 1024+16q5)
 //   ((x >> 8) & 0x000F000F) | 0x64006400 -> (1024+q2, 1024+q6)
 //   ((x >> 8) & 0x00F000F0) | 0x64006400 -> (1024+16q3, 1024+16q7)
-// then one packed fp16 add of -(1024+z) (or -(1024+16z)) per pair, which
-// leaves q-z (or 16(q-z)) exactly, and one v_dot2_f32_f16 against the
-// matching activation pair into one of two fp32 accumulators (the 1x and
-// 16x families).  Every product a*(q-z) is exact in fp32, so the rounding
-// error of the sum is relative to sum |a*(q-z)|.  Per block the families are
-// combined exactly (hi/16 + lo) and the fp16 scale applied by one FMA:
-//   acc += (hi/16 + lo) * s.
+// then per pair one packed fp16 operation that leaves the exact integers
+// q - z: an add of -(1024+z) for the (1024+q) pairs, and an fma by 1/16
+// with the addend -(64+z) for the (1024+16q) pairs ((1024+16q)/16 = 64+q is
+// exact).  One v_dot2_f32_f16 per pair against the matching activation pair
+// then adds into the block's single fp32 chain.  Every product a*(q-z) is
+// exact in fp32, so the rounding error of the sum is relative to
+// sum |a*(q-z)|.  The block's fp16 scale is applied by one fp32 FMA:
+//   acc = fma(block_sum, s, acc).
 //
 // Reduction: a fixed DPP tree across the group's lanes inside a wave, then
 // (multi-wave groups) a fixed-order sum over waves through LDS.  No atomics:

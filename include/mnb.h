@@ -116,9 +116,12 @@ typedef enum {
  *
  * Asynchronous: returns after the launch is queued.  Inputs must stay valid
  * and unmodified until the stream reaches this work.  The fp32 summation
- * order is fixed by (m, K, N) and the device's compute-unit count, so equal
- * inputs give bitwise equal outputs on the same device, and the bf16 output
- * equals the fp16 output of the same call narrowed to bf16.
+ * order is fixed by (m, K) for m <= 8 (never by N or the device), and by
+ * (m, K, N) and the device's compute-unit count for m > 8 (which tiling
+ * runs, and whether it splits K, depends on how the tiles fill the device).
+ * So equal inputs give bitwise equal outputs on the same device, column
+ * shards of one matrix give the bits of the whole at m <= 8, and the bf16
+ * output equals the fp16 output of the same call narrowed to bf16.
  * Thread safety: may be called from several host threads at once.
  */
 int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
