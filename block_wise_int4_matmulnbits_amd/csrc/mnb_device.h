@@ -91,6 +91,15 @@ __device__ __forceinline__ ZeroPoint zero_point_pairs(uint32_t z)
     return ZeroPoint{0xE400E400u | zz, 0xD400D400u | (zz << 4)};
 }
 
+// The same pairs for z = nib + zdef from two constants of the launch
+// (zero_point_pairs(zdef)): the fields are z*0x00010001 and z*0x00100010
+// added to the constants' bit patterns, with no carries, since z <= 15 only
+// fills the bits the constants leave clear.  Two v_mad_u32_u24 per block.
+__device__ __forceinline__ ZeroPoint zero_point_pairs(uint32_t nib, ZeroPoint base)
+{
+    return ZeroPoint{nib * 0x00010001u + base.zneg1, nib * 0x00100010u + base.zfma};
+}
+
 // magic: the fp16 pair (1024, 1024), 0x64006400, held in a VGPR (see
 // vgpr_constant).
 __device__ __forceinline__ void unpack_dword(uint32_t x, ZeroPoint zp, uint32_t magic,
@@ -190,6 +199,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 {
     const int n = bytes >= kOutOfRange ? (int)kOutOfRange : (int)bytes;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, kRsrcWord3);
+}
+
+// A resource of fewer than kOutOfRange bytes (no clamp, no 64-bit compare).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc_small(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kRsrcWord3);
 }
 
 }  // namespace mnb

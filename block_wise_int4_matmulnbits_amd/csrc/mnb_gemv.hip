@@ -195,6 +195,7 @@ void mnb_gemv_kernel(Params p)
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const int zshift = (lane & 1) * 4;          // block parity == lane parity (lpc even)
     const uint32_t zdef = p.zp ? 0u : 8u;       // zero point 8 when none are given
+    const ZeroPoint zbase = zero_point_pairs(zdef);
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
 
     uint32_t act[M][BPL][16];                   // permuted fp16 pairs
@@ -335,10 +336,11 @@ void mnb_gemv_kernel(Params p)
                 const int64_t col = c0 + c;
                 const bool in = col < p.N;
                 const int64_t cc = in ? col : 0;
-                const __amdgpu_buffer_rsrc_t rB = make_rsrc(p.B + cc * row_bytes, in ? row_bytes : 0);
-                const __amdgpu_buffer_rsrc_t rS = make_rsrc(p.scales + cc * nb, in ? 2 * nb : 0);
+                // K <= MNB_MAX_K keeps every size far below kOutOfRange.
+                const __amdgpu_buffer_rsrc_t rB = make_rsrc_small(p.B + cc * row_bytes, in ? row_bytes : 0);
+                const __amdgpu_buffer_rsrc_t rS = make_rsrc_small(p.scales + cc * nb, in ? 2 * nb : 0);
                 const __amdgpu_buffer_rsrc_t rZ =
-                    make_rsrc(p.zp ? p.zp + cc * zb : p.B, in && p.zp ? zb : 0);
+                    make_rsrc_small(p.zp ? p.zp + cc * zb : p.B, in && p.zp ? zb : 0);
 #pragma unroll
                 for (int j = 0; j < BPL; ++j) {
                     t.w[c][j] = __builtin_amdgcn_raw_buffer_load_b128(rB, ow[j], 0, kNontemporal);
@@ -376,7 +378,9 @@ void mnb_gemv_kernel(Params p)
         for (int c = 0; c < NC; ++c) {
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
-                const ZeroPoint zp = zero_point_pairs(((t.zq[c][j] >> zshift) & 0xFu) | zdef);
+                // With no zero points the loads return 0 and zdef = 8 is the
+                // zero point; otherwise zdef = 0.
+                const ZeroPoint zp = zero_point_pairs(__builtin_amdgcn_ubfe(t.zq[c][j], zshift, 4), zbase);
                 float s[M];
 #pragma unroll
                 for (int r = 0; r < M; ++r) s[r] = 0.f;
