@@ -93,6 +93,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     const uint32_t B0 = (uint32_t)(16 * BPL * wv);
     const int zshift = (g & 1) * 4;         // block parity == group parity (B0 even)
     const uint32_t zdef = p.zp ? 0u : 8u;   // zero point 8 when none are given
+    const ZeroPoint zbase = zero_point_pairs(zdef);
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);   // fp16 pair (1024, 1024)
 
     // Column quads [q_first, q_stop) of this workgroup.
@@ -212,6 +213,10 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         for (int k = 0; k < SD; ++k) st[64 * k + lane] = t.sd[k];
 #pragma unroll
         for (int k = 0; k < ZD; ++k) st[64 * (SD + k) + lane] = t.zd[k];
+        // Lanes read bytes that other lanes of the wave wrote: the fence keeps
+        // the compiler from moving those reads above the writes (the hardware
+        // runs one wave's LDS operations in order, so no wait is emitted).
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
         const uint8_t* sb = reinterpret_cast<const uint8_t*>(st);
 #pragma unroll
         for (int n = 0; n < NC; ++n) {
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 #pragma unroll
             for (int j = 0; j < BPL; ++j) {
                 const uint32_t zq = sb[zread[n] + 8 * j];
-                zp[j] = zero_point_pairs(((zq >> zshift) & 0xFu) | zdef);
+                zp[j] = zero_point_pairs(__builtin_amdgcn_ubfe(zq, zshift, 4), zbase);   // + zdef
                 sf[j] = (float)*reinterpret_cast<const _Float16*>(sb + sread[n] + 32 * j);
             }
             float4_t dsum[BPL][RQ];
