@@ -3,6 +3,7 @@
 // is tested, without a GPU.  The kernels and their launch live in
 // mnb_gemv.hip.
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <stdint.h>
 
@@ -156,6 +157,99 @@ int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap
 
 }  // namespace mnb
 
+namespace {
+
+// Prefill tilings of engine 2 (row tiles, columns, waves) and their fitted
+// cost in microseconds on gfx950:
+//   t0 + a*K*(R-1) + g*(R-1) + d*K + h*W
+// with K in thousands, R = ceil(tiles / CUs) rounds of tiles over the
+// compute units, and W the MB of weights (with scales and zero points) per
+// CU.  a and g price the rounds after the first, d and t0 the first (a CU
+// with one tile runs it faster than two that share it), h the weights that
+// stream from HBM when few row tiles share them.
+struct Tiling {
+    int32_t rt, cols, waves;
+    double t0, a, g, d, h;
+};
+constexpr Tiling kTilings[] = {
+    {1, 32, 4, 4.9015, 1.4779, 2.4480, 1.9788, 2.3637},    // K split over the four waves
+    {1, 64, 2, 0.9346, 2.2109, 1.7990, 5.5025, 12.8276},
+    {1, 128, 4, 1.3449, 4.3843, 2.5791, 5.5492, 13.7113},
+    {2, 128, 4, 3.3989, 5.7639, 2.5161, 6.0604, 5.8080},
+    {4, 128, 4, 4.4375, 12.1654, 3.6343, 11.4995, 0.0000},
+    {1, 256, 8, 0.0000, 9.3855, 2.9618, 8.9537, 35.6323},
+    {2, 256, 8, 0.8653, 12.1826, 4.3959, 10.5332, 22.8419},
+    {4, 256, 8, 4.4401, 17.7932, 11.0806, 16.0319, 3.2216},
+    {8, 256, 8, 6.3832, 33.6052, 0.0000, 25.2688, 4.1478},   // 256 x 256, weights through LDS
+};
+// The decode plan per launch of r <= 8 rows:
+//   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
+// but no less than its weight bytes at 6.5 TB/s (the fit's exponents come
+// from shapes where fixed costs dominate; far beyond them the weights set
+// the time) and no less than 3 us, about what one launch takes however
+// small.
+constexpr double kDecode[4] = {2.1635, 0.5726, 0.5924, 0.2067};
+constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
+constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
+constexpr double kDecodeLaunchUs = 3.0;
+
+int64_t prefill_tiles(const Tiling& t, int64_t m, int64_t N)
+{
+    const int64_t rows = t.rt == 8 ? 256 : 32 * (int64_t)t.rt;
+    return ceil_div(m, rows) * ceil_div(N, t.cols);
+}
+
+double tiling_cost(const Tiling& t, int64_t m, int64_t K, int64_t N, int num_cus)
+{
+    const double R = (double)ceil_div(prefill_tiles(t, m, N), num_cus);
+    const double k = (double)K / 1e3;
+    const double w = (double)N * (double)K * kBytesPerWeight / num_cus / 1e6;
+    return t.t0 + t.a * k * (R - 1) + t.g * (R - 1) + t.d * k + t.h * w;
+}
+
+double decode_cost(int64_t m, int64_t K, int64_t N)
+{
+    const double bytes_us = (double)N * (double)K * kBytesPerWeight / kDecodeBytesPerUs;
+    const double floor_us = bytes_us > kDecodeLaunchUs ? bytes_us : kDecodeLaunchUs;
+    auto one = [&](int64_t r) {
+        const double t = std::exp(kDecode[0]) * std::pow((double)K / 4096, kDecode[1]) *
+                         std::pow((double)N / 4096, kDecode[2]) * std::pow((double)r / 8, kDecode[3]);
+        return t > floor_us ? t : floor_us;
+    };
+    const int64_t full = m / MNB_MAX_M, rem = m % MNB_MAX_M;
+    return (double)full * one(MNB_MAX_M) + (rem ? one(rem) : 0.0);
+}
+
+struct PrefillChoice {
+    Tiling t;
+    bool decode;
+};
+
+// The cheapest plan by the model among the tilings the plan check accepts
+// for (m, K, N) and the decode plan; ties go to the earlier tiling.
+PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus)
+{
+    PrefillChoice best{kTilings[0], true};
+    double best_cost = decode_cost(m, K, N);
+    for (const Tiling& t : kTilings) {
+        mnb_plan q{};
+        q.engine = 2;
+        q.row_tiles = t.rt;
+        q.cols_per_tile = t.cols;
+        q.waves_per_wg = t.waves;
+        q.workgroups = 1;
+        if (mnb_plan_check(m, K, N, &q) != MNB_OK) continue;
+        const double c = tiling_cost(t, m, K, N, num_cus);
+        if (c < best_cost) {
+            best_cost = c;
+            best = PrefillChoice{t, false};
+        }
+    }
+    return best;
+}
+
+}  // namespace
+
 extern "C" {
 
 int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
@@ -224,112 +318,23 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     *plan = mnb_plan{};
 
     if (m > MNB_MAX_M) {
-        // Prefill: the largest tile (rows first: every unpacked weight feeds
-        // 32 * row_tiles rows; then columns: every activation operand read
-        // feeds cols_per_tile / 128 matrix products) that still gives every
-        // compute unit a workgroup; one resident generation walking the tiles.
-        int64_t rt = 1;
-        while (rt < 4 && 32 * rt < m) rt *= 2;
-        while (rt > 1 && (uint64_t)64 * rt * (uint64_t)K > mnb::kPrefillRowBlockBytes) rt /= 2;
-        auto tiles = [&](int64_t r, int64_t c) { return ceil_div(m, 32 * r) * ceil_div(N, c); };
-        // Narrow the columns, then the rows, only while the tiles would give
-        // fewer than 85% of the CUs one: a last round with a few idle CUs
-        // costs less than halving every tile's rows (gate_up, µs: m = 64
-        // 84.2 -> 57.5, m = 96 106.9 -> 74.2, m = 128 113.7 -> 78.1, m = 256
-        // 154.4 -> 111.4).
-        auto fills = [&](int64_t r, int64_t c) { return 100 * tiles(r, c) >= 85 * (int64_t)num_cus; };
-        int64_t cols = 256;
-        while (cols > 128 && !fills(rt, cols)) cols /= 2;
-        while (rt > 1 && !fills(rt, cols)) rt /= 2;
-        // Tiles for at most half of the CUs even at one row block: 64
-        // columns on two waves double them (down projection m = 64: 134 ->
-        // 109 us, m = 128: 134.5 -> 112.5).  With more tiles than that, 128
-        // columns stay ahead, since the narrower tiles convert each
-        // activation for half as many columns (gate_up m = 16: 45.8 vs 49.3).
-        if (cols == 128 && 2 * tiles(rt, cols) <= (int64_t)num_cus) cols = 64;
-        // One or two row tiles: 128 columns on four waves rather than 256 on
-        // eight; the finer tiles end the last round sooner (K = 4096, m =
-        // 24, us: 65536 columns 64.6 -> 58.7, 81920 110.3 -> 80.7, 131072
-        // 122.9 -> 106.5, 151936 166.4 -> 131.1; level at 57344 and at
-        // 8192 x 100000).
-        if (rt <= 2 && cols == 256) cols = 128;
-        // One row tile whose tiles overflow one round where two row tiles
-        // fit in it: two, since a tile's cost is mostly its dequantization
-        // (us, one -> two row tiles: down projection m = 384 154.6 -> 99.6;
-        // 4096 x 6144 m = 192 44.7 -> 32.1, m = 256 46.0 -> 32.9).  Not four:
-        // those tiles cost more (4096 x 6144 m = 384 57.7 against 51.0).
-        if (rt == 1 && m > 32 && tiles(1, cols) > (int64_t)num_cus && tiles(2, cols) <= (int64_t)num_cus &&
-            (uint64_t)64 * 2 * (uint64_t)K <= mnb::kPrefillRowBlockBytes)
-            rt = 2;
-        // Four row tiles whose 128-column tiles would overflow one round
-        // while 256-column tiles fit in it: 256 columns (on eight waves).
-        // Interleaved A/B, us: 4096 x 4096 m = 1152 116.7 -> 81.5; 4096 x
-        // 6144 m = 768 110.0 -> 74.8; 14336 x 4096 m = 1152 355.0 -> 241.2;
-        // 14336 x 14336 m = 320 335.8 -> 237.9; 13 of 13 such shapes 29-32%
-        // faster.  (Keeping four row tiles where the rows were halved to
-        // fill the CUs instead lost 7-13% on every shape tried.)
-        if (rt == 4 && cols == 128 && tiles(4, 128) > (int64_t)num_cus && tiles(4, 256) <= (int64_t)num_cus)
-            cols = 256;
-        // 256 x 256 tiles with the weights staged through LDS when they give
-        // at least 85% of the CUs a tile (gate_up, interleaved A/B against
-        // the 128-row tiles: m = 512 185 vs 216 us, m = 1024 394 vs 432,
-        // m = 2048 787 vs 773).
-        const int64_t t8 = ceil_div(m, 256) * ceil_div(N, 256);
-        if (m > 128 && 100 * t8 >= 85 * (int64_t)num_cus &&
-            (uint64_t)64 * 8 * (uint64_t)K <= mnb::kPrefillRowBlockBytes) {
-            rt = 8;
-            cols = 256;
-        } else if (m > 128 && rt == 4 && cols == 256 && tiles(4, 256) > (int64_t)num_cus && t8 <= (int64_t)num_cus &&
-                   (uint64_t)64 * 8 * (uint64_t)K <= mnb::kPrefillRowBlockBytes) {
-            // 128 x 256 tiles that would overflow one round while 256 x 256
-            // tiles fit in it: the latter (interleaved A/B, us: down
-            // projection m = 2176 509.1 -> 395.7, m = 3072 508.9 -> 404.9;
-            // 4096 x 6144 m = 1536 154.3 -> 115.6; 4096 x 14336 m = 640
-            // 152.7 -> 113.8; 26 of 26 such shapes 17-25% faster).
-            rt = 8;
-        }
-        // 256 x 256 tiles against 128 x 256 ones by rounds of tiles over the
-        // CUs: a 256 x 256 tile holds a CU for one unit, a 128 x 256 tile
-        // (two per CU) for 0.625 (half the rows, 25% less efficient per
-        // row).  This picks the faster of the two on each of 26 shapes where
-        // the last 256-row block wastes at least 10% of its rows (us: 4096 x
-        // 14336 m = 1152 253.9 -> 178.7; lm_head 4096 x 151936 m = 384 722.1
-        // -> 624.0; kept at m = 640, 1064.7 against 1076.2), and on every
-        // earlier tall measurement (gate_up m = 384, 1024, 2048 and 4096 stay
-        // on 256 x 256).
-        if (rt == 8 && 5 * ceil_div(ceil_div(m, 128) * ceil_div(N, 256), num_cus) < 8 * ceil_div(t8, num_cus))
-            rt = 4;
-        // Few columns: 32-row, 32-column tiles whose K four waves split,
-        // while there are at most two such tiles per CU, and either more
-        // than 16 rows or at least half of the CUs get one (us, before ->
-        // after: down projection m = 24 57.5 -> 47.2, m = 48 101 -> 46.1, m =
-        // 64 103 -> 48.3, m = 128 105 -> 92.4; 4096 x 6144 m = 32 46.7 ->
-        // 17.9, m = 12 20.4 -> 16.9; 8192 x 8192 m = 12 61.0 -> 29.6; at three
-        // tiles per CU, down m = 192, 131.5 vs 135.6, the wider tiles stay;
-        // 8192 x 4096 m = 12 27.9 -> 22.5, 14336 x 4096 m = 16 38.8 -> 36.5).
-        // Otherwise, with up to 16 rows whose tiles would leave more than
-        // half of the CUs idle (2048 columns: 64 tiles for 256 CUs), the
-        // decode kernels in launches of 8 rows (14336 x 2048 m = 9: 24.1
-        // against 34.8 split).
-        const int64_t t32 = ceil_div(m, 32) * ceil_div(N, 32);
-        const bool split = (m > 2 * MNB_MAX_M || 2 * t32 >= (int64_t)num_cus) && t32 <= 2 * (int64_t)num_cus;
-        if (split) {
-            rt = 1;
-            cols = 32;
-        } else if (2 * tiles(rt, cols) < (int64_t)num_cus && m <= 2 * MNB_MAX_M) {
-            return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
-        }
+        // Prefill: every tiling of the prefill kernel that the plan check
+        // accepts, and the 8-row decode plan run once per 8 rows, priced by
+        // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
+        // out, 54 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
+        // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
+        // those shapes the cheapest modelled plan runs 0.22% slower than
+        // the fastest measured one on average, 4.0% at most.
+        const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
+        if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
+        const int64_t tiles = prefill_tiles(c.t, m, N);
         int64_t wgs = per_cu * num_cus;
-        if (wgs > tiles(rt, cols)) wgs = tiles(rt, cols);
+        if (wgs > tiles) wgs = tiles;
         plan->engine = 2;
-        plan->row_tiles = (int32_t)rt;
-        plan->cols_per_tile = (int32_t)cols;
-        // 256-column tiles run as eight waves of 32 columns rather than four
-        // of 64: faster on the gate_up shape (757 vs 831 us at m = 2048),
-        // within 5% on the down projection, 0-8% faster at one or two row
-        // tiles.  64 columns run on two waves, 32 (K split) and 128 on four.
-        plan->waves_per_wg = cols == 64 ? 2 : cols == 256 ? 8 : 4;
+        plan->row_tiles = c.t.rt;
+        plan->cols_per_tile = c.t.cols;
+        plan->waves_per_wg = c.t.waves;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -1,0 +1,192 @@
+"""Tune the prefill planner's cost model (m > 8).
+
+The planner (``mnb_plan_default`` in csrc/mnb_api.cpp) prices every prefill
+tiling, and the 8-row decode plan run once per 8 rows, with a fitted cost
+and takes the cheapest.  This script produces both halves of that:
+
+  python -m block_wise_int4_matmulnbits_amd.plan_tune sweep OUT.json
+      (GPU) times every tiling that mnb_plan_check accepts, each with one
+      resident generation of workgroups, and the decode plan for m <= 16,
+      on a fixed list of shapes (bf16 in and out, random weights).
+  python -m block_wise_int4_matmulnbits_amd.plan_tune fit IN.json
+      (CPU) fits the cost of each tiling by non-negative least squares on
+      relative error and prints the table the planner holds, and the
+      regret of the fitted choice on every measured shape.
+
+Cost of a tiling (µs), with R = ceil(tiles / CUs) rounds of tiles over the
+compute units, K in thousands and W the weight bytes per CU in MB (0.578
+bytes per weight with the scales and zero points):
+    t0 + a*K*(R-1) + g*(R-1) + d*K + h*W
+Cost of the decode plan: per launch of r rows,
+    max(exp(c0) * (K/4096)^c1 * (N/4096)^c2 * (r/8)^c3, weight bytes / 6.5 TB/s, 3 us),
+summed over the ceil(m/8) launches.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+import sys
+
+TILINGS = [(1, 32, 4), (1, 64, 2), (1, 128, 4), (2, 128, 4), (4, 128, 4),
+           (1, 256, 8), (2, 256, 8), (4, 256, 8), (8, 256, 8)]
+BYTES_PER_WEIGHT = 0.578   # 4 bits + a 2-byte scale and a 4-bit zero point per 32
+
+SHAPES = [(64, 4096, 28672), (128, 4096, 28672), (256, 4096, 28672), (16, 4096, 28672), (64, 14336, 4096),
+          (128, 14336, 4096), (24, 14336, 4096), (32, 4096, 6144), (128, 4096, 6144), (192, 14336, 4096),
+          (24, 4096, 151936), (64, 4096, 151936), (12, 4096, 6144), (9, 2048, 8192), (16, 14336, 8192),
+          (32, 4096, 65536), (384, 14336, 4096), (192, 4096, 6144), (256, 4096, 6144), (1152, 4096, 4096),
+          (768, 4096, 6144), (320, 14336, 14336), (384, 4096, 6144), (2176, 14336, 4096), (2048, 14336, 4096),
+          (1536, 4096, 6144), (640, 4096, 14336), (384, 4096, 151936), (640, 4096, 151936), (1152, 4096, 14336),
+          (1024, 4096, 28672), (128, 4096, 151936), (256, 14336, 4096), (1024, 14336, 4096),
+          (16, 14336, 4096), (9, 4096, 151936), (16, 4096, 151936), (12, 4096, 4096), (9, 8192, 2048),
+          (16, 14336, 2048), (12, 8192, 28672), (512, 4096, 28672), (2048, 4096, 28672), (512, 14336, 4096),
+          (48, 14336, 4096), (96, 14336, 4096), (32, 14336, 4096), (4096, 4096, 28672), (16, 4096, 4096),
+          (64, 4096, 4096), (32, 8192, 8192), (512, 4096, 4096), (96, 4096, 151936), (160, 14336, 4096)]
+
+
+def key_of(t):
+    return "%d,%d,%d" % t
+
+
+def tiles_of(t, m, N):
+    rt, cols, _ = t
+    rows = 256 if rt == 8 else 32 * rt
+    return -(-m // rows) * -(-N // cols)
+
+
+def tiling_features(t, m, K, N, cus):
+    R = -(-tiles_of(t, m, N) // cus)
+    return [1.0, K / 1e3 * (R - 1), float(R - 1), K / 1e3, N * K * BYTES_PER_WEIGHT / cus / 1e6]
+
+
+DECODE_BYTES_PER_US = 6.5e6   # floors of a decode launch: its weight bytes at 6.5 TB/s,
+DECODE_LAUNCH_US = 3.0        # and the time one launch takes however small
+
+
+def decode_cost(p, m, K, N):
+    floor_us = max(N * K * BYTES_PER_WEIGHT / DECODE_BYTES_PER_US, DECODE_LAUNCH_US)
+
+    def one(r):
+        return max(math.exp(p[0]) * (K / 4096) ** p[1] * (N / 4096) ** p[2] * (r / 8) ** p[3], floor_us)
+    full, rem = divmod(m, 8)
+    return full * one(8) + (one(rem) if rem else 0.0)
+
+
+def sweep(out_path):
+    import ctypes
+    import torch
+    import block_wise_int4_matmulnbits_amd as mnb
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    L = mnb.lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    props = torch.cuda.get_device_properties(0)
+    res = {"cus": cus, "device": props.name, "arch": getattr(props, "gcnArchName", ""), "shapes": {}}
+
+    def timed(raw, plan):
+        pp = ctypes.byref(plan)
+
+        def go():
+            st = L.matmul_nbits_planned(*raw, pp)
+            assert st == 0, mnb.mnb_status_string(st)
+        go()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        go()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        n = int(min(200, max(3, 20000 / max(e0.elapsed_time(e1) * 1e3, 1.0))))
+        best = float("inf")
+        for _ in range(3):
+            e0.record(stream)
+            for _ in range(n):
+                go()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+        return best
+
+    for m, K, N in SHAPES:
+        A = (torch.randn(m, K, device=dev) * 0.5).to(torch.bfloat16)
+        B = torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev)
+        S = (torch.rand(N, K // 32, device=dev) * 0.01 + 0.001).to(torch.float16)
+        Z = torch.randint(0, 256, (N, (K // 32 + 1) // 2), dtype=torch.uint8, device=dev)
+        O = torch.empty(m, N, dtype=torch.bfloat16, device=dev)
+        raw = (A.data_ptr(), mnb.MNB_BF16, m, K, N, B.data_ptr(), S.data_ptr(), Z.data_ptr(), 32,
+               O.data_ptr(), mnb.MNB_BF16, stream.cuda_stream)
+        row = {}
+        for t in TILINGS:
+            rt, cols, waves = t
+            p = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=1)
+            if mnb.mnb_plan_check(m, K, N, p) != 0:
+                continue
+            occ = mnb.mnb_get_kernel_info(m, K, p)["wgs_per_cu"]
+            tiles = tiles_of(t, m, N)
+            p = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves,
+                             workgroups=max(1, min(tiles, occ * cus)))
+            row[key_of(t)] = {"us": round(timed(raw, p), 3), "occ": occ, "tiles": tiles}
+        if m <= 16:
+            row["decode"] = {"us": round(timed(raw, mnb.plan_for_device(8, K, N, cus)), 3)}
+        res["shapes"][key_of((m, K, N))] = row
+        print(key_of((m, K, N)), " ".join("%s=%.1f" % (k, v["us"]) for k, v in row.items()), flush=True)
+        del A, B, S, Z, O
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
+def fit_model(data):
+    """(table, decode): the cost coefficients of every tiling, fitted by
+    non-negative least squares on relative error, and the decode plan's."""
+    import numpy as np
+    from scipy.optimize import least_squares, nnls
+    cus = data["cus"]
+    shapes = [(tuple(map(int, k.split(","))), row) for k, row in data["shapes"].items()]
+    table = {}
+    for t in TILINGS:
+        X, y = [], []
+        for (m, K, N), row in shapes:
+            if key_of(t) in row:
+                X.append(tiling_features(t, m, K, N, cus))
+                y.append(row[key_of(t)]["us"])
+        X, y = np.array(X), np.array(y)
+        table[t], _ = nnls(X / y[:, None], np.ones_like(y))
+    pts = [((m, K, N), row["decode"]["us"]) for (m, K, N), row in shapes if "decode" in row]
+    dec = least_squares(lambda p: [decode_cost(p, *s) / us - 1 for s, us in pts], [2.5, 0.7, 0.5, 0.2]).x
+    return table, dec
+
+
+def model_pick(table, dec, m, K, N, cus, candidates):
+    """The cheapest of `candidates` (tiling keys and "decode") by the model."""
+    cost = {}
+    for t in TILINGS:
+        if key_of(t) in candidates:
+            cost[key_of(t)] = sum(f * c for f, c in zip(tiling_features(t, m, K, N, cus), table[t]))
+    if "decode" in candidates:
+        cost["decode"] = decode_cost(dec, m, K, N)
+    return min(cost, key=cost.get)
+
+
+def fit(path):
+    data = json.load(open(path))
+    table, dec = fit_model(data)
+    print("// rt, cols, waves, t0, a, g, d, h")
+    for t in TILINGS:
+        print("    {%d, %d, %d, %s}," % (*t, ", ".join("%.4ff" % v for v in table[t])))
+    print("// decode: %s" % ", ".join("%.4f" % v for v in dec))
+    regrets = []
+    for key, row in sorted(data["shapes"].items()):
+        m, K, N = map(int, key.split(","))
+        pick = model_pick(table, dec, m, K, N, data["cus"], row)
+        best = min(v["us"] for v in row.values())
+        regrets.append(row[pick]["us"] / best - 1)
+        print("%-18s pick %-8s %8.2f us  best %8.2f  regret %4.1f%%" % (key, pick, row[pick]["us"], best,
+                                                                          100 * regrets[-1]))
+    print("mean regret %.2f%%, max %.1f%%" % (100 * sum(regrets) / len(regrets), 100 * max(regrets)))
+
+
+if __name__ == "__main__":
+    if len(sys.argv) != 3 or sys.argv[1] not in ("sweep", "fit"):
+        sys.exit("usage: python -m block_wise_int4_matmulnbits_amd.plan_tune sweep|fit FILE.json")
+    (sweep if sys.argv[1] == "sweep" else fit)(os.path.abspath(sys.argv[2]))

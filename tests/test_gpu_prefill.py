@@ -50,25 +50,32 @@ def _gpu():
     mnb.lib()
 
 
-@pytest.mark.parametrize("m,K,N,a_dtype,asym", [
-    (9, 4096, 1000, W.F16, True),       # smallest prefill height, one 16-row tile
-    (16, 4096, 64, W.BF16, True),       # exactly one tile
-    (17, 1024, 130, W.F16, False),      # ragged rows and columns, zero point 8
-    (12, 4096, 6144, W.BF16, True),     # K split over four waves at 12 rows
-    (9, 2048, 8200, W.F16, False),      # the same at 9 rows, ragged columns
-    (100, 32 * 37, 77, W.BF16, True),   # K not a whole number of 128-wide steps
-    (130, 14336, 300, W.BF16, True),    # down-projection K, row tail of 2
-    (256, 4096, 1024, W.F16, True),     # several row and column blocks
-    (192, 4096, 6144, W.BF16, True),    # two row tiles where one would overflow a round
-    (40, 4096, 65536, W.F16, True),     # 128-column tiles at two row tiles, many rounds
-    (1152, 1024, 4096, W.BF16, True),   # 256 columns kept at four row tiles: one round
-    (640, 512, 14336, W.F16, True),     # one round of 256 x 256 tiles, not two of 128 x 256
-    (1152, 512, 14336, W.BF16, True),   # 128 x 256 tiles: two rounds where 256 x 256 take two of more work
+# The planner's cost model picks these plans at 256 CUs (row tiles, columns,
+# waves), or "decode" for the 8-row decode plan run per 8 rows.
+@pytest.mark.parametrize("m,K,N,a_dtype,asym,want", [
+    (9, 4096, 1000, W.F16, True, "decode"),          # few columns: two decode launches
+    (16, 4096, 64, W.BF16, True, "decode"),          # exactly two decode launches
+    (17, 1024, 130, W.F16, False, (1, 64, 2)),       # ragged rows and columns, zero point 8
+    (12, 4096, 6144, W.BF16, True, (1, 32, 4)),      # K split over four waves at 12 rows
+    (9, 2048, 8200, W.F16, False, (1, 64, 2)),       # 64 columns on two waves, ragged columns
+    (100, 32 * 37, 77, W.BF16, True, (1, 32, 4)),    # K not a whole number of 128-wide steps
+    (130, 14336, 300, W.BF16, True, (1, 32, 4)),     # down-projection K, row tail of 2
+    (256, 4096, 1024, W.F16, True, (1, 32, 4)),      # several row and column blocks
+    (192, 4096, 6144, W.BF16, True, (2, 128, 4)),    # two 32-row tiles of 128 columns
+    (40, 4096, 65536, W.F16, True, (2, 256, 8)),     # 256 columns on eight waves, several rounds
+    (1152, 1024, 4096, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles
+    (640, 512, 14336, W.F16, True, (8, 256, 8)),     # 256 x 256 tiles, weights through LDS
+    (1152, 512, 14336, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles where 256 x 256 would take more rounds
 ])
-def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym):
+def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym, want):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
-    plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
-    assert plan.engine == 2 or m <= 16     # few tiles: the decode kernels per 8 rows
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    plan = mnb.plan_for_device(m, K, N, cus)
+    if cus == 256:
+        if want == "decode":
+            assert plan.engine != 2 and plan.as_dict() == mnb.plan_for_device(8, K, N, cus).as_dict()
+        else:
+            assert plan.engine == 2 and (plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) == want
     assert_prefill(oracle_mod, d, m, "prefill", None)
 
 
