@@ -172,15 +172,15 @@ struct Tiling {
     double t0, a, g, d, h;
 };
 constexpr Tiling kTilings[] = {
-    {1, 32, 4, 4.9015, 1.4779, 2.4480, 1.9788, 2.3637},    // K split over the four waves
-    {1, 64, 2, 0.9346, 2.2109, 1.7990, 5.5025, 12.8276},
-    {1, 128, 4, 1.3449, 4.3843, 2.5791, 5.5492, 13.7113},
-    {2, 128, 4, 3.3989, 5.7639, 2.5161, 6.0604, 5.8080},
-    {4, 128, 4, 4.4375, 12.1654, 3.6343, 11.4995, 0.0000},
-    {1, 256, 8, 0.0000, 9.3855, 2.9618, 8.9537, 35.6323},
-    {2, 256, 8, 0.8653, 12.1826, 4.3959, 10.5332, 22.8419},
-    {4, 256, 8, 4.4401, 17.7932, 11.0806, 16.0319, 3.2216},
-    {8, 256, 8, 6.3832, 33.6052, 0.0000, 25.2688, 4.1478},   // 256 x 256, weights through LDS
+    {1, 32, 4, 4.8475, 1.4817, 2.4322, 1.9701, 2.4904},    // K split over the four waves
+    {1, 64, 2, 0.9193, 2.2306, 1.7426, 5.4721, 12.7983},
+    {1, 128, 4, 1.2223, 4.4069, 2.5190, 5.5476, 13.6243},
+    {2, 128, 4, 3.4232, 5.9089, 2.2675, 6.0605, 5.9666},
+    {4, 128, 4, 4.6225, 12.1937, 3.5565, 11.3333, 0.0000},
+    {1, 256, 8, 0.0000, 9.4523, 2.9394, 9.0044, 35.4125},
+    {2, 256, 8, 0.9400, 12.3151, 3.7048, 10.4578, 23.5812},
+    {4, 256, 8, 3.7336, 18.1389, 6.1795, 14.7794, 6.1496},
+    {8, 256, 8, 6.5596, 33.1800, 0.0000, 24.2550, 10.8708},   // 256 x 256, weights through LDS
 };
 // The decode plan per launch of r <= 8 rows:
 //   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
@@ -188,7 +188,7 @@ constexpr Tiling kTilings[] = {
 // from shapes where fixed costs dominate; far beyond them the weights set
 // the time) and no less than 3 us, about what one launch takes however
 // small.
-constexpr double kDecode[4] = {2.1635, 0.5726, 0.5924, 0.2067};
+constexpr double kDecode[4] = {2.1604, 0.5756, 0.5979, 0.2272};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
 constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
@@ -323,8 +323,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
         // out, 54 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
-        // those shapes the cheapest modelled plan runs 0.22% slower than
-        // the fastest measured one on average, 4.0% at most.
+        // those shapes the cheapest modelled plan runs 0.12% slower than
+        // the fastest measured one on average, 2.8% at most.
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;

@@ -112,11 +112,16 @@ __device__ __forceinline__ uint32_t pair_bf16(uint32_t x, uint32_t y, bool hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
 }
 
-// LDS slot of 16-byte piece d (k = 8d .. 8d+7) of row r: the XOR spreads
-// the 16-byte reads of 8 or 16 consecutive rows over all banks.
+// LDS slot of 16-byte piece d (k = 8d .. 8d+7) of row r (rows are 64
+// bytes, four slots).  An MFMA operand read has lane (j, h) take piece 2h+v
+// of row j; XOR-ing the slot with bits 2..3 of the row spreads those reads
+// over all banks.  Measured with eight waves sharing a CU's LDS, cycles per
+// 16-byte read per wave: 32.0 with this swizzle, the same as consecutive
+// lanes reading consecutive 16 bytes; 56.1 with the XOR of bits 1..2 and
+// 3..4 used before; 106.7 with none.
 __device__ __forceinline__ int a_slot(int d, int r)
 {
-    return d ^ (((r >> 1) ^ (r >> 3)) & 3);
+    return d ^ ((r >> 2) & 3);
 }
 
 // KS > 1 splits K over the waves: KS slices of W / KS waves, slice s
@@ -530,11 +535,14 @@ __global__ __launch_bounds__(512) void mnb_gemm_lds_kernel(GemmParams p)
             const uint32_t zn = ((q.z >> (4 * bu)) & 0xFu) | zdef;
             const ZeroPoint zp = zero_point_pairs(zn);
             const uint32_t s2 = __builtin_amdgcn_perm(q.s, q.s, 0x01000100u);
+            // Threads 2c and 2c+1 write blocks 0 and 1 of column c, 16 KB
+            // apart: the slot also XORs 2 * block, so the two land in
+            // different banks (a read takes one block, so it stays spread).
 #pragma unroll
             for (int d = 0; d < 4; ++d) {
                 uint32_t bq[4];
                 unpack_dword(q.w[d], zp, magic, bq);
-                b_lds[buf * QB + (bu * NT + bc) * 4 + a_slot(d, bc)] =
+                b_lds[buf * QB + (bu * NT + bc) * 4 + (a_slot(d, bc) ^ (2 * bu))] =
                     make_uint4(hmul2(bq[0], s2), hmul2(bq[1], s2), hmul2(bq[2], s2), hmul2(bq[3], s2));
             }
         };
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(512) void mnb_gemm_lds_kernel(GemmParams p)
 #pragma unroll
                     for (int ct = 0; ct < CTW; ++ct) {
                         const int col = wc * 64 + ct * 32 + j;
-                        const uint4 x = b_lds[buf * QB + (i * NT + col) * 4 + a_slot(2 * h + v, col)];
+                        const uint4 x = b_lds[buf * QB + (i * NT + col) * 4 + (a_slot(2 * h + v, col) ^ (2 * i))];
                         fb[ct] = __builtin_bit_cast(half8_t, u32x4{x.x, x.y, x.z, x.w});
                     }
 #pragma unroll
