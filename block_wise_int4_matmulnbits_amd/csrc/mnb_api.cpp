@@ -172,15 +172,17 @@ struct Tiling {
     double t0, a, g, d, h;
 };
 constexpr Tiling kTilings[] = {
-    {1, 32, 4, 4.8475, 1.4817, 2.4322, 1.9701, 2.4904},    // K split over the four waves
-    {1, 64, 2, 0.9193, 2.2306, 1.7426, 5.4721, 12.7983},
-    {1, 128, 4, 1.2223, 4.4069, 2.5190, 5.5476, 13.6243},
-    {2, 128, 4, 3.4232, 5.9089, 2.2675, 6.0605, 5.9666},
-    {4, 128, 4, 4.6225, 12.1937, 3.5565, 11.3333, 0.0000},
-    {1, 256, 8, 0.0000, 9.4523, 2.9394, 9.0044, 35.4125},
-    {2, 256, 8, 0.9400, 12.3151, 3.7048, 10.4578, 23.5812},
-    {4, 256, 8, 3.7336, 18.1389, 6.1795, 14.7794, 6.1496},
-    {8, 256, 8, 6.5596, 33.1800, 0.0000, 24.2550, 10.8708},   // 256 x 256, weights through LDS
+    {1, 16, 4, 3.7955, 1.4178, 1.8649, 1.8878, 0.0000},    // 16 columns on a 32-column tile, K split over the waves
+    {1, 16, 8, 5.9735, 2.0027, 1.9798, 1.7233, 0.0000},
+    {1, 32, 4, 4.8657, 1.4799, 2.4373, 1.9743, 2.3661},    // K split over the four waves
+    {1, 64, 2, 0.9055, 2.2250, 1.7934, 5.4761, 12.5822},
+    {1, 128, 4, 1.1800, 4.3899, 2.6609, 5.5548, 13.7114},
+    {2, 128, 4, 3.4199, 5.8978, 2.4268, 6.0782, 5.1620},
+    {4, 128, 4, 4.5934, 12.0761, 4.0745, 11.3475, 0.0000},
+    {1, 256, 8, 0.0000, 9.4018, 3.1089, 8.9950, 35.8779},
+    {2, 256, 8, 0.8697, 12.2400, 4.3995, 10.4644, 23.6112},
+    {4, 256, 8, 3.6742, 17.6862, 8.5875, 14.7773, 6.8313},
+    {8, 256, 8, 6.5368, 33.2951, 0.0000, 24.2467, 11.1644},   // 256 x 256, weights through LDS
 };
 // The decode plan per launch of r <= 8 rows:
 //   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
@@ -188,7 +190,7 @@ constexpr Tiling kTilings[] = {
 // from shapes where fixed costs dominate; far beyond them the weights set
 // the time) and no less than 3 us, about what one launch takes however
 // small.
-constexpr double kDecode[4] = {2.1604, 0.5756, 0.5979, 0.2272};
+constexpr double kDecode[4] = {2.1636, 0.5746, 0.5954, 0.2069};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
 constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
@@ -263,7 +265,9 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->engine == 2) {
         const bool shape_ok =
             plan->row_tiles == 8 ? (plan->waves_per_wg == 8 && plan->cols_per_tile == 256)
-                                 : ((plan->waves_per_wg == 4 && plan->cols_per_tile == 32 && plan->row_tiles == 1) ||
+                                 : ((plan->row_tiles == 1 && ((plan->cols_per_tile == 32 && plan->waves_per_wg == 4) ||
+                                                              (plan->cols_per_tile == 16 &&
+                                                               (plan->waves_per_wg == 4 || plan->waves_per_wg == 8)))) ||
                                     (plan->waves_per_wg == 2 && plan->cols_per_tile == 64) ||
                                     (plan->waves_per_wg == 4 && is_pow2_in(plan->cols_per_tile, 128, 256)) ||
                                     (plan->waves_per_wg == 8 && plan->cols_per_tile == 256));
@@ -323,8 +327,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
         // out, 54 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
-        // those shapes the cheapest modelled plan runs 0.12% slower than
-        // the fastest measured one on average, 2.8% at most.
+        // those shapes the cheapest modelled plan runs 0.16% slower than
+        // the fastest measured one on average, 2.9% at most.
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;

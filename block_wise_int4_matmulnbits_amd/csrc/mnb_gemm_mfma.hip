@@ -128,15 +128,19 @@ __device__ __forceinline__ int a_slot(int d, int r)
 // walking quads s, s + KS, s + 2 KS, ... of the same columns; at the end the
 // slices' accumulators meet in LDS and slice 0 adds them in slice order and
 // stores.  More waves then walk a tile's K at once where the tiles are too
-// few to fill the chip (the down projection's 4096 columns).
-template <int RT, int CT, int W, bool VEC, bool ABF16, int KS>
+// few to fill the chip (the down projection's 4096 columns).  CW = 16 (with
+// one 32-column MFMA tile per wave) gives a wave 16 real columns: lanes
+// j >= 16 load zeros and store nothing, which doubles the tiles where the
+// 32-column ones leave CUs idle.
+template <int RT, int CT, int W, bool VEC, bool ABF16, int KS, int CW = 32>
 __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 {
     constexpr int THREADS = 64 * W;
     constexpr int WC = W / KS;               // waves per K slice
     static_assert(WC * KS == W, "whole slices");
+    static_assert(CW == 32 || (CW == 16 && CT == 1), "16 columns: one MFMA tile per wave");
     constexpr int MT = 32 * RT;              // rows per workgroup tile
-    constexpr int NT = 32 * CT * WC;         // columns per workgroup tile
+    constexpr int NT = CW * CT * WC;         // columns per workgroup tile
     constexpr int QAQ = 16 * MT;             // 16-byte pieces of activations per quad
     constexpr int QA = KS * QAQ;             // per step: one quad per slice
     constexpr int SPT = QA / THREADS;        // pieces per thread
@@ -182,9 +186,9 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         // L2) and walk the column blocks.
         const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
         const int64_t r0 = tm * MT;
-        const int64_t col0 = tn * NT + 32 * CT * wcol;   // this wave's 32*CT columns
+        const int64_t col0 = tn * NT + CW * CT * wcol;   // this wave's CW*CT columns
         const int64_t left = p.N - col0;
-        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < 32 * CT ? left : 32 * CT);
+        const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < CW * CT ? left : CW * CT);
         const int64_t cb = left <= 0 ? 0 : col0;
         // Buffer resources over the wave's column rows and the tile's
         // activation rows; loads past their end (columns past N, rows past
@@ -404,7 +408,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const int64_t col = col0 + 32 * c + j;
-            if (col < p.N) {
+            if (j < CW && col < p.N) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
@@ -657,11 +661,18 @@ GemmFn lookup_gemm_ct(int rt)
 
 // Two waves with one 32-column tile each (64 columns), four waves with one
 // or two (128 or 256 columns), or eight waves with one (256 columns); or
-// one 32-row, 32-column tile whose K four waves split.
+// one 32-row tile whose K the waves split: 32 columns over four waves, 16
+// over four or eight.  (32 columns over eight waves was never faster than
+// over four in the planner's sweep.)
 template <bool VEC, bool ABF16>
 GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 {
-    if (waves == 4 && cols == 32) return rt == 1 ? mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4> : nullptr;
+    if (cols == 32 || cols == 16) {
+        if (rt != 1) return nullptr;
+        if (cols == 32) return waves == 4 ? mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4> : nullptr;
+        if (waves == 4) return mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4, 16>;
+        return waves == 8 ? mnb_gemm_mfma_kernel<1, 1, 8, VEC, ABF16, 8, 16> : nullptr;
+    }
     if (waves == 2 && cols == 64) return lookup_gemm_ct<1, 2, VEC, ABF16>(rt);
     if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16>(rt);
     if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16>(rt);
@@ -690,8 +701,9 @@ size_t gemm_lds_bytes(const mnb_plan& plan)
 {
     if (plan.row_tiles == 8)   // two stages of activations and weights
         return (size_t)2 * (kLdsTileRows + kLdsTileCols) * 2 * 4 * 16;
-    // Two steps of 32*rt rows x 128 k (one quad per K slice), fp16.
-    const size_t slices = plan.cols_per_tile == 32 ? 4 : 1;
+    // Two steps of 32*rt rows x 128 k (one quad per K slice, one slice per
+    // wave of a 32- or 16-column tile), fp16.
+    const size_t slices = plan.cols_per_tile <= 32 ? (size_t)plan.waves_per_wg : 1;
     return (size_t)2 * slices * 4 * 32 * plan.row_tiles * 4 * 16;
 }
 

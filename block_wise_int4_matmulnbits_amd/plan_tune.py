@@ -28,7 +28,7 @@ import math
 import os
 import sys
 
-TILINGS = [(1, 32, 4), (1, 64, 2), (1, 128, 4), (2, 128, 4), (4, 128, 4),
+TILINGS = [(1, 16, 4), (1, 16, 8), (1, 32, 4), (1, 64, 2), (1, 128, 4), (2, 128, 4), (4, 128, 4),
            (1, 256, 8), (2, 256, 8), (4, 256, 8), (8, 256, 8)]
 BYTES_PER_WEIGHT = 0.578   # 4 bits + a 2-byte scale and a 4-bit zero point per 32
 

@@ -151,6 +151,12 @@ def test_plan_check_engines_and_rows():
     for bad in (dict(row_tiles=2), dict(row_tiles=4), dict(waves_per_wg=2), dict(waves_per_wg=8)):
         q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=1, cols_per_tile=32, waves_per_wg=4, workgroups=1), **bad))
         assert mnb.mnb_plan_check(20, 4096, 100, q) == 9, bad         # MNB_ERR_PLAN
+    for waves in (4, 8):                                               # 16 columns, K split over 4 or 8 waves
+        q = mnb.mnb_plan(engine=2, row_tiles=1, cols_per_tile=16, waves_per_wg=waves, workgroups=3)
+        assert mnb.mnb_plan_check(20, 4096, 100, q) == 0 and q.threads_per_wg == 64 * waves and q.k_chunks == 32
+    for bad in (dict(row_tiles=2), dict(waves_per_wg=2), dict(waves_per_wg=16)):
+        q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=1, cols_per_tile=16, waves_per_wg=4, workgroups=1), **bad))
+        assert mnb.mnb_plan_check(20, 4096, 100, q) == 9, bad
     q8 = mnb.mnb_plan(engine=2, row_tiles=8, cols_per_tile=256, waves_per_wg=8, workgroups=1)
     assert mnb.mnb_plan_check(20, 4096, 100, q8) == 0              # 256 x 256, weights through LDS
     for bad in (dict(row_tiles=3), dict(row_tiles=16), dict(row_tiles=8, waves_per_wg=4),

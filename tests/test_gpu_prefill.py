@@ -55,14 +55,14 @@ def _gpu():
 @pytest.mark.parametrize("m,K,N,a_dtype,asym,want", [
     (9, 4096, 1000, W.F16, True, "decode"),          # few columns: two decode launches
     (16, 4096, 64, W.BF16, True, "decode"),          # exactly two decode launches
-    (17, 1024, 130, W.F16, False, (1, 64, 2)),       # ragged rows and columns, zero point 8
+    (17, 1024, 130, W.F16, False, (1, 16, 4)),       # ragged rows and columns, zero point 8, 16-column tiles
     (12, 4096, 6144, W.BF16, True, (1, 32, 4)),      # K split over four waves at 12 rows
     (9, 2048, 8200, W.F16, False, (1, 64, 2)),       # 64 columns on two waves, ragged columns
-    (100, 32 * 37, 77, W.BF16, True, (1, 32, 4)),    # K not a whole number of 128-wide steps
-    (130, 14336, 300, W.BF16, True, (1, 32, 4)),     # down-projection K, row tail of 2
+    (100, 32 * 37, 77, W.BF16, True, (1, 16, 4)),    # K not a whole number of 128-wide steps
+    (130, 14336, 300, W.BF16, True, (1, 16, 8)),     # down-projection K, row tail of 2, K over eight waves
     (256, 4096, 1024, W.F16, True, (1, 32, 4)),      # several row and column blocks
     (192, 4096, 6144, W.BF16, True, (2, 128, 4)),    # two 32-row tiles of 128 columns
-    (40, 4096, 65536, W.F16, True, (2, 256, 8)),     # 256 columns on eight waves, several rounds
+    (40, 4096, 65536, W.F16, True, (2, 128, 4)),     # two row tiles of 128 columns, several rounds
     (1152, 1024, 4096, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles
     (640, 512, 14336, W.F16, True, (8, 256, 8)),     # 256 x 256 tiles, weights through LDS
     (1152, 512, 14336, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles where 256 x 256 would take more rounds
@@ -110,28 +110,30 @@ def test_prefill_lds_staged_tiles(oracle_mod, m, K, N, a_dtype, asym):
         assert_prefill(oracle_mod, d, m, "prefill lds-staged wg=%d" % wg, plan)
 
 
+@pytest.mark.parametrize("cols,waves", [(32, 4), (16, 4), (16, 8)])
 @pytest.mark.parametrize("m,K,N", [(5, 32 * 61, 300), (37, 32 * 61, 300), (100, 32 * 61, 300),
-                                   (40, 32, 77), (33, 0, 64), (64, 4096, 1000)])
-def test_prefill_k_split_tiles(oracle_mod, m, K, N):
-    """32-row, 32-column tiles whose K four waves split (slice s takes
-    quads s, s + 4, ...; an odd quad count, a single block, K = 0), with 1,
-    3 and 13 workgroups and the default grid; ragged rows and columns."""
+                                   (40, 32, 77), (33, 0, 64), (64, 4096, 1000), (20, 32 * 13, 90)])
+def test_prefill_k_split_tiles(oracle_mod, m, K, N, cols, waves):
+    """32-row tiles of 32 columns whose K four waves split, or of 16 columns
+    split over four or eight waves (slice s takes quads s, s + waves, ...; an odd quad count, fewer quads
+    than slices, a single block, K = 0), with 1, 3 and 13 workgroups and the
+    default grid; ragged rows and columns."""
     d = W.generate(m, K, N, W.BF16 if m % 2 else W.F16, m != 40, 0.002, 0.02, 1.0, 900 + m)
-    for wg in (1, 3, 13, -(-m // 32) * -(-N // 32)):
-        plan = dict(engine=2, row_tiles=1, cols_per_tile=32, waves_per_wg=4, workgroups=wg)
-        assert_prefill(oracle_mod, d, m, "prefill k-split wg=%d" % wg, plan)
+    for wg in (1, 3, 13, -(-m // 32) * -(-N // cols)):
+        plan = dict(engine=2, row_tiles=1, cols_per_tile=cols, waves_per_wg=waves, workgroups=wg)
+        assert_prefill(oracle_mod, d, m, "prefill k-split %dx%d wg=%d" % (cols, waves, wg), plan)
 
 
 @pytest.mark.parametrize("m", [23, 32, 48, 64])
 def test_down_projection_k_split_default(oracle_mod, m):
-    """The down projection (K = 14336, N = 4096) with 17..128 rows: the
-    default plan splits K over four waves of 32-column tiles; check 1 on
-    sampled columns, check 2 on every output."""
+    """The down projection (K = 14336, N = 4096) with 23..64 rows: the
+    default plan splits K over the waves of 16- or 32-column tiles; check 1
+    on sampled columns, check 2 on every output."""
     K, N = 14336, 4096
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 920 + m)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = mnb.plan_for_device(m, K, N, cus)
-    assert (plan.engine, plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) == (2, 1, 32, 4)
+    assert (plan.engine, plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) in ((2, 1, 32, 4), (2, 1, 16, 4), (2, 1, 16, 8))
     G.log("[parity] down m=%d k-split, plan %s" % (m, plan.as_dict()))
     y16, c = run(d, m, W.F16)
     assert c["launches"] == 1
