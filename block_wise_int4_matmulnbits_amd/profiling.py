@@ -153,9 +153,15 @@ def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs
             f.write("| %s | %.6g |\n" % (c, vals[c]))
         f.write("\nDerived:\n\n")
         if "GRBM_GUI_ACTIVE" in vals:
-            f.write("- shader clock: %.2f GHz (GRBM_GUI_ACTIVE / 8 XCDs / kernel time)\n"
-                    % (vals["GRBM_GUI_ACTIVE"] / 8 / (pmc_mean * 1e3)))
-        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals:
+            ghz = vals["GRBM_GUI_ACTIVE"] / 8 / (pmc_mean * 1e3)
+            if ghz <= 2.45:
+                f.write("- shader clock: %.2f GHz (GRBM_GUI_ACTIVE / 8 XCDs / kernel time)\n" % ghz)
+            else:   # the counter spans more than a short kernel: no clock
+                f.write("- GRBM_GUI_ACTIVE / 8 XCDs / kernel time: %.2f GHz, above the part's 2.4 GHz: on a "
+                        "launch this short the counter spans more than the kernel, so it gives no clock "
+                        "(and no MFMA-busy fraction)\n" % ghz)
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in vals and "GRBM_GUI_ACTIVE" in vals and \
+                vals["GRBM_GUI_ACTIVE"] / 8 / (pmc_mean * 1e3) <= 2.45:
             f.write("- MFMA busy: %.1f%% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs)\n"
                     % (100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] / 8 * 1024)))
         if "SQ_INSTS_VALU" in vals and "SQ_INSTS_MFMA" in vals:
