@@ -649,7 +649,7 @@ def prefill(stream, L, cus, rotate_mb):
                 "pct_of_fp16_mfma_peak": round(100 * tflops / PEAK_FP16_MFMA_TFLOPS, 2),
                 "weight_GB/s": round(wbytes / (us * 1e3), 1), "rotated_copies": len(copies),
                 "plan": {k: v for k, v in plan.as_dict().items()
-                         if k in ("engine", "row_tiles", "cols_per_tile", "waves_per_wg", "workgroups")}}
+                         if k in ("engine", "row_tiles", "cols_per_tile", "waves_per_wg", "workgroups", "k_splits")}}
             log("[bench] prefill %s m=%d: %.1f us, %.1f TFLOP/s" % (name, m, us, tflops))
             del A, o, copies
     return out

@@ -20,6 +20,7 @@ MNB_F16 = 0
 MNB_BF16 = 1
 MNB_MAX_M = 8            # decode kernels; prefill up to MNB_MAX_ROWS
 MNB_MAX_ROWS = 1 << 20
+MNB_MAX_SPLIT_WORKSPACE = 32 << 20   # bytes of K-split partial sums a default plan may take
 MNB_LAYOUT_NATURAL = 0   # stored weight layouts (mnb_repack_weights)
 MNB_LAYOUT_EVEN_ODD = 1
 
@@ -51,7 +52,8 @@ class mnb_plan(ctypes.Structure):
                 ("threads_per_wg", ctypes.c_int32),
                 ("k_chunks", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32),
-                ("b_layout", ctypes.c_int32)]
+                ("b_layout", ctypes.c_int32),
+                ("k_splits", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -43,6 +43,9 @@ bool overlaps(const void* a, int64_t an, const void* b, int64_t bn)
 // Nominal resident waves per CU, used to size the grid when the occupancy of
 // the chosen kernel variant is not known (host-only planning).
 constexpr int kTargetWavesPerCu = 16;
+constexpr int kMaxKSplits = 64;   // K slices over workgroups (engine 2)
+// Largest workspace a default plan uses (K split over workgroups).
+constexpr size_t kMaxSplitWorkspaceBytes = MNB_MAX_SPLIT_WORKSPACE;
 
 int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
              const uint8_t* Bpacked, const uint16_t* scales,
@@ -103,25 +106,38 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
             if (st != MNB_OK) return st;
         }
     }
-    // One launch, or for a decode plan with more than MNB_MAX_M rows one
-    // launch per MNB_MAX_M rows (rows are independent in those kernels).
+    // One launch (two with K split over workgroups: the tiles, then the sum
+    // of their slices), or for a decode plan with more than MNB_MAX_M rows
+    // one launch per MNB_MAX_M rows (rows are independent in those kernels).
     const int64_t step = plan.engine == 2 ? m : MNB_MAX_M;
     const size_t a_row = (size_t)K * 2, out_row = (size_t)N * 2;
+    const int per_launch = plan.k_splits > 1 ? 2 : 1;
+    void* ws = nullptr;
+    const size_t ws_bytes = mnb::workspace_bytes(m, N, plan);
+    if (ws_bytes) {
+        int e = mnb::workspace_acquire(ws_bytes, stream, &ws);
+        if (e != 0) {
+            t_last_hip_error = e;
+            return MNB_ERR_HIP;
+        }
+    }
     int64_t launched = 0, batched = 0;
     for (int64_t r0 = 0; r0 < m; r0 += step) {
         const int64_t mc = std::min<int64_t>(step, m - r0);
         mnb::GemvArgs args{static_cast<const uint8_t*>(A) + r0 * a_row, Bpacked, scales, zero_points,
                            static_cast<uint8_t*>(out) + r0 * out_row, mc, K, N,
-                           a_dtype == MNB_BF16, out_dtype == MNB_BF16};
+                           a_dtype == MNB_BF16, out_dtype == MNB_BF16, ws};
         int e = mnb::launch_gemv(args, plan, stream);
         if (e != 0) {
             t_last_hip_error = e;
             g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
+            if (ws) mnb::workspace_release();
             return MNB_ERR_HIP;
         }
-        ++launched;
+        launched += per_launch;
         if (mc > 1) ++batched;
     }
+    if (ws) mnb::workspace_release();
     g_calls.fetch_add(1, std::memory_order_relaxed);
     g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
     if (out_dtype == MNB_BF16) g_bf16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
@@ -133,6 +149,11 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
 }  // namespace
 
 namespace mnb {
+
+size_t workspace_bytes(int64_t m, int64_t N, const mnb_plan& plan)
+{
+    return plan.engine == 2 && plan.k_splits > 1 ? (size_t)plan.k_splits * (size_t)m * (size_t)N * 4 : 0;
+}
 
 int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap)
 {
@@ -159,30 +180,52 @@ int64_t gemv_lds_bytes(int64_t m, int64_t N, const mnb_plan& plan, int32_t* tcap
 
 namespace {
 
-// Prefill tilings of engine 2 (row tiles, columns, waves) and their fitted
-// cost in microseconds on gfx950:
-//   t0 + a*K*(R-1) + g*(R-1) + d*K + h*W
-// with K in thousands, R = ceil(tiles / CUs) rounds of tiles over the
-// compute units, and W the MB of weights (with scales and zero points) per
-// CU.  a and g price the rounds after the first, d and t0 the first (a CU
+// Prefill tilings of engine 2 (row tiles, columns, waves, K splits over
+// workgroups) and their fitted cost in microseconds on gfx950:
+//   t0 + a*k*(R-1) + g*(R-1) + d*k + h*W + u*U
+// with k the thousands of K per workgroup (K / splits), R = ceil(tiles /
+// CUs) rounds of tiles over the compute units (a split multiplies the
+// tiles), W the MB of weights (with scales and zero points) per CU and U the
+// MB of fp32 partial sums per CU that a split writes and its second launch
+// reads.  a and g price the rounds after the first, d and t0 the first (a CU
 // with one tile runs it faster than two that share it), h the weights that
-// stream from HBM when few row tiles share them.
+// stream from HBM when few row tiles share them, u the partial sums.
 struct Tiling {
-    int32_t rt, cols, waves;
-    double t0, a, g, d, h;
+    int32_t rt, cols, waves, splits;
+    double t0, a, g, d, h, u;
 };
 constexpr Tiling kTilings[] = {
-    {1, 16, 4, 3.7955, 1.4178, 1.8649, 1.8878, 0.0000},    // 16 columns on a 32-column tile, K split over the waves
-    {1, 16, 8, 5.9735, 2.0027, 1.9798, 1.7233, 0.0000},
-    {1, 32, 4, 4.8657, 1.4799, 2.4373, 1.9743, 2.3661},    // K split over the four waves
-    {1, 64, 2, 0.9055, 2.2250, 1.7934, 5.4761, 12.5822},
-    {1, 128, 4, 1.1800, 4.3899, 2.6609, 5.5548, 13.7114},
-    {2, 128, 4, 3.4199, 5.8978, 2.4268, 6.0782, 5.1620},
-    {4, 128, 4, 4.5934, 12.0761, 4.0745, 11.3475, 0.0000},
-    {1, 256, 8, 0.0000, 9.4018, 3.1089, 8.9950, 35.8779},
-    {2, 256, 8, 0.8697, 12.2400, 4.3995, 10.4644, 23.6112},
-    {4, 256, 8, 3.6742, 17.6862, 8.5875, 14.7773, 6.8313},
-    {8, 256, 8, 6.5368, 33.2951, 0.0000, 24.2467, 11.1644},   // 256 x 256, weights through LDS
+    {1, 16, 4, 1, 3.7668, 1.4434, 2.2049, 2.0973, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
+    {1, 16, 8, 1, 6.3507, 1.9841, 2.1654, 1.7113, 0.0000, 0.0000},
+    {1, 32, 4, 1, 5.2063, 1.5600, 2.5006, 2.1180, 2.5214, 0.0000},   // K split over the four waves
+    {1, 64, 2, 1, 1.4704, 2.1873, 1.6887, 5.1474, 12.8967, 0.0000},
+    {1, 128, 4, 1, 2.1704, 4.2481, 2.5462, 5.7416, 14.4049, 0.0000},
+    {2, 128, 4, 1, 4.4850, 5.8660, 2.3649, 6.0841, 5.4424, 0.0000},
+    {4, 128, 4, 1, 6.8342, 12.4151, 4.9069, 11.2720, 0.0000, 0.0000},
+    {1, 256, 8, 1, 0.4677, 9.2681, 3.5522, 8.5856, 37.9079, 0.0000},
+    {2, 256, 8, 1, 1.5547, 12.6639, 2.2566, 9.4077, 30.3611, 0.0000},
+    {4, 256, 8, 1, 5.8140, 18.5306, 7.1242, 14.6185, 7.3874, 0.0000},
+    {8, 256, 8, 1, 7.4983, 33.2511, 0.0000, 24.0385, 9.3608, 0.0000},   // 256 x 256, weights through LDS
+    {1, 128, 4, 2, 5.7811, 3.6323, 0.0000, 5.6003, 10.2803, 215.4830},   // K split over 2..16 workgroups, a second launch adds the slices
+    {1, 128, 4, 4, 6.8609, 3.7349, 0.0000, 5.1529, 13.1255, 155.0454},
+    {1, 128, 4, 8, 6.5596, 0.0000, 1.7791, 5.3929, 16.7617, 144.6631},
+    {1, 128, 4, 16, 7.8648, 0.0000, 0.0000, 5.6286, 0.0000, 102.2949},
+    {2, 128, 4, 2, 6.9190, 4.1592, 0.0000, 5.8821, 3.8639, 202.7498},
+    {2, 128, 4, 4, 7.9035, 4.0848, 1.7138, 5.6569, 5.5715, 145.3534},
+    {2, 128, 4, 8, 7.7753, 0.0000, 2.8980, 5.9179, 10.9718, 131.0167},
+    {2, 128, 4, 16, 8.4022, 0.0000, 0.0000, 6.4012, 0.0000, 138.0253},
+    {4, 128, 4, 2, 8.4784, 11.4083, 0.0000, 10.9586, 8.0516, 185.2008},
+    {4, 128, 4, 4, 9.6877, 11.8197, 0.0000, 10.7060, 4.5588, 162.3002},
+    {4, 128, 4, 8, 9.3536, 0.0000, 10.4738, 11.2795, 20.1193, 102.0845},
+    {4, 128, 4, 16, 9.8888, 0.0000, 0.0000, 12.5392, 0.0000, 111.9602},
+    {1, 256, 8, 2, 4.4415, 8.7483, 0.0000, 8.6096, 19.1656, 196.3301},
+    {1, 256, 8, 4, 6.2731, 9.1836, 0.0000, 8.3648, 14.3106, 156.0304},
+    {1, 256, 8, 8, 7.1303, 12.1292, 0.0000, 8.4066, 22.5730, 57.5258},
+    {1, 256, 8, 16, 8.6743, 0.0000, 5.5817, 5.4426, 31.8635, 53.2031},
+    {2, 256, 8, 2, 4.8779, 8.6598, 0.0000, 9.4053, 15.7518, 217.3709},
+    {2, 256, 8, 4, 7.0630, 10.3611, 0.0000, 9.1982, 13.4039, 144.4728},
+    {2, 256, 8, 8, 7.2377, 12.4821, 0.0000, 9.5998, 21.8696, 104.3872},
+    {2, 256, 8, 16, 9.2107, 0.0000, 6.9512, 6.0303, 40.1321, 65.4203},
 };
 // The decode plan per launch of r <= 8 rows:
 //   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
@@ -190,7 +233,7 @@ constexpr Tiling kTilings[] = {
 // from shapes where fixed costs dominate; far beyond them the weights set
 // the time) and no less than 3 us, about what one launch takes however
 // small.
-constexpr double kDecode[4] = {2.1636, 0.5746, 0.5954, 0.2069};
+constexpr double kDecode[4] = {2.1488, 0.5730, 0.6001, 0.2345};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
 constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
@@ -198,15 +241,16 @@ constexpr double kDecodeLaunchUs = 3.0;
 int64_t prefill_tiles(const Tiling& t, int64_t m, int64_t N)
 {
     const int64_t rows = t.rt == 8 ? 256 : 32 * (int64_t)t.rt;
-    return ceil_div(m, rows) * ceil_div(N, t.cols);
+    return ceil_div(m, rows) * ceil_div(N, t.cols) * t.splits;
 }
 
 double tiling_cost(const Tiling& t, int64_t m, int64_t K, int64_t N, int num_cus)
 {
     const double R = (double)ceil_div(prefill_tiles(t, m, N), num_cus);
-    const double k = (double)K / 1e3;
+    const double k = (double)K / t.splits / 1e3;
     const double w = (double)N * (double)K * kBytesPerWeight / num_cus / 1e6;
-    return t.t0 + t.a * k * (R - 1) + t.g * (R - 1) + t.d * k + t.h * w;
+    const double ws = t.splits > 1 ? (double)t.splits * (double)m * (double)N * 4 / num_cus / 1e6 : 0.0;
+    return t.t0 + t.a * k * (R - 1) + t.g * (R - 1) + t.d * k + t.h * w + t.u * ws;
 }
 
 double decode_cost(int64_t m, int64_t K, int64_t N)
@@ -239,8 +283,14 @@ PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus)
         q.row_tiles = t.rt;
         q.cols_per_tile = t.cols;
         q.waves_per_wg = t.waves;
+        q.k_splits = t.splits;
         q.workgroups = 1;
         if (mnb_plan_check(m, K, N, &q) != MNB_OK) continue;
+        // A K split is there to fill the device: only while its tiles fit
+        // in less than two rounds over the CUs, within the workspace bound.
+        if (t.splits > 1 && (prefill_tiles(t, m, N) >= 2 * (int64_t)num_cus ||
+                             mnb::workspace_bytes(m, N, q) > kMaxSplitWorkspaceBytes))
+            continue;
         const double c = tiling_cost(t, m, K, N, num_cus);
         if (c < best_cost) {
             best_cost = c;
@@ -274,10 +324,18 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
         if (!is_pow2_in(plan->row_tiles, 1, 8) || !shape_ok ||
             (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
             return MNB_ERR_PLAN;
+        // K split over workgroups: at least one 128-wide step per slice, not
+        // for the LDS-staged 256 x 256 tiles, and a workspace below 2^31
+        // floats per slice plane.
+        if (plan->k_splits < 0 || plan->k_splits > kMaxKSplits) return MNB_ERR_PLAN;
+        if (plan->k_splits > 1 && (plan->row_tiles == 8 || plan->k_splits > ceil_div(nb, 4) ||
+                                   m * N > (int64_t)INT32_MAX))
+            return MNB_ERR_PLAN;
         plan->threads_per_wg = 64 * plan->waves_per_wg;
         plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
         return MNB_OK;
     }
+    if (plan->k_splits > 1) return MNB_ERR_PLAN;
     // Decode engines: a launch serves at most MNB_MAX_M rows; more rows run
     // as launches of MNB_MAX_M rows (the last one fewer) under this plan, so
     // the plan must fit MNB_MAX_M rows.
@@ -323,12 +381,15 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
 
     if (m > MNB_MAX_M) {
         // Prefill: every tiling of the prefill kernel that the plan check
-        // accepts, and the 8-row decode plan run once per 8 rows, priced by
+        // accepts (with K split over workgroups where that fills the
+        // device), and the 8-row decode plan run once per 8 rows, priced by
         // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
-        // out, 54 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
+        // out, 64 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
-        // those shapes the cheapest modelled plan runs 0.16% slower than
-        // the fastest measured one on average, 2.9% at most.
+        // those shapes the cheapest modelled plan runs 0.62% slower than
+        // the fastest measured one on average (9.8% at most, where a split
+        // the model ranks second would have won), and never slower than
+        // the fastest plan without a K split (12.8% faster on average).
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
@@ -339,6 +400,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         plan->row_tiles = c.t.rt;
         plan->cols_per_tile = c.t.cols;
         plan->waves_per_wg = c.t.waves;
+        plan->k_splits = c.t.splits;
         plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

@@ -77,6 +77,8 @@ struct GemmParams {
     int32_t K, nb, zb;
     uint32_t zero;           // always 0 (see vgpr_constant)
     int32_t a_bf16, out_bf16;
+    int32_t splits;          // K slices over workgroups (1: none)
+    float* ws;               // splits > 1: [splits][M][N] fp32 partial sums
 };
 
 // Weight quads in flight per column tile (the per-block loads of the
@@ -157,7 +159,6 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
     const int j = lane & 31, h = lane >> 5;
     const int nb = p.nb;
     const int nq = (nb + 3) / 4;
-    const int nsteps = (nq + KS - 1) / KS;   // steps of KS quads
     const uint32_t row_bytes = (uint32_t)p.K / 2;
     const uint32_t zdef = p.zp ? 0u : 8u;    // zero point 8 when none are given
     const uint32_t magic = vgpr_constant(0x64006400u, p.zero);
@@ -181,11 +182,19 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         pc_off[s] = (uint32_t)row * (uint32_t)p.K * 2 + 256 * qo + 64 * blk + 16 * d;
     }
 
-    for (int64_t tile = blockIdx.x; tile < tiles_m * tiles_n; tile += gridDim.x) {
+    const int64_t tiles_mn = tiles_m * tiles_n;
+    for (int64_t tile = blockIdx.x; tile < tiles_mn * p.splits; tile += gridDim.x) {
         // Consecutive workgroups share a row block (its activations stay in
-        // L2) and walk the column blocks.
-        const int64_t tm = tile / tiles_n, tn = tile - tm * tiles_n;
+        // L2) and walk the column blocks; with K split over workgroups, K
+        // slice ks of every tile comes after slice ks - 1 of all of them.
+        const int64_t ks = tile / tiles_mn, tmn = tile - ks * tiles_mn;
+        const int64_t tm = tmn / tiles_n, tn = tmn - tm * tiles_n;
         const int64_t r0 = tm * MT;
+        // Quads [qa, qb) of K: the workgroup's slice (all of K when
+        // splits = 1); blocks from bend on load zeros.
+        const int qa = (int)(nq * ks / p.splits), qb = (int)(nq * (ks + 1) / p.splits);
+        const uint32_t bend = (uint32_t)(4 * qb < nb ? 4 * qb : nb);
+        const int nsteps = (qb - qa + KS - 1) / KS;   // steps of KS quads
         const int64_t col0 = tn * NT + CW * CT * wcol;   // this wave's CW*CT columns
         const int64_t left = p.N - col0;
         const uint32_t ncols = left <= 0 ? 0u : (uint32_t)(left < CW * CT ? left : CW * CT);
@@ -204,7 +213,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         // Column tile c of the wave: columns col0 + 32c + j; step t of
         // the slice is quad KS t + slice.
         auto issue = [&](WQuad (&qs)[CT], int t) {
-            const uint32_t b = 4 * (uint32_t)(KS * t + slice);
+            const uint32_t b = 4 * (uint32_t)(qa + KS * t + slice);
 #pragma unroll
             for (int c = 0; c < CT; ++c) {
                 WQuad& q = qs[c];
@@ -215,35 +224,36 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                 for (int u = 0; u < 2; ++u)
                     q.w[u] = __builtin_amdgcn_raw_buffer_load_b128(
-                        rB, b + 2 * u + h < (uint32_t)nb ? wbase + 16 * (b + 2 * u) : kOutOfRange, 0,
+                        rB, b + 2 * u + h < bend ? wbase + 16 * (b + 2 * u) : kOutOfRange, 0,
                         kPrefillLoadPolicy);
                 if constexpr (VEC) {
                     const u32x2 sv = __builtin_amdgcn_raw_buffer_load_b64(
-                        rS, b < (uint32_t)nb ? sbase + 2 * b : kOutOfRange, 0, kPrefillLoadPolicy);
+                        rS, b < bend ? sbase + 2 * b : kOutOfRange, 0, kPrefillLoadPolicy);
                     q.s[0] = sv[0];
                     q.s[1] = sv[1];
                     q.z[0] = __builtin_amdgcn_raw_buffer_load_b16(
-                        rZ, b < (uint32_t)nb ? zbase + b / 2 : kOutOfRange, 0, kPrefillLoadPolicy);
+                        rZ, b < bend ? zbase + b / 2 : kOutOfRange, 0, kPrefillLoadPolicy);
                 } else {
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         q.s[i] = __builtin_amdgcn_raw_buffer_load_b16(
-                            rS, b + i < (uint32_t)nb ? sbase + 2 * (b + i) : kOutOfRange, 0, kPrefillLoadPolicy);
+                            rS, b + i < bend ? sbase + 2 * (b + i) : kOutOfRange, 0, kPrefillLoadPolicy);
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
                         q.z[i] = __builtin_amdgcn_raw_buffer_load_b8(
-                            rZ, b / 2 + i < (uint32_t)p.zb ? zbase + b / 2 + i : kOutOfRange, 0, kPrefillLoadPolicy);
+                            rZ, b + 2 * i < bend ? zbase + b / 2 + i : kOutOfRange, 0, kPrefillLoadPolicy);
                 }
             }
         };
 
-        // Activations of step t: quads KS t .. KS t + KS - 1 (zeros past M
-        // and K).
+        // Activations of step t: quads qa + KS t .. qa + KS t + KS - 1
+        // (zeros past M and past the slice).
         auto fetch_a = [&](uint4 (&v)[SPT], int t) {
+            const uint32_t q0 = (uint32_t)(qa + KS * t);
 #pragma unroll
             for (int s = 0; s < SPT; ++s) {
                 const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(
-                    rA, 4 * KS * t + pc_blk[s] < nb ? pc_off[s] + 256 * KS * (uint32_t)t : kOutOfRange, 0, 0);
+                    rA, 4 * q0 + pc_blk[s] < bend ? pc_off[s] + 256 * q0 : kOutOfRange, 0, 0);
                 v[s] = make_uint4(x[0], x[1], x[2], x[3]);
             }
         };
@@ -402,9 +412,11 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                         for (int q = 0; q < 16; ++q) acc[rt][c][q] += part[at(k, rt, c, q)];
         }
-        // Epilogue: fp32 -> fp16 (RNE), optionally -> bf16 (RNE), store.
-        // Accumulator element q of lane (j, h) is row (q%4) + 4h + 8(q/4),
-        // column j of its 32 x 32 tile.
+        // Epilogue: fp32 -> fp16 (RNE), optionally -> bf16 (RNE), store; or,
+        // with K split over workgroups, the fp32 sums of the slice into its
+        // plane of the workspace.  Accumulator element q of lane (j, h) is
+        // row (q%4) + 4h + 8(q/4), column j of its 32 x 32 tile.
+        float* const plane = p.ws + ks * p.M * p.N;
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const int64_t col = col0 + 32 * c + j;
@@ -414,7 +426,9 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const int64_t row = r0 + rt * 32 + (q & 3) + 4 * h + 8 * (q >> 2);
-                        if (row < p.M) {
+                        if (row < p.M && p.splits > 1) {
+                            plane[row * p.N + col] = acc[rt][c][q];
+                        } else if (row < p.M) {
                             const _Float16 hv = (_Float16)acc[rt][c][q];
                             uint16_t bits = __builtin_bit_cast(uint16_t, hv);
                             if (p.out_bf16) bits = f16_to_bf16(bits);
@@ -646,6 +660,34 @@ __global__ __launch_bounds__(512) void mnb_gemm_lds_kernel(GemmParams p)
     }
 }
 
+// K split over workgroups, second launch: output e of the M x N result is
+// the sum of its `splits` partial sums in slice order (fp32, slice 0 first),
+// rounded to fp16 (RNE) and, for bf16 output, narrowed to bf16 (RNE): the
+// store of the tile kernel.  One thread per output, consecutive threads on
+// consecutive outputs.
+__global__ __launch_bounds__(256) void mnb_split_reduce_kernel(const float* ws, int32_t splits, int64_t MN,
+                                                               uint16_t* out, int32_t out_bf16)
+{
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < MN; e += (int64_t)gridDim.x * 256) {
+        // Eight slices' loads in flight at a time, added in order (slices
+        // past the last are skipped, not added as +0, which would turn a -0
+        // sum into +0).
+        float v = 0.f;
+        for (int k0 = 0; k0 < splits; k0 += 8) {
+            float x[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = k0 + u < splits ? ws[(int64_t)(k0 + u) * MN + e] : 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (k0 + u < splits) v = k0 + u == 0 ? x[u] : v + x[u];
+        }
+        const _Float16 hv = (_Float16)v;
+        uint16_t bits = __builtin_bit_cast(uint16_t, hv);
+        if (out_bf16) bits = f16_to_bf16(bits);
+        out[e] = bits;
+    }
+}
+
 typedef void (*GemmFn)(GemmParams);
 
 template <int CT, int W, bool VEC, bool ABF16>
@@ -725,13 +767,23 @@ int launch_gemm(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.zero = 0;
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
+    p.splits = plan.k_splits > 1 ? plan.k_splits : 1;
+    p.ws = static_cast<float*>(a.ws);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn),
                                    dim3((unsigned)plan.workgroups), dim3(64 * plan.waves_per_wg), args,
-                                   gemm_lds_bytes(plan), static_cast<hipStream_t>(stream));
+                                   gemm_lds_bytes(plan), s);
     if (e == hipSuccess) e = hipGetLastError();
-    return (int)e;
+    if (e != hipSuccess || p.splits == 1) return (int)e;
+    const int64_t MN = a.m * a.N;
+    const int64_t groups = (MN + 255) / 256;
+    const unsigned grid = (unsigned)(groups < 4096 ? groups : 4096);
+    hipLaunchKernelGGL(mnb_split_reduce_kernel, dim3(grid), dim3(256), 0, s, static_cast<const float*>(p.ws),
+                       p.splits, MN, p.out, p.out_bf16);
+    return (int)hipGetLastError();
 }
+
 
 int gemm_workgroups_per_cu(const mnb_plan& plan)
 {

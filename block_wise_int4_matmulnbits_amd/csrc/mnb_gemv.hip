@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <thread>
 #include <type_traits>
 
 #include "mnb.h"
@@ -671,6 +672,87 @@ int current_device_cus(int* num_cus)
     *num_cus = n;
     return 0;
 }
+
+namespace {
+
+// Workspace buffers, one per (device, stream) and, for the per-thread
+// default stream, per host thread: work on one stream runs in order, so a
+// stream's buffer is free again for the stream's next call.  A buffer grows
+// (after its stream has drained) when a call needs more; the oldest entry
+// is given up (after the device has drained) when the table is full.  One
+// mutex, held from acquire to release, keeps two host threads from
+// interleaving their launches on the same buffer.
+struct WsEntry {
+    int dev;
+    hipStream_t stream;
+    std::thread::id thread;
+    void* ptr;
+    size_t bytes;
+    uint64_t last_use;
+};
+constexpr int kWsEntries = 32;
+std::mutex g_ws_mu;
+WsEntry g_ws[kWsEntries];
+int g_ws_used = 0;
+uint64_t g_ws_clock = 0;
+
+int acquire_locked(size_t bytes, hipStream_t stream, void** ptr)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    const std::thread::id tid = stream == hipStreamPerThread ? std::this_thread::get_id() : std::thread::id();
+    WsEntry* hit = nullptr;
+    for (int i = 0; i < g_ws_used; ++i)
+        if (g_ws[i].dev == dev && g_ws[i].stream == stream && g_ws[i].thread == tid) hit = &g_ws[i];
+    if (!hit) {
+        if (g_ws_used < kWsEntries) {
+            hit = &g_ws[g_ws_used++];
+        } else {
+            hit = &g_ws[0];
+            for (int i = 1; i < kWsEntries; ++i)
+                if (g_ws[i].last_use < hit->last_use) hit = &g_ws[i];
+            // Its stream may be gone; drain its device before freeing.
+            int cur = dev;
+            if (hit->dev != cur) (void)hipSetDevice(hit->dev);
+            e = hipDeviceSynchronize();
+            if (e == hipSuccess) e = hipFree(hit->ptr);
+            if (hit->dev != cur) (void)hipSetDevice(cur);
+            if (e != hipSuccess) return (int)e;
+        }
+        *hit = WsEntry{dev, stream, tid, nullptr, 0, 0};
+    }
+    if (hit->bytes < bytes) {
+        if (hit->ptr) {
+            e = hipStreamSynchronize(stream);   // the stream's earlier calls may still read it
+            if (e == hipSuccess) e = hipFree(hit->ptr);
+            hit->ptr = nullptr;
+            hit->bytes = 0;
+            if (e != hipSuccess) return (int)e;
+        }
+        e = hipMalloc(&hit->ptr, bytes);
+        if (e != hipSuccess) {
+            hit->ptr = nullptr;
+            return (int)e;
+        }
+        hit->bytes = bytes;
+    }
+    hit->last_use = ++g_ws_clock;
+    *ptr = hit->ptr;
+    return 0;
+}
+
+}  // namespace
+
+int workspace_acquire(size_t bytes, void* stream, void** ptr)
+{
+    g_ws_mu.lock();
+    const int e = acquire_locked(bytes, static_cast<hipStream_t>(stream), ptr);
+    if (e != 0) g_ws_mu.unlock();
+    return e;
+}
+
+void workspace_release() { g_ws_mu.unlock(); }
 
 namespace {
 

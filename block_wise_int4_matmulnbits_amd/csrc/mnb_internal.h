@@ -17,6 +17,7 @@ struct GemvArgs {
     void* out;
     int64_t m, K, N;
     int a_bf16, out_bf16;
+    void* ws;               // device workspace of workspace_bytes(), or null
 };
 
 // Queue one GEMV launch.  `plan` has passed mnb_plan_check.  Returns the
@@ -37,6 +38,9 @@ int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
 // addressed with 32-bit buffer offsets: 64 * row_tiles * K must stay within
 // this many bytes.
 constexpr uint64_t kPrefillRowBlockBytes = 0xFFFFFFF0u;
+// With plan.k_splits > 1 the workgroups each take one of k_splits slices of
+// K and leave fp32 partial sums in args.ws; a second launch adds them in
+// slice order and stores the narrowed result.
 int launch_gemm(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int gemm_workgroups_per_cu(const mnb_plan& plan);
 int gemm_kernel_info(const mnb_plan& plan, mnb_kernel_info* info);
@@ -46,6 +50,19 @@ size_t gemm_lds_bytes(const mnb_plan& plan);
 // weights from src_layout to dst_layout.  Returns a hipError_t.
 int launch_repack(const uint8_t* src, int src_layout, uint8_t* dst, int dst_layout, int64_t words,
                   void* stream);
+
+// Device workspace a launch under `plan` needs for m x N outputs: the fp32
+// partial sums of a K split over workgroups (k_splits x m x N x 4 bytes),
+// else 0.  Host-only arithmetic (mnb_api.cpp).
+size_t workspace_bytes(int64_t m, int64_t N, const mnb_plan& plan);
+
+// The library's workspace for launches on `stream` (a buffer per device and
+// stream, kept for the process and grown with hipMalloc when a call needs
+// more): on success (0) the buffer is held until workspace_release(), which
+// must follow once the launches that use it are queued; otherwise a
+// hipError_t and nothing is held.
+int workspace_acquire(size_t bytes, void* stream, void** ptr);
+void workspace_release();
 
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);

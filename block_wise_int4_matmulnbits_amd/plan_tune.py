@@ -14,9 +14,11 @@ and takes the cheapest.  This script produces both halves of that:
       regret of the fitted choice on every measured shape.
 
 Cost of a tiling (µs), with R = ceil(tiles / CUs) rounds of tiles over the
-compute units, K in thousands and W the weight bytes per CU in MB (0.578
-bytes per weight with the scales and zero points):
-    t0 + a*K*(R-1) + g*(R-1) + d*K + h*W
+compute units (a tiling that splits K over S workgroups has S times the
+tiles), k the thousands of K per workgroup (K / S), W the weight bytes per
+CU in MB (0.578 bytes per weight with the scales and zero points) and U the
+MB per CU of fp32 partial sums a split writes (S * m * N * 4 / CUs):
+    t0 + a*k*(R-1) + g*(R-1) + d*k + h*W + u*U
 Cost of the decode plan: per launch of r rows,
     max(exp(c0) * (K/4096)^c1 * (N/4096)^c2 * (r/8)^c3, weight bytes / 6.5 TB/s, 3 us),
 summed over the ceil(m/8) launches.
@@ -28,8 +30,12 @@ import math
 import os
 import sys
 
-TILINGS = [(1, 16, 4), (1, 16, 8), (1, 32, 4), (1, 64, 2), (1, 128, 4), (2, 128, 4), (4, 128, 4),
-           (1, 256, 8), (2, 256, 8), (4, 256, 8), (8, 256, 8)]
+# (row tiles, columns, waves, K splits over workgroups)
+TILINGS = ([(1, 16, 4, 1), (1, 16, 8, 1), (1, 32, 4, 1), (1, 64, 2, 1), (1, 128, 4, 1), (2, 128, 4, 1),
+            (4, 128, 4, 1), (1, 256, 8, 1), (2, 256, 8, 1), (4, 256, 8, 1), (8, 256, 8, 1)] +
+           [(rt, cols, waves, s) for rt, cols, waves in ((1, 128, 4), (2, 128, 4), (4, 128, 4), (1, 256, 8), (2, 256, 8))
+            for s in (2, 4, 8, 16)])
+MAX_SPLIT_WORKSPACE = 32 << 20   # bytes of partial sums a default plan may take (MNB_MAX_SPLIT_WORKSPACE)
 BYTES_PER_WEIGHT = 0.578   # 4 bits + a 2-byte scale and a 4-bit zero point per 32
 
 SHAPES = [(64, 4096, 28672), (128, 4096, 28672), (256, 4096, 28672), (16, 4096, 28672), (64, 14336, 4096),
@@ -42,22 +48,41 @@ SHAPES = [(64, 4096, 28672), (128, 4096, 28672), (256, 4096, 28672), (16, 4096, 
           (16, 14336, 4096), (9, 4096, 151936), (16, 4096, 151936), (12, 4096, 4096), (9, 8192, 2048),
           (16, 14336, 2048), (12, 8192, 28672), (512, 4096, 28672), (2048, 4096, 28672), (512, 14336, 4096),
           (48, 14336, 4096), (96, 14336, 4096), (32, 14336, 4096), (4096, 4096, 28672), (16, 4096, 4096),
-          (64, 4096, 4096), (32, 8192, 8192), (512, 4096, 4096), (96, 4096, 151936), (160, 14336, 4096)]
+          (64, 4096, 4096), (32, 8192, 8192), (512, 4096, 4096), (96, 4096, 151936), (160, 14336, 4096),
+          (9, 14336, 4096), (12, 14336, 4096), (24, 4096, 4096), (48, 4096, 4096), (96, 4096, 6144),
+          (64, 8192, 2048), (32, 14336, 2048), (256, 4096, 4096), (48, 4096, 28672), (80, 14336, 4096)]
 
 
 def key_of(t):
+    """"rt,cols,waves" for a tiling without a K split, "rt,cols,waves,sS" with one
+    (and "m,K,N" for a shape)."""
+    if len(t) == 4:
+        return "%d,%d,%d" % t[:3] if t[3] == 1 else "%d,%d,%d,s%d" % t
     return "%d,%d,%d" % t
 
 
 def tiles_of(t, m, N):
-    rt, cols, _ = t
+    rt, cols, _, splits = t
     rows = 256 if rt == 8 else 32 * rt
-    return -(-m // rows) * -(-N // cols)
+    return -(-m // rows) * -(-N // cols) * splits
+
+
+def workspace_bytes(t, m, N):
+    return t[3] * m * N * 4 if t[3] > 1 else 0
+
+
+def admitted(t, m, N, cus):
+    """A tiling the planner considers: one that splits K over workgroups only
+    while its tiles fit in less than two rounds over the compute units (the
+    split is there to fill the device, not to add rounds)."""
+    return t[3] == 1 or tiles_of(t, m, N) < 2 * cus
 
 
 def tiling_features(t, m, K, N, cus):
     R = -(-tiles_of(t, m, N) // cus)
-    return [1.0, K / 1e3 * (R - 1), float(R - 1), K / 1e3, N * K * BYTES_PER_WEIGHT / cus / 1e6]
+    k = K / t[3] / 1e3
+    return [1.0, k * (R - 1), float(R - 1), k, N * K * BYTES_PER_WEIGHT / cus / 1e6,
+            workspace_bytes(t, m, N) / cus / 1e6]
 
 
 DECODE_BYTES_PER_US = 6.5e6   # floors of a decode launch: its weight bytes at 6.5 TB/s,
@@ -118,14 +143,15 @@ def sweep(out_path):
                O.data_ptr(), mnb.MNB_BF16, stream.cuda_stream)
         row = {}
         for t in TILINGS:
-            rt, cols, waves = t
-            p = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=1)
-            if mnb.mnb_plan_check(m, K, N, p) != 0:
+            rt, cols, waves, splits = t
+            p = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=1,
+                             k_splits=splits)
+            if mnb.mnb_plan_check(m, K, N, p) != 0 or workspace_bytes(t, m, N) > MAX_SPLIT_WORKSPACE:
                 continue
             occ = mnb.mnb_get_kernel_info(m, K, p)["wgs_per_cu"]
             tiles = tiles_of(t, m, N)
             p = mnb.mnb_plan(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves,
-                             workgroups=max(1, min(tiles, occ * cus)))
+                             workgroups=max(1, min(tiles, occ * cus)), k_splits=splits)
             row[key_of(t)] = {"us": round(timed(raw, p), 3), "occ": occ, "tiles": tiles}
         if m <= 16:
             row["decode"] = {"us": round(timed(raw, mnb.plan_for_device(8, K, N, cus)), 3)}
@@ -147,7 +173,7 @@ def fit_model(data):
     for t in TILINGS:
         X, y = [], []
         for (m, K, N), row in shapes:
-            if key_of(t) in row:
+            if key_of(t) in row and admitted(t, m, N, cus):
                 X.append(tiling_features(t, m, K, N, cus))
                 y.append(row[key_of(t)]["us"])
         X, y = np.array(X), np.array(y)
@@ -161,7 +187,7 @@ def model_pick(table, dec, m, K, N, cus, candidates):
     """The cheapest of `candidates` (tiling keys and "decode") by the model."""
     cost = {}
     for t in TILINGS:
-        if key_of(t) in candidates:
+        if key_of(t) in candidates and admitted(t, m, N, cus):
             cost[key_of(t)] = sum(f * c for f, c in zip(tiling_features(t, m, K, N, cus), table[t]))
     if "decode" in candidates:
         cost["decode"] = decode_cost(dec, m, K, N)
@@ -171,19 +197,23 @@ def model_pick(table, dec, m, K, N, cus, candidates):
 def fit(path):
     data = json.load(open(path))
     table, dec = fit_model(data)
-    print("// rt, cols, waves, t0, a, g, d, h")
+    print("// rt, cols, waves, splits, t0, a, g, d, h, u")
     for t in TILINGS:
-        print("    {%d, %d, %d, %s}," % (*t, ", ".join("%.4ff" % v for v in table[t])))
+        print("    {%d, %d, %d, %d, %s}," % (*t, ", ".join("%.4f" % v for v in table[t])))
     print("// decode: %s" % ", ".join("%.4f" % v for v in dec))
-    regrets = []
+    regrets, vs_unsplit = [], []
     for key, row in sorted(data["shapes"].items()):
         m, K, N = map(int, key.split(","))
         pick = model_pick(table, dec, m, K, N, data["cus"], row)
         best = min(v["us"] for v in row.values())
+        unsplit = min(v["us"] for k, v in row.items() if ",s" not in k)
         regrets.append(row[pick]["us"] / best - 1)
-        print("%-18s pick %-8s %8.2f us  best %8.2f  regret %4.1f%%" % (key, pick, row[pick]["us"], best,
-                                                                          100 * regrets[-1]))
-    print("mean regret %.2f%%, max %.1f%%" % (100 * sum(regrets) / len(regrets), 100 * max(regrets)))
+        vs_unsplit.append(row[pick]["us"] / unsplit - 1)
+        print("%-18s pick %-12s %8.2f us  best %8.2f  regret %4.1f%%  vs best unsplit %+5.1f%%" % (
+            key, pick, row[pick]["us"], best, 100 * regrets[-1], 100 * vs_unsplit[-1]))
+    print("mean regret %.2f%%, max %.1f%%; against the best plan without a K split: mean %+.2f%%, worst %+.1f%%" % (
+        100 * sum(regrets) / len(regrets), 100 * max(regrets), 100 * sum(vs_unsplit) / len(vs_unsplit),
+        100 * max(vs_unsplit)))
 
 
 if __name__ == "__main__":

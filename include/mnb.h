@@ -25,13 +25,14 @@
 #ifndef MNB_H
 #define MNB_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 4
+#define MNB_ABI_VERSION 5
 
 /* Element types of A and of the output. */
 typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
@@ -84,10 +85,15 @@ typedef enum {
 #define MNB_MAX_ROWS (1 << 20)
 /* Largest K accepted (blocks are indexed with 32-bit integers). */
 #define MNB_MAX_K (1 << 24)
+/* Largest device workspace (bytes) a default plan takes: the planner splits K
+ * over workgroups (fp32 partial sums, k_splits * m * N * 4 bytes) only
+ * within it. */
+#define MNB_MAX_SPLIT_WORKSPACE ((size_t)32 << 20)
 
 /*
- * matmul_nbits -- y = A * dequant(B)^T, kernel launches on `stream`: one,
- * or for a decode plan with m > 8 one per 8 rows.
+ * matmul_nbits -- y = A * dequant(B)^T, kernel launches on `stream`: one;
+ * two for a prefill plan that splits K over workgroups (the tiles, then the
+ * sum of their slices); or for a decode plan with m > 8 one per 8 rows.
  *
  *   A            device, [m][K] row-major, fp16 or bf16 per a_dtype; 16-byte
  *                aligned.  Must hold finite values that are finite in fp16.
@@ -115,14 +121,23 @@ typedef enum {
  *   stream       hipStream_t, or NULL for the default stream.
  *
  * Asynchronous: returns after the launch is queued.  Inputs must stay valid
- * and unmodified until the stream reaches this work.  The fp32 summation
- * order is fixed by (m, K) for m <= 8 (never by N or the device), and by
+ * and unmodified until the stream reaches this work.
+ * Device memory: a plan that splits K over workgroups (prefill, few
+ * columns; at most MNB_MAX_SPLIT_WORKSPACE bytes for a default plan) keeps
+ * its fp32 partial sums in a workspace the library holds per device and
+ * stream (per host thread on hipStreamPerThread) for the life of the
+ * process.  The first such call on a stream, and a call that needs more
+ * than the stream's workspace holds, allocate it with hipMalloc (a larger
+ * one after the stream has drained); other calls allocate nothing.
+ * The fp32 summation order is fixed by (m, K) for m <= 8 (never by N or
+ * the device), and by
  * (m, K, N) and the device's compute-unit count for m > 8 (which tiling
  * runs, and whether it splits K, depends on how the tiles fill the device).
  * So equal inputs give bitwise equal outputs on the same device, column
  * shards of one matrix give the bits of the whole at m <= 8, and the bf16
  * output equals the fp16 output of the same call narrowed to bf16.
- * Thread safety: may be called from several host threads at once.
+ * Thread safety: may be called from several host threads at once (calls
+ * that split K queue their two launches under one library lock).
  */
 int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
                  const uint8_t* Bpacked, const uint16_t* scales,
@@ -144,8 +159,11 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
  * dequantized to fp16 and v_mfma_f32_32x32x16_f16 accumulating over all of
  * K.  With 32 columns (row_tiles 1, waves_per_wg 4) the four waves split K
  * instead (wave s takes the 128-wide steps s, s + 4, ...) and their fp32
- * sums are added in wave order at the end.  Also accepted for any m >= 1
- * as an explicit plan.
+ * sums are added in wave order at the end.  With k_splits > 1 the tiles
+ * also split K over workgroups: slice s of k_splits takes the 128-wide
+ * steps [S*s/k_splits, S*(s+1)/k_splits) of the S steps, its fp32 sums go
+ * to a workspace, and a second launch adds the slices in order and
+ * narrows.  Also accepted for any m >= 1 as an explicit plan.
  * engine 3 (4x4x4 MFMA kernel, m <= 8): a workgroup of waves_per_wg waves
  * walks its columns cols_per_tile (4 or 8) at a time; lane i of each group
  * of four lanes holds column i of a quad and rows i and 4 + i of the
@@ -173,6 +191,13 @@ typedef struct {
     int32_t row_tiles;       /* engine 2: 32-row tiles per workgroup, 1, 2 or 4  */
     int32_t b_layout;        /* MNB_LAYOUT_* of Bpacked; engine 2 takes
                                 MNB_LAYOUT_NATURAL only                         */
+    int32_t k_splits;        /* engine 2 with row_tiles 1, 2 or 4: K split into
+                                this many slices over the workgroups, whose fp32
+                                partial sums a second launch adds in slice order
+                                (workspace: k_splits * m * N * 4 bytes, taken
+                                from a stream-ordered pool the library keeps per
+                                device); 0 or 1: no split.  Must be 0 or 1 for
+                                the other engines.                             */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`

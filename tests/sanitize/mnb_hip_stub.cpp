@@ -20,5 +20,11 @@ int current_device_cus(int* num_cus)
 }
 int workgroups_per_cu(int64_t, int64_t, int64_t, const mnb_plan&) { return 0; }
 int kernel_info(int64_t, int64_t, const mnb_plan&, mnb_kernel_info*) { return kNoDevice; }
+int workspace_acquire(size_t, void*, void** ptr)
+{
+    *ptr = nullptr;
+    return kNoDevice;
+}
+void workspace_release() {}
 
 }  // namespace mnb

@@ -126,14 +126,18 @@ def test_default_prefill_plans():
             assert mnb.mnb_plan_check(m, K, N, q) == 0
             assert q.threads_per_wg == 64 * p.waves_per_wg and q.k_chunks == (K // 32 + 3) // 4
             rows = 256 if p.row_tiles == 8 else 32 * p.row_tiles
-            tiles = -(-m // rows) * -(-N // p.cols_per_tile)
+            splits = max(p.k_splits, 1)
+            tiles = -(-m // rows) * -(-N // p.cols_per_tile) * splits
             assert 1 <= p.workgroups <= min(tiles, max(occ, 1) * cus), (m, K, N, cus)
-    # The benchmark's prefill shapes (gate_up m = 512 and 2048, down m =
-    # 512 and 2048), on the tilings measured fastest for them.
-    for m, K, N, want in ((512, 4096, 28672, (8, 256, 8)), (2048, 4096, 28672, (8, 256, 8)),
-                          (512, 14336, 4096, (2, 128, 4)), (2048, 14336, 4096, (4, 256, 8))):
+            if splits > 1:   # to fill the device: under two rounds, within the workspace bound
+                assert tiles < 2 * cus and splits * m * N * 4 <= mnb.MNB_MAX_SPLIT_WORKSPACE, (m, K, N, cus)
+    # The benchmark's prefill shapes (gate_up m = 512 and 2048, down m = 16,
+    # 64, 512 and 2048), on the tilings measured fastest for them.
+    for m, K, N, want in ((512, 4096, 28672, (8, 256, 8, 1)), (2048, 4096, 28672, (8, 256, 8, 1)),
+                          (16, 14336, 4096, (1, 256, 8, 16)), (64, 14336, 4096, (2, 128, 4, 8)),
+                          (512, 14336, 4096, (2, 256, 8, 2)), (2048, 14336, 4096, (4, 256, 8, 1))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
-        assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg) == want, (m, K, N)
+        assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg, max(p.k_splits, 1)) == want, (m, K, N)
 
 
 def test_plan_check_engines_and_rows():
@@ -167,6 +171,22 @@ def test_plan_check_engines_and_rows():
         q = mnb.mnb_plan(**dict(dict(engine=2, row_tiles=4, cols_per_tile=128, waves_per_wg=4,
                                      workgroups=3), **bad))
         assert mnb.mnb_plan_check(20, 4096, 100, q) == 9
+    # K split over workgroups: 1..64 slices of at least one 128-wide step,
+    # not for the 256 x 256 tiles nor the decode engines (0 and 1 mean none).
+    for splits in (0, 1, 2, 16, 32):
+        q = mnb.mnb_plan(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=1, k_splits=splits)
+        assert mnb.mnb_plan_check(20, 4096, 100, q) == 0, splits
+    for splits in (-1, 33, 65):   # K = 4096: 32 steps
+        q = mnb.mnb_plan(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=1, k_splits=splits)
+        assert mnb.mnb_plan_check(20, 4096, 100, q) == 9, splits
+    q = mnb.mnb_plan(engine=2, row_tiles=8, cols_per_tile=256, waves_per_wg=8, workgroups=1, k_splits=2)
+    assert mnb.mnb_plan_check(20, 4096, 100, q) == 9
+    q = mnb.mnb_plan(engine=2, row_tiles=1, cols_per_tile=16, waves_per_wg=8, workgroups=1, k_splits=4)
+    assert mnb.mnb_plan_check(20, 4096, 100, q) == 0                 # with the K split over waves too
+    for m in (1, 4):
+        d = mnb.mnb_plan_default(m, 4096, 4096, 256, 0)
+        d.k_splits = 2
+        assert mnb.mnb_plan_check(m, 4096, 4096, d) == 9
     # 32-bit activation offsets within a workgroup's rows: 64 * row_tiles * K
     # bytes at most 2^32 - 16.
     big = 1 << 24

@@ -6,13 +6,14 @@ exact weights, check 2 (bf16 output bit-identical to the narrowing of the
 fp16 output), counters, no stale element.  The prefill kernel multiplies
 weights rounded to fp16, so it is also held to a much tighter bound against
 the oracle run with the same rounded weights: the only difference left is
-fp32 accumulation, at most (K/32 + 32) roundings of 2^-24 relative to
-sum |a w| (one chained MFMA per block, 32 products each), plus one fp16 ulp
-for the output rounding (the tiles that split K over four waves add the
-slices' fp32 sums at the end: fewer roundings in a chain, not more).  The
-summation order of an output depends only on K and on whether the plan
-splits K, so rows computed in launches of different heights under tilings
-that do not split K are bit-identical.
+fp32 accumulation, at most (K/32 + 32 + S) roundings of 2^-24 relative to
+sum |a w| (one chained MFMA per block, 32 products each, and S - 1 sums of
+K slices), plus one fp16 ulp for the output rounding (the tiles that split
+K over their waves or over workgroups add the slices' fp32 sums at the end:
+fewer roundings in a chain, not more).  The summation order of an output
+depends only on K and on how the plan splits K, so rows computed in
+launches of different heights under tilings that do not split K are
+bit-identical.
 """
 import numpy as np
 import pytest
@@ -25,18 +26,25 @@ from tests.hand_cases import build_case, load_cases
 from tests.test_gpu_parity import assert_parity, effective_plan, run
 
 
+def fp16_weight_tol(oracle_mod, ref, K, splits=1):
+    """Bound of the prefill kernel against the oracle run with the kernel's
+    fp16 weights: the fp32 roundings of one output's chain, plus one ulp."""
+    return (K // 32 + 32 + max(splits, 1)) * 2.0 ** -24 * ref["abs"] + oracle_mod.f16_ulp(ref["f16"])
+
+
 def assert_prefill(oracle_mod, d, m, label, plan=None):
     """Checks 1 and 2; when the call runs the prefill kernel, also the bound
     of its fp16-weight reading."""
     y16, _, _ = assert_parity(oracle_mod, d, m, label, plan)
-    if effective_plan(m, d["K"], d["N"], plan).get("engine") != 2:
+    eff = effective_plan(m, d["K"], d["N"], plan)
+    if eff.get("engine") != 2:
         return y16
     K = d["K"]
     ref = oracle_mod.matmul_nbits(d["A"][:m], d["a_dtype"] == W.BF16, d["B"], d["scales"],
                                   d["zp"], m, K, d["N"], weights_f16=True)
     g = G.f16_values(y16)
     err = np.abs(g - ref["f64"])
-    tol = (K // 32 + 32) * 2.0 ** -24 * ref["abs"] + oracle_mod.f16_ulp(ref["f16"])
+    tol = fp16_weight_tol(oracle_mod, ref, K, eff.get("k_splits", 1))
     bad = ~(err <= tol)
     assert not bad.any(), "fp16-weight bound failed at %d of %d outputs" % (bad.sum(), bad.size)
     G.log("[parity] %s: within %.3g of the fp16-weight bound" % (label, float(np.max(err / tol))))
@@ -51,21 +59,22 @@ def _gpu():
 
 
 # The planner's cost model picks these plans at 256 CUs (row tiles, columns,
-# waves), or "decode" for the 8-row decode plan run per 8 rows.
+# waves, K splits over workgroups), or "decode" for the 8-row decode plan
+# run per 8 rows.
 @pytest.mark.parametrize("m,K,N,a_dtype,asym,want", [
-    (9, 4096, 1000, W.F16, True, "decode"),          # few columns: two decode launches
-    (16, 4096, 64, W.BF16, True, "decode"),          # exactly two decode launches
-    (17, 1024, 130, W.F16, False, (1, 16, 4)),       # ragged rows and columns, zero point 8, 16-column tiles
-    (12, 4096, 6144, W.BF16, True, (1, 32, 4)),      # K split over four waves at 12 rows
-    (9, 2048, 8200, W.F16, False, (1, 64, 2)),       # 64 columns on two waves, ragged columns
-    (100, 32 * 37, 77, W.BF16, True, (1, 16, 4)),    # K not a whole number of 128-wide steps
-    (130, 14336, 300, W.BF16, True, (1, 16, 8)),     # down-projection K, row tail of 2, K over eight waves
-    (256, 4096, 1024, W.F16, True, (1, 32, 4)),      # several row and column blocks
-    (192, 4096, 6144, W.BF16, True, (2, 128, 4)),    # two 32-row tiles of 128 columns
-    (40, 4096, 65536, W.F16, True, (2, 128, 4)),     # two row tiles of 128 columns, several rounds
-    (1152, 1024, 4096, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles
-    (640, 512, 14336, W.F16, True, (8, 256, 8)),     # 256 x 256 tiles, weights through LDS
-    (1152, 512, 14336, W.BF16, True, (4, 256, 8)),   # 128 x 256 tiles where 256 x 256 would take more rounds
+    (9, 4096, 1000, W.F16, True, "decode"),            # few columns: two decode launches
+    (16, 4096, 64, W.BF16, True, "decode"),            # exactly two decode launches
+    (17, 1024, 130, W.F16, False, (1, 16, 4, 1)),      # ragged rows and columns, zero point 8, 16-column tiles
+    (12, 4096, 6144, W.BF16, True, (1, 256, 8, 8)),    # K over eight workgroups at 12 rows
+    (9, 2048, 8200, W.F16, False, (1, 256, 8, 4)),     # K over four workgroups, ragged columns
+    (100, 32 * 37, 77, W.BF16, True, (1, 16, 4, 1)),   # K not a whole number of 128-wide steps
+    (130, 14336, 300, W.BF16, True, (1, 128, 4, 16)),  # down-projection K over 16 workgroups, row tail of 2
+    (256, 4096, 1024, W.F16, True, (1, 256, 8, 8)),    # several row and column blocks, K over eight
+    (192, 4096, 6144, W.BF16, True, (2, 128, 4, 1)),   # two 32-row tiles of 128 columns
+    (40, 4096, 65536, W.F16, True, (2, 256, 8, 1)),    # two row tiles of 256 columns, several rounds
+    (1152, 1024, 4096, W.BF16, True, (4, 256, 8, 1)),  # 128 x 256 tiles
+    (640, 512, 14336, W.F16, True, (8, 256, 8, 1)),    # 256 x 256 tiles, weights through LDS
+    (1152, 512, 14336, W.BF16, True, (4, 256, 8, 1)),  # 128 x 256 tiles where 256 x 256 would take more rounds
 ])
 def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym, want):
     d = W.generate(m, K, N, a_dtype, asym, 0.001, 0.01, 0.5, 700 + m)
@@ -75,7 +84,8 @@ def test_prefill_default_plan(oracle_mod, m, K, N, a_dtype, asym, want):
         if want == "decode":
             assert plan.engine != 2 and plan.as_dict() == mnb.plan_for_device(8, K, N, cus).as_dict()
         else:
-            assert plan.engine == 2 and (plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) == want
+            got = (plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg, max(plan.k_splits, 1))
+            assert plan.engine == 2 and got == want
     assert_prefill(oracle_mod, d, m, "prefill", None)
 
 
@@ -124,19 +134,22 @@ def test_prefill_k_split_tiles(oracle_mod, m, K, N, cols, waves):
         assert_prefill(oracle_mod, d, m, "prefill k-split %dx%d wg=%d" % (cols, waves, wg), plan)
 
 
-@pytest.mark.parametrize("m", [23, 32, 48, 64])
+@pytest.mark.parametrize("m", [16, 23, 32, 48, 64, 128])
 def test_down_projection_k_split_default(oracle_mod, m):
-    """The down projection (K = 14336, N = 4096) with 23..64 rows: the
-    default plan splits K over the waves of 16- or 32-column tiles; check 1
-    on sampled columns, check 2 on every output."""
+    """The down projection (K = 14336, N = 4096) with 16..128 rows: the
+    default plan splits K over workgroups (two launches: the tiles, then the
+    sum of their slices); check 1 on sampled columns, check 2 on every
+    output."""
     K, N = 14336, 4096
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 920 + m)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = mnb.plan_for_device(m, K, N, cus)
-    assert (plan.engine, plan.row_tiles, plan.cols_per_tile, plan.waves_per_wg) in ((2, 1, 32, 4), (2, 1, 16, 4), (2, 1, 16, 8))
+    assert plan.engine == 2
+    if cus == 256:
+        assert plan.k_splits > 1
     G.log("[parity] down m=%d k-split, plan %s" % (m, plan.as_dict()))
     y16, c = run(d, m, W.F16)
-    assert c["launches"] == 1
+    assert c["launches"] == (2 if plan.k_splits > 1 else 1)
     ybf, _ = run(d, m, W.BF16)
     assert not np.any(y16 == 0xFFFF)
     assert G.check2(ybf, y16, oracle_mod).all()
@@ -148,11 +161,11 @@ def test_down_projection_k_split_default(oracle_mod, m):
 
 @pytest.mark.parametrize("m", [9, 16])
 def test_few_tiles_run_decode_kernels_per_8_rows(oracle_mod, m):
-    """The down projection's K over 2048 columns with 9..16 rows: 64
-    tiles of 32 columns for 256 CUs, so the default plan runs the decode
-    kernels in launches of 8 rows: against the oracle, and each block of 8
-    rows bit-equal to its own launch."""
-    K, N = 14336, 2048
+    """The down projection's K over 512 columns with 9..16 rows: too few
+    tiles even with K split over workgroups, so the default plan runs the
+    decode kernels in launches of 8 rows: against the oracle, and each block
+    of 8 rows bit-equal to its own launch."""
+    K, N = 14336, 512
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 860 + m)
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     plan = mnb.plan_for_device(m, K, N, cus)
@@ -213,9 +226,10 @@ def test_prefill_full_size_sampled(oracle_mod, name, K, N, m):
     row), check 2 on every output."""
     d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 750 + m)
     G.log("[parity] prefill %s m=%d K=%d N=%d default plan" % (name, m, K, N))
+    plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
     y16, c16 = run(d, m, W.F16)
     ybf, _ = run(d, m, W.BF16)
-    assert c16["launches"] == 1
+    assert c16["launches"] == (2 if plan.k_splits > 1 else 1)
     assert not np.any(y16 == 0xFFFF) and not np.any(ybf == 0xFFFF)
     assert G.check2(ybf, y16, oracle_mod).all()
     rng = np.random.default_rng(751)
@@ -227,8 +241,7 @@ def test_prefill_full_size_sampled(oracle_mod, name, K, N, m):
     ref16 = oracle_mod.matmul_nbits(A, True, d["B"], d["scales"], d["zp"], m, K, N, cols=cols,
                                     weights_f16=True)
     err = np.abs(G.f16_values(y16[:, cols]) - ref16["f64"])
-    tol = (K // 32 + 32) * 2.0 ** -24 * ref16["abs"] + oracle_mod.f16_ulp(ref16["f16"])
-    assert (err <= tol).all()
+    assert (err <= fp16_weight_tol(oracle_mod, ref16, K, plan.k_splits)).all()
     G.log("[parity] prefill %s m=%d ok: max err %.3f fp16 ulp vs exact weights" % (name, m, max_ulps))
 
 
@@ -295,3 +308,56 @@ def test_hand_case_through_prefill_engine(case):
         ybf, _ = run(d, m, W.BF16, plan)
         assert np.array_equal(y16, np.tile(c["f16"], (reps, 1))), [hex(v) for v in y16[:c["m"]].ravel()]
         assert np.array_equal(ybf, np.tile(c["bf16"], (reps, 1))), [hex(v) for v in ybf[:c["m"]].ravel()]
+
+
+@pytest.mark.parametrize("rt,cols,waves", [(1, 128, 4), (2, 128, 4), (4, 128, 4), (1, 256, 8), (2, 256, 8),
+                                           (1, 64, 2), (1, 32, 4), (1, 16, 8)])
+@pytest.mark.parametrize("m,K,N,splits", [(37, 32 * 61, 300, 3),    # ragged rows, columns, odd block count
+                                          (9, 4096, 513, 7),        # 32 steps in 7 unequal slices
+                                          (70, 32 * 13, 90, 4),     # 4 steps, one per slice (the last ragged)
+                                          (20, 14336, 260, 16)])    # long K, 16 slices
+def test_prefill_k_split_over_workgroups(oracle_mod, rt, cols, waves, m, K, N, splits):
+    """K split over workgroups: each workgroup takes one slice of K for its
+    tile and leaves fp32 partial sums, a second launch adds the slices in
+    order and narrows.  Every tiling that takes a split, with 1, 3 and 13
+    workgroups and the full grid; zero points absent in one case."""
+    d = W.generate(m, K, N, W.BF16 if m % 2 else W.F16, m != 70, 0.002, 0.02, 1.0, 960 + m + rt + cols)
+    tiles = -(-m // (32 * rt)) * -(-N // cols) * splits
+    for wg in (1, 3, 13, tiles):
+        plan = dict(engine=2, row_tiles=rt, cols_per_tile=cols, waves_per_wg=waves, workgroups=wg,
+                    k_splits=splits)
+        assert_prefill(oracle_mod, d, m, "prefill %dx%dx%d split %d wg=%d" % (rt, cols, waves, splits, wg), plan)
+
+
+def test_k_split_is_deterministic_across_workspace_reuse():
+    """Split plans of different workspace sizes in a row on one stream, then
+    on a second stream: every call of a plan gives the same bits, and the
+    launch counter counts the tiles and the sum of the slices."""
+    m, K, N = 40, 14336, 1000
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 990)
+    big = dict(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=256, k_splits=16)
+    small = dict(engine=2, row_tiles=1, cols_per_tile=256, waves_per_wg=8, workgroups=64, k_splits=2)
+    y_big, c = run(d, m, W.BF16, big)
+    assert c["launches"] == 2
+    y_small, _ = run(d, m, W.BF16, small)
+    y_big2, _ = run(d, m, W.BF16, big)
+    assert np.array_equal(y_big, y_big2)
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        y_small2, _ = run(d, m, W.BF16, small)
+        y_big3, _ = run(d, m, W.BF16, big)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_small, y_small2) and np.array_equal(y_big, y_big3)
+    _, c1 = run(d, m, W.BF16, dict(big, k_splits=1))
+    assert c1["launches"] == 1
+
+
+def test_k_split_default_few_columns(oracle_mod):
+    """9 and 16 rows of the down projection's K over 2048 columns: the
+    default plan splits K over workgroups; full parity."""
+    for m in (9, 16):
+        K, N = 14336, 2048
+        d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 995 + m)
+        plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
+        G.log("[parity] %dx%dx%d default plan %s" % (m, K, N, plan.as_dict()))
+        assert_prefill(oracle_mod, d, m, "split default m=%d" % m, None)

@@ -16,7 +16,7 @@ import torch
 import block_wise_int4_matmulnbits_amd as mnb
 from block_wise_int4_matmulnbits_amd import workloads as W
 from tests import gpu_util as G
-from tests.test_gpu_parity import launch_rows
+from tests.test_gpu_parity import launch_count
 
 pytestmark = pytest.mark.gpu
 
@@ -119,6 +119,6 @@ def test_concurrent_host_threads():
     for (_, _, _, _, alone, out) in jobs:
         assert np.array_equal(G.bits(alone), G.bits(out))
     c1 = mnb.mnb_counters_get()
-    per_call = sum(len(launch_rows(m, K, N)) for (m, K, N, _) in shapes)   # 40 rows: 5 launches
+    per_call = sum(launch_count(m, K, N) for (m, K, N, _) in shapes)
     assert c1["launches"] - c0["launches"] == reps * per_call
     assert c1["calls"] - c0["calls"] == reps * len(jobs)

@@ -1,11 +1,12 @@
 """The prefill planner's cost model against measured timings (no GPU).
 
 tests/data/prefill_tilings_gfx950.json holds the time of every prefill tiling
-(and of the 8-row decode plan at m <= 16) on 54 shapes, measured on gfx950
-with block_wise_int4_matmulnbits_amd.plan_tune.  mnb_plan_default prices
-those candidates with a fitted table and takes the cheapest; these tests
-check its choice against the measured times and against a fresh fit of the
-same data, so a stale table or a wrong formula in the C++ fails here."""
+(with and without a K split over workgroups, and of the 8-row decode plan at
+m <= 16) on 64 shapes, measured on gfx950 with
+block_wise_int4_matmulnbits_amd.plan_tune.  mnb_plan_default prices those
+candidates with a fitted table and takes the cheapest; these tests check its
+choice against the measured times and against a fresh fit of the same data,
+so a stale table or a wrong formula in the C++ fails here."""
 import json
 import os
 
@@ -24,18 +25,32 @@ def planner_pick(m, K, N):
     if p.engine != 2:
         assert p.as_dict() == mnb.mnb_plan_default(8, K, N, DATA["cus"], 0).as_dict()
         return "decode"
-    return "%d,%d,%d" % (p.row_tiles, p.cols_per_tile, p.waves_per_wg)
+    return plan_tune.key_of((p.row_tiles, p.cols_per_tile, p.waves_per_wg, max(p.k_splits, 1)))
 
 
 def test_planner_choice_is_near_the_measured_fastest():
+    # Against the fastest measured plan: close on average, and where the
+    # model misses a K split that would have won, by at most 10%.
     regrets = []
     for (m, K, N), row in SHAPES:
         pick = planner_pick(m, K, N)
         assert pick in row, (m, K, N, pick)
         best = min(v["us"] for v in row.values())
         regrets.append(row[pick]["us"] / best - 1)
-        assert regrets[-1] <= 0.045, ((m, K, N), pick, row[pick]["us"], best)
-    assert sum(regrets) / len(regrets) <= 0.005
+        assert regrets[-1] <= 0.10, ((m, K, N), pick, row[pick]["us"], best)
+    assert sum(regrets) / len(regrets) <= 0.01
+
+
+def test_k_splits_never_cost_time():
+    # Against the fastest measured plan without a K split (the choices the
+    # planner had before splits): never slower, and faster on average.
+    gains = []
+    for (m, K, N), row in SHAPES:
+        pick = planner_pick(m, K, N)
+        unsplit = min(v["us"] for k, v in row.items() if ",s" not in k)
+        gains.append(row[pick]["us"] / unsplit - 1)
+        assert gains[-1] <= 0.01, ((m, K, N), pick, row[pick]["us"], unsplit)
+    assert sum(gains) / len(gains) <= -0.05
 
 
 def test_planner_table_is_the_fit_of_the_measurements():
@@ -46,10 +61,29 @@ def test_planner_table_is_the_fit_of_the_measurements():
 
 
 def test_every_candidate_the_model_can_pick_was_measured():
-    # The sweep times each tiling that mnb_plan_check accepts; the planner
-    # considers the same set, so a measured row lists all of them.
+    # The sweep times each tiling that mnb_plan_check accepts (a K split only
+    # within the default plans' workspace bound); the planner considers a
+    # subset of those, so a measured row lists all of them.
     for (m, K, N), row in SHAPES:
         for t in plan_tune.TILINGS:
-            q = mnb.mnb_plan(engine=2, row_tiles=t[0], cols_per_tile=t[1], waves_per_wg=t[2], workgroups=1)
-            assert (mnb.mnb_plan_check(m, K, N, q) == 0) == (plan_tune.key_of(t) in row), (m, K, N, t)
+            q = mnb.mnb_plan(engine=2, row_tiles=t[0], cols_per_tile=t[1], waves_per_wg=t[2], workgroups=1,
+                             k_splits=t[3])
+            ok = mnb.mnb_plan_check(m, K, N, q) == 0 and plan_tune.workspace_bytes(t, m, N) <= mnb.MNB_MAX_SPLIT_WORKSPACE
+            assert ok == (plan_tune.key_of(t) in row), (m, K, N, t)
         assert ("decode" in row) == (m <= 16)
+
+
+def test_split_plans_stay_within_the_workspace_bound():
+    # Default plans split K only while the tiles fill less than two rounds
+    # and the partial sums fit MNB_MAX_SPLIT_WORKSPACE.
+    for m in (9, 16, 24, 64, 128, 512, 2048):
+        for K in (2048, 4096, 14336):
+            for N in (1024, 4096, 6144, 28672, 151936):
+                for cus in (80, 256, 304):
+                    p = mnb.mnb_plan_default(m, K, N, cus, 0)
+                    if p.engine == 2 and p.k_splits > 1:
+                        assert p.k_splits * m * N * 4 <= mnb.MNB_MAX_SPLIT_WORKSPACE, (m, K, N, cus)
+                        rows = 32 * p.row_tiles
+                        tiles = -(-m // rows) * -(-N // p.cols_per_tile) * p.k_splits
+                        assert tiles < 2 * cus, (m, K, N, cus, p.as_dict())
+                        assert mnb.mnb_plan_check(m, K, N, p) == 0
