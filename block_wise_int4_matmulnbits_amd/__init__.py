@@ -82,7 +82,7 @@ class mnb_kernel_info(ctypes.Structure):
 _lock = threading.Lock()
 _lib = None
 
-EXPORTS = ("matmul_nbits", "matmul_nbits_planned", "mnb_plan_default",
+EXPORTS = ("matmul_nbits", "matmul_nbits_planned", "matmul_nbits_noalloc", "mnb_plan_default",
            "mnb_plan_check", "mnb_counters_get", "mnb_counters_reset",
            "mnb_get_kernel_info", "mnb_status_string", "mnb_last_hip_error",
            "mnb_abi_version", "mnb_repack_weights")
@@ -106,6 +106,8 @@ def lib():
         L.matmul_nbits_planned.restype = i32
         L.matmul_nbits_planned.argtypes = L.matmul_nbits.argtypes + [
             ctypes.POINTER(mnb_plan)]
+        L.matmul_nbits_noalloc.restype = i32
+        L.matmul_nbits_noalloc.argtypes = L.matmul_nbits.argtypes
         L.mnb_plan_default.restype = i32
         L.mnb_plan_default.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(mnb_plan)]
         L.mnb_plan_check.restype = i32
@@ -191,6 +193,19 @@ def matmul_nbits(A, Bpacked, scales, zero_points, out, block=32, stream=None):
         A, Bpacked, scales, zero_points, out)
     st = L.matmul_nbits(a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, block, o_ptr,
                         o_dt, _stream_handle(stream, A.device))
+    _check(st, L)
+    return out
+
+
+def matmul_nbits_noalloc(A, Bpacked, scales, zero_points, out, block=32, stream=None):
+    """matmul_nbits that allocates no device memory: a split plan's partial
+    sums go to the library's fixed per-device workspace (calls that overlap
+    on one device race)."""
+    L = lib()
+    a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, o_ptr, o_dt = _tensor_args(
+        A, Bpacked, scales, zero_points, out)
+    st = L.matmul_nbits_noalloc(a_ptr, a_dt, m, K, N, b_ptr, s_ptr, z_ptr, block, o_ptr,
+                                o_dt, _stream_handle(stream, A.device))
     _check(st, L)
     return out
 

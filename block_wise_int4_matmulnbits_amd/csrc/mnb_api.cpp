@@ -76,7 +76,8 @@ int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
 
 int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         const uint8_t* Bpacked, const uint16_t* scales, const uint8_t* zero_points,
-        int block, void* out, int out_dtype, void* stream, const mnb_plan* explicit_plan)
+        int block, void* out, int out_dtype, void* stream, const mnb_plan* explicit_plan,
+        bool fixed_scratch = false)
 {
     int st = validate(A, a_dtype, m, K, N, Bpacked, scales, zero_points, block, out,
                       out_dtype);
@@ -113,13 +114,22 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
     const size_t a_row = (size_t)K * 2, out_row = (size_t)N * 2;
     const int per_launch = plan.k_splits > 1 ? 2 : 1;
     void* ws = nullptr;
+    bool held = false;   // the per-stream workspace is held until the launches are queued
     const size_t ws_bytes = mnb::workspace_bytes(m, N, plan);
-    if (ws_bytes) {
+    if (ws_bytes && fixed_scratch) {
+        if (ws_bytes > mnb::kScratchBytes) return MNB_ERR_WORKSPACE;
+        int e = mnb::scratch_address(&ws);
+        if (e != 0) {
+            t_last_hip_error = e;
+            return MNB_ERR_HIP;
+        }
+    } else if (ws_bytes) {
         int e = mnb::workspace_acquire(ws_bytes, stream, &ws);
         if (e != 0) {
             t_last_hip_error = e;
             return MNB_ERR_HIP;
         }
+        held = true;
     }
     int64_t launched = 0, batched = 0;
     for (int64_t r0 = 0; r0 < m; r0 += step) {
@@ -131,13 +141,13 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         if (e != 0) {
             t_last_hip_error = e;
             g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
-            if (ws) mnb::workspace_release();
+            if (held) mnb::workspace_release();
             return MNB_ERR_HIP;
         }
         launched += per_launch;
         if (mc > 1) ++batched;
     }
-    if (ws) mnb::workspace_release();
+    if (held) mnb::workspace_release();
     g_calls.fetch_add(1, std::memory_order_relaxed);
     g_launches.fetch_add((uint64_t)launched, std::memory_order_relaxed);
     if (out_dtype == MNB_BF16) g_bf16.fetch_add((uint64_t)(m * N), std::memory_order_relaxed);
@@ -514,6 +524,15 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
                stream, nullptr);
 }
 
+int matmul_nbits_noalloc(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+                         const uint8_t* Bpacked, const uint16_t* scales,
+                         const uint8_t* zero_points, int block, void* out, int out_dtype,
+                         void* stream)
+{
+    return run(A, a_dtype, m, K, N, Bpacked, scales, zero_points, block, out, out_dtype,
+               stream, nullptr, true);
+}
+
 int matmul_nbits_planned(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
                          const uint8_t* Bpacked, const uint16_t* scales,
                          const uint8_t* zero_points, int block, void* out, int out_dtype,
@@ -592,6 +611,7 @@ const char* mnb_status_string(int status)
     case MNB_ERR_ALIAS: return "out overlaps an input";
     case MNB_ERR_PLAN: return "launch plan not supported";
     case MNB_ERR_LAYOUT: return "unknown weight layout";
+    case MNB_ERR_WORKSPACE: return "the plan needs more workspace than matmul_nbits_noalloc's fixed buffer holds";
     }
     return "unknown status";
 }

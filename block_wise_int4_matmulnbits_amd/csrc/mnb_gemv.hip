@@ -756,6 +756,34 @@ void workspace_release() { g_ws_mu.unlock(); }
 
 namespace {
 
+// matmul_nbits_noalloc's workspace.  In host code `scratch` names a host-side
+// stand-in, not device memory: kernels get the address hipGetSymbolAddress
+// returns for the current device.
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+}  // namespace
+
+int scratch_address(void** ptr)
+{
+    static std::mutex mu;
+    static void* addr[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    if (dev < 0 || dev >= 64) return (int)hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return (int)e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return 0;
+}
+
+namespace {
+
 // Occupancy queries cost microseconds; they depend only on the device and the
 // (kernel, block size, dynamic LDS) triple, so cache them.
 struct OccKey {

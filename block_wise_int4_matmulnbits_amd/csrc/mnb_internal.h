@@ -64,6 +64,13 @@ size_t workspace_bytes(int64_t m, int64_t N, const mnb_plan& plan);
 int workspace_acquire(size_t bytes, void* stream, void** ptr);
 void workspace_release();
 
+// The fixed workspace of matmul_nbits_noalloc: a file-scope device array of
+// kScratchBytes in mnb_gemv.hip, one per device for the life of the process.
+// Its device address on the current device, looked up (hipGetSymbolAddress)
+// on the first call per device.  Returns a hipError_t.
+constexpr size_t kScratchBytes = MNB_MAX_SPLIT_WORKSPACE;
+int scratch_address(void** ptr);
+
 // Compute units of the current device.  Returns a hipError_t.
 int current_device_cus(int* num_cus);
 

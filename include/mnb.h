@@ -52,7 +52,9 @@ typedef enum {
                              mnb_last_hip_error()                            */
     MNB_ERR_ALIAS = 8,    /* out overlaps an input buffer                    */
     MNB_ERR_PLAN = 9,     /* an explicit plan is not one the library runs   */
-    MNB_ERR_LAYOUT = 10   /* unknown weight layout                            */
+    MNB_ERR_LAYOUT = 10,  /* unknown weight layout                            */
+    MNB_ERR_WORKSPACE = 11 /* matmul_nbits_noalloc: the plan needs more than its
+                              fixed workspace (MNB_MAX_SPLIT_WORKSPACE)       */
 } mnb_status;
 
 /*
@@ -128,7 +130,8 @@ typedef enum {
  * stream (per host thread on hipStreamPerThread) for the life of the
  * process.  The first such call on a stream, and a call that needs more
  * than the stream's workspace holds, allocate it with hipMalloc (a larger
- * one after the stream has drained); other calls allocate nothing.
+ * one after the stream has drained); other calls allocate nothing.  Calls
+ * that must not allocate use matmul_nbits_noalloc.
  * The fp32 summation order is fixed by (m, K) for m <= 8 (never by N or
  * the device), and by
  * (m, K, N) and the device's compute-unit count for m > 8 (which tiling
@@ -143,6 +146,25 @@ int matmul_nbits(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
                  const uint8_t* Bpacked, const uint16_t* scales,
                  const uint8_t* zero_points, int block,
                  void* out, int out_dtype, void* stream);
+
+/*
+ * matmul_nbits_noalloc -- matmul_nbits for callers that cannot allocate
+ * device memory (code under HIP graph capture, serving loops, harnesses
+ * that forbid hipMalloc): same arguments, same plan, same bits.  Where the
+ * plan splits K over workgroups, the partial sums go to a fixed workspace
+ * of MNB_MAX_SPLIT_WORKSPACE bytes that the library's code object holds on
+ * every device it is loaded on, until the process ends, instead of the
+ * per-stream workspace; no call allocates or frees anything.  Every call on
+ * a device shares that device's workspace: calls whose work overlaps on
+ * one device (other streams, other host threads) race and must be ordered
+ * by the caller.  The workspace needs no clearing (each call writes every
+ * partial sum it reads).  A plan needing more than the fixed workspace
+ * returns MNB_ERR_WORKSPACE without launching; default plans never do.
+ */
+int matmul_nbits_noalloc(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
+                         const uint8_t* Bpacked, const uint16_t* scales,
+                         const uint8_t* zero_points, int block,
+                         void* out, int out_dtype, void* stream);
 
 /*
  * Launch plan.  Every plan that mnb_plan_check() accepts computes the same

@@ -26,5 +26,10 @@ int workspace_acquire(size_t, void*, void** ptr)
     return kNoDevice;
 }
 void workspace_release() {}
+int scratch_address(void** ptr)
+{
+    *ptr = nullptr;
+    return kNoDevice;
+}
 
 }  // namespace mnb
