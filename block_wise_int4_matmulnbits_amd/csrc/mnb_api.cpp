@@ -205,37 +205,37 @@ struct Tiling {
     double t0, a, g, d, h, u;
 };
 constexpr Tiling kTilings[] = {
-    {1, 16, 4, 1, 3.7668, 1.4434, 2.2049, 2.0973, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
-    {1, 16, 8, 1, 6.3507, 1.9841, 2.1654, 1.7113, 0.0000, 0.0000},
-    {1, 32, 4, 1, 5.2063, 1.5600, 2.5006, 2.1180, 2.5214, 0.0000},   // K split over the four waves
-    {1, 64, 2, 1, 1.4704, 2.1873, 1.6887, 5.1474, 12.8967, 0.0000},
-    {1, 128, 4, 1, 2.1704, 4.2481, 2.5462, 5.7416, 14.4049, 0.0000},
-    {2, 128, 4, 1, 4.4850, 5.8660, 2.3649, 6.0841, 5.4424, 0.0000},
-    {4, 128, 4, 1, 6.8342, 12.4151, 4.9069, 11.2720, 0.0000, 0.0000},
-    {1, 256, 8, 1, 0.4677, 9.2681, 3.5522, 8.5856, 37.9079, 0.0000},
-    {2, 256, 8, 1, 1.5547, 12.6639, 2.2566, 9.4077, 30.3611, 0.0000},
-    {4, 256, 8, 1, 5.8140, 18.5306, 7.1242, 14.6185, 7.3874, 0.0000},
-    {8, 256, 8, 1, 7.4983, 33.2511, 0.0000, 24.0385, 9.3608, 0.0000},   // 256 x 256, weights through LDS
-    {1, 128, 4, 2, 5.7811, 3.6323, 0.0000, 5.6003, 10.2803, 215.4830},   // K split over 2..16 workgroups, a second launch adds the slices
-    {1, 128, 4, 4, 6.8609, 3.7349, 0.0000, 5.1529, 13.1255, 155.0454},
-    {1, 128, 4, 8, 6.5596, 0.0000, 1.7791, 5.3929, 16.7617, 144.6631},
-    {1, 128, 4, 16, 7.8648, 0.0000, 0.0000, 5.6286, 0.0000, 102.2949},
-    {2, 128, 4, 2, 6.9190, 4.1592, 0.0000, 5.8821, 3.8639, 202.7498},
-    {2, 128, 4, 4, 7.9035, 4.0848, 1.7138, 5.6569, 5.5715, 145.3534},
-    {2, 128, 4, 8, 7.7753, 0.0000, 2.8980, 5.9179, 10.9718, 131.0167},
-    {2, 128, 4, 16, 8.4022, 0.0000, 0.0000, 6.4012, 0.0000, 138.0253},
-    {4, 128, 4, 2, 8.4784, 11.4083, 0.0000, 10.9586, 8.0516, 185.2008},
-    {4, 128, 4, 4, 9.6877, 11.8197, 0.0000, 10.7060, 4.5588, 162.3002},
-    {4, 128, 4, 8, 9.3536, 0.0000, 10.4738, 11.2795, 20.1193, 102.0845},
-    {4, 128, 4, 16, 9.8888, 0.0000, 0.0000, 12.5392, 0.0000, 111.9602},
-    {1, 256, 8, 2, 4.4415, 8.7483, 0.0000, 8.6096, 19.1656, 196.3301},
-    {1, 256, 8, 4, 6.2731, 9.1836, 0.0000, 8.3648, 14.3106, 156.0304},
-    {1, 256, 8, 8, 7.1303, 12.1292, 0.0000, 8.4066, 22.5730, 57.5258},
-    {1, 256, 8, 16, 8.6743, 0.0000, 5.5817, 5.4426, 31.8635, 53.2031},
-    {2, 256, 8, 2, 4.8779, 8.6598, 0.0000, 9.4053, 15.7518, 217.3709},
-    {2, 256, 8, 4, 7.0630, 10.3611, 0.0000, 9.1982, 13.4039, 144.4728},
-    {2, 256, 8, 8, 7.2377, 12.4821, 0.0000, 9.5998, 21.8696, 104.3872},
-    {2, 256, 8, 16, 9.2107, 0.0000, 6.9512, 6.0303, 40.1321, 65.4203},
+    {1, 16, 4, 1, 3.9244, 1.3980, 1.8903, 1.8873, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
+    {1, 16, 8, 1, 5.9552, 2.0069, 1.9272, 1.7161, 0.0000, 0.0000},
+    {1, 32, 4, 1, 4.9487, 1.4837, 2.3526, 1.9108, 3.2582, 0.0000},   // K split over the four waves
+    {1, 64, 2, 1, 0.9597, 2.2652, 1.7304, 5.5067, 9.9036, 0.0000},
+    {1, 128, 4, 1, 1.3772, 4.5039, 2.3544, 5.5933, 12.4768, 0.0000},
+    {2, 128, 4, 1, 3.6968, 6.1140, 2.1443, 6.0116, 6.3987, 0.0000},
+    {4, 128, 4, 1, 4.8230, 12.4917, 3.5210, 11.2838, 0.0000, 0.0000},
+    {1, 256, 8, 1, 0.0000, 9.4982, 3.9897, 8.9907, 33.0263, 0.0000},
+    {2, 256, 8, 1, 1.4780, 12.7663, 4.5713, 10.2833, 22.3049, 0.0000},
+    {4, 256, 8, 1, 3.9098, 18.6270, 8.7240, 14.5974, 7.9110, 0.0000},
+    {8, 256, 8, 1, 7.5499, 34.4270, 0.0000, 24.0344, 9.0054, 0.0000},   // 256 x 256, weights through LDS
+    {1, 128, 4, 2, 5.7362, 3.9585, 0.0000, 4.8435, 6.7972, 198.7372},   // K split over 2..16 workgroups, a second launch adds the slices
+    {1, 128, 4, 4, 6.6096, 3.9520, 0.0000, 4.4306, 10.5003, 161.8492},
+    {1, 128, 4, 8, 6.4151, 3.7590, 1.0284, 5.1502, 8.6722, 110.4932},
+    {1, 128, 4, 16, 7.5472, 1.7829, 1.4252, 3.1608, 22.8446, 113.3746},
+    {2, 128, 4, 2, 6.0819, 4.5161, 0.0000, 5.9733, 1.0932, 204.3010},
+    {2, 128, 4, 4, 7.2117, 5.2799, 0.0000, 5.8215, 3.1945, 131.6582},
+    {2, 128, 4, 8, 7.3576, 5.2841, 0.3055, 6.1671, 6.5950, 112.8108},
+    {2, 128, 4, 16, 8.2182, 2.8579, 2.2764, 6.0666, 0.0000, 120.4394},
+    {4, 128, 4, 2, 6.6830, 11.4857, 0.0000, 11.1286, 0.2157, 201.6521},
+    {4, 128, 4, 4, 8.0122, 12.0687, 0.0000, 10.5646, 9.9742, 151.3090},
+    {4, 128, 4, 8, 7.5276, 10.7261, 4.7451, 12.0561, 7.8627, 111.5904},
+    {4, 128, 4, 16, 9.3827, 7.8021, 7.8584, 10.9310, 0.0000, 106.5257},
+    {1, 256, 8, 2, 3.5601, 7.2971, 0.0000, 8.5310, 23.8684, 201.0858},
+    {1, 256, 8, 4, 5.6509, 8.2060, 0.0000, 8.4668, 13.7726, 127.5536},
+    {1, 256, 8, 8, 6.3480, 9.1871, 0.0000, 8.8180, 16.2886, 81.5570},
+    {1, 256, 8, 16, 8.0913, 8.2569, 1.4076, 7.2531, 17.3491, 54.7710},
+    {2, 256, 8, 2, 4.6189, 12.1103, 0.0000, 10.3512, 14.2284, 196.9201},
+    {2, 256, 8, 4, 6.2785, 12.0003, 0.0000, 10.3495, 6.4116, 144.7644},
+    {2, 256, 8, 8, 6.2775, 12.8870, 0.0000, 10.6790, 16.4136, 115.8997},
+    {2, 256, 8, 16, 8.0027, 9.6598, 4.7357, 8.9057, 20.8932, 82.4020},
 };
 // The decode plan per launch of r <= 8 rows:
 //   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
@@ -243,7 +243,7 @@ constexpr Tiling kTilings[] = {
 // from shapes where fixed costs dominate; far beyond them the weights set
 // the time) and no less than 3 us, about what one launch takes however
 // small.
-constexpr double kDecode[4] = {2.1488, 0.5730, 0.6001, 0.2345};
+constexpr double kDecode[4] = {2.1476, 0.5698, 0.6076, 0.2224};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
 constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
@@ -297,8 +297,8 @@ PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus)
         q.workgroups = 1;
         if (mnb_plan_check(m, K, N, &q) != MNB_OK) continue;
         // A K split is there to fill the device: only while its tiles fit
-        // in less than two rounds over the CUs, within the workspace bound.
-        if (t.splits > 1 && (prefill_tiles(t, m, N) >= 2 * (int64_t)num_cus ||
+        // in less than four rounds over the CUs, within the workspace bound.
+        if (t.splits > 1 && (prefill_tiles(t, m, N) >= 4 * (int64_t)num_cus ||
                              mnb::workspace_bytes(m, N, q) > kMaxSplitWorkspaceBytes))
             continue;
         const double c = tiling_cost(t, m, K, N, num_cus);
@@ -335,11 +335,14 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
             (uint64_t)64 * plan->row_tiles * (uint64_t)K > mnb::kPrefillRowBlockBytes)
             return MNB_ERR_PLAN;
         // K split over workgroups: at least one 128-wide step per slice, not
-        // for the LDS-staged 256 x 256 tiles, and a workspace below 2^31
-        // floats per slice plane.
+        // for the LDS-staged 256 x 256 tiles, a workspace below 2^31 floats
+        // per slice plane, and fewer than 2^31 tiles (the kernel's slice
+        // arithmetic is 32-bit).
         if (plan->k_splits < 0 || plan->k_splits > kMaxKSplits) return MNB_ERR_PLAN;
-        if (plan->k_splits > 1 && (plan->row_tiles == 8 || plan->k_splits > ceil_div(nb, 4) ||
-                                   m * N > (int64_t)INT32_MAX))
+        if (plan->k_splits > 1 &&
+            (plan->row_tiles == 8 || plan->k_splits > ceil_div(nb, 4) || m * N > (int64_t)INT32_MAX ||
+             ceil_div(m, 32 * (int64_t)plan->row_tiles) * ceil_div(N, (int64_t)plan->cols_per_tile) *
+                     plan->k_splits > (int64_t)INT32_MAX))
             return MNB_ERR_PLAN;
         plan->threads_per_wg = 64 * plan->waves_per_wg;
         plan->k_chunks = (int32_t)ceil_div(nb, 4);   // 128-wide steps of K
@@ -396,10 +399,11 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
         // out, 64 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
-        // those shapes the cheapest modelled plan runs 0.62% slower than
-        // the fastest measured one on average (9.8% at most, where a split
-        // the model ranks second would have won), and never slower than
-        // the fastest plan without a K split (12.8% faster on average).
+        // those shapes the cheapest modelled plan runs 0.38% slower than
+        // the fastest measured one on average (6.5% at most, where a split
+        // the model ranks second would have won), and 12.1% faster on
+        // average than the fastest plan without a K split (never more than
+        // 2.2% slower: a choice between unsplit tilings).
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;

@@ -133,8 +133,11 @@ __device__ __forceinline__ int a_slot(int d, int r)
 // few to fill the chip (the down projection's 4096 columns).  CW = 16 (with
 // one 32-column MFMA tile per wave) gives a wave 16 real columns: lanes
 // j >= 16 load zeros and store nothing, which doubles the tiles where the
-// 32-column ones leave CUs idle.
-template <int RT, int CT, int W, bool VEC, bool ABF16, int KS, int CW = 32>
+// 32-column ones leave CUs idle.  SPLIT: K is also split over workgroups
+// (p.splits slices of 128-wide steps), each tile's slice leaving its fp32
+// sums in the workspace for mnb_split_reduce_kernel; a separate variant, so
+// that the tiles without it keep their registers and code.
+template <int RT, int CT, int W, bool VEC, bool ABF16, int KS, int CW = 32, bool SPLIT = false>
 __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 {
     constexpr int THREADS = 64 * W;
@@ -183,17 +186,27 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
     }
 
     const int64_t tiles_mn = tiles_m * tiles_n;
-    for (int64_t tile = blockIdx.x; tile < tiles_mn * p.splits; tile += gridDim.x) {
+    const int64_t tiles_all = SPLIT ? tiles_mn * p.splits : tiles_mn;
+    for (int64_t tile = blockIdx.x; tile < tiles_all; tile += gridDim.x) {
         // Consecutive workgroups share a row block (its activations stay in
         // L2) and walk the column blocks; with K split over workgroups, K
         // slice ks of every tile comes after slice ks - 1 of all of them.
-        const int64_t ks = tile / tiles_mn, tmn = tile - ks * tiles_mn;
+        // (With a split the host keeps tiles_mn * splits below 2^31 and the
+        // slice arithmetic in 32 bits; nq * splits < 2^24.)
+        uint32_t ks = 0;
+        int64_t tmn = tile;
+        int qa = 0, qb = nq;
+        if constexpr (SPLIT) {
+            ks = (uint32_t)tile / (uint32_t)tiles_mn;
+            tmn = (int64_t)((uint32_t)tile - ks * (uint32_t)tiles_mn);
+            qa = (int)((uint32_t)nq * ks / (uint32_t)p.splits);
+            qb = (int)((uint32_t)nq * (ks + 1) / (uint32_t)p.splits);
+        }
         const int64_t tm = tmn / tiles_n, tn = tmn - tm * tiles_n;
         const int64_t r0 = tm * MT;
         // Quads [qa, qb) of K: the workgroup's slice (all of K when
         // splits = 1); blocks from bend on load zeros.
-        const int qa = (int)(nq * ks / p.splits), qb = (int)(nq * (ks + 1) / p.splits);
-        const uint32_t bend = (uint32_t)(4 * qb < nb ? 4 * qb : nb);
+        const uint32_t bend = SPLIT ? (uint32_t)(4 * qb < nb ? 4 * qb : nb) : (uint32_t)nb;
         const int nsteps = (qb - qa + KS - 1) / KS;   // steps of KS quads
         const int64_t col0 = tn * NT + CW * CT * wcol;   // this wave's CW*CT columns
         const int64_t left = p.N - col0;
@@ -416,7 +429,7 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
         // with K split over workgroups, the fp32 sums of the slice into its
         // plane of the workspace.  Accumulator element q of lane (j, h) is
         // row (q%4) + 4h + 8(q/4), column j of its 32 x 32 tile.
-        float* const plane = p.ws + ks * p.M * p.N;
+        float* const plane = p.ws + (int64_t)ks * p.M * p.N;
 #pragma unroll
         for (int c = 0; c < CT; ++c) {
             const int64_t col = col0 + 32 * c + j;
@@ -426,8 +439,8 @@ __global__ __launch_bounds__(64 * W) void mnb_gemm_mfma_kernel(GemmParams p)
 #pragma unroll
                     for (int q = 0; q < 16; ++q) {
                         const int64_t row = r0 + rt * 32 + (q & 3) + 4 * h + 8 * (q >> 2);
-                        if (row < p.M && p.splits > 1) {
-                            plane[row * p.N + col] = acc[rt][c][q];
+                        if constexpr (SPLIT) {
+                            if (row < p.M) plane[row * p.N + col] = acc[rt][c][q];
                         } else if (row < p.M) {
                             const _Float16 hv = (_Float16)acc[rt][c][q];
                             uint16_t bits = __builtin_bit_cast(uint16_t, hv);
@@ -690,13 +703,13 @@ __global__ __launch_bounds__(256) void mnb_split_reduce_kernel(const float* ws, 
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int CT, int W, bool VEC, bool ABF16>
+template <int CT, int W, bool VEC, bool ABF16, bool SPLIT>
 GemmFn lookup_gemm_ct(int rt)
 {
     switch (rt) {
-    case 1: return mnb_gemm_mfma_kernel<1, CT, W, VEC, ABF16, 1>;
-    case 2: return mnb_gemm_mfma_kernel<2, CT, W, VEC, ABF16, 1>;
-    case 4: return mnb_gemm_mfma_kernel<4, CT, W, VEC, ABF16, 1>;
+    case 1: return mnb_gemm_mfma_kernel<1, CT, W, VEC, ABF16, 1, 32, SPLIT>;
+    case 2: return mnb_gemm_mfma_kernel<2, CT, W, VEC, ABF16, 1, 32, SPLIT>;
+    case 4: return mnb_gemm_mfma_kernel<4, CT, W, VEC, ABF16, 1, 32, SPLIT>;
     }
     return nullptr;
 }
@@ -706,30 +719,39 @@ GemmFn lookup_gemm_ct(int rt)
 // one 32-row tile whose K the waves split: 32 columns over four waves, 16
 // over four or eight.  (32 columns over eight waves was never faster than
 // over four in the planner's sweep.)
-template <bool VEC, bool ABF16>
+template <bool VEC, bool ABF16, bool SPLIT>
 GemmFn lookup_gemm_shape(int rt, int cols, int waves)
 {
     if (cols == 32 || cols == 16) {
         if (rt != 1) return nullptr;
-        if (cols == 32) return waves == 4 ? mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4> : nullptr;
-        if (waves == 4) return mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4, 16>;
-        return waves == 8 ? mnb_gemm_mfma_kernel<1, 1, 8, VEC, ABF16, 8, 16> : nullptr;
+        if (cols == 32) return waves == 4 ? mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4, 32, SPLIT> : nullptr;
+        if (waves == 4) return mnb_gemm_mfma_kernel<1, 1, 4, VEC, ABF16, 4, 16, SPLIT>;
+        return waves == 8 ? mnb_gemm_mfma_kernel<1, 1, 8, VEC, ABF16, 8, 16, SPLIT> : nullptr;
     }
-    if (waves == 2 && cols == 64) return lookup_gemm_ct<1, 2, VEC, ABF16>(rt);
-    if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16>(rt);
-    if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16>(rt);
-    if (waves == 8 && cols == 256) return lookup_gemm_ct<1, 8, VEC, ABF16>(rt);
+    if (waves == 2 && cols == 64) return lookup_gemm_ct<1, 2, VEC, ABF16, SPLIT>(rt);
+    if (waves == 4 && cols == 128) return lookup_gemm_ct<1, 4, VEC, ABF16, SPLIT>(rt);
+    if (waves == 4 && cols == 256) return lookup_gemm_ct<2, 4, VEC, ABF16, SPLIT>(rt);
+    if (waves == 8 && cols == 256) return lookup_gemm_ct<1, 8, VEC, ABF16, SPLIT>(rt);
     return nullptr;
+}
+
+template <bool SPLIT>
+GemmFn lookup_gemm_split(int rt, int cols, int w, bool vec, bool a_bf16)
+{
+    if (vec)
+        return a_bf16 ? lookup_gemm_shape<true, true, SPLIT>(rt, cols, w) : lookup_gemm_shape<true, false, SPLIT>(rt, cols, w);
+    return a_bf16 ? lookup_gemm_shape<false, true, SPLIT>(rt, cols, w) : lookup_gemm_shape<false, false, SPLIT>(rt, cols, w);
 }
 
 GemmFn lookup_gemm(const mnb_plan& plan, bool vec, bool a_bf16)
 {
     const int rt = plan.row_tiles, cols = plan.cols_per_tile, w = plan.waves_per_wg;
     if (rt == 8)   // 256 x 256, weights through LDS (any scale alignment)
-        return cols == kLdsTileCols && w == 8 ? (a_bf16 ? mnb_gemm_lds_kernel<true> : mnb_gemm_lds_kernel<false>)
-                                              : nullptr;
-    if (vec) return a_bf16 ? lookup_gemm_shape<true, true>(rt, cols, w) : lookup_gemm_shape<true, false>(rt, cols, w);
-    return a_bf16 ? lookup_gemm_shape<false, true>(rt, cols, w) : lookup_gemm_shape<false, false>(rt, cols, w);
+        return cols == kLdsTileCols && w == 8 && plan.k_splits <= 1
+                   ? (a_bf16 ? mnb_gemm_lds_kernel<true> : mnb_gemm_lds_kernel<false>)
+                   : nullptr;
+    return plan.k_splits > 1 ? lookup_gemm_split<true>(rt, cols, w, vec, a_bf16)
+                             : lookup_gemm_split<false>(rt, cols, w, vec, a_bf16);
 }
 
 bool gemm_vec_ok(int64_t K, const void* scales, const void* zp)

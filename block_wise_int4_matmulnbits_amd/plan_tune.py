@@ -73,9 +73,9 @@ def workspace_bytes(t, m, N):
 
 def admitted(t, m, N, cus):
     """A tiling the planner considers: one that splits K over workgroups only
-    while its tiles fit in less than two rounds over the compute units (the
+    while its tiles fit in less than four rounds over the compute units (the
     split is there to fill the device, not to add rounds)."""
-    return t[3] == 1 or tiles_of(t, m, N) < 2 * cus
+    return t[3] == 1 or tiles_of(t, m, N) < 4 * cus
 
 
 def tiling_features(t, m, K, N, cus):

@@ -129,13 +129,13 @@ def test_default_prefill_plans():
             splits = max(p.k_splits, 1)
             tiles = -(-m // rows) * -(-N // p.cols_per_tile) * splits
             assert 1 <= p.workgroups <= min(tiles, max(occ, 1) * cus), (m, K, N, cus)
-            if splits > 1:   # to fill the device: under two rounds, within the workspace bound
-                assert tiles < 2 * cus and splits * m * N * 4 <= mnb.MNB_MAX_SPLIT_WORKSPACE, (m, K, N, cus)
+            if splits > 1:   # to fill the device: under four rounds, within the workspace bound
+                assert tiles < 4 * cus and splits * m * N * 4 <= mnb.MNB_MAX_SPLIT_WORKSPACE, (m, K, N, cus)
     # The benchmark's prefill shapes (gate_up m = 512 and 2048, down m = 16,
     # 64, 512 and 2048), on the tilings measured fastest for them.
     for m, K, N, want in ((512, 4096, 28672, (8, 256, 8, 1)), (2048, 4096, 28672, (8, 256, 8, 1)),
-                          (16, 14336, 4096, (1, 256, 8, 16)), (64, 14336, 4096, (2, 128, 4, 8)),
-                          (512, 14336, 4096, (2, 256, 8, 2)), (2048, 14336, 4096, (4, 256, 8, 1))):
+                          (16, 14336, 4096, (1, 128, 4, 8)), (64, 14336, 4096, (2, 128, 4, 8)),
+                          (512, 14336, 4096, (2, 128, 4, 1)), (2048, 14336, 4096, (4, 256, 8, 1))):
         p = mnb.mnb_plan_default(m, K, N, 256, 0)
         assert (p.row_tiles, p.cols_per_tile, p.waves_per_wg, max(p.k_splits, 1)) == want, (m, K, N)
 

@@ -65,11 +65,11 @@ def _gpu():
     (9, 4096, 1000, W.F16, True, "decode"),            # few columns: two decode launches
     (16, 4096, 64, W.BF16, True, "decode"),            # exactly two decode launches
     (17, 1024, 130, W.F16, False, (1, 16, 4, 1)),      # ragged rows and columns, zero point 8, 16-column tiles
-    (12, 4096, 6144, W.BF16, True, (1, 256, 8, 8)),    # K over eight workgroups at 12 rows
+    (12, 4096, 6144, W.BF16, True, (1, 128, 4, 4)),    # K over four workgroups at 12 rows
     (9, 2048, 8200, W.F16, False, (1, 256, 8, 4)),     # K over four workgroups, ragged columns
     (100, 32 * 37, 77, W.BF16, True, (1, 16, 4, 1)),   # K not a whole number of 128-wide steps
     (130, 14336, 300, W.BF16, True, (1, 128, 4, 16)),  # down-projection K over 16 workgroups, row tail of 2
-    (256, 4096, 1024, W.F16, True, (1, 256, 8, 8)),    # several row and column blocks, K over eight
+    (256, 4096, 1024, W.F16, True, (1, 32, 4, 1)),     # several row and column blocks, K over four waves
     (192, 4096, 6144, W.BF16, True, (2, 128, 4, 1)),   # two 32-row tiles of 128 columns
     (40, 4096, 65536, W.F16, True, (2, 256, 8, 1)),    # two row tiles of 256 columns, several rounds
     (1152, 1024, 4096, W.BF16, True, (4, 256, 8, 1)),  # 128 x 256 tiles
