@@ -164,9 +164,18 @@ def counters_summary(tag, trace_dir, out_md, flops, cmd_trace, cmd_pmc, pmc_dirs
                 vals["GRBM_GUI_ACTIVE"] / 8 / (pmc_mean * 1e3) <= 2.45:
             f.write("- MFMA busy: %.1f%% of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs)\n"
                     % (100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (vals["GRBM_GUI_ACTIVE"] / 8 * 1024)))
-        if "SQ_INSTS_VALU" in vals and "SQ_INSTS_MFMA" in vals:
+        if "SQ_INSTS_VALU" in vals and vals.get("SQ_INSTS_MFMA", 0) > 0:
             f.write("- other VALU instructions per MFMA: %.2f\n"
                     % ((vals["SQ_INSTS_VALU"] - vals["SQ_INSTS_MFMA"]) / vals["SQ_INSTS_MFMA"]))
+        if vals.get("SQ_WAVES", 0) > 0:
+            f.write("- waves: %d, %.2f per SIMD of the 1024 over the dispatch\n"
+                    % (vals["SQ_WAVES"], vals["SQ_WAVES"] / 1024))
+            for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_INSTS_VMEM"):
+                if c in vals:
+                    f.write("- %s per wave: %.0f\n" % (c, vals[c] / vals["SQ_WAVES"]))
+        if vals.get("SQ_WAVE_CYCLES", 0) > 0 and "SQ_WAIT_ANY" in vals:
+            f.write("- waiting: SQ_WAIT_ANY / SQ_WAVE_CYCLES = %.0f%% of wave cycles\n"
+                    % (100 * vals["SQ_WAIT_ANY"] / vals["SQ_WAVE_CYCLES"]))
         if "FETCH_SIZE" in vals:
             f.write("- HBM fetch: %.1f MB per call (FETCH_SIZE KiB x 1024 x %.4f, the device-copy "
                     "factor of profiles/hbm_traffic.json)\n"
