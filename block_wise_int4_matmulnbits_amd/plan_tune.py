@@ -12,6 +12,11 @@ and takes the cheapest.  This script produces both halves of that:
       (CPU) fits the cost of each tiling by non-negative least squares on
       relative error and prints the table the planner holds, and the
       regret of the fitted choice on every measured shape.
+  python -m block_wise_int4_matmulnbits_amd.plan_tune sweep-grid OUT.json
+      (GPU) times the 4x4x4 MFMA decode kernel (2 <= m <= 8) under its
+      default lane split with whole workgroups per CU, from half a CU's
+      worth to one resident generation, on a list of decode shapes (bf16,
+      weights rotated over enough copies that none stays in cache).
 
 Cost of a tiling (µs), with R = ceil(tiles / CUs) rounds of tiles over the
 compute units (a tiling that splits K over S workgroups has S times the
@@ -162,6 +167,69 @@ def sweep(out_path):
         json.dump(res, f, indent=1)
 
 
+GRID_SHAPES = [(4096, 28672), (4096, 151936), (4096, 6144), (4096, 4096), (14336, 4096), (4096, 14336),
+               (8192, 8192), (2048, 8192)]
+
+
+def sweep_grid(out_path):
+    import ctypes
+    import torch
+    import block_wise_int4_matmulnbits_amd as mnb
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    L = mnb.lib()
+    props = torch.cuda.get_device_properties(0)
+    cus = props.multi_processor_count
+    res = {"cus": cus, "device": props.name, "arch": getattr(props, "gcnArchName", ""), "shapes": {}}
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for K, N in GRID_SHAPES:
+        for m in (2, 3, 4, 6, 8):
+            base = mnb.plan_for_device(m, K, N, cus)
+            if base.engine != 3:
+                continue
+            A = (torch.randn(m, K, device=dev) * 0.5).to(torch.bfloat16)
+            wbytes = N * K // 2 + N * K // 16 + N * K // 64
+            ncopy = max(1, min(8, int(512e6 // wbytes)))
+            copies = [(torch.randint(0, 256, (N, K // 2), dtype=torch.uint8, device=dev),
+                       (torch.rand(N, K // 32, device=dev) * 0.01 + 0.001).to(torch.float16),
+                       torch.randint(0, 256, (N, (K // 32 + 1) // 2), dtype=torch.uint8, device=dev))
+                      for _ in range(ncopy)]
+            O = torch.empty(m, N, dtype=torch.bfloat16, device=dev)
+            occ = mnb.mnb_get_kernel_info(m, K, base)["wgs_per_cu"]
+            tiles = -(-N // base.cols_per_tile)
+            row = {}
+            for f in (0.5, 1, 1.5, 2, 3, 4, 5, 6, 8):
+                if f > occ:
+                    continue
+                wg = max(1, min(-(-tiles // 2), int(f * cus)))
+                p = mnb.mnb_plan(**dict(base.as_dict(), workgroups=wg))
+                assert mnb.mnb_plan_check(m, K, N, p) == 0
+
+                def go(i):
+                    B, S, Z = copies[i % ncopy]
+                    st = L.matmul_nbits_planned(A.data_ptr(), mnb.MNB_BF16, m, K, N, B.data_ptr(), S.data_ptr(),
+                                                Z.data_ptr(), 32, O.data_ptr(), mnb.MNB_BF16, stream.cuda_stream,
+                                                ctypes.byref(p))
+                    assert st == 0, mnb.mnb_status_string(st)
+                for i in range(30):
+                    go(i)
+                n = max(100, min(2000, int(0.05 / (wbytes / 5e12))))
+                best = float("inf")
+                for _ in range(3):
+                    e0.record(stream)
+                    for i in range(n):
+                        go(i)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    best = min(best, e0.elapsed_time(e1) * 1e3 / n)
+                row[str(wg)] = round(best, 3)
+            res["shapes"][key_of((m, K, N))] = {"occ": occ, "tiles": tiles, "us": row}
+            print(key_of((m, K, N)), "occ", occ, " ".join("%s:%.2f" % kv for kv in row.items()), flush=True)
+            del A, copies, O
+    with open(out_path, "w") as f:
+        json.dump(res, f, indent=1)
+
+
 def fit_model(data):
     """(table, decode): the cost coefficients of every tiling, fitted by
     non-negative least squares on relative error, and the decode plan's."""
@@ -217,6 +285,7 @@ def fit(path):
 
 
 if __name__ == "__main__":
-    if len(sys.argv) != 3 or sys.argv[1] not in ("sweep", "fit"):
-        sys.exit("usage: python -m block_wise_int4_matmulnbits_amd.plan_tune sweep|fit FILE.json")
-    (sweep if sys.argv[1] == "sweep" else fit)(os.path.abspath(sys.argv[2]))
+    cmds = {"sweep": sweep, "fit": fit, "sweep-grid": sweep_grid}
+    if len(sys.argv) != 3 or sys.argv[1] not in cmds:
+        sys.exit("usage: python -m block_wise_int4_matmulnbits_amd.plan_tune sweep|fit|sweep-grid FILE.json")
+    cmds[sys.argv[1]](os.path.abspath(sys.argv[2]))

@@ -243,10 +243,13 @@ def test_default_plan_shapes():
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
     # Two or more rows: the 4x4x4 MFMA kernel, seven waves of four blocks per
     # lane group for the 14336-long K, four waves of two for 4096; four
-    # columns per tile, at least two tiles per workgroup.
+    # columns per tile; whole workgroups per CU, about 10 * K/4096 tiles each
+    # within one resident generation (the grids measured fastest or within
+    # 7% of it).
     for m, K, N, occ, shape in ((2, 14336, 4096, 1, (7, 4, 4, 256)), (8, 14336, 4096, 1, (7, 4, 4, 256)),
-                                (4, 4096, 28672, 4, (4, 2, 4, 1024)), (8, 4096, 151936, 4, (4, 2, 4, 1024)),
-                                (8, 4096, 6144, 4, (4, 2, 4, 768))):
+                                (4, 4096, 28672, 4, (4, 2, 4, 768)), (8, 4096, 151936, 4, (4, 2, 4, 1024)),
+                                (8, 4096, 6144, 4, (4, 2, 4, 256)), (4, 8192, 8192, 3, (4, 4, 4, 256)),
+                                (4, 4096, 14336, 4, (4, 2, 4, 512))):
         p = mnb.mnb_plan_default(m, K, N, 256, occ)
         assert p.engine == 3
         assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape

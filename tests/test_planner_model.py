@@ -17,6 +17,9 @@ from block_wise_int4_matmulnbits_amd import plan_tune
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 DATA = json.load(open(os.path.join(ROOT, "tests", "data", "prefill_tilings_gfx950.json")))
+# The 4x4x4 MFMA decode kernel (2 <= m <= 8) timed over whole workgroups per
+# CU on 40 shapes (plan_tune.py sweep-grid).
+GRID = json.load(open(os.path.join(ROOT, "tests", "data", "decode_grid_gfx950.json")))
 SHAPES = sorted((tuple(map(int, k.split(","))), row) for k, row in DATA["shapes"].items())
 
 
@@ -88,3 +91,24 @@ def test_split_plans_stay_within_the_workspace_bound():
                         tiles = -(-m // rows) * -(-N // p.cols_per_tile) * p.k_splits
                         assert tiles < 4 * cus, (m, K, N, cus, p.as_dict())
                         assert mnb.mnb_plan_check(m, K, N, p) == 0
+
+
+def test_decode_grid_near_the_measured_fastest():
+    """The grid mnb_plan_default gives the 4x4x4 MFMA kernel (whole
+    workgroups per CU, about 10 * K/4096 column quads each, within one
+    resident generation) on every measured shape: within 8% of the fastest
+    measured grid, 2% on average, and faster on average than one resident
+    generation (the rule it replaced)."""
+    regrets, gains = [], []
+    for key, row in GRID["shapes"].items():
+        m, K, N = map(int, key.split(","))
+        p = mnb.mnb_plan_default(m, K, N, GRID["cus"], row["occ"])
+        assert p.engine == 3, key
+        us = {int(w): t for w, t in row["us"].items()}
+        assert p.workgroups in us, (key, p.workgroups)
+        regrets.append(us[p.workgroups] / min(us.values()) - 1)
+        assert regrets[-1] <= 0.08, (key, p.workgroups, us)
+        generation = min(row["occ"] * GRID["cus"], -(-row["tiles"] // 2))
+        gains.append(us[generation] / us[p.workgroups] - 1)
+    assert sum(regrets) / len(regrets) <= 0.02
+    assert sum(gains) / len(gains) >= 0.05
