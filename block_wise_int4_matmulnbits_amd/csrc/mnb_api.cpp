@@ -205,37 +205,37 @@ struct Tiling {
     double t0, a, g, d, h, u;
 };
 constexpr Tiling kTilings[] = {
-    {1, 16, 4, 1, 3.9244, 1.3980, 1.8903, 1.8873, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
-    {1, 16, 8, 1, 5.9552, 2.0069, 1.9272, 1.7161, 0.0000, 0.0000},
-    {1, 32, 4, 1, 4.9487, 1.4837, 2.3526, 1.9108, 3.2582, 0.0000},   // K split over the four waves
-    {1, 64, 2, 1, 0.9597, 2.2652, 1.7304, 5.5067, 9.9036, 0.0000},
-    {1, 128, 4, 1, 1.3772, 4.5039, 2.3544, 5.5933, 12.4768, 0.0000},
-    {2, 128, 4, 1, 3.6968, 6.1140, 2.1443, 6.0116, 6.3987, 0.0000},
-    {4, 128, 4, 1, 4.8230, 12.4917, 3.5210, 11.2838, 0.0000, 0.0000},
-    {1, 256, 8, 1, 0.0000, 9.4982, 3.9897, 8.9907, 33.0263, 0.0000},
-    {2, 256, 8, 1, 1.4780, 12.7663, 4.5713, 10.2833, 22.3049, 0.0000},
-    {4, 256, 8, 1, 3.9098, 18.6270, 8.7240, 14.5974, 7.9110, 0.0000},
-    {8, 256, 8, 1, 7.5499, 34.4270, 0.0000, 24.0344, 9.0054, 0.0000},   // 256 x 256, weights through LDS
-    {1, 128, 4, 2, 5.7362, 3.9585, 0.0000, 4.8435, 6.7972, 198.7372},   // K split over 2..16 workgroups, a second launch adds the slices
-    {1, 128, 4, 4, 6.6096, 3.9520, 0.0000, 4.4306, 10.5003, 161.8492},
-    {1, 128, 4, 8, 6.4151, 3.7590, 1.0284, 5.1502, 8.6722, 110.4932},
-    {1, 128, 4, 16, 7.5472, 1.7829, 1.4252, 3.1608, 22.8446, 113.3746},
-    {2, 128, 4, 2, 6.0819, 4.5161, 0.0000, 5.9733, 1.0932, 204.3010},
-    {2, 128, 4, 4, 7.2117, 5.2799, 0.0000, 5.8215, 3.1945, 131.6582},
-    {2, 128, 4, 8, 7.3576, 5.2841, 0.3055, 6.1671, 6.5950, 112.8108},
-    {2, 128, 4, 16, 8.2182, 2.8579, 2.2764, 6.0666, 0.0000, 120.4394},
-    {4, 128, 4, 2, 6.6830, 11.4857, 0.0000, 11.1286, 0.2157, 201.6521},
-    {4, 128, 4, 4, 8.0122, 12.0687, 0.0000, 10.5646, 9.9742, 151.3090},
-    {4, 128, 4, 8, 7.5276, 10.7261, 4.7451, 12.0561, 7.8627, 111.5904},
-    {4, 128, 4, 16, 9.3827, 7.8021, 7.8584, 10.9310, 0.0000, 106.5257},
-    {1, 256, 8, 2, 3.5601, 7.2971, 0.0000, 8.5310, 23.8684, 201.0858},
-    {1, 256, 8, 4, 5.6509, 8.2060, 0.0000, 8.4668, 13.7726, 127.5536},
-    {1, 256, 8, 8, 6.3480, 9.1871, 0.0000, 8.8180, 16.2886, 81.5570},
-    {1, 256, 8, 16, 8.0913, 8.2569, 1.4076, 7.2531, 17.3491, 54.7710},
-    {2, 256, 8, 2, 4.6189, 12.1103, 0.0000, 10.3512, 14.2284, 196.9201},
-    {2, 256, 8, 4, 6.2785, 12.0003, 0.0000, 10.3495, 6.4116, 144.7644},
-    {2, 256, 8, 8, 6.2775, 12.8870, 0.0000, 10.6790, 16.4136, 115.8997},
-    {2, 256, 8, 16, 8.0027, 9.6598, 4.7357, 8.9057, 20.8932, 82.4020},
+    {1, 16, 4, 1, 3.8340, 1.3859, 1.9290, 1.8916, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
+    {1, 16, 8, 1, 5.9311, 2.0056, 1.9337, 1.7159, 0.0000, 0.0000},
+    {1, 32, 4, 1, 4.9712, 1.4728, 2.3830, 1.9080, 3.2798, 0.0000},   // K split over the four waves
+    {1, 64, 2, 1, 1.0460, 2.2102, 1.7282, 5.4993, 10.5152, 0.0000},
+    {1, 128, 4, 1, 1.3374, 4.3992, 2.3826, 5.5956, 12.9251, 0.0000},
+    {2, 128, 4, 1, 3.7060, 5.9468, 1.7442, 6.0080, 6.0939, 0.0000},
+    {4, 128, 4, 1, 4.9318, 12.3730, 3.1977, 11.2751, 0.0000, 0.0000},
+    {1, 256, 8, 1, 0.0000, 9.3921, 3.4783, 8.9757, 33.9676, 0.0000},
+    {2, 256, 8, 1, 1.4985, 12.4081, 4.1295, 10.2612, 23.1617, 0.0000},
+    {4, 256, 8, 1, 3.9435, 18.2621, 7.3530, 14.5957, 7.7044, 0.0000},
+    {8, 256, 8, 1, 7.3793, 33.3495, 0.0000, 24.0483, 10.0588, 0.0000},   // 256 x 256, weights through LDS
+    {1, 128, 4, 2, 5.6301, 3.8688, 0.0000, 4.8511, 7.3033, 201.3994},   // K split over 2..16 workgroups, a second launch adds the slices
+    {1, 128, 4, 4, 6.6484, 3.9026, 0.0000, 4.4085, 10.4412, 161.6338},
+    {1, 128, 4, 8, 6.9289, 4.0388, 0.5154, 4.7957, 9.5581, 104.3326},
+    {1, 128, 4, 16, 8.2099, 1.9890, 1.0604, 2.4660, 23.3252, 111.7309},
+    {2, 128, 4, 2, 6.1735, 4.3650, 0.0000, 5.9472, 1.7217, 197.8562},
+    {2, 128, 4, 4, 7.2291, 5.1918, 0.0000, 5.7808, 3.6334, 127.1426},
+    {2, 128, 4, 8, 7.6480, 5.2229, 0.2642, 6.0680, 5.0173, 108.6896},
+    {2, 128, 4, 16, 8.5537, 3.1457, 2.1555, 5.4861, 0.0000, 116.9556},
+    {4, 128, 4, 2, 6.7748, 11.3025, 0.0000, 11.0931, 1.9220, 194.3587},
+    {4, 128, 4, 4, 7.9754, 11.9994, 0.0150, 10.5488, 11.0137, 148.8075},
+    {4, 128, 4, 8, 7.6336, 10.5853, 4.7926, 11.8893, 9.7610, 108.4946},
+    {4, 128, 4, 16, 9.4308, 7.9438, 7.8174, 10.8791, 0.0000, 104.3491},
+    {1, 256, 8, 2, 3.6615, 7.2457, 0.0000, 8.5204, 24.3173, 192.8554},
+    {1, 256, 8, 4, 5.6659, 8.0348, 0.0000, 8.4239, 14.3902, 127.5766},
+    {1, 256, 8, 8, 6.5065, 9.2005, 0.0000, 8.6915, 16.8964, 75.7921},
+    {1, 256, 8, 16, 8.4639, 8.6377, 1.1101, 6.6610, 17.6608, 53.5782},
+    {2, 256, 8, 2, 4.7200, 11.7755, 0.0000, 10.3403, 14.3167, 188.1865},
+    {2, 256, 8, 4, 6.3459, 11.7508, 0.0000, 10.3318, 6.8384, 138.2939},
+    {2, 256, 8, 8, 6.3744, 12.7835, 0.0000, 10.6592, 15.3238, 111.8707},
+    {2, 256, 8, 16, 8.2109, 9.5054, 4.7560, 8.5407, 20.3536, 80.7178},
 };
 // The decode plan per launch of r <= 8 rows:
 //   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
@@ -243,7 +243,7 @@ constexpr Tiling kTilings[] = {
 // from shapes where fixed costs dominate; far beyond them the weights set
 // the time) and no less than 3 us, about what one launch takes however
 // small.
-constexpr double kDecode[4] = {2.1476, 0.5698, 0.6076, 0.2224};
+constexpr double kDecode[4] = {2.0226, 0.6523, 0.6318, 0.1647};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
 constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
@@ -399,11 +399,11 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // a cost model fitted to timings on gfx950 (256 CUs, bf16 in and
         // out, 64 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
-        // those shapes the cheapest modelled plan runs 0.38% slower than
+        // those shapes the cheapest modelled plan runs 0.37% slower than
         // the fastest measured one on average (6.5% at most, where a split
-        // the model ranks second would have won), and 12.1% faster on
+        // the model ranks second would have won), and 12.2% faster on
         // average than the fastest plan without a K split (never more than
-        // 2.2% slower: a choice between unsplit tilings).
+        // 2.0% slower: a choice between unsplit tilings).
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
