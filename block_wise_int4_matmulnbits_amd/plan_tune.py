@@ -7,7 +7,10 @@ and takes the cheapest.  This script produces both halves of that:
   python -m block_wise_int4_matmulnbits_amd.plan_tune sweep OUT.json
       (GPU) times every tiling that mnb_plan_check accepts, each with one
       resident generation of workgroups, and the decode plan for m <= 16,
-      on a fixed list of shapes (bf16 in and out, random weights).
+      on a fixed list of shapes (bf16 in and out, random weights).  One
+      weight copy per shape: at the few-row heights it stays in the 256 MB
+      last-level cache, so those times run below a call on cold weights;
+      the model uses their ranking.
   python -m block_wise_int4_matmulnbits_amd.plan_tune fit IN.json
       (CPU) fits the cost of each tiling by non-negative least squares on
       relative error and prints the table the planner holds, and the
