@@ -361,3 +361,34 @@ def test_k_split_default_few_columns(oracle_mod):
         plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
         G.log("[parity] %dx%dx%d default plan %s" % (m, K, N, plan.as_dict()))
         assert_prefill(oracle_mod, d, m, "split default m=%d" % m, None)
+
+
+def test_k_split_workspace_growth_and_eviction():
+    """The per-stream workspace: a small split call and then a larger one on
+    a new stream (the buffer grows after the stream drains), and split calls
+    on more streams than the library's table holds (the least recently used
+    buffer is given up after the device drains): every output equals the
+    same call on the default stream."""
+    small = dict(engine=2, row_tiles=1, cols_per_tile=128, waves_per_wg=4, workgroups=64, k_splits=2)
+    big = dict(engine=2, row_tiles=2, cols_per_tile=128, waves_per_wg=4, workgroups=256, k_splits=16)
+    d_small = W.generate(9, 4096, 300, W.BF16, True, 0.001, 0.01, 0.5, 1101)
+    d_big = W.generate(40, 14336, 1000, W.BF16, True, 0.001, 0.01, 0.5, 1102)
+    ref_small, _ = run(d_small, 9, W.BF16, small)
+    ref_big, _ = run(d_big, 40, W.BF16, big)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        y1, _ = run(d_small, 9, W.BF16, small)      # 9 * 300 * 2 floats
+        y2, _ = run(d_big, 40, W.BF16, big)         # 40 * 1000 * 16 floats: grows
+        y3, _ = run(d_small, 9, W.BF16, small)
+    assert np.array_equal(y1, ref_small) and np.array_equal(y2, ref_big) and np.array_equal(y3, ref_small)
+    streams = [torch.cuda.Stream() for _ in range(40)]   # more than the 32 entries of the table
+    outs = []
+    for st in streams:
+        with torch.cuda.stream(st):
+            y, _ = run(d_small, 9, W.BF16, small)
+            outs.append(y)
+    with torch.cuda.stream(streams[0]):               # its entry was given up: a new one
+        y, _ = run(d_big, 40, W.BF16, big)
+    torch.cuda.synchronize()
+    assert all(np.array_equal(o, ref_small) for o in outs)
+    assert np.array_equal(y, ref_big)
