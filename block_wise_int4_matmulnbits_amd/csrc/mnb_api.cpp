@@ -282,11 +282,12 @@ struct PrefillChoice {
 };
 
 // The cheapest plan by the model among the tilings the plan check accepts
-// for (m, K, N) and the decode plan; ties go to the earlier tiling.
-PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus)
+// for (m, K, N) and, with `decode`, the decode plan; ties go to the earlier
+// tiling.
+PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus, bool decode = true)
 {
-    PrefillChoice best{kTilings[0], true};
-    double best_cost = decode_cost(m, K, N);
+    PrefillChoice best{kTilings[0], decode};
+    double best_cost = decode ? decode_cost(m, K, N) : HUGE_VAL;
     for (const Tiling& t : kTilings) {
         mnb_plan q{};
         q.engine = 2;
@@ -308,6 +309,23 @@ PrefillChoice cheapest_prefill(int64_t m, int64_t K, int64_t N, int num_cus)
         }
     }
     return best;
+}
+
+// The prefill plan of tiling t: one resident generation of workgroups, at
+// most one per tile.
+int prefill_plan(const Tiling& t, int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_cu, mnb_plan* plan)
+{
+    const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
+    const int64_t tiles = prefill_tiles(t, m, N);
+    int64_t wgs = per_cu * num_cus;
+    if (wgs > tiles) wgs = tiles;
+    plan->engine = 2;
+    plan->row_tiles = t.rt;
+    plan->cols_per_tile = t.cols;
+    plan->waves_per_wg = t.waves;
+    plan->k_splits = t.splits;
+    plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
+    return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
 }
 
 }  // namespace
@@ -406,17 +424,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // 2.0% slower: a choice between unsplit tilings).
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
-        const int64_t per_cu = wgs_per_cu > 0 ? wgs_per_cu : 1;
-        const int64_t tiles = prefill_tiles(c.t, m, N);
-        int64_t wgs = per_cu * num_cus;
-        if (wgs > tiles) wgs = tiles;
-        plan->engine = 2;
-        plan->row_tiles = c.t.rt;
-        plan->cols_per_tile = c.t.cols;
-        plan->waves_per_wg = c.t.waves;
-        plan->k_splits = c.t.splits;
-        plan->workgroups = (int32_t)(wgs < 1 ? 1 : wgs);
-        return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
+        return prefill_plan(c.t, m, K, N, num_cus, wgs_per_cu, plan);
     }
     const int64_t nb = K / 32;
     const int64_t bmax = max_blocks_per_lane(m);
@@ -478,6 +486,19 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         if (bpl > bmax) bpl = bmax;
     }
 
+    // Two or more rows whose K the lane split cannot cover in one pass (eight
+    // waves of one to four blocks per lane, as registers allow: K > 16384 at
+    // five to eight rows, K > 32768 at three or four): the chunked passes
+    // take one tile at a time and reload the activations per chunk (K =
+    // 28672, N = 4096, m = 8: 178 us against 26 at m = 4), so the prefill
+    // tiles run instead, K split over workgroups, priced by the prefill cost
+    // model (that shape 31.8 us; 28672 x 8192 m = 8 345 -> 52.4, 20480 x 8192
+    // 320 -> 44.4, 65536 x 4096 342 -> 59.2).  Whether this happens depends
+    // on (m, K) only; which tiling runs then depends on N and the CUs, as
+    // for m > 8.
+    if (m >= 2 && nb > 0 && ceil_div(nb, lpc * bpl) > 1)
+        return prefill_plan(cheapest_prefill(m, K, N, num_cus, false).t, m, K, N, num_cus, wgs_per_cu, plan);
+
     // 2. Column tile: two columns per lane group in a wave; one column per
     //    multi-wave group, whose waves then keep the next column's loads in
     //    flight (measured on the down-projection shape).
@@ -488,9 +509,14 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     //    weights as one front.  In-wave groups: about five tiles per group,
     //    in whole rounds of the CU count, between half and three times one
     //    resident generation of workgroups (measured best on the lm_head
-    //    and gate_up shapes).  Multi-wave
-    //    groups: half a resident generation, at least one workgroup per CU
-    //    (more tiles per workgroup share its activation fetch).
+    //    and gate_up shapes).  Multi-wave groups: whole workgroups per CU,
+    //    about eight waves per CU (more tiles per workgroup share its
+    //    activation fetch).  Measured at m = 1 on 11 shapes with K from 6144
+    //    to 28672 against half a resident generation (2.5 four-wave
+    //    workgroups per CU, which leaves the CUs uneven): the down projection
+    //    10.39 -> 9.57 us, 8192 x 14336 14.52 -> 13.69, 16384 x 16384 29.32
+    //    -> 26.28; best or within 1% of the best count on eight of the 11,
+    //    4.7% from it on the other three.
     const bool inwave = lpc <= 64;
     const int64_t gpw = inwave ? 256 / lpc : 1;
     const int64_t waves_per_wg = inwave ? 4 : lpc / 64;
@@ -503,6 +529,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     while (inwave && nc > 1 && ceil_div(ceil_div(N, nc), gpw) < resident / 2) nc /= 2;
     const int64_t tiles = ceil_div(N, nc);
     int64_t wgs = resident / 2 > num_cus ? resident / 2 : num_cus;
+    if (!inwave) {
+        int64_t c = (8 + waves_per_wg / 2) / waves_per_wg;   // ~8 waves per CU
+        if (c > per_cu) c = per_cu;
+        if (c < 1) c = 1;
+        wgs = c * num_cus;
+    }
     if (inwave) {
         wgs = num_cus * ceil_div(ceil_div(tiles, 5 * gpw), num_cus);   // whole rounds of CUs
         const int64_t lo = resident / 2 > 0 ? resident / 2 : 1;

@@ -100,12 +100,15 @@ typedef enum {
  *   A            device, [m][K] row-major, fp16 or bf16 per a_dtype; 16-byte
  *                aligned.  Must hold finite values that are finite in fp16.
  *   a_dtype      MNB_F16 or MNB_BF16.
- *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels; m > 8:
- *                prefill kernel, except that up to 16 rows whose 32-column
- *                prefill tiles would leave more than half of the compute
- *                units idle run the decode kernels in launches of
- *                8 rows).  m == 0 or
- *                N == 0: nothing to do, MNB_OK.
+ *   m            rows, 0 <= m <= MNB_MAX_ROWS (m <= 8: decode kernels,
+ *                except that two or more rows whose K the decode lane split
+ *                would walk in several passes -- K > 65536 at two rows,
+ *                > 32768 at three or four, > 16384 at five to eight -- run
+ *                the prefill kernel; m > 8: prefill kernel, except that up
+ *                to 16 rows whose 32-column prefill tiles would leave more
+ *                than half of the compute units idle run the decode kernels
+ *                in launches of 8 rows).  m == 0 or N == 0: nothing to do,
+ *                MNB_OK.
  *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).
  *   N            output columns.
  *   Bpacked      device, [N][K/2] bytes; byte k/2 of row n holds weight k,
@@ -132,13 +135,14 @@ typedef enum {
  * than the stream's workspace holds, allocate it with hipMalloc (a larger
  * one after the stream has drained); other calls allocate nothing.  Calls
  * that must not allocate use matmul_nbits_noalloc.
- * The fp32 summation order is fixed by (m, K) for m <= 8 (never by N or
- * the device), and by
- * (m, K, N) and the device's compute-unit count for m > 8 (which tiling
- * runs, and whether it splits K, depends on how the tiles fill the device).
- * So equal inputs give bitwise equal outputs on the same device, column
- * shards of one matrix give the bits of the whole at m <= 8, and the bf16
- * output equals the fp16 output of the same call narrowed to bf16.
+ * The fp32 summation order is fixed by (m, K) where the decode kernels run
+ * at m <= 8 (never by N or the device), and by (m, K, N) and the device's
+ * compute-unit count where the prefill kernel runs (which tiling runs, and
+ * whether it splits K, depends on how the tiles fill the device).  So equal
+ * inputs give bitwise equal outputs on the same device, column shards of
+ * one matrix give the bits of the whole at m <= 8 wherever the decode
+ * kernels run, and the bf16 output equals the fp16 output of the same call
+ * narrowed to bf16.
  * Thread safety: may be called from several host threads at once (calls
  * that split K queue their two launches under one library lock).
  */
@@ -216,9 +220,9 @@ typedef struct {
     int32_t k_splits;        /* engine 2 with row_tiles 1, 2 or 4: K split into
                                 this many slices over the workgroups, whose fp32
                                 partial sums a second launch adds in slice order
-                                (workspace: k_splits * m * N * 4 bytes, taken
-                                from a stream-ordered pool the library keeps per
-                                device); 0 or 1: no split.  Must be 0 or 1 for
+                                (workspace: k_splits * m * N * 4 bytes, the
+                                buffer the library keeps per device and
+                                stream); 0 or 1: no split.  Must be 0 or 1 for
                                 the other engines.                             */
 } mnb_plan;
 

@@ -94,8 +94,16 @@ def test_default_plans_are_valid_and_cover_k():
                 tiles = -(-(-(-N // 4)) // (p.cols_per_tile // 4))
                 assert 1 <= p.workgroups <= max(1, -(-tiles // 2))   # two tiles per workgroup
                 continue
+            if p.engine == 2:
+                # Two or more rows whose K the decode lane split would walk
+                # in chunks (more blocks than 512 lanes of 8 // m blocks
+                # each): the prefill tiles, K split over workgroups.
+                assert 2 <= m <= 8 and nb > 512 * max(1, min(4, 8 // m)), (m, K)
+                assert q.threads_per_wg == 64 * p.waves_per_wg and q.k_chunks == (nb + 3) // 4
+                continue
             assert p.engine == 0 and not (m >= 2 and 1 <= nb <= 512)
             lpc, bpl, nc = p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile
+            assert m == 1 or p.k_chunks == 1      # chunked passes only at one row
             assert lpc * bpl * p.k_chunks >= K // 32
             assert m * bpl <= 8 and nc * bpl <= 8 and nc * m <= 32
             assert p.threads_per_wg in (256, lpc) and p.threads_per_wg <= 512
@@ -210,15 +218,20 @@ def test_plan_check_engines_and_rows():
 
 
 def test_summation_order_does_not_depend_on_n_or_device():
-    """The lane split (which fixes the fp32 summation order of a column)
-    depends only on (m, K): the same inputs give the same bits for any N
-    and on any compute-unit count."""
+    """Up to 8 rows, the engine is a function of (m, K) (the prefill tiles
+    only where the decode lane split would need K in chunks at two or more
+    rows), and the decode lane split (which fixes the fp32 summation order
+    of a column) depends only on (m, K): the same inputs give the same bits
+    for any N and on any compute-unit count."""
     for m in range(1, 9):
-        for K in (32, 1024, 4096, 14336, 65536):
-            splits = {(p.lanes_per_col, p.blocks_per_lane, p.k_chunks)
-                      for N in (1, 1000, 151936) for cus in (1, 256, 304)
-                      for occ in (0, 1, 5)
-                      for p in [mnb.mnb_plan_default(m, K, N, cus, occ)]}
+        for K in (32, 1024, 4096, 14336, 32768, 65536, 131072):
+            plans = [mnb.mnb_plan_default(m, K, N, cus, occ)
+                     for N in (1, 1000, 151936) for cus in (1, 256, 304) for occ in (0, 1, 5)]
+            engines = {p.engine for p in plans}
+            assert engines == {2} or 2 not in engines, (m, K, engines)
+            if engines == {2}:
+                continue
+            splits = {(p.engine, p.lanes_per_col, p.waves_per_wg, p.blocks_per_lane, p.k_chunks) for p in plans}
             assert len(splits) == 1, (m, K, splits)
 
 

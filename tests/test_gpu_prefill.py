@@ -392,3 +392,17 @@ def test_k_split_workspace_growth_and_eviction():
     torch.cuda.synchronize()
     assert all(np.array_equal(o, ref_small) for o in outs)
     assert np.array_equal(y, ref_big)
+
+
+@pytest.mark.parametrize("m,K,N", [(5, 32 * 611, 150), (8, 28672, 600), (3, 36864, 300), (2, 65568, 70)])
+def test_long_k_rows_run_prefill_tiles(oracle_mod, m, K, N):
+    """Two to eight rows whose K the decode lane split would walk in chunks
+    (K > 16384 at five or more rows, > 32768 at three or four, > 65536 at
+    two): the default plan runs the prefill tiles instead, with K split over
+    workgroups where the model prices it lower; full parity, including a
+    ragged K."""
+    d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 1300 + m)
+    plan = mnb.plan_for_device(m, K, N, torch.cuda.get_device_properties(0).multi_processor_count)
+    assert plan.engine == 2, plan.as_dict()
+    G.log("[parity] long K m=%d K=%d N=%d plan %s" % (m, K, N, plan.as_dict()))
+    assert_prefill(oracle_mod, d, m, "long K rows", None)
