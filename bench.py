@@ -155,7 +155,7 @@ class Resident:
 def plan_fields(plan):
     """The fields of a decode plan that its engine reads."""
     keys = {0: ("lanes_per_col", "blocks_per_lane", "cols_per_tile", "workgroups"),
-            3: ("waves_per_wg", "blocks_per_lane", "cols_per_tile", "workgroups")}
+            3: ("waves_per_wg", "blocks_per_lane", "cols_per_tile", "workgroups", "a_via_lds")}
     d = plan.as_dict()
     return dict({"engine": d["engine"]}, **{k: d[k] for k in keys.get(d["engine"], ())})
 

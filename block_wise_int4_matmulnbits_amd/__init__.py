@@ -53,7 +53,8 @@ class mnb_plan(ctypes.Structure):
                 ("k_chunks", ctypes.c_int32),
                 ("row_tiles", ctypes.c_int32),
                 ("b_layout", ctypes.c_int32),
-                ("k_splits", ctypes.c_int32)]
+                ("k_splits", ctypes.c_int32),
+                ("a_via_lds", ctypes.c_int32)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -339,6 +339,7 @@ int mnb_plan_check(int64_t m, int64_t K, int64_t N, mnb_plan* plan)
     if (plan->b_layout != MNB_LAYOUT_NATURAL &&
         !(plan->b_layout == MNB_LAYOUT_EVEN_ODD && (plan->engine == 0 || plan->engine == 3)))
         return MNB_ERR_PLAN;
+    if (plan->a_via_lds != 0 && (plan->a_via_lds != 1 || plan->engine != 3)) return MNB_ERR_PLAN;
     const int64_t nb = K / 32;
     if (plan->engine == 2) {
         const bool shape_ok =
@@ -447,6 +448,13 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // m = 4 16.7 -> 12.7, gate_up m = 8 25.9 -> 24.4), 1.1% above the
     // fastest grid on average, 7.3% at most; at m = 2 on 4096 and 6144
     // columns it is 4.6-6.6% slower than two tiles per workgroup.
+    // Activations through LDS from three rows up where K or N exceeds 8192
+    // (interleaved A/B, same bits, us: down projection m = 3 12.5 -> 11.5,
+    // m = 4 13.6 -> 11.9, m = 7 17.5 -> 15.4, m = 8 18.3 -> 15.7; gate_up
+    // m = 4 18.7 -> 17.0, m = 8 24.3 -> 22.3; lm_head m = 3 -2.0%, m = 6
+    // -1.7%); at 8192 x 8192, 4096 x 6144 and 4096 x 4096 it was 2-4.5%
+    // slower, and at m = 2, where half of the lanes' own loads read nothing,
+    // 0-4% slower.
     if (m >= 2 && nb >= 1 && nb <= 512) {
         int64_t bpl3 = 1;
         while (bpl3 < 4 && ceil_div(nb, 16 * bpl3) > 4) bpl3 *= 2;
@@ -463,6 +471,7 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         plan->waves_per_wg = (int32_t)w3;
         plan->blocks_per_lane = (int32_t)bpl3;
         plan->cols_per_tile = 4;
+        plan->a_via_lds = m >= 3 && (K > 8192 || N > 8192);
         plan->workgroups = (int32_t)(wgs3 < 1 ? 1 : wgs3);
         return mnb_plan_check(m, K, N, plan) == MNB_OK ? MNB_OK : MNB_ERR_PLAN;
     }

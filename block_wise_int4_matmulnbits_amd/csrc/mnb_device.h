@@ -31,13 +31,38 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t w, float c)
                                   __builtin_bit_cast(half2_t, w), c, false);
 }
 
-// Two bf16 -> two fp16, round to nearest even: the exact fp32 values of
-// both halves, then one packed RNE conversion (v_cvt_pk_f16_f32).
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v)
+// Two values -> one fp16 pair, round to nearest even (v_cvt_pk_f16_f32):
+// the fp32 values are exact (bf16 halves widened by a shift or a mask).
+__device__ __forceinline__ uint32_t f16_pair(float lo, float hi)
 {
     typedef float float2_t __attribute__((ext_vector_type(2)));
-    const float2_t f = {__uint_as_float(v << 16), __uint_as_float(v & 0xFFFF0000u)};
+    const float2_t f = {lo, hi};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, half2_t));
+}
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// One 16-byte piece of eight activations a0..a7 (fp16, or bf16 rounded to
+// fp16 RNE) as four fp16 pairs in the order the unpack yields the weights:
+// (a0,a4) (a1,a5) (a2,a6) (a3,a7) for natural weights, (a0,a1) (a2,a3)
+// (a4,a5) (a6,a7) for the even/odd layout.  bf16 halves are widened one by
+// one and each pair is built by its own packed conversion, so the reorder
+// costs nothing (three operations per pair); fp16 halves are reordered with
+// one byte permute (v_perm_b32) per pair.
+__device__ __forceinline__ u32x4 f16_pairs(u32x4 v, int a_bf16, int eo_pairs)
+{
+    const uint32_t x = v[0], y = v[1], z = v[2], w = v[3];   // (a0,a1) (a2,a3) (a4,a5) (a6,a7)
+    if (a_bf16) {
+        if (eo_pairs)
+            return u32x4{f16_pair(bf16_lo(x), bf16_hi(x)), f16_pair(bf16_lo(y), bf16_hi(y)),
+                         f16_pair(bf16_lo(z), bf16_hi(z)), f16_pair(bf16_lo(w), bf16_hi(w))};
+        return u32x4{f16_pair(bf16_lo(x), bf16_lo(z)), f16_pair(bf16_hi(x), bf16_hi(z)),
+                     f16_pair(bf16_lo(y), bf16_lo(w)), f16_pair(bf16_hi(y), bf16_hi(w))};
+    }
+    if (eo_pairs) return v;
+    // v_perm_b32 picks bytes 0-3 from its second operand, 4-7 from its first.
+    return u32x4{__builtin_amdgcn_perm(z, x, 0x05040100u), __builtin_amdgcn_perm(z, x, 0x07060302u),
+                 __builtin_amdgcn_perm(w, y, 0x05040100u), __builtin_amdgcn_perm(w, y, 0x07060302u)};
 }
 
 // fp16 bits -> bf16 bits: exact widening to fp32, then RNE on the bit
@@ -130,32 +155,15 @@ __device__ __forceinline__ void transpose_rows(uint32_t (&r)[4])
 }
 
 // Activations of one 32-weight block (four 16-byte pieces of fp16 or bf16,
-// k = 0..31) as fp16 pairs in the order the unpack yields the weights:
-// (a_e, a_e+4) per 8 k for natural weights, (a_2e, a_2e+1) for the even/odd
-// layout.  bf16 is rounded to fp16 (RNE).
+// k = 0..31) as fp16 pairs in the order the unpack yields the weights.
 __device__ __forceinline__ void activation_pairs(const u32x4 (&raw)[4], int a_bf16, int eo_pairs,
                                                  uint32_t (&act)[16])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t x = raw[i][0], y = raw[i][1], z = raw[i][2], w = raw[i][3];
-        if (a_bf16) {
-            x = bf16x2_to_f16x2(x);
-            y = bf16x2_to_f16x2(y);
-            z = bf16x2_to_f16x2(z);
-            w = bf16x2_to_f16x2(w);
-        }
-        if (eo_pairs) {
-            act[4 * i + 0] = x;
-            act[4 * i + 1] = y;
-            act[4 * i + 2] = z;
-            act[4 * i + 3] = w;
-        } else {
-            act[4 * i + 0] = (x & 0xFFFFu) | (z << 16);       // (a0,a4)
-            act[4 * i + 1] = (x >> 16) | (z & 0xFFFF0000u);   // (a1,a5)
-            act[4 * i + 2] = (y & 0xFFFFu) | (w << 16);       // (a2,a6)
-            act[4 * i + 3] = (y >> 16) | (w & 0xFFFF0000u);   // (a3,a7)
-        }
+        const u32x4 o = f16_pairs(raw[i], a_bf16, eo_pairs);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) act[4 * i + e] = o[e];
     }
 }
 

@@ -226,21 +226,8 @@ void mnb_gemv_kernel(Params p)
     // Eight activations (one uint4) to fp16 (bf16 rounded to nearest even),
     // permuted into the unpack's pair order.
     auto to_pairs = [&](uint4 v) {
-        uint32_t x = v.x, y = v.y, z = v.z, w = v.w;
-        if (p.a_bf16) {
-            x = bf16x2_to_f16x2(x);
-            y = bf16x2_to_f16x2(y);
-            z = bf16x2_to_f16x2(z);
-            w = bf16x2_to_f16x2(w);
-        }
-        // halves: x=(a0,a1) y=(a2,a3) z=(a4,a5) w=(a6,a7)
-        if (p.eo_pairs) return make_uint4(x, y, z, w);   // already the unpack's order
-        uint4 o;
-        o.x = (x & 0xFFFFu) | (z << 16);          // (a0,a4)
-        o.y = (x >> 16) | (z & 0xFFFF0000u);      // (a1,a5)
-        o.z = (y & 0xFFFFu) | (w << 16);          // (a2,a6)
-        o.w = (y >> 16) | (w & 0xFFFF0000u);      // (a3,a7)
-        return o;
+        const u32x4 o = f16_pairs(u32x4{v.x, v.y, v.z, v.w}, p.a_bf16, p.eo_pairs);
+        return make_uint4(o[0], o[1], o[2], o[3]);
     };
 
     auto place_acts = [&](const RawActs& raw) {

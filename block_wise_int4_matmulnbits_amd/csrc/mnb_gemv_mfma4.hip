@@ -25,8 +25,9 @@
 // and 4 + i of the activations.  Wave w owns the 16 BPL consecutive K blocks
 // from 16 BPL w, and its group g the blocks 16 BPL w + 16 j + g (j < BPL);
 // together the waves cover all of K in one pass.  The lane's activations are
-// loaded once, converted to fp16, permuted into the unpack's pair order and
-// kept in VGPRs.  Per block and column the lane loads its 16 bytes of
+// loaded once (from three rows up a row at a time, 1 KB per load, and handed
+// to their lanes through a wave-private LDS buffer), converted to fp16,
+// permuted into the unpack's pair order and kept in VGPRs.  Per block and column the lane loads its 16 bytes of
 // weights (the four lanes of a group read four columns, the sixteen groups
 // of a wave 256 contiguous bytes of each).  A wave's scales and zero points
 // of a column are one contiguous run, read as whole dwords (full lines, any
@@ -63,11 +64,18 @@ struct Mfma4Params {
                              // yields (k, k+1) pairs, activations keep their order
 };
 
+// Per wave of an XP variant: an LDS buffer through which the activations
+// reach their lanes (four rows of 65 16-byte pieces); the launch gives
+// waves_per_wg of them as dynamic LDS.
+constexpr int kXposePieces = 4 * 65;
+constexpr size_t kXposeBytesPerWave = kXposePieces * 16;
+
 // RQ row quads (m <= 4 * RQ), BPL blocks per lane group, NC column quads per
-// tile.  The tile loop is straight-line code, two tiles per pass: each wave
+// tile; XP: activations loaded a row at a time and passed through LDS (below),
+// else each lane loads its own row and block directly.  The tile loop is straight-line code, two tiles per pass: each wave
 // leaves its totals of the pass's two tiles in LDS, and one barrier, the
 // sums over waves and another barrier close the pass.
-template <int RQ, int BPL, int NC>
+template <int RQ, int BPL, int NC, bool XP>
 __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 {
     constexpr int NV = 16 * NC * RQ;        // results of one tile (columns x rows)
@@ -78,6 +86,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     constexpr int ZD = (NCOL * DZ + 63) / 64;   // zero-point dwords loaded per lane and tile
     __shared__ float part[2][8][NV];        // per-wave totals of a pass's two tiles
     __shared__ uint32_t stage[8][64 * (SD + ZD)];   // a wave's scales and zero points of one tile
+    extern __shared__ u32x4 xpose_lds[];            // kXposePieces per wave
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -102,19 +111,36 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     const int64_t q_stop = nq * (blockIdx.x + 1) / gridDim.x;
     const int64_t c_stop = 4 * q_stop < p.N ? 4 * q_stop : p.N;
 
-    // Activations: rows qi and 4 + qi of this group's blocks; rows past m and
-    // blocks past K load zeros.
+    // Activations: rows 4 rq + qi of this group's blocks B0 + 16 j + g; rows
+    // past m and blocks past K load zeros.  With XP, load i of row quad rq
+    // and block group j reads row 4 rq + i over the wave's 16 blocks B0 +
+    // 16 j .. B0 + 16 j + 15, 1 KB contiguous (lane l takes piece l % 4 of
+    // block l / 4), and the pieces reach their lanes through LDS below.
+    // The direct loads (16 bytes of four rows per lane, 64 bytes apart)
+    // take 2-4 times as many cache lines per load, which leaves the staging
+    // slower from three rows up on long K or many columns (down projection
+    // m = 3, 4 and 8: 12.5, 13.6 and 18.3 us direct against 11.5, 11.9 and
+    // 15.7 with XP); the plan's a_via_lds selects XP.
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(p.A, (uint64_t)p.m * (uint64_t)p.K * 2);
     u32x4 raw[RQ][BPL][4];
 #pragma unroll
     for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
         for (int j = 0; j < BPL; ++j) {
-            const uint32_t b = B0 + 16 * (uint32_t)j + (uint32_t)g;
-            const uint32_t base = (uint32_t)(4 * rq + qi) * (uint32_t)p.K * 2 + 64 * b;
+            if constexpr (XP) {
+                const uint32_t b = B0 + 16 * (uint32_t)j + (uint32_t)(lane >> 2);
+                const uint32_t base = 64 * (B0 + 16 * (uint32_t)j) + 16 * (uint32_t)lane;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                raw[rq][j][i] = __builtin_amdgcn_raw_buffer_load_b128(rA, b < nb ? base + 16 * i : kOutOfRange, 0, 0);
+                for (int i = 0; i < 4; ++i)
+                    raw[rq][j][i] = __builtin_amdgcn_raw_buffer_load_b128(
+                        rA, b < nb ? (uint32_t)(4 * rq + i) * (uint32_t)p.K * 2 + base : kOutOfRange, 0, 0);
+            } else {
+                const uint32_t b = B0 + 16 * (uint32_t)j + (uint32_t)g;
+                const uint32_t base = (uint32_t)(4 * rq + qi) * (uint32_t)p.K * 2 + 64 * b;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    raw[rq][j][i] = __builtin_amdgcn_raw_buffer_load_b128(rA, b < nb ? base + 16 * i : kOutOfRange, 0, 0);
+            }
         }
 
     struct Tile {
@@ -197,11 +223,32 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     // fp16 (bf16 rounded to nearest even), in the order in which the unpack
     // yields the weights: pairs (a_e, a_e+4) per 8 k, or (a_2e, a_2e+1) for
     // even/odd weights.
+    // With XP each (row quad, block group) passes through the wave's LDS
+    // buffer (four rows of 64 pieces, rows 65 pieces apart so that eight
+    // lanes read 32 distinct banks): lane (g, qi) reads back the four pieces
+    // of row 4 rq + qi, block B0 + 16 j + g.  The fences keep the compiler
+    // from moving the reads above the writes of other lanes, or the next
+    // writes above the reads (one wave's LDS operations run in order, so no
+    // wait is emitted).
     uint32_t act[RQ][BPL][16];
 #pragma unroll
     for (int rq = 0; rq < RQ; ++rq)
 #pragma unroll
-        for (int j = 0; j < BPL; ++j) activation_pairs(raw[rq][j], p.a_bf16, p.eo_pairs, act[rq][j]);
+        for (int j = 0; j < BPL; ++j) {
+            if constexpr (XP) {
+                u32x4* const xw = xpose_lds + wv * kXposePieces;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xw[65 * i + lane] = raw[rq][j][i];
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                u32x4 mine[4];
+#pragma unroll
+                for (int pc = 0; pc < 4; ++pc) mine[pc] = xw[65 * qi + 4 * g + pc];
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                activation_pairs(mine, p.a_bf16, p.eo_pairs, act[rq][j]);
+            } else {
+                activation_pairs(raw[rq][j], p.a_bf16, p.eo_pairs, act[rq][j]);
+            }
+        }
 
     // Per block: the exact products of each row quad in one 4x4 result
     // (eight chained MFMAs over the block's 32 k), then acc += D * s.
@@ -322,32 +369,39 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 
 typedef void (*Mfma4Fn)(Mfma4Params);
 
-template <int RQ, int BPL>
+template <int RQ, int BPL, bool XP>
 Mfma4Fn by_nc(int nc)
 {
     switch (nc) {
-    case 1: return mnb_gemv_mfma4_kernel<RQ, BPL, 1>;
-    case 2: return mnb_gemv_mfma4_kernel<RQ, BPL, 2>;
+    case 1: return mnb_gemv_mfma4_kernel<RQ, BPL, 1, XP>;
+    case 2: return mnb_gemv_mfma4_kernel<RQ, BPL, 2, XP>;
     }
     return nullptr;
 }
 
-template <int RQ>
+template <int RQ, bool XP>
 Mfma4Fn by_bpl(int bpl, int nc)
 {
     switch (bpl) {
-    case 1: return by_nc<RQ, 1>(nc);
-    case 2: return by_nc<RQ, 2>(nc);
-    case 4: return by_nc<RQ, 4>(nc);
+    case 1: return by_nc<RQ, 1, XP>(nc);
+    case 2: return by_nc<RQ, 2, XP>(nc);
+    case 4: return by_nc<RQ, 4, XP>(nc);
     }
     return nullptr;
+}
+
+
+size_t mfma4_dynamic_lds(const mnb_plan& plan)
+{
+    return plan.a_via_lds ? (size_t)(plan.threads_per_wg / 64) * kXposeBytesPerWave : 0;
 }
 
 Mfma4Fn lookup_mfma4(int64_t m, const mnb_plan& plan)
 {
     const int nc = plan.cols_per_tile / 4;
-    if (m >= 1 && m <= 4) return by_bpl<1>(plan.blocks_per_lane, nc);
-    if (m >= 5 && m <= 8) return by_bpl<2>(plan.blocks_per_lane, nc);
+    const bool xp = plan.a_via_lds != 0;
+    if (m >= 1 && m <= 4) return xp ? by_bpl<1, true>(plan.blocks_per_lane, nc) : by_bpl<1, false>(plan.blocks_per_lane, nc);
+    if (m >= 5 && m <= 8) return xp ? by_bpl<2, true>(plan.blocks_per_lane, nc) : by_bpl<2, false>(plan.blocks_per_lane, nc);
     return nullptr;
 }
 
@@ -374,7 +428,7 @@ int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.eo_pairs = plan.b_layout == MNB_LAYOUT_EVEN_ODD;
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)plan.workgroups),
-                                   dim3((unsigned)plan.threads_per_wg), args, 0,
+                                   dim3((unsigned)plan.threads_per_wg), args, mfma4_dynamic_lds(plan),
                                    static_cast<hipStream_t>(stream));
     if (e == hipSuccess) e = hipGetLastError();
     return (int)e;
@@ -385,7 +439,7 @@ int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan)
     Mfma4Fn fn = lookup_mfma4(m, plan);
     if (!fn) return 0;
     (void)N;
-    return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, 0);
+    return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, mfma4_dynamic_lds(plan));
 }
 
 int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
@@ -397,7 +451,7 @@ int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
     if (e != hipSuccess) return (int)e;
     info->vgprs = attr.numRegs;
     info->sgprs = 0;
-    info->lds_bytes = (int32_t)attr.sharedSizeBytes;
+    info->lds_bytes = (int32_t)(attr.sharedSizeBytes + mfma4_dynamic_lds(plan));
     info->max_threads = attr.maxThreadsPerBlock;
     info->wgs_per_cu = mfma4_workgroups_per_cu(m, 1, plan);
     return 0;

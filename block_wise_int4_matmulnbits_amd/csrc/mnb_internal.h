@@ -26,7 +26,8 @@ int launch_gemv(const GemvArgs& args, const mnb_plan& plan, void* stream);
 
 // The 4x4x4 MFMA kernel (engine 3), mnb_gemv_mfma4.hip: W waves per
 // workgroup whose 16 W lane groups cover K in one pass (16 W * blocks_per_lane
-// >= K/32), cols_per_tile = 4 or 8.  No dynamic LDS.
+// >= K/32), cols_per_tile = 4 or 8.  With plan.a_via_lds, dynamic LDS of 4160
+// bytes per wave, through which the activations reach their lanes.
 int launch_mfma4(const GemvArgs& args, const mnb_plan& plan, void* stream);
 int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan);
 int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);

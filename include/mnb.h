@@ -32,7 +32,7 @@
 extern "C" {
 #endif
 
-#define MNB_ABI_VERSION 5
+#define MNB_ABI_VERSION 6
 
 /* Element types of A and of the output. */
 typedef enum { MNB_F16 = 0, MNB_BF16 = 1 } mnb_dtype;
@@ -197,7 +197,11 @@ int matmul_nbits_noalloc(const void* A, int a_dtype, int64_t m, int64_t K, int64
  * blocks_per_lane blocks each and together cover K in one pass; per block
  * the exact products come from v_mfma_f32_4x4x4_16b_f16 and the block scale
  * is applied in fp32, as in engine 0.  Needs 16 * waves_per_wg *
- * blocks_per_lane >= K/32 (so K <= 16384).
+ * blocks_per_lane >= K/32 (so K <= 16384).  With a_via_lds each load of
+ * activations reads one row's 1 KB run of a wave's 16 blocks and the pieces
+ * reach their lanes through LDS (4160 bytes per wave); otherwise each lane
+ * loads its own rows and blocks (16 bytes of four rows, 64 bytes apart).
+ * Both give the same bits.
  */
 typedef struct {
     int32_t engine;          /* 0: lane-split dot2 kernel; 2: prefill kernel;
@@ -224,6 +228,10 @@ typedef struct {
                                 buffer the library keeps per device and
                                 stream); 0 or 1: no split.  Must be 0 or 1 for
                                 the other engines.                             */
+    int32_t a_via_lds;       /* engine 3: 1 = activations loaded a row at a time
+                                and passed to their lanes through LDS, 0 = each
+                                lane loads its own; must be 0 for the other
+                                engines                                         */
 } mnb_plan;
 
 /* The plan matmul_nbits uses for (m, K, N) on a device with `num_cus`

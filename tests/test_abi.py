@@ -215,6 +215,16 @@ def test_plan_check_engines_and_rows():
     e3 = mnb.mnb_plan(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=8, workgroups=1)
     assert mnb.mnb_plan_check(4, 14336, 100, e3) == 0
     assert mnb.mnb_plan_check(40, 14336, 100, e3) == 9         # 8 rows: registers
+    # Activations through LDS: engine 3 only, 0 or 1.
+    for m in (1, 4, 8):
+        e3 = mnb.mnb_plan(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=4, workgroups=1, a_via_lds=1)
+        assert mnb.mnb_plan_check(m, 14336, 100, e3) == 0
+    e3.a_via_lds = 2
+    assert mnb.mnb_plan_check(4, 14336, 100, e3) == 9
+    d.a_via_lds = 1
+    assert mnb.mnb_plan_check(8, 4096, 100, d) == 9
+    q = mnb.mnb_plan(engine=2, row_tiles=1, cols_per_tile=128, waves_per_wg=4, workgroups=1, a_via_lds=1)
+    assert mnb.mnb_plan_check(40, 4096, 100, q) == 9
 
 
 def test_summation_order_does_not_depend_on_n_or_device():
@@ -266,6 +276,11 @@ def test_default_plan_shapes():
         p = mnb.mnb_plan_default(m, K, N, 256, occ)
         assert p.engine == 3
         assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape
+    # Activations through LDS from three rows up where K or N exceeds 8192.
+    for m, K, N, via in ((2, 14336, 4096, 0), (3, 14336, 4096, 1), (8, 14336, 4096, 1), (4, 4096, 28672, 1),
+                         (8, 4096, 151936, 1), (6, 8192, 8192, 0), (8, 4096, 6144, 0), (5, 4096, 4096, 0),
+                         (2, 4096, 151936, 0), (1, 4096, 151936, 0)):
+        assert mnb.mnb_plan_default(m, K, N, 256, 2).a_via_lds == via, (m, K, N)
 
 
 def test_plan_check_rows_limit():

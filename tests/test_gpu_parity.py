@@ -321,12 +321,14 @@ def test_kernel_info():
 
 
 # ------------------------------------------------- 4x4x4 MFMA kernel (engine 3)
-def test_mfma4_engine_every_variant_ragged(oracle_mod):
+@pytest.mark.parametrize("via_lds", [0, 1])
+def test_mfma4_engine_every_variant_ragged(oracle_mod, via_lds):
     """The 4x4x4 MFMA kernel for every m, every (blocks per lane, column
-    quads per tile) variant, ragged N (not a multiple of 4) and K (a ragged
-    last pass of the lane groups), one to eight waves, more or fewer
-    workgroups than column tiles."""
-    rng = np.random.default_rng(3)
+    quads per tile) variant, with the activations loaded by each lane and
+    through LDS, ragged N (not a multiple of 4) and K (a ragged last pass of
+    the lane groups), one to eight waves, more or fewer workgroups than
+    column tiles."""
+    rng = np.random.default_rng(3 + via_lds)
     i = 0
     for m in range(1, 9):
         for bpl in (1, 2, 4):
@@ -338,7 +340,7 @@ def test_mfma4_engine_every_variant_ragged(oracle_mod):
                 K, N = 32 * nb, int(rng.integers(1, 70))
                 d = W.generate(m, K, N, W.BF16 if i % 2 else W.F16, i % 3 != 1, 0.002, 0.02, 1.0, 400 + i)
                 plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols,
-                            workgroups=int(rng.integers(1, 25)))
+                            workgroups=int(rng.integers(1, 25)), a_via_lds=via_lds)
                 assert_parity(oracle_mod, d, m, "mfma4", plan)
                 i += 1
 
@@ -357,16 +359,19 @@ def test_mfma4_engine_shapes(oracle_mod):
     ]
     for i, (m, K, N, w, bpl, cols, wg) in enumerate(cases):
         d = W.generate(m, K, N, W.BF16, i % 2 == 0, 0.001, 0.01, 0.5, 430 + i)
-        plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols, workgroups=wg)
-        assert_parity(oracle_mod, d, m, "mfma4", plan)
+        for via_lds in (0, 1):
+            plan = dict(engine=3, waves_per_wg=w, blocks_per_lane=bpl, cols_per_tile=cols, workgroups=wg,
+                        a_via_lds=via_lds)
+            assert_parity(oracle_mod, d, m, "mfma4", plan)
 
 
-def test_mfma4_engine_rows_and_columns_match():
+@pytest.mark.parametrize("via_lds", [0, 1])
+def test_mfma4_engine_rows_and_columns_match(via_lds):
     """Under one 4x4x4 MFMA plan, row r of an m-row launch is bit-identical
     to a one-row launch on row r, and a column shard gives the bits of the
     whole (the lane split fixes the summation order of every column)."""
     d = W.generate(8, 14336, 203, W.BF16, True, 0.001, 0.01, 0.5, 440)
-    plan = dict(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=4, workgroups=9)
+    plan = dict(engine=3, waves_per_wg=7, blocks_per_lane=4, cols_per_tile=4, workgroups=9, a_via_lds=via_lds)
     y8, _ = run(d, 8, W.BF16, plan)
     for r in (0, 3, 5, 7):
         y1, _ = run(dict(d, A=d["A"][r:r + 1]), 1, W.BF16, plan)
@@ -375,6 +380,31 @@ def test_mfma4_engine_rows_and_columns_match():
     shard = dict(d, B=d["B"][lo:hi], scales=d["scales"][lo:hi], zp=d["zp"][lo:hi], N=hi - lo)
     ys, _ = run(shard, 8, W.BF16, dict(plan, workgroups=4))
     assert np.array_equal(ys, y8[:, lo:hi])
+
+
+@pytest.mark.parametrize("layout", ["natural", "even_odd"])
+def test_mfma4_activations_via_lds_give_the_same_bits(layout):
+    """The two activation paths of the 4x4x4 MFMA kernel (each lane loading
+    its own rows and blocks, or a row at a time through LDS) move the same
+    values into the same registers: equal bits for every m, fp16 and bf16
+    activations, ragged K and N, both weight layouts."""
+    for m in range(1, 9):
+        K, N = 32 * (301 + 17 * m), 37 + 29 * m
+        a_dt = W.BF16 if m % 2 else W.F16
+        d = W.generate(m, K, N, a_dt, m % 3 != 0, 0.001, 0.01, 0.5, 470 + m)
+        A, B, S, Z = G.to_dev(d, m)
+        base = dict(engine=3, waves_per_wg=-(-K // 32 // 64), blocks_per_lane=4, cols_per_tile=4, workgroups=7)
+        if layout == "even_odd":
+            B = mnb.mnb_repack_weights(B, mnb.MNB_LAYOUT_NATURAL, torch.empty_like(B), mnb.MNB_LAYOUT_EVEN_ODD)
+            base["b_layout"] = mnb.MNB_LAYOUT_EVEN_ODD
+        outs = []
+        for via_lds in (0, 1):
+            out = G.new_out(m, N, W.BF16)
+            mnb.matmul_nbits_planned(A, B, S, Z, out, dict(base, a_via_lds=via_lds))
+            torch.cuda.synchronize()
+            outs.append(G.bits(out))
+        assert not np.any(outs[0] == 0xFFFF)
+        assert np.array_equal(outs[0], outs[1]), (m, layout)
 
 
 def test_mfma4_engine_any_scale_and_zero_point_alignment():
