@@ -175,21 +175,31 @@ __device__ __forceinline__ float row_ror_add(float v)
     return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// Sum over the 16 lane groups (of four lanes) of a wave of the value held by
-// lane (g, i): two rotations inside each 16-lane row, then the rows exchanged
-// with v_permlane32_swap and v_permlane16_swap.  Every lane ends with the
-// total of its column lane i, in an order that depends only on g.
-__device__ __forceinline__ float column_sum(float v)
+// Sums over the 16 lane groups (of four lanes) of a wave of four values
+// per lane, rows 0-3 of the column lane i = lane % 4 holds.  The rows are
+// paired so that each exchange serves two of them: v_permlane32_swap of
+// rows 0 and 1 (and of rows 2 and 3) plus one add leaves each row summed
+// over the two 32-lane halves, in the lower half for the first row and the
+// upper for the second; v_permlane16_swap of those two results plus one add
+// sums over the 16-lane rows of each half; two rotations inside each 16-lane
+// row sum its four lane groups.  Every lane of 16-lane row h ends with the
+// total of row quad_total_row(h) = 0, 2, 1, 3 (h = 0..3) for its column.
+// Eight VALU operations for four rows (one row at a time took six each);
+// each row's total is ((h0 + h2) + (h1 + h3)) over the 16-lane rows, then
+// the lane groups in rotation order, whatever the other rows hold.
+__device__ __forceinline__ float quad_totals(float r0, float r1, float r2, float r3)
 {
-    v = row_ror_add<0x124>(v);   // row_ror:4
-    v = row_ror_add<0x128>(v);   // row_ror:8
-    const uint32_t u = __float_as_uint(v);
-    const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);   // (rows 0-1, rows 2-3) per lane
-    v = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    const uint32_t w = __float_as_uint(v);
-    const auto r = __builtin_amdgcn_permlane16_swap(w, w, false, false);   // (even row, odd row) per lane
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    auto halves = [](float x, float y) {
+        const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+        return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    };
+    const float a = halves(r0, r1), b = halves(r2, r3);
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float t = __uint_as_float(q[0]) + __uint_as_float(q[1]);
+    t = row_ror_add<0x124>(t);   // row_ror:4
+    return row_ror_add<0x128>(t);   // row_ror:8
 }
+__device__ __forceinline__ int quad_total_row(int h) { return ((h & 1) << 1) | (h >> 1); }
 
 __device__ __forceinline__ half4_t as_half4(uint32_t lo, uint32_t hi)
 {

@@ -37,9 +37,9 @@
 // lane unpacks its weights to the exact fp16 integers q - z, and per row
 // quad eight chained MFMAs give the block's exact 4 x 4 product, which one
 // FMA per row scales into the lane's fp32 accumulators.  Partial sums meet through a
-// fixed tree inside the wave (two DPP row rotations, then the rows swapped by
-// v_permlane32_swap and v_permlane16_swap) and a wave-ordered sum in LDS, so
-// the summation order depends only on (K, W, BPL).
+// fixed tree inside the wave (rows paired through v_permlane32_swap and
+// v_permlane16_swap, then two DPP row rotations) and a wave-ordered sum in
+// LDS, so the summation order depends only on (K, W, BPL).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -321,20 +321,14 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         }
     };
     auto finish = [&](float4_t (&acc)[NC][RQ], int k) {
+        const int row = quad_total_row(lane >> 4);
 #pragma unroll
         for (int n = 0; n < NC; ++n)
 #pragma unroll
-            for (int rq = 0; rq < RQ; ++rq)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) acc[n][rq][r] = column_sum(acc[n][rq][r]);
-        if (g == 0) {
-#pragma unroll
-            for (int n = 0; n < NC; ++n)
-#pragma unroll
-                for (int rq = 0; rq < RQ; ++rq)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + r] = acc[n][rq][r];
-        }
+            for (int rq = 0; rq < RQ; ++rq) {
+                const float t = quad_totals(acc[n][rq][0], acc[n][rq][1], acc[n][rq][2], acc[n][rq][3]);
+                if ((lane & 12) == 0) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + row] = t;
+            }
     };
 
     // Two tiles per pass; an odd last tile is followed by one past the
