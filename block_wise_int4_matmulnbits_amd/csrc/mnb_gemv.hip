@@ -100,6 +100,25 @@ __device__ __forceinline__ float group_sum(float v)
     return v;
 }
 
+// Totals over all 64 lanes of two values in one register: v_permlane32_swap
+// plus one add sums each value over the two 32-lane halves (a into lanes
+// 0-31, b into 32-63), the row-local DPP steps of group_sum sum each 16-lane
+// row, and v_permlane16_swap plus one add joins rows 0 and 1 (a) and rows 2
+// and 3 (b).  Eight VALU operations for two values (group_sum<64> takes six
+// per value); both values get the same association whatever the other one
+// holds.
+__device__ __forceinline__ float pair_total64(float a, float b)
+{
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    x = dpp_add<0xB1>(x);    // quad_perm [1,0,3,2]
+    x = dpp_add<0x4E>(x);    // quad_perm [2,3,0,1]
+    x = dpp_add<0x141>(x);   // row_half_mirror
+    x = dpp_add<0x140>(x);   // row_mirror
+    const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 __device__ __forceinline__ int64_t uniform64(int64_t v)
 {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -413,15 +432,6 @@ void mnb_gemv_kernel(Params p)
     // kernel (no barrier per tile), else they happen after every tile.
     auto finish = [&](int k, int64_t c0, float (&acc)[NC][M]) {
         const int span = xwave ? 64 : lpc;
-#pragma unroll
-        for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int r = 0; r < M; ++r) {
-                if (UNI || span == 64) acc[c][r] = group_sum<64>(acc[c][r]);
-                else if (span == 32) acc[c][r] = group_sum<32>(acc[c][r]);
-                else acc[c][r] = group_sum<16>(acc[c][r]);
-            }
-
         // Value `idx` (row idx / NC, column idx % NC) out of the registers.
         auto pick = [&](int idx) {
             float v = 0.f;
@@ -430,21 +440,50 @@ void mnb_gemv_kernel(Params p)
                 if (idx == i) v = acc[i % NC][i / NC];
             return v;
         };
-
-        // The totals sit in the last 16-lane row of each group.
-        const int first = (xwave ? 64 : lpc) - 16;
         const int wl = xwave ? (tid & 63) : lane;
+        // emit(idx, v) for the values whose total this lane holds.
+        auto totals = [&](auto emit) {
+            if constexpr (NC % 2 == 0) {
+                if (UNI || span == 64) {
+                    // Columns 2i and 2i + 1 of a row share one register
+                    // (value 2i in lanes 0-31, 2i + 1 in lanes 32-63), so a
+                    // row pairs the same values whatever the launch's rows;
+                    // lane j and lane 32 + j emit the pairs j, j + 16, ...
+                    constexpr int NP = NV / 2;
+                    float t[NP];
+#pragma unroll
+                    for (int i = 0; i < NP; ++i)
+                        t[i] = pair_total64(acc[(2 * i) % NC][(2 * i) / NC], acc[(2 * i + 1) % NC][(2 * i + 1) / NC]);
+                    if ((wl & 31) < 16) {
+                        const int half = wl >> 5;
+#pragma unroll
+                        for (int i = 0; i < NP; ++i)
+                            if (i % 16 == (wl & 15)) emit(2 * i + half, t[i]);
+                    }
+                    return;
+                }
+            }
+            // One value at a time: the totals sit in the last 16-lane row of
+            // each group.
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int r = 0; r < M; ++r) {
+                    if (UNI || span == 64) acc[c][r] = group_sum<64>(acc[c][r]);
+                    else if (span == 32) acc[c][r] = group_sum<32>(acc[c][r]);
+                    else acc[c][r] = group_sum<16>(acc[c][r]);
+                }
+            const int first = span - 16;
+            if (wl >= first)
+                for (int idx = wl - first; idx < NV; idx += 16) emit(idx, pick(idx));
+        };
+
         if constexpr (!xwave) {
-            if (wl >= first)
-                for (int idx = wl - first; idx < NV; idx += 16) store(c0, idx, pick(idx));
+            totals([&](int idx, float v) { store(c0, idx, v); });
         } else if (p.tcap > 0) {
-            if (wl >= first && k < p.tcap)
-                for (int idx = wl - first; idx < NV; idx += 16)
-                    part[(k * nw + wv) * NV + idx] = pick(idx);
+            if (k < p.tcap) totals([&](int idx, float v) { part[(k * nw + wv) * NV + idx] = v; });
         } else {
-            if (wl >= first)
-                for (int idx = wl - first; idx < NV; idx += 16)
-                    part[(buf * nw + wv) * NV + idx] = pick(idx);
+            totals([&](int idx, float v) { part[(buf * nw + wv) * NV + idx] = v; });
             __syncthreads();
             if (tid < NV) {
                 float v = part[(buf * nw) * NV + tid];
