@@ -437,7 +437,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // 26.9, m = 3 25.4 -> 20.0; down m = 8 26.1 -> 18.5, m = 3 15.6 -> 12.9;
     // the 6144-column shape gains at m = 8 and loses up to 1 us at m <= 3).
     // Lane split, a function of K only: the fewest blocks per lane group that
-    // cover K with at most four waves (else eight).  Four columns per tile.
+    // cover K with at most four waves, else eight waves, of which the kernel
+    // gives the fewest that need them four blocks per lane group and the
+    // rest three (K = 14336: four of each, against seven waves of four,
+    // interleaved A/B, us: m = 2 11.0 -> 10.4, m = 4 11.7 -> 11.3, m = 6
+    // 14.8 -> 13.8, m = 8 15.2 -> 14.1; 10240 x 4096 m = 4 10.3 -> 9.5,
+    // 12288 x 8192 m = 8 19.8 -> 18.2).  Four columns per tile.
     // Grid: whole workgroups per CU, about 10 * K/4096 tiles (column quads)
     // each, within one resident generation and at least two tiles each (the
     // tile loop runs in pairs).  Every workgroup stages all of K's
@@ -458,7 +463,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     if (m >= 2 && nb >= 1 && nb <= 512) {
         int64_t bpl3 = 1;
         while (bpl3 < 4 && ceil_div(nb, 16 * bpl3) > 4) bpl3 *= 2;
-        const int64_t w3 = ceil_div(nb, 16 * bpl3);
+        int64_t w3 = ceil_div(nb, 16 * bpl3);
+        if (w3 > 4) w3 = 8;   // two waves per SIMD; the kernel gives some three blocks per lane group
         const int64_t tiles3 = ceil_div(N, 4);
         const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
         const double per_wg = 10.0 * (double)K / 4096.0;

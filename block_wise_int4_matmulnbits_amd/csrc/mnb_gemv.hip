@@ -848,7 +848,7 @@ int occupancy(const void* fn, int threads, size_t lds) { return cached_occupancy
 int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 {
     if (plan.engine == 2) return gemm_workgroups_per_cu(plan);
-    if (plan.engine == 3) return mfma4_workgroups_per_cu(m, N, plan);
+    if (plan.engine == 3) return mfma4_workgroups_per_cu(m, K, plan);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return 0;
     int32_t tcap = 0;
@@ -859,7 +859,7 @@ int workgroups_per_cu(int64_t m, int64_t K, int64_t N, const mnb_plan& plan)
 int kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
 {
     if (plan.engine == 2) return gemm_kernel_info(plan, info);
-    if (plan.engine == 3) return mfma4_kernel_info(m, plan, info);
+    if (plan.engine == 3) return mfma4_kernel_info(m, K, plan, info);
     KernelFn fn = lookup(m, K, plan);
     if (!fn) return -1;
     hipFuncAttributes attr;

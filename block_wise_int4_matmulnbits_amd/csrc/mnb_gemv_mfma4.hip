@@ -60,6 +60,8 @@ struct Mfma4Params {
     int32_t m, K, nb, zb;
     uint32_t zero;           // always 0 (see vgpr_constant)
     int32_t a_bf16, out_bf16;
+    int32_t waves_hi;        // four blocks per lane group: waves [0, waves_hi) take
+                             // four, the others three (see the kernel)
     int32_t eo_pairs;        // weights in the even/odd nibble layout: the unpack
                              // yields (k, k+1) pairs, activations keep their order
 };
@@ -75,8 +77,18 @@ constexpr size_t kXposeBytesPerWave = kXposePieces * 16;
 // else each lane loads its own row and block directly.  The tile loop is straight-line code, two tiles per pass: each wave
 // leaves its totals of the pass's two tiles in LDS, and one barrier, the
 // sums over waves and another barrier close the pass.
+template <int BPL, int NC>
+constexpr int stage_dwords()   // a wave's LDS stage of one tile's scale and zero-point dwords
+{
+    return 64 * ((4 * NC * (8 * BPL + 1) + 63) / 64 + (4 * NC * (2 * BPL + 1) + 63) / 64);
+}
+
+// The wave's work (see the kernel): blocks B0 + 16 j + g of K (j < BPL) for
+// every tile of the workgroup.  part: [2][8][NV] per-wave totals of a pass's
+// two tiles, shared by all waves; st: this wave's stage.
 template <int RQ, int BPL, int NC, bool XP>
-__global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
+__device__ __forceinline__ void mfma4_wave(const Mfma4Params& p, const uint32_t B0, float* const part,
+                                           uint32_t* const st)
 {
     constexpr int NV = 16 * NC * RQ;        // results of one tile (columns x rows)
     constexpr int NCOL = 4 * NC;            // columns of a tile
@@ -84,8 +96,6 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     constexpr int DZ = 2 * BPL + 1;         // dwords covering its 16 BPL zero-point nibbles
     constexpr int SD = (NCOL * DS + 63) / 64;   // scale dwords loaded per lane and tile
     constexpr int ZD = (NCOL * DZ + 63) / 64;   // zero-point dwords loaded per lane and tile
-    __shared__ float part[2][8][NV];        // per-wave totals of a pass's two tiles
-    __shared__ uint32_t stage[8][64 * (SD + ZD)];   // a wave's scales and zero points of one tile
     extern __shared__ u32x4 xpose_lds[];            // kXposePieces per wave
 
     const int tid = threadIdx.x;
@@ -95,11 +105,10 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     const int qi = lane & 3, g = lane >> 2;
     const uint32_t nb = (uint32_t)p.nb, zb = (uint32_t)p.zb;
     const uint32_t row_bytes = (uint32_t)p.K / 2;
-    // Wave wv owns the 16 BPL consecutive blocks from B0; lane group g takes
+    // The wave owns the 16 BPL consecutive blocks from B0; lane group g takes
     // blocks B0 + 16 j + g (j < BPL), so each load instruction of a wave reads
     // 256 contiguous bytes of each of four columns, and a wave's scales (and
     // zero points) of a column are one contiguous run.
-    const uint32_t B0 = (uint32_t)(16 * BPL * wv);
     const int zshift = (g & 1) * 4;         // block parity == group parity (B0 even)
     const uint32_t zdef = p.zp ? 0u : 8u;   // zero point 8 when none are given
     const ZeroPoint zbase = zero_point_pairs(zdef);
@@ -255,7 +264,6 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
     auto compute = [&](const Tile& t, float4_t (&acc)[NC][RQ]) {
         // The tile's scale and zero-point dwords into the wave's stage, then
         // each lane's own (the wave's DS operations run in order).
-        uint32_t* st = stage[wv];
 #pragma unroll
         for (int k = 0; k < SD; ++k) st[64 * k + lane] = t.sd[k];
 #pragma unroll
@@ -327,7 +335,7 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
 #pragma unroll
             for (int rq = 0; rq < RQ; ++rq) {
                 const float t = quad_totals(acc[n][rq][0], acc[n][rq][1], acc[n][rq][2], acc[n][rq][3]);
-                if ((lane & 12) == 0) part[k][wv][((4 * n + qi) * RQ + rq) * 4 + row] = t;
+                if ((lane & 12) == 0) part[(k * 8 + wv) * NV + ((4 * n + qi) * RQ + rq) * 4 + row] = t;
             }
     };
 
@@ -353,35 +361,70 @@ __global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
         __syncthreads();
         for (int e = tid; e < 2 * NV; e += (int)blockDim.x) {   // 2 NV can exceed one wave
             const int t = e / NV, idx = e - t * NV;
-            float v = part[t][0][idx];
-            for (int w = 1; w < W; ++w) v += part[t][w][idx];
+            float v = part[t * 8 * NV + idx];
+            for (int w = 1; w < W; ++w) v += part[(t * 8 + w) * NV + idx];
             store(qs + (int64_t)t * NC, idx, v);
         }
         __syncthreads();   // the slots are refilled by the next pass
     }
 }
 
+// W waves cover K in one pass.  With four blocks per lane group the fewest
+// waves that need four take four (waves_hi of them) and the rest three, so
+// that a K whose blocks do not fill W waves of four still spreads evenly
+// over the SIMDs (K = 14336 on eight waves: four of 64 blocks and four of 48,
+// two waves of 3.5 blocks' work per SIMD, where seven waves of 64 put two on
+// three SIMDs and one on the fourth).  With every wave at four (waves_hi = W)
+// this is the plain split, compiled without the second body (MIX false).
+template <int RQ, int BPL, int NC, bool XP, bool MIX>
+__global__ __launch_bounds__(512) void mnb_gemv_mfma4_kernel(Mfma4Params p)
+{
+    constexpr int NV = 16 * NC * RQ;
+    constexpr int ST = stage_dwords<BPL, NC>();
+    __shared__ float part[2 * 8 * NV];      // per-wave totals of a pass's two tiles
+    __shared__ uint32_t stage[8 * ST];      // each wave's scales and zero points of one tile
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (MIX) {
+        if (wv >= p.waves_hi) {
+            mfma4_wave<RQ, 3, NC, XP>(p, (uint32_t)(64 * p.waves_hi + 48 * (wv - p.waves_hi)), part, stage + wv * ST);
+            return;
+        }
+    }
+    mfma4_wave<RQ, BPL, NC, XP>(p, (uint32_t)(16 * BPL * wv), part, stage + wv * ST);
+}
+
 typedef void (*Mfma4Fn)(Mfma4Params);
 
-template <int RQ, int BPL, bool XP>
+template <int RQ, int BPL, bool XP, bool MIX>
 Mfma4Fn by_nc(int nc)
 {
     switch (nc) {
-    case 1: return mnb_gemv_mfma4_kernel<RQ, BPL, 1, XP>;
-    case 2: return mnb_gemv_mfma4_kernel<RQ, BPL, 2, XP>;
+    case 1: return mnb_gemv_mfma4_kernel<RQ, BPL, 1, XP, MIX>;
+    case 2: return mnb_gemv_mfma4_kernel<RQ, BPL, 2, XP, MIX>;
     }
     return nullptr;
 }
 
 template <int RQ, bool XP>
-Mfma4Fn by_bpl(int bpl, int nc)
+Mfma4Fn by_bpl(int bpl, int nc, bool mix)
 {
     switch (bpl) {
-    case 1: return by_nc<RQ, 1, XP>(nc);
-    case 2: return by_nc<RQ, 2, XP>(nc);
-    case 4: return by_nc<RQ, 4, XP>(nc);
+    case 1: return by_nc<RQ, 1, XP, false>(nc);
+    case 2: return by_nc<RQ, 2, XP, false>(nc);
+    case 4: return mix ? by_nc<RQ, 4, XP, true>(nc) : by_nc<RQ, 4, XP, false>(nc);
     }
     return nullptr;
+}
+
+// Waves with four blocks per lane group (plan.blocks_per_lane = 4): the
+// fewest that, with three for the rest, cover K's nb blocks; all of them
+// otherwise.
+int mfma4_waves_hi(int64_t K, const mnb_plan& plan)
+{
+    const int64_t w = plan.threads_per_wg / 64;
+    if (plan.blocks_per_lane != 4) return (int)w;
+    int64_t hi = (K / 32 - 48 * w + 15) / 16;
+    return (int)(hi < 0 ? 0 : (hi > w ? w : hi));
 }
 
 
@@ -390,12 +433,14 @@ size_t mfma4_dynamic_lds(const mnb_plan& plan)
     return plan.a_via_lds ? (size_t)(plan.threads_per_wg / 64) * kXposeBytesPerWave : 0;
 }
 
-Mfma4Fn lookup_mfma4(int64_t m, const mnb_plan& plan)
+Mfma4Fn lookup_mfma4(int64_t m, int64_t K, const mnb_plan& plan)
 {
     const int nc = plan.cols_per_tile / 4;
     const bool xp = plan.a_via_lds != 0;
-    if (m >= 1 && m <= 4) return xp ? by_bpl<1, true>(plan.blocks_per_lane, nc) : by_bpl<1, false>(plan.blocks_per_lane, nc);
-    if (m >= 5 && m <= 8) return xp ? by_bpl<2, true>(plan.blocks_per_lane, nc) : by_bpl<2, false>(plan.blocks_per_lane, nc);
+    const bool mix = mfma4_waves_hi(K, plan) < plan.threads_per_wg / 64;
+    const int bpl = plan.blocks_per_lane;
+    if (m >= 1 && m <= 4) return xp ? by_bpl<1, true>(bpl, nc, mix) : by_bpl<1, false>(bpl, nc, mix);
+    if (m >= 5 && m <= 8) return xp ? by_bpl<2, true>(bpl, nc, mix) : by_bpl<2, false>(bpl, nc, mix);
     return nullptr;
 }
 
@@ -403,7 +448,7 @@ Mfma4Fn lookup_mfma4(int64_t m, const mnb_plan& plan)
 
 int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
 {
-    Mfma4Fn fn = lookup_mfma4(a.m, plan);
+    Mfma4Fn fn = lookup_mfma4(a.m, a.K, plan);
     if (!fn) return (int)hipErrorInvalidDeviceFunction;
     Mfma4Params p;
     p.A = static_cast<const uint16_t*>(a.A);
@@ -420,6 +465,7 @@ int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
     p.a_bf16 = a.a_bf16;
     p.out_bf16 = a.out_bf16;
     p.eo_pairs = plan.b_layout == MNB_LAYOUT_EVEN_ODD;
+    p.waves_hi = mfma4_waves_hi(a.K, plan);
     void* args[] = {&p};
     hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(fn), dim3((unsigned)plan.workgroups),
                                    dim3((unsigned)plan.threads_per_wg), args, mfma4_dynamic_lds(plan),
@@ -428,17 +474,16 @@ int launch_mfma4(const GemvArgs& a, const mnb_plan& plan, void* stream)
     return (int)e;
 }
 
-int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan)
+int mfma4_workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan)
 {
-    Mfma4Fn fn = lookup_mfma4(m, plan);
+    Mfma4Fn fn = lookup_mfma4(m, K, plan);
     if (!fn) return 0;
-    (void)N;
     return occupancy(reinterpret_cast<const void*>(fn), plan.threads_per_wg, mfma4_dynamic_lds(plan));
 }
 
-int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
+int mfma4_kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info)
 {
-    Mfma4Fn fn = lookup_mfma4(m, plan);
+    Mfma4Fn fn = lookup_mfma4(m, K, plan);
     if (!fn) return -1;
     hipFuncAttributes attr;
     hipError_t e = hipFuncGetAttributes(&attr, reinterpret_cast<const void*>(fn));
@@ -447,7 +492,7 @@ int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info)
     info->sgprs = 0;
     info->lds_bytes = (int32_t)(attr.sharedSizeBytes + mfma4_dynamic_lds(plan));
     info->max_threads = attr.maxThreadsPerBlock;
-    info->wgs_per_cu = mfma4_workgroups_per_cu(m, 1, plan);
+    info->wgs_per_cu = mfma4_workgroups_per_cu(m, K, plan);
     return 0;
 }
 

@@ -29,8 +29,8 @@ int launch_gemv(const GemvArgs& args, const mnb_plan& plan, void* stream);
 // >= K/32), cols_per_tile = 4 or 8.  With plan.a_via_lds, dynamic LDS of 4160
 // bytes per wave, through which the activations reach their lanes.
 int launch_mfma4(const GemvArgs& args, const mnb_plan& plan, void* stream);
-int mfma4_workgroups_per_cu(int64_t m, int64_t N, const mnb_plan& plan);
-int mfma4_kernel_info(int64_t m, const mnb_plan& plan, mnb_kernel_info* info);
+int mfma4_workgroups_per_cu(int64_t m, int64_t K, const mnb_plan& plan);
+int mfma4_kernel_info(int64_t m, int64_t K, const mnb_plan& plan, mnb_kernel_info* info);
 
 // The prefill kernel (engine 2), mnb_gemm_mfma.hip: a workgroup of 4 or 8
 // waves owns 32 * row_tiles rows by cols_per_tile columns (4 waves: 128 or

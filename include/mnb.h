@@ -194,7 +194,9 @@ int matmul_nbits_noalloc(const void* A, int a_dtype, int64_t m, int64_t K, int64
  * walks its columns cols_per_tile (4 or 8) at a time; lane i of each group
  * of four lanes holds column i of a quad and rows i and 4 + i of the
  * activations (in VGPRs); the 16 * waves_per_wg lane groups own
- * blocks_per_lane blocks each and together cover K in one pass; per block
+ * blocks_per_lane blocks each and together cover K in one pass (with four
+ * blocks per lane group, the fewest waves that need four take four and the
+ * others three, so that the waves' work is even); per block
  * the exact products come from v_mfma_f32_4x4x4_16b_f16 and the block scale
  * is applied in fp32, as in engine 0.  Needs 16 * waves_per_wg *
  * blocks_per_lane >= K/32 (so K <= 16384).  With a_via_lds each load of

@@ -85,8 +85,11 @@ def test_default_plans_are_valid_and_cover_k():
                 # depends on K only.
                 assert 2 <= m <= 8 and 1 <= nb <= 512
                 w, bpl = p.waves_per_wg, p.blocks_per_lane
-                assert 1 <= w <= 8 and bpl in (1, 2, 4) and 16 * w * bpl >= nb > 16 * (w - 1) * bpl
-                assert bpl == 1 or 16 * 4 * (bpl // 2) < nb      # fewest blocks for <= 4 waves
+                assert bpl in (1, 2, 4) and 16 * w * bpl >= nb
+                if w <= 4:      # the fewest waves, and the fewest blocks for <= 4 waves
+                    assert nb > 16 * (w - 1) * bpl and (bpl == 1 or 16 * 4 * (bpl // 2) < nb)
+                else:           # more than four waves of four: eight (some of three blocks)
+                    assert w == 8 and bpl == 4 and nb > 256
                 assert p.cols_per_tile == 4
                 assert split3.setdefault(K, (w, bpl)) == (w, bpl)
                 assert q.k_chunks == 1 and q.threads_per_wg == 64 * w
@@ -264,12 +267,12 @@ def test_default_plan_shapes():
     assert p.workgroups == 15 * 256             # ~5 tiles per group, whole rounds of CUs
     p = mnb.mnb_plan_default(1, 4096, 28672, 256, 6)
     assert p.workgroups == 6 * 256 // 2         # about five tiles per group, >= half a generation
-    # Two or more rows: the 4x4x4 MFMA kernel, seven waves of four blocks per
-    # lane group for the 14336-long K, four waves of two for 4096; four
-    # columns per tile; whole workgroups per CU, about 10 * K/4096 tiles each
-    # within one resident generation (the grids measured fastest or within
-    # 7% of it).
-    for m, K, N, occ, shape in ((2, 14336, 4096, 1, (7, 4, 4, 256)), (8, 14336, 4096, 1, (7, 4, 4, 256)),
+    # Two or more rows: the 4x4x4 MFMA kernel, eight waves for the 14336-long
+    # K (four of four blocks per lane group and four of three), four waves of
+    # two for 4096; four columns per tile; whole workgroups per CU, about
+    # 10 * K/4096 tiles each within one resident generation (the grids
+    # measured fastest or within 7% of it).
+    for m, K, N, occ, shape in ((2, 14336, 4096, 1, (8, 4, 4, 256)), (8, 14336, 4096, 1, (8, 4, 4, 256)),
                                 (4, 4096, 28672, 4, (4, 2, 4, 768)), (8, 4096, 151936, 4, (4, 2, 4, 1024)),
                                 (8, 4096, 6144, 4, (4, 2, 4, 256)), (4, 8192, 8192, 3, (4, 4, 4, 256)),
                                 (4, 4096, 14336, 4, (4, 2, 4, 512))):
