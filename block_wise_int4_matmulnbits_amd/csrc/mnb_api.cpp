@@ -205,47 +205,47 @@ struct Tiling {
     double t0, a, g, d, h, u;
 };
 constexpr Tiling kTilings[] = {
-    {1, 16, 4, 1, 3.8340, 1.3859, 1.9290, 1.8916, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
-    {1, 16, 8, 1, 5.9311, 2.0056, 1.9337, 1.7159, 0.0000, 0.0000},
-    {1, 32, 4, 1, 4.9712, 1.4728, 2.3830, 1.9080, 3.2798, 0.0000},   // K split over the four waves
-    {1, 64, 2, 1, 1.0460, 2.2102, 1.7282, 5.4993, 10.5152, 0.0000},
-    {1, 128, 4, 1, 1.3374, 4.3992, 2.3826, 5.5956, 12.9251, 0.0000},
-    {2, 128, 4, 1, 3.7060, 5.9468, 1.7442, 6.0080, 6.0939, 0.0000},
-    {4, 128, 4, 1, 4.9318, 12.3730, 3.1977, 11.2751, 0.0000, 0.0000},
-    {1, 256, 8, 1, 0.0000, 9.3921, 3.4783, 8.9757, 33.9676, 0.0000},
-    {2, 256, 8, 1, 1.4985, 12.4081, 4.1295, 10.2612, 23.1617, 0.0000},
-    {4, 256, 8, 1, 3.9435, 18.2621, 7.3530, 14.5957, 7.7044, 0.0000},
-    {8, 256, 8, 1, 7.3793, 33.3495, 0.0000, 24.0483, 10.0588, 0.0000},   // 256 x 256, weights through LDS
-    {1, 128, 4, 2, 5.6301, 3.8688, 0.0000, 4.8511, 7.3033, 201.3994},   // K split over 2..16 workgroups, a second launch adds the slices
-    {1, 128, 4, 4, 6.6484, 3.9026, 0.0000, 4.4085, 10.4412, 161.6338},
-    {1, 128, 4, 8, 6.9289, 4.0388, 0.5154, 4.7957, 9.5581, 104.3326},
-    {1, 128, 4, 16, 8.2099, 1.9890, 1.0604, 2.4660, 23.3252, 111.7309},
-    {2, 128, 4, 2, 6.1735, 4.3650, 0.0000, 5.9472, 1.7217, 197.8562},
-    {2, 128, 4, 4, 7.2291, 5.1918, 0.0000, 5.7808, 3.6334, 127.1426},
-    {2, 128, 4, 8, 7.6480, 5.2229, 0.2642, 6.0680, 5.0173, 108.6896},
-    {2, 128, 4, 16, 8.5537, 3.1457, 2.1555, 5.4861, 0.0000, 116.9556},
-    {4, 128, 4, 2, 6.7748, 11.3025, 0.0000, 11.0931, 1.9220, 194.3587},
-    {4, 128, 4, 4, 7.9754, 11.9994, 0.0150, 10.5488, 11.0137, 148.8075},
-    {4, 128, 4, 8, 7.6336, 10.5853, 4.7926, 11.8893, 9.7610, 108.4946},
-    {4, 128, 4, 16, 9.4308, 7.9438, 7.8174, 10.8791, 0.0000, 104.3491},
-    {1, 256, 8, 2, 3.6615, 7.2457, 0.0000, 8.5204, 24.3173, 192.8554},
-    {1, 256, 8, 4, 5.6659, 8.0348, 0.0000, 8.4239, 14.3902, 127.5766},
-    {1, 256, 8, 8, 6.5065, 9.2005, 0.0000, 8.6915, 16.8964, 75.7921},
-    {1, 256, 8, 16, 8.4639, 8.6377, 1.1101, 6.6610, 17.6608, 53.5782},
-    {2, 256, 8, 2, 4.7200, 11.7755, 0.0000, 10.3403, 14.3167, 188.1865},
-    {2, 256, 8, 4, 6.3459, 11.7508, 0.0000, 10.3318, 6.8384, 138.2939},
-    {2, 256, 8, 8, 6.3744, 12.7835, 0.0000, 10.6592, 15.3238, 111.8707},
-    {2, 256, 8, 16, 8.2109, 9.5054, 4.7560, 8.5407, 20.3536, 80.7178},
+    {1, 16, 4, 1, 3.8610, 1.3850, 1.9342, 1.8901, 0.0000, 0.0000},   // 16 columns on a 32-column tile, K split over the waves
+    {1, 16, 8, 1, 5.8870, 2.0036, 1.9578, 1.7275, 0.0000, 0.0000},
+    {1, 32, 4, 1, 4.9887, 1.4723, 2.3993, 1.9066, 3.2569, 0.0000},   // K split over the four waves
+    {1, 64, 2, 1, 1.0704, 2.2076, 1.7534, 5.4974, 10.5770, 0.0000},
+    {1, 128, 4, 1, 1.3403, 4.3963, 2.3819, 5.5898, 13.0526, 0.0000},
+    {2, 128, 4, 1, 3.5663, 5.8118, 2.3400, 6.0021, 6.7267, 0.0000},
+    {4, 128, 4, 1, 4.8855, 12.3022, 3.1521, 11.2704, 0.0000, 0.0000},
+    {1, 256, 8, 1, 0.0000, 9.4388, 3.2051, 8.9528, 34.2933, 0.0000},
+    {2, 256, 8, 1, 1.2841, 12.2381, 4.1168, 10.2565, 24.1162, 0.0000},
+    {4, 256, 8, 1, 3.7579, 17.8627, 7.8076, 14.5888, 8.0399, 0.0000},
+    {8, 256, 8, 1, 7.1312, 33.1356, 0.0000, 24.0315, 10.5656, 0.0000},   // 256 x 256, weights through LDS
+    {1, 128, 4, 2, 5.6571, 3.8579, 0.0000, 4.8528, 7.4596, 198.7183},   // K split over 2..16 workgroups, a second launch adds the slices
+    {1, 128, 4, 4, 6.4293, 3.9396, 0.0000, 4.4597, 10.4470, 161.6987},
+    {1, 128, 4, 8, 5.9191, 3.4284, 1.3289, 5.3852, 9.2180, 115.3103},
+    {1, 128, 4, 16, 6.7797, 1.6008, 1.9160, 4.2164, 17.8949, 115.9995},
+    {2, 128, 4, 2, 6.1070, 4.2767, 0.0000, 5.9467, 2.2971, 197.8420},
+    {2, 128, 4, 4, 7.1911, 5.1908, 0.0000, 5.7611, 3.9607, 124.0901},
+    {2, 128, 4, 8, 7.1840, 4.8146, 0.7588, 6.3397, 3.3817, 110.2482},
+    {2, 128, 4, 16, 7.5359, 2.1214, 2.8233, 6.5482, 0.0000, 122.8116},
+    {4, 128, 4, 2, 6.8219, 11.1767, 0.0000, 11.0433, 3.0875, 190.7041},
+    {4, 128, 4, 4, 8.1219, 11.8653, 0.1360, 10.4706, 12.1705, 145.6724},
+    {4, 128, 4, 8, 7.4293, 10.2051, 5.1548, 12.0446, 8.9930, 111.4425},
+    {4, 128, 4, 16, 9.2655, 7.5497, 8.0509, 11.1810, 0.0000, 104.2306},
+    {1, 256, 8, 2, 3.7288, 7.2387, 0.0000, 8.5014, 23.7040, 193.0096},
+    {1, 256, 8, 4, 5.5982, 7.9531, 0.0000, 8.4352, 15.2034, 128.6234},
+    {1, 256, 8, 8, 6.1386, 9.1381, 0.0000, 8.8607, 17.0575, 79.5319},
+    {1, 256, 8, 16, 7.3761, 7.1060, 2.1161, 7.8029, 18.2416, 59.4031},
+    {2, 256, 8, 2, 4.8553, 11.6227, 0.0000, 10.3156, 13.5775, 182.9153},
+    {2, 256, 8, 4, 6.4314, 11.4627, 0.0000, 10.2646, 8.3824, 133.9338},
+    {2, 256, 8, 8, 6.2573, 12.3964, 0.3921, 10.7960, 14.1889, 108.8004},
+    {2, 256, 8, 16, 7.6852, 8.0358, 5.4080, 9.0132, 20.0183, 85.1982},
 };
-// The decode plan per launch of r <= 8 rows:
-//   exp(c0) * (K / 4096)^c1 * (N / 4096)^c2 * (r / 8)^c3,
-// but no less than its weight bytes at 6.5 TB/s (the fit's exponents come
-// from shapes where fixed costs dominate; far beyond them the weights set
-// the time) and no less than 3 us, about what one launch takes however
-// small.
-constexpr double kDecode[4] = {2.0226, 0.6523, 0.6318, 0.1647};
+// The decode plan per launch of r <= 8 rows: a part that grows with K (the
+// activation staging and the per-wave work of each workgroup) and a part
+// linear in the weight MB (with scales and zero points) at a rate per row,
+//   exp(c0) * (K / 4096)^c1 + MB * (c2 + c3 * r / 8),
+// and no less than 3 us, about what one launch takes however small.  (A
+// power law in N, as first fitted, ran 15-20% below the launches on 151936
+// columns, where the time is linear in the weights.)
+constexpr double kDecode[4] = {1.6501, 0.1652, 0.1290, 0.0767};
 constexpr double kBytesPerWeight = 0.578;   // 4 bits, and a 2-byte scale and a 4-bit zero point per 32
-constexpr double kDecodeBytesPerUs = 6.5e6;   // 6.5 TB/s
 constexpr double kDecodeLaunchUs = 3.0;
 
 int64_t prefill_tiles(const Tiling& t, int64_t m, int64_t N)
@@ -265,12 +265,11 @@ double tiling_cost(const Tiling& t, int64_t m, int64_t K, int64_t N, int num_cus
 
 double decode_cost(int64_t m, int64_t K, int64_t N)
 {
-    const double bytes_us = (double)N * (double)K * kBytesPerWeight / kDecodeBytesPerUs;
-    const double floor_us = bytes_us > kDecodeLaunchUs ? bytes_us : kDecodeLaunchUs;
+    const double mb = (double)N * (double)K * kBytesPerWeight / 1e6;
     auto one = [&](int64_t r) {
-        const double t = std::exp(kDecode[0]) * std::pow((double)K / 4096, kDecode[1]) *
-                         std::pow((double)N / 4096, kDecode[2]) * std::pow((double)r / 8, kDecode[3]);
-        return t > floor_us ? t : floor_us;
+        const double t = std::exp(kDecode[0]) * std::pow((double)K / 4096, kDecode[1]) +
+                         mb * (kDecode[2] + kDecode[3] * (double)r / 8);
+        return t > kDecodeLaunchUs ? t : kDecodeLaunchUs;
     };
     const int64_t full = m / MNB_MAX_M, rem = m % MNB_MAX_M;
     return (double)full * one(MNB_MAX_M) + (rem ? one(rem) : 0.0);
@@ -419,10 +418,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // out, 64 shapes from 9 x 2048 x 8192 to 4096 x 4096 x 28672 and
         // 640 x 4096 x 151936; plan_tune.py measures and fits it).  On
         // those shapes the cheapest modelled plan runs 0.37% slower than
-        // the fastest measured one on average (6.5% at most, where a split
-        // the model ranks second would have won), and 12.2% faster on
+        // the fastest measured one on average (6.9% at most, where a split
+        // the model ranks second would have won), and 11.9% faster on
         // average than the fastest plan without a K split (never more than
-        // 2.0% slower: a choice between unsplit tilings).
+        // 2.7% slower: a choice between unsplit tilings).
         const PrefillChoice c = cheapest_prefill(m, K, N, num_cus);
         if (c.decode) return mnb_plan_default(MNB_MAX_M, K, N, num_cus, wgs_per_cu, plan);
         return prefill_plan(c.t, m, K, N, num_cus, wgs_per_cu, plan);
@@ -447,12 +446,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // each, within one resident generation and at least two tiles each (the
     // tile loop runs in pairs).  Every workgroup stages all of K's
     // activations, so fewer, longer-lived workgroups win until the CUs run
-    // short of waves.  Fitted to a sweep of 40 shapes (m = 2..8, K = 2048..
-    // 14336, N = 4096..151936, bf16): 7.9% faster on average than one
-    // resident generation (4096 x 6144 m = 8 11.5 -> 9.2 us, 8192 x 8192
-    // m = 4 16.7 -> 12.7, gate_up m = 8 25.9 -> 24.4), 1.1% above the
-    // fastest grid on average, 7.3% at most; at m = 2 on 4096 and 6144
-    // columns it is 4.6-6.6% slower than two tiles per workgroup.
+    // short of waves (at one or two rows, two workgroups per CU at least,
+    // below).  On a sweep of 40 shapes (m = 2..8, K = 2048..14336, N =
+    // 4096..151936, bf16): 8.1% faster on average than one resident
+    // generation, 0.35% above the fastest grid on average, 5.0% at most.
     // Activations through LDS from three rows up where K or N exceeds 8192
     // (interleaved A/B, same bits, us: down projection m = 3 12.5 -> 11.5,
     // m = 4 13.6 -> 11.9, m = 7 17.5 -> 15.4, m = 8 18.3 -> 15.7; gate_up
@@ -469,6 +466,10 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
         const double per_wg = 10.0 * (double)K / 4096.0;
         int64_t c3 = (int64_t)std::ceil((double)tiles3 / (double)num_cus / per_wg);
+        // One or two rows stage their activations with the lanes' own loads,
+        // half of which read nothing: two workgroups per CU at least (4096 x
+        // 4096 m = 2 5.72 -> 5.22 us, 8192 x 8192 12.0 -> 11.1).
+        if (m <= 2 && c3 < 2) c3 = 2;
         if (c3 < 1) c3 = 1;
         if (c3 > per_cu3) c3 = per_cu3;
         int64_t wgs3 = c3 * num_cus;

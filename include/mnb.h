@@ -104,11 +104,10 @@ typedef enum {
  *                except that two or more rows whose K the decode lane split
  *                would walk in several passes -- K > 65536 at two rows,
  *                > 32768 at three or four, > 16384 at five to eight -- run
- *                the prefill kernel; m > 8: prefill kernel, except that up
- *                to 16 rows whose 32-column prefill tiles would leave more
- *                than half of the compute units idle run the decode kernels
- *                in launches of 8 rows).  m == 0 or N == 0: nothing to do,
- *                MNB_OK.
+ *                the prefill kernel; m > 8: prefill kernel, or, for up to
+ *                16 rows where the planner's cost model prices them lower,
+ *                the decode kernels in launches of 8 rows).  m == 0 or
+ *                N == 0: nothing to do, MNB_OK.
  *   K            reduction length, a multiple of 32 (K == 0 gives y = +0).
  *   N            output columns.
  *   Bpacked      device, [N][K/2] bytes; byte k/2 of row n holds weight k,
