@@ -278,9 +278,13 @@ int mnb_repack_weights(const uint8_t* src, int src_layout, uint8_t* dst, int dst
                        int64_t N, int64_t K, void* stream);
 
 /*
- * Counters, updated atomically by every successful launch.  Tests assert
- * them so that a silent change of route fails instead of passing (first
- * page, "Tests" paragraph: the direct-store counter).
+ * Counters, updated atomically on the host for every launch that was queued
+ * successfully, from the launch's arguments (rows, columns, output type):
+ * they record the route each call took, not what a kernel did, so tests
+ * pair them with the output bits (the bf16 outputs must equal the fp16
+ * outputs narrowed, which a kernel ignoring the flag would fail).  Tests
+ * assert them so that a silent change of route fails instead of passing
+ * (first page, "Tests" paragraph: the direct-store counter).
  */
 typedef struct {
     uint64_t calls;                /* matmul_nbits* calls that returned MNB_OK */
