@@ -6,6 +6,8 @@
 #include <cmath>
 #include <atomic>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 #include "mnb.h"
 #include "mnb_internal.h"
@@ -74,6 +76,33 @@ int validate(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
     return MNB_OK;
 }
 
+// MNB_LOG set to anything but "0" in the environment (read once): each call
+// that reaches its launches prints its shape and plan to stderr, one line.
+bool log_enabled()
+{
+    static const bool on = [] {
+        const char* v = getenv("MNB_LOG");
+        return v && *v && !(v[0] == '0' && v[1] == 0);
+    }();
+    return on;
+}
+
+void log_plan(int64_t m, int64_t K, int64_t N, int a_dtype, int out_dtype, const mnb_plan& p, bool explicit_plan,
+              bool fixed_scratch)
+{
+    const int64_t step = p.engine == 2 ? m : MNB_MAX_M;
+    const int64_t launches = (m + step - 1) / step * (p.k_splits > 1 ? 2 : 1);
+    fprintf(stderr,
+            "mnb: m=%lld K=%lld N=%lld a=%s out=%s %s plan: engine=%d lanes_per_col=%d blocks_per_lane=%d "
+            "cols_per_tile=%d waves_per_wg=%d row_tiles=%d k_splits=%d a_via_lds=%d b_layout=%d interleave=%d "
+            "workgroups=%d threads_per_wg=%d k_chunks=%d launches=%lld%s\n",
+            (long long)m, (long long)K, (long long)N, a_dtype == MNB_BF16 ? "bf16" : "f16",
+            out_dtype == MNB_BF16 ? "bf16" : "f16", explicit_plan ? "explicit" : "default", p.engine,
+            p.lanes_per_col, p.blocks_per_lane, p.cols_per_tile, p.waves_per_wg, p.row_tiles, p.k_splits,
+            p.a_via_lds, p.b_layout, p.interleave, p.workgroups, p.threads_per_wg, p.k_chunks,
+            (long long)launches, fixed_scratch ? " fixed-scratch" : "");
+}
+
 int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
         const uint8_t* Bpacked, const uint16_t* scales, const uint8_t* zero_points,
         int block, void* out, int out_dtype, void* stream, const mnb_plan* explicit_plan,
@@ -107,6 +136,7 @@ int run(const void* A, int a_dtype, int64_t m, int64_t K, int64_t N,
             if (st != MNB_OK) return st;
         }
     }
+    if (log_enabled()) log_plan(m, K, N, a_dtype, out_dtype, plan, explicit_plan != nullptr, fixed_scratch);
     // One launch (two with K split over workgroups: the tiles, then the sum
     // of their slices), or for a decode plan with more than MNB_MAX_M rows
     // one launch per MNB_MAX_M rows (rows are independent in those kernels).

@@ -278,6 +278,13 @@ int mnb_repack_weights(const uint8_t* src, int src_layout, uint8_t* dst, int dst
                        int64_t N, int64_t K, void* stream);
 
 /*
+ * Environment: MNB_LOG set to anything but "0" (read once per process)
+ * prints one line per call to stderr, once its plan is fixed and before
+ * its launches: the shape, the types, whether the plan was explicit or the
+ * default, every plan field, and the number of launches.
+ */
+
+/*
  * Counters, updated atomically on the host for every launch that was queued
  * successfully, from the launch's arguments (rows, columns, output type):
  * they record the route each call took, not what a kernel did, so tests
