@@ -184,6 +184,14 @@ __device__ __forceinline__ void mfma4_wave(const Mfma4Params& p, const uint32_t 
         const uint32_t item = 64 * (uint32_t)k + (uint32_t)lane, c = item / DZ, kk = item % DZ;
         ozd[k] = c < NCOL ? ((mz + c * zb + B0 / 2) & ~3u) + 4 * kk : kOutOfRange;
     }
+    // Blocks of this lane group past K: their weights and activations load
+    // zeros, but the bytes the scale dwords bring for them lie past the
+    // column's scales (the next column's, or past the array for the last
+    // column, where they may hold anything), so their scale is taken as 0:
+    // a product of 0 and a NaN or infinity read there would poison the sum.
+    bool in_k[BPL];
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) in_k[j] = B0 + 16 * (uint32_t)j + (uint32_t)g < nb;
     // Where this lane finds its own scale and zero point of column 4n + qi,
     // block B0 + 16 j + g, in the wave's stage (bytes; + 32 j and + 8 j).
     uint32_t sread[NC], zread[NC];
@@ -281,7 +289,8 @@ __device__ __forceinline__ void mfma4_wave(const Mfma4Params& p, const uint32_t 
             for (int j = 0; j < BPL; ++j) {
                 const uint32_t zq = sb[zread[n] + 8 * j];
                 zp[j] = zero_point_pairs(__builtin_amdgcn_ubfe(zq, zshift, 4), zbase);   // + zdef
-                sf[j] = (float)*reinterpret_cast<const _Float16*>(sb + sread[n] + 32 * j);
+                const uint16_t sbits = *reinterpret_cast<const uint16_t*>(sb + sread[n] + 32 * j);
+                sf[j] = (float)__builtin_bit_cast(_Float16, in_k[j] ? sbits : (uint16_t)0);
             }
             float4_t dsum[BPL][RQ];
 #pragma unroll

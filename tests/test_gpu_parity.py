@@ -407,6 +407,47 @@ def test_mfma4_activations_via_lds_give_the_same_bits(layout):
         assert np.array_equal(outs[0], outs[1]), (m, layout)
 
 
+@pytest.mark.parametrize("via_lds", [0, 1])
+def test_blocks_past_k_ignore_what_lies_past_the_scales(oracle_mod, via_lds):
+    """Lane groups whose blocks lie past K read no weights and no activations,
+    but the 4x4x4 MFMA kernel reads scales as whole dwords of each column's
+    run, so their scale bytes come from past the column (the next column's
+    scales, or past the array for the last column).  Those blocks must add
+    exactly zero whatever the bytes hold: the scales sit at the start of a
+    buffer whose tail holds NaN and infinities, and every output, the last
+    column's included, must pass check 1 with no NaN (engine 3 with one to
+    eight waves, mixed four- and three-block waves, both activation paths;
+    the other engines' defaults as well)."""
+    cases = [  # m, K, N, plan (None: the default)
+        (5, 32 * 67, 1189, dict(engine=3, waves_per_wg=3, blocks_per_lane=2, cols_per_tile=4, workgroups=149)),
+        (2, 32 * 61, 37, dict(engine=3, waves_per_wg=2, blocks_per_lane=2, cols_per_tile=4, workgroups=3)),
+        (8, 32 * 443, 13, dict(engine=3, waves_per_wg=8, blocks_per_lane=4, cols_per_tile=4, workgroups=2)),
+        (3, 32 * 9, 5, dict(engine=3, waves_per_wg=1, blocks_per_lane=1, cols_per_tile=4, workgroups=1)),
+        (1, 32 * 67, 301, None), (3, 32 * 1101, 77, None), (24, 32 * 67, 301, None), (40, 32 * 39, 130, None),
+    ]
+    for i, (m, K, N, plan) in enumerate(cases):
+        if plan is not None:
+            plan = dict(plan, a_via_lds=via_lds)
+        elif via_lds:
+            continue
+        d = W.generate(m, K, N, W.BF16, True, 0.001, 0.01, 0.5, 490 + i)
+        A, B, S, Z = G.to_dev(d, m)
+        tail = torch.full((S.numel() + 64,), float("nan"), dtype=torch.float16, device="cuda")
+        tail[S.numel() + 1::2] = float("inf")
+        S2 = tail[:S.numel()].view(S.shape)
+        S2.copy_(S)
+        out = G.new_out(m, N, W.F16)
+        if plan is None:
+            mnb.matmul_nbits(A, B, S2, Z, out)
+        else:
+            mnb.matmul_nbits_planned(A, B, S2, Z, out, plan)
+        torch.cuda.synchronize()
+        y = G.bits(out)
+        assert not np.any(np.isnan(G.f16_values(y))), (m, K, N, plan)
+        ok, _ = G.check1(y, oracle_ref(oracle_mod, d, m), oracle_mod)
+        assert ok.all(), (m, K, N, plan, np.argwhere(~ok)[:8])
+
+
 def test_mfma4_engine_any_scale_and_zero_point_alignment():
     """Scales and zero points are read as whole dwords from 4-byte-aligned
     bases: arrays starting 2 bytes (scales) or 1 to 3 bytes (zero points)
