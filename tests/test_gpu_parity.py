@@ -448,6 +448,44 @@ def test_blocks_past_k_ignore_what_lies_past_the_scales(oracle_mod, via_lds):
         assert ok.all(), (m, K, N, plan, np.argwhere(~ok)[:8])
 
 
+def test_default_plans_ignore_bytes_past_every_input(oracle_mod):
+    """Random shapes through the default plans (all three engines, ragged K
+    and N, both activation types, with and without zero points), each input
+    array at the start of a larger buffer whose tail is poison: NaN and
+    infinities after the activations and the scales, 0xFF bytes after the
+    weights and the zero points.  Nothing past an array may reach an output:
+    check 1 on every output and no NaN."""
+    rng = np.random.default_rng(2027)
+    for i in range(24):
+        m = int(rng.choice([1, 2, 3, 5, 8, 11, 24]))
+        K = 32 * int(rng.integers(1, 600))
+        N = int(rng.integers(1, 1500))
+        a_dt = W.BF16 if i % 2 else W.F16
+        d = W.generate(m, K, N, a_dt, i % 3 != 0, 0.001, 0.02, 0.5, 3000 + i)
+        A, B, S, Z = G.to_dev(d, m)
+
+        def poisoned(x, fill):
+            buf = torch.empty(x.numel() + 256, dtype=x.dtype, device="cuda")
+            buf.fill_(fill)
+            if x.dtype in (torch.float16, torch.bfloat16):
+                buf[x.numel() + 1::2] = float("inf")
+            v = buf[:x.numel()].view(x.shape)
+            v.copy_(x)
+            return v
+        A2 = poisoned(A, float("nan"))
+        B2 = poisoned(B, 255)
+        S2 = poisoned(S, float("nan"))
+        Z2 = None if Z is None else poisoned(Z, 255)
+        out = G.new_out(m, N, W.F16)
+        mnb.matmul_nbits(A2, B2, S2, Z2, out)
+        torch.cuda.synchronize()
+        y = G.bits(out)
+        plan = effective_plan(m, K, N)
+        assert not np.any(np.isnan(G.f16_values(y))), (m, K, N, plan)
+        ok, _ = G.check1(y, oracle_ref(oracle_mod, d, m), oracle_mod)
+        assert ok.all(), (m, K, N, plan, np.argwhere(~ok)[:8])
+
+
 def test_mfma4_engine_any_scale_and_zero_point_alignment():
     """Scales and zero points are read as whole dwords from 4-byte-aligned
     bases: arrays starting 2 bytes (scales) or 1 to 3 bytes (zero points)
