@@ -448,12 +448,13 @@ def test_blocks_past_k_ignore_what_lies_past_the_scales(oracle_mod, via_lds):
         assert ok.all(), (m, K, N, plan, np.argwhere(~ok)[:8])
 
 
-def test_default_plans_ignore_bytes_past_every_input(oracle_mod):
+def test_default_plans_ignore_bytes_around_every_input(oracle_mod):
     """Random shapes through the default plans (all three engines, ragged K
     and N, both activation types, with and without zero points), each input
-    array at the start of a larger buffer whose tail is poison: NaN and
-    infinities after the activations and the scales, 0xFF bytes after the
-    weights and the zero points.  Nothing past an array may reach an output:
+    array inside a larger buffer of poison: NaN and infinities around the
+    activations and the scales, 0xFF bytes around the weights and the zero
+    points, the scales and zero points also starting past a 4-byte boundary
+    with poison before them.  Nothing outside an array may reach an output:
     check 1 on every output and no NaN."""
     rng = np.random.default_rng(2027)
     for i in range(24):
@@ -464,18 +465,20 @@ def test_default_plans_ignore_bytes_past_every_input(oracle_mod):
         d = W.generate(m, K, N, a_dt, i % 3 != 0, 0.001, 0.02, 0.5, 3000 + i)
         A, B, S, Z = G.to_dev(d, m)
 
-        def poisoned(x, fill):
-            buf = torch.empty(x.numel() + 256, dtype=x.dtype, device="cuda")
+        def poisoned(x, fill, head=0):
+            buf = torch.empty(x.numel() + head + 256, dtype=x.dtype, device="cuda")
             buf.fill_(fill)
             if x.dtype in (torch.float16, torch.bfloat16):
-                buf[x.numel() + 1::2] = float("inf")
-            v = buf[:x.numel()].view(x.shape)
+                buf[1::2] = float("inf")
+            v = buf[head:head + x.numel()].view(x.shape)
             v.copy_(x)
             return v
+        # Activations and weights keep their 16-byte alignment; scales and
+        # zero points may also start past a 4-byte boundary, poison before.
         A2 = poisoned(A, float("nan"))
         B2 = poisoned(B, 255)
-        S2 = poisoned(S, float("nan"))
-        Z2 = None if Z is None else poisoned(Z, 255)
+        S2 = poisoned(S, float("nan"), head=i % 2)
+        Z2 = None if Z is None else poisoned(Z, 255, head=i % 4)
         out = G.new_out(m, N, W.F16)
         mnb.matmul_nbits(A2, B2, S2, Z2, out)
         torch.cuda.synchronize()
