@@ -24,9 +24,11 @@
 // g = lane / 4) holds column 4n + i of each quad n and, as the A side, rows i
 // and 4 + i of the activations.  Wave w owns the 16 BPL consecutive K blocks
 // from 16 BPL w, and its group g the blocks 16 BPL w + 16 j + g (j < BPL);
-// together the waves cover all of K in one pass.  The lane's activations are
-// loaded once (from three rows up a row at a time, 1 KB per load, and handed
-// to their lanes through a wave-private LDS buffer), converted to fp16,
+// together the waves cover all of K in one pass (where K does not fill W
+// waves of BPL, the later waves take three blocks of four: see the kernel).
+// The lane's activations are loaded once (under the plan's a_via_lds a row
+// at a time, 1 KB per load, and handed to their lanes through a
+// wave-private LDS buffer), converted to fp16,
 // permuted into the unpack's pair order and kept in VGPRs.  Per block and column the lane loads its 16 bytes of
 // weights (the four lanes of a group read four columns, the sixteen groups
 // of a wave 256 contiguous bytes of each).  A wave's scales and zero points
