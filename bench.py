@@ -17,11 +17,15 @@ them changed since).
 Besides the headline figure the line carries (skipped with --no-extras):
   attainable   a read-only streaming kernel over the same bytes (the in-repo
                probe): what one launch of this size can pull from HBM;
+  launch_floor_us  the read probe over one 16-byte piece, launched back to
+               back (one workgroup, and one per CU): the cost of a launch
+               before it moves a byte;
   configs      every synthetic configuration in its own output type(s):
                microseconds per call (median and range of 5 timed passes),
-               algorithmic GB/s and fraction of 8 TB/s, the plan, VGPRs and
-               occupancy, and the rocprofv3 kernel time and FETCH_SIZE
-               fraction of the committed profile;
+               algorithmic GB/s and fraction of 8 TB/s, the read probe over
+               the same weight copies and the fraction of it reached, the
+               plan, VGPRs and occupancy, and the rocprofv3 kernel time and
+               FETCH_SIZE fraction of the committed profile;
   staged_route the fp16 GEMV followed by a separate fp16 -> bf16 cast launch,
                against the direct bf16 store (bits compared);
   decode_step  a decode step of GEMVs (4 layers of q/k/v/o, gate_up and down,
@@ -278,6 +282,7 @@ def main():
         if att:
             result["roofline"]["attainable"] = att
             result["roofline"]["frac_of_attainable"] = round(gbs / att["gbs"], 4)
+        result["launch_floor_us"] = launch_floor(stream, cus)
         result["configs"] = decode_configs(args, stream, cus)
         if w.name == "lm_head" and m == 1:
             result["staged_route"] = staged_route(res, stream, L)
@@ -324,11 +329,38 @@ def attainable(res, stream, cus):
             "kernel": "read probe, unroll %d, %d workgroups/CU" % (best[1], best[2])}
 
 
+def launch_floor(stream, cus):
+    """Microseconds per launch of the read probe over one 16-byte piece,
+    launched back to back on one stream: with one workgroup, and with one
+    per CU (each of its threads past the piece loads nothing).  What any
+    launch on this stream costs before it moves a byte."""
+    path = os.path.join(ROOT, "block_wise_int4_matmulnbits_amd", "libmnb_probe.so")
+    if not os.path.exists(path):
+        return None
+    import torch
+    P = ctypes.CDLL(path)
+    P.mnb_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                 ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    buf = torch.zeros(4, dtype=torch.int32, device="cuda")
+    out = {}
+    for key, wg in (("one_workgroup", 1), ("one_per_cu", cus)):
+        sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+
+        def go(i):
+            P.mnb_probe_read(buf.data_ptr(), 16, sink.data_ptr(), wg, 1, stream.cuda_stream)
+        for i in range(100):
+            go(i)
+        out[key] = round(sorted(event_time_us(stream, go, 2000) for _ in range(3))[1], 3)
+    log("[bench] launch floor: %s us" % out)
+    return out
+
+
 def decode_configs(args, stream, cus, passes=5):
     """Every synthetic configuration in its own output type(s), default
     plan, rotated weight copies (the 1024 x 1024 one stays cache-resident):
     microseconds per call as the median and range of `passes` timed passes,
-    algorithmic GB/s, the plan, VGPRs and occupancy, and the committed
+    algorithmic GB/s, the read probe over the same weight copies (and the
+    fraction of it reached), the plan, VGPRs and occupancy, and the committed
     rocprofv3 kernel time and FETCH_SIZE fraction when they were taken on
     the current sources."""
     import block_wise_int4_matmulnbits_amd as mnb
@@ -369,6 +401,9 @@ def decode_configs(args, stream, cus, passes=5):
             if m > 1:
                 flops = 2.0 * m * w.N * w.K
                 e["fp32_valu_floor_us"] = round(flops / (PEAK_FP32_VALU_TFLOPS * 1e12) * 1e6, 3)
+            att = attainable(res, stream, cus)
+            e["attainable"] = att
+            e["frac_of_attainable"] = round(gbs / att["gbs"], 4) if att else None
             prof = measured_profile(name, m, odt)
             if prof is not None:
                 e["rocprof"] = {k: prof[k] for k in ("kernel_mean_us", "fetch_bytes", "write_bytes",
