@@ -472,14 +472,17 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // interleaved A/B, us: m = 2 11.0 -> 10.4, m = 4 11.7 -> 11.3, m = 6
     // 14.8 -> 13.8, m = 8 15.2 -> 14.1; 10240 x 4096 m = 4 10.3 -> 9.5,
     // 12288 x 8192 m = 8 19.8 -> 18.2).  Four columns per tile.
-    // Grid: whole workgroups per CU, about 10 * K/4096 tiles (column quads)
+    // Grid: whole workgroups per CU, about 12 * K/4096 tiles (column quads)
     // each, within one resident generation and at least two tiles each (the
     // tile loop runs in pairs).  Every workgroup stages all of K's
     // activations, so fewer, longer-lived workgroups win until the CUs run
     // short of waves (at one or two rows, two workgroups per CU at least,
-    // below).  On a sweep of 40 shapes (m = 2..8, K = 2048..14336, N =
-    // 4096..151936, bf16): 8.1% faster on average than one resident
-    // generation, 0.35% above the fastest grid on average, 5.0% at most.
+    // below).  On a sweep of 50 shapes (m = 2..8, K = 2048..14336, N =
+    // 4096..151936, bf16): 0.30% above the fastest grid on average, 6.1% at
+    // most (10 * K/4096, fitted on an earlier sweep, gave 0.63% and 8.2% on
+    // this one: 2048 x 28672 at six and eight rows took six workgroups per
+    // CU where five are 8% faster; 14 * K/4096 and above put 4096 x 14336
+    // at three rows on one workgroup per CU, 22% slower).
     // Activations through LDS from three rows up where K or N exceeds 8192
     // (interleaved A/B, same bits, us: down projection m = 3 12.5 -> 11.5,
     // m = 4 13.6 -> 11.9, m = 7 17.5 -> 15.4, m = 8 18.3 -> 15.7; gate_up
@@ -488,14 +491,29 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // slower, and at m = 2, where half of the lanes' own loads read nothing,
     // 0-4% slower.
     if (m >= 2 && nb >= 1 && nb <= 512) {
-        int64_t bpl3 = 1;
+        // Up to four rows, at least two blocks per lane group where that
+        // still leaves two waves: K = 2048 runs two waves of two blocks
+        // instead of four of one (m = 2: 8.2 -> 7.1 us at N = 14336, 11.9 ->
+        // 10.4 at 28672, 40.3 -> 34.8 at 151936, 5.8 -> 5.2 at 8192; m = 4
+        // 8-13% faster from N = 14336 up, 3% slower at 8192).  From five
+        // rows it lost at N = 8192 (m = 8: 7.3 -> 8.2 us), so there the
+        // four waves of one stay.  A function of (m, K), like the rest of
+        // the lane split.
+        int64_t bpl3 = nb >= 64 && m <= 4 ? 2 : 1;
         while (bpl3 < 4 && ceil_div(nb, 16 * bpl3) > 4) bpl3 *= 2;
         int64_t w3 = ceil_div(nb, 16 * bpl3);
         if (w3 > 4) w3 = 8;   // two waves per SIMD; the kernel gives some three blocks per lane group
         const int64_t tiles3 = ceil_div(N, 4);
         const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
-        const double per_wg = 10.0 * (double)K / 4096.0;
+        const double per_wg = 12.0 * (double)K / 4096.0;
         int64_t c3 = (int64_t)std::ceil((double)tiles3 / (double)num_cus / per_wg);
+        // Two-wave workgroups of two blocks: whole multiples of four per CU
+        // (eight waves), about 16 column quads each (K = 2048: four per CU
+        // within 1% of the fastest grid up to N = 28672, eight at 151936,
+        // where four are 4.5% slower; three or six per CU ran 10-15% slower
+        // than four).
+        if (w3 == 2 && bpl3 == 2)
+            c3 = 4 * std::max<int64_t>(1, std::llround((double)tiles3 / ((double)num_cus * 64.0)));
         // One or two rows stage their activations with the lanes' own loads,
         // half of which read nothing: two workgroups per CU at least (4096 x
         // 4096 m = 2 5.72 -> 5.22 us, 8192 x 8192 12.0 -> 11.1).

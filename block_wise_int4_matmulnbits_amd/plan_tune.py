@@ -18,8 +18,9 @@ and takes the cheapest.  This script produces both halves of that:
   python -m block_wise_int4_matmulnbits_amd.plan_tune sweep-grid OUT.json
       (GPU) times the 4x4x4 MFMA decode kernel (2 <= m <= 8) under its
       default lane split with whole workgroups per CU, from half a CU's
-      worth to one resident generation, on a list of decode shapes (bf16,
-      weights rotated over enough copies that none stays in cache).
+      worth to one resident generation (always timed), and the planner's
+      own grid, on a list of decode shapes (bf16, weights rotated over
+      enough copies that none stays in cache).
 
 Cost of a tiling (µs), with R = ceil(tiles / CUs) rounds of tiles over the
 compute units (a tiling that splits K over S workgroups has S times the
@@ -174,7 +175,7 @@ def sweep(out_path):
 
 
 GRID_SHAPES = [(4096, 28672), (4096, 151936), (4096, 6144), (4096, 4096), (14336, 4096), (4096, 14336),
-               (8192, 8192), (2048, 8192)]
+               (8192, 8192), (2048, 8192), (2048, 28672), (2048, 151936)]
 
 
 def sweep_grid(out_path):
@@ -204,10 +205,10 @@ def sweep_grid(out_path):
             occ = mnb.mnb_get_kernel_info(m, K, base)["wgs_per_cu"]
             tiles = -(-N // base.cols_per_tile)
             row = {}
-            for f in (0.5, 1, 1.5, 2, 3, 4, 5, 6, 8):
-                if f > occ:
-                    continue
-                wg = max(1, min(-(-tiles // 2), int(f * cus)))
+            grids = {max(1, min(-(-tiles // 2), int(f * cus))) for f in (0.5, 1, 1.5, 2, 3, 4, 5, 6, 8) if f <= occ}
+            grids.add(base.workgroups)   # the planner's own pick is always timed,
+            grids.add(max(1, min(-(-tiles // 2), occ * cus)))   # and one resident generation
+            for wg in sorted(grids):
                 p = mnb.mnb_plan(**dict(base.as_dict(), workgroups=wg))
                 assert mnb.mnb_plan_check(m, K, N, p) == 0
 

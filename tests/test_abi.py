@@ -270,12 +270,17 @@ def test_default_plan_shapes():
     # Two or more rows: the 4x4x4 MFMA kernel, eight waves for the 14336-long
     # K (four of four blocks per lane group and four of three), four waves of
     # two for 4096; four columns per tile; whole workgroups per CU, about
-    # 10 * K/4096 tiles each within one resident generation (the grids
+    # 12 * K/4096 tiles each within one resident generation (the grids
     # measured fastest or within 7% of it).
     for m, K, N, occ, shape in ((2, 14336, 4096, 1, (8, 4, 4, 256)), (8, 14336, 4096, 1, (8, 4, 4, 256)),
                                 (4, 4096, 28672, 4, (4, 2, 4, 768)), (8, 4096, 151936, 4, (4, 2, 4, 1024)),
                                 (8, 4096, 6144, 4, (4, 2, 4, 256)), (4, 8192, 8192, 3, (4, 4, 4, 256)),
-                                (4, 4096, 14336, 4, (4, 2, 4, 512))):
+                                (4, 4096, 14336, 4, (4, 2, 4, 512)),
+                                # K = 2048: two waves of two blocks up to four rows, in
+                                # multiples of four workgroups per CU; four waves of one
+                                # from five rows
+                                (2, 2048, 28672, 10, (2, 2, 4, 1024)), (4, 2048, 151936, 10, (2, 2, 4, 2048)),
+                                (3, 2048, 8192, 10, (2, 2, 4, 1024)), (8, 2048, 28672, 7, (4, 1, 4, 1280))):
         p = mnb.mnb_plan_default(m, K, N, 256, occ)
         assert p.engine == 3
         assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape

@@ -365,6 +365,19 @@ def test_mfma4_engine_shapes(oracle_mod):
             assert_parity(oracle_mod, d, m, "mfma4", plan)
 
 
+def test_mfma4_default_split_at_k2048(oracle_mod):
+    """K = 2048: the default plan runs two waves of two blocks per lane
+    group for two to four rows and four waves of one from five rows up;
+    both against the oracle, on full and ragged column counts."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for i, (m, N) in enumerate(((2, 8192), (3, 4099), (4, 28672), (5, 1031), (8, 8192))):
+        p = mnb.plan_for_device(m, 2048, N, cus)
+        want = (2, 2) if m <= 4 else (4, 1)
+        assert (p.engine, p.waves_per_wg, p.blocks_per_lane) == (3,) + want, (m, N, p.as_dict())
+        d = W.generate(m, 2048, N, W.BF16, i % 2 == 0, 0.001, 0.01, 0.5, 470 + i)
+        assert_parity(oracle_mod, d, m, "mfma4 default K=2048")
+
+
 @pytest.mark.parametrize("via_lds", [0, 1])
 def test_mfma4_engine_rows_and_columns_match(via_lds):
     """Under one 4x4x4 MFMA plan, row r of an m-row launch is bit-identical

@@ -95,7 +95,7 @@ def test_split_plans_stay_within_the_workspace_bound():
 
 def test_decode_grid_near_the_measured_fastest():
     """The grid mnb_plan_default gives the 4x4x4 MFMA kernel (whole
-    workgroups per CU, about 10 * K/4096 column quads each, within one
+    workgroups per CU, about 12 * K/4096 column quads each, within one
     resident generation) on every measured shape: within 8% of the fastest
     measured grid, 2% on average, and faster on average than one resident
     generation (the rule it replaced)."""
