@@ -514,6 +514,12 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // than four).
         if (w3 == 2 && bpl3 == 2)
             c3 = 4 * std::max<int64_t>(1, std::llround((double)tiles3 / ((double)num_cus * 64.0)));
+        // With twelve or more column quads per CU, at least two workgroups
+        // per CU: one workgroup of three or four waves leaves the CU short
+        // of waves (5120 x 14336, m = 4 / 6 / 8: 16.1 / 19.1 / 19.2 -> 14.1
+        // / 17.4 / 17.8 us; 6144 x 14336 16.8 / 20.2 / 20.3 -> 15.2 / 19.4 /
+        // 19.8; 8192 x 14336 m = 4 18.4 -> 18.2, m = 6 and 8 1% slower).
+        if (tiles3 >= 12 * num_cus && c3 < 2) c3 = 2;
         // One or two rows stage their activations with the lanes' own loads,
         // half of which read nothing: two workgroups per CU at least (4096 x
         // 4096 m = 2 5.72 -> 5.22 us, 8192 x 8192 12.0 -> 11.1).

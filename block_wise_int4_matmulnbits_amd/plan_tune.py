@@ -175,7 +175,7 @@ def sweep(out_path):
 
 
 GRID_SHAPES = [(4096, 28672), (4096, 151936), (4096, 6144), (4096, 4096), (14336, 4096), (4096, 14336),
-               (8192, 8192), (2048, 8192), (2048, 28672), (2048, 151936)]
+               (8192, 8192), (2048, 8192), (2048, 28672), (2048, 151936), (5120, 14336), (6144, 14336)]
 
 
 def sweep_grid(out_path):
