@@ -501,8 +501,14 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         // the lane split.
         int64_t bpl3 = nb >= 64 && m <= 4 ? 2 : 1;
         while (bpl3 < 4 && ceil_div(nb, 16 * bpl3) > 4) bpl3 *= 2;
+        // Three waves of four blocks (4096 < K <= 6144) leave one SIMD of
+        // each workgroup idle: five or six waves of two instead (5120 x
+        // 4096 m = 4 / 6 / 8 7.4 / 9.4 / 9.9 -> 7.0 / 8.4 / 9.3 us; 6144 x
+        // 4096 m = 2 / 8 7.6 / 10.5 -> 7.0 / 9.8, 6144 x 14336 m = 6 / 8
+        // 19.4 / 19.8 -> 18.4 / 18.5; at 28672 columns 0.5-2.6% slower).
+        if (bpl3 == 4 && ceil_div(nb, 64) == 3) bpl3 = 2;
         int64_t w3 = ceil_div(nb, 16 * bpl3);
-        if (w3 > 4) w3 = 8;   // two waves per SIMD; the kernel gives some three blocks per lane group
+        if (w3 > 4 && bpl3 == 4) w3 = 8;   // two waves per SIMD; the kernel gives some three blocks per lane group
         const int64_t tiles3 = ceil_div(N, 4);
         const int64_t per_cu3 = wgs_per_cu > 0 ? wgs_per_cu : (w3 >= 4 ? 2 : 4);
         const double per_wg = 12.0 * (double)K / 4096.0;
@@ -515,11 +521,13 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
         if (w3 == 2 && bpl3 == 2)
             c3 = 4 * std::max<int64_t>(1, std::llround((double)tiles3 / ((double)num_cus * 64.0)));
         // With twelve or more column quads per CU, at least two workgroups
-        // per CU: one workgroup of three or four waves leaves the CU short
-        // of waves (5120 x 14336, m = 4 / 6 / 8: 16.1 / 19.1 / 19.2 -> 14.1
-        // / 17.4 / 17.8 us; 6144 x 14336 16.8 / 20.2 / 20.3 -> 15.2 / 19.4 /
-        // 19.8; 8192 x 14336 m = 4 18.4 -> 18.2, m = 6 and 8 1% slower).
-        if (tiles3 >= 12 * num_cus && c3 < 2) c3 = 2;
+        // per CU where one would leave the CU fewer than six waves (three
+        // waves of four blocks at 5120 and 6144 x 14336, m = 4 / 6 / 8: 16.1
+        // / 19.1 / 19.2 -> 14.1 / 17.4 / 17.8 us and 16.8 / 20.2 / 20.3 ->
+        // 15.2 / 19.4 / 19.8; four waves at 8192 x 14336 m = 4 18.4 -> 18.2,
+        // m = 6 and 8 1% slower; six waves of two at 6144 x 14336 ran 1-7%
+        // faster at one per CU).
+        if (tiles3 >= 12 * num_cus && c3 < 2 && w3 < 6) c3 = 2;
         // One or two rows stage their activations with the lanes' own loads,
         // half of which read nothing: two workgroups per CU at least (4096 x
         // 4096 m = 2 5.72 -> 5.22 us, 8192 x 8192 12.0 -> 11.1).

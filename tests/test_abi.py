@@ -280,7 +280,9 @@ def test_default_plan_shapes():
                                 # multiples of four workgroups per CU; four waves of one
                                 # from five rows
                                 (2, 2048, 28672, 10, (2, 2, 4, 1024)), (4, 2048, 151936, 10, (2, 2, 4, 2048)),
-                                (3, 2048, 8192, 10, (2, 2, 4, 1024)), (8, 2048, 28672, 7, (4, 1, 4, 1280))):
+                                (3, 2048, 8192, 10, (2, 2, 4, 1024)), (8, 2048, 28672, 7, (4, 1, 4, 1280)),
+                                # K = 5120 and 6144: five and six waves of two blocks
+                                (4, 5120, 4096, 3, (5, 2, 4, 256)), (8, 6144, 14336, 2, (6, 2, 4, 256))):
         p = mnb.mnb_plan_default(m, K, N, 256, occ)
         assert p.engine == 3
         assert (p.waves_per_wg, p.blocks_per_lane, p.cols_per_tile, p.workgroups) == shape

@@ -365,17 +365,21 @@ def test_mfma4_engine_shapes(oracle_mod):
             assert_parity(oracle_mod, d, m, "mfma4", plan)
 
 
-def test_mfma4_default_split_at_k2048(oracle_mod):
-    """K = 2048: the default plan runs two waves of two blocks per lane
-    group for two to four rows and four waves of one from five rows up;
-    both against the oracle, on full and ragged column counts."""
+def test_mfma4_default_splits(oracle_mod):
+    """The default lane splits that are not the fewest blocks per lane group
+    covering K on four waves: K = 2048 runs two waves of two blocks for two
+    to four rows (four waves of one from five rows up), and K = 5120 and
+    6144 five and six waves of two (not three of four); each against the
+    oracle, on full and ragged column counts."""
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    for i, (m, N) in enumerate(((2, 8192), (3, 4099), (4, 28672), (5, 1031), (8, 8192))):
-        p = mnb.plan_for_device(m, 2048, N, cus)
-        want = (2, 2) if m <= 4 else (4, 1)
-        assert (p.engine, p.waves_per_wg, p.blocks_per_lane) == (3,) + want, (m, N, p.as_dict())
-        d = W.generate(m, 2048, N, W.BF16, i % 2 == 0, 0.001, 0.01, 0.5, 470 + i)
-        assert_parity(oracle_mod, d, m, "mfma4 default K=2048")
+    cases = [(2, 2048, 8192, (2, 2)), (3, 2048, 4099, (2, 2)), (4, 2048, 28672, (2, 2)), (5, 2048, 1031, (4, 1)),
+             (8, 2048, 8192, (4, 1)), (2, 5120, 4099, (5, 2)), (8, 5120, 14336, (5, 2)), (4, 6144, 1031, (6, 2)),
+             (6, 6144, 4096, (6, 2))]
+    for i, (m, K, N, want) in enumerate(cases):
+        p = mnb.plan_for_device(m, K, N, cus)
+        assert (p.engine, p.waves_per_wg, p.blocks_per_lane) == (3,) + want, (m, K, N, p.as_dict())
+        d = W.generate(m, K, N, W.BF16, i % 2 == 0, 0.001, 0.01, 0.5, 470 + i)
+        assert_parity(oracle_mod, d, m, "mfma4 default split")
 
 
 @pytest.mark.parametrize("via_lds", [0, 1])
