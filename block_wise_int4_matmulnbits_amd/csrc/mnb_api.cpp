@@ -465,7 +465,8 @@ int mnb_plan_default(int64_t m, int64_t K, int64_t N, int num_cus, int wgs_per_c
     // lm_head m = 2 82.9 -> 69.7 us, m = 8 104 -> 90.6; gate_up m = 8 70.4 ->
     // 26.9, m = 3 25.4 -> 20.0; down m = 8 26.1 -> 18.5, m = 3 15.6 -> 12.9;
     // the 6144-column shape gains at m = 8 and loses up to 1 us at m <= 3).
-    // Lane split, a function of K only: the fewest blocks per lane group that
+    // Lane split, a function of (m, K) only (the exceptions below): the
+    // fewest blocks per lane group that
     // cover K with at most four waves, else eight waves, of which the kernel
     // gives the fewest that need them four blocks per lane group and the
     // rest three (K = 14336: four of each, against seven waves of four,
